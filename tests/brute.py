@@ -1,0 +1,97 @@
+"""A brute-force encoder in pure Python loops, for tiny inputs only.
+
+Written independently of the vectorised oracle (scalar loops over explicit
+indices, the math module only) so that an indexing, transposition or
+dropped-term mistake in either one shows up as a mismatch.  Used by the
+oracle's pin tests; never by the HIP path.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _embed(dims, w, frames):
+    B, T, H, W, _ = frames.shape
+    kt, p, D = dims["tubelet"], dims["patch"], dims["dim"]
+    Tt, Hp, Wp = T // kt, H // p, W // p
+    Wpe, bpe, pos = w["enc.patch_embed.weight"], w["enc.patch_embed.bias"], w["enc.pos_embed"]
+    out = []
+    for b in range(B):
+        toks = []
+        if dims["has_cls"]:
+            toks.append([float(w["enc.cls_token"][d]) for d in range(D)])
+        for tt in range(Tt):
+            for i in range(Hp):
+                for j in range(Wp):
+                    v = []
+                    for dt in range(kt):
+                        for dy in range(p):
+                            for dx in range(p):
+                                for c in range(3):
+                                    u = int(frames[b, tt * kt + dt, i * p + dy, j * p + dx, c])
+                                    v.append((u / 255.0 - dims["mean"][c]) / dims["std"][c])
+                    toks.append([float(bpe[d]) + sum(float(Wpe[d, k]) * v[k] for k in range(len(v)))
+                                 for d in range(D)])
+        out.append([[toks[n][d] + float(pos[n, d]) for d in range(D)] for n in range(len(toks))])
+    return out
+
+
+def _ln(row, g, bta, eps):
+    D = len(row)
+    mu = sum(row) / D
+    var = sum((r - mu) ** 2 for r in row) / D
+    return [(row[d] - mu) / math.sqrt(var + eps) * float(g[d]) + float(bta[d]) for d in range(D)]
+
+
+def _lin(row, W, bias):
+    return [float(bias[o]) + sum(float(W[o, i]) * row[i] for i in range(len(row)))
+            for o in range(W.shape[0])]
+
+
+def _may_attend(dims, i, j):
+    if dims["mask"] == "bidir":
+        return True
+    per_slot = (dims["img_h"] // dims["patch"]) * (dims["img_w"] // dims["patch"])
+    c = int(dims["has_cls"])
+    if c and i == 0:
+        return True            # CLS sees every token
+    if c and j == 0:
+        return False           # no patch token sees CLS
+    return (j - c) // per_slot <= (i - c) // per_slot
+
+
+def encode(dims, w, frames):
+    """frames uint8 [B, T, H, W, 3] -> list [B][N][D] of floats."""
+    D, H = dims["dim"], dims["heads"]
+    dh = D // H
+    eps = dims["ln_eps"]
+    X = _embed(dims, w, frames)
+    for li in range(dims["depth"]):
+        p = f"enc.blk.{li}."
+        for b in range(len(X)):
+            x = X[b]
+            N = len(x)
+            qkv = [_lin(_ln(x[n], w[p + "ln1.weight"], w[p + "ln1.bias"], eps),
+                        w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"]) for n in range(N)]
+            o = [[0.0] * D for _ in range(N)]
+            for a in range(H):
+                for i in range(N):
+                    js = [j for j in range(N) if _may_attend(dims, i, j)]
+                    s = [sum(qkv[i][a * dh + t] * qkv[j][D + a * dh + t] for t in range(dh))
+                         / math.sqrt(dh) for j in js]
+                    m = max(s)
+                    e = [math.exp(v - m) for v in s]
+                    z = sum(e)
+                    for t in range(dh):
+                        o[i][a * dh + t] = sum(e[q] / z * qkv[js[q]][2 * D + a * dh + t]
+                                               for q in range(len(js)))
+            att = [_lin(o[n], w[p + "attn_out.weight"], w[p + "attn_out.bias"]) for n in range(N)]
+            x = [[x[n][d] + att[n][d] for d in range(D)] for n in range(N)]
+            mlp = []
+            for n in range(N):
+                h = _lin(_ln(x[n], w[p + "ln2.weight"], w[p + "ln2.bias"], eps),
+                         w[p + "ffn_up.weight"], w[p + "ffn_up.bias"])
+                h = [0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))) for z in h]
+                mlp.append(_lin(h, w[p + "ffn_down.weight"], w[p + "ffn_down.bias"]))
+            X[b] = [[x[n][d] + mlp[n][d] for d in range(D)] for n in range(N)]
+    return [[_ln(r, w["enc.norm.weight"], w["enc.norm.bias"], eps) for r in xb] for xb in X]
