@@ -1,0 +1,240 @@
+"""Throughput of the JEPA ViT encoder forward on one MI355X.
+
+One step = one whole forward of a batch (patchify + patch-embed + every block +
+final LayerNorm) plus the pool the workload reports, with frames already
+resident in HBM.  Default workload: the LeVJEPA-style ViT-L/16 video encoder,
+16 frames of 224x224, tubelet 1, block-causal, bf16, batch 4 (3137 tokens per
+clip), synthetic seeded frames and N(0, 0.02) weights.
+
+Prints one JSON line: tokens/s (whole job), clips/s, MFMA utilisation of the
+whole forward against the dense bf16/f16 peak, the roofline of the dominant
+kernel (algorithmic work per launch / its HIP-event-timed average duration
+inside the timed region), and the CPU oracle timed on a bounded sample.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--breakdown]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from vision_transformer_amd import synth  # noqa: E402
+
+METRIC = "encoder tokens/sec + clips/sec (ViT-L/16, 16 frames), MFMA util % of peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def attention_pairs(dims: dict) -> int:
+    """Allowed (query, key) pairs of one item."""
+    N = synth.n_tokens(dims)
+    if dims["mask"] == "bidir":
+        return N * N
+    T, h, w = synth.grid(dims)
+    per = h * w
+    pairs = per * per * T * (T + 1) // 2
+    return pairs + (N if dims["has_cls"] else 0)
+
+
+def class_flops(dims: dict, B: int) -> dict:
+    """Algorithmic FLOPs of one launch of each kernel class."""
+    D, F = dims["dim"], dims["mlp_dim"]
+    M = B * synth.n_tokens(dims)
+    return {
+        "gemm_patch": 2 * B * synth.n_patches(dims) * synth.patch_dim(dims) * D,
+        "gemm_qkv": 2 * M * 3 * D * D,
+        "gemm_out": 2 * M * D * D,
+        "gemm_fc1": 2 * M * F * D,
+        "gemm_fc2": 2 * M * D * F,
+        "attention": 4 * B * attention_pairs(dims) * D,
+    }
+
+
+def forward_flops(dims: dict, B: int) -> int:
+    f = class_flops(dims, B)
+    per_layer = f["gemm_qkv"] + f["gemm_out"] + f["gemm_fc1"] + f["gemm_fc2"] + f["attention"]
+    return f["gemm_patch"] + dims["depth"] * per_layer
+
+
+def class_bytes(dims: dict, B: int) -> dict:
+    """Algorithmic HBM bytes of one launch of the bandwidth-bound classes."""
+    D = dims["dim"]
+    M = B * synth.n_tokens(dims)
+    es = 4 if dims["act_dtype"] == "f32" else 2
+    return {"layernorm": M * D * (4 + es), "final_ln": M * D * 8}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(dims: dict, stored: list, frames: np.ndarray, sample_blocks: int) -> dict:
+    from oracle import encoder as E
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    ds = dict(dims, depth=sample_blocks)
+    names = {n for n, _, _ in synth.tensor_specs(ds)}
+    w = E.weights_f64([t for t in stored if t["name"] in names])
+    clip = frames[:1]
+    load0 = os.getloadavg()[0]
+    t0 = time.perf_counter()
+    E.encode(ds, w, clip)
+    dt = time.perf_counter() - t0
+    per_clip = dt * dims["depth"] / sample_blocks
+    N = synth.n_tokens(dims)
+    return {"value": N / per_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 clip, {sample_blocks} of {dims['depth']} blocks (float64 numpy oracle), "
+                      f"{dt:.1f} s, scaled x{dims['depth'] / sample_blocks:g} to a whole clip",
+            "clips_per_s": 1.0 / per_clip, "load_avg_1min_before": load0,
+            "load_avg_1min_after": os.getloadavg()[0]}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="levjepa_vit_l16_16f_bf16_b4",
+                    choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=2)
+    ap.add_argument("--breakdown", action="store_true", help="print per-kernel-class times to stderr")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the encoder path is built and measured on a single "
+              "MI355X (multi-GPU data/sequence parallelism is design-only here). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from vision_transformer_amd import _lib
+    from vision_transformer_amd.encoder import Encoder
+
+    wl = synth.workload(args.workload)
+    dims = wl["dims"]
+    B = args.batch or wl["batch"]
+    N = synth.n_tokens(dims)
+    act = dims["act_dtype"]
+    print(f"[bench] workload {args.workload}: B={B} N={N} D={dims['dim']} L={dims['depth']} "
+          f"{dims['mask']} act={act} weights={dims['mat_dtype']}", file=sys.stderr, flush=True)
+
+    frames = synth.make_frames(dims, B, wl["frame_seed"])
+    stored = synth.stored_weights(dims, synth.make_f32_weights(dims, wl["weight_seed"]),
+                                  quantize=_lib.jepa_quantize)
+    enc = Encoder(dims, stored)
+    fr = torch.from_numpy(frames).cuda()
+    tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, device="cuda")
+    pool_mode = "cls" if dims["has_cls"] else "mean"
+    pooled = torch.empty((B, dims["dim"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        enc.encode(fr, tokens)
+        enc.pool(pool_mode, B, pooled)
+
+    # a short profiled pass (not timed) finds the dominant kernel class
+    classes = list(_lib.jepa_kernel_stats(enc.ctx).keys())
+    _lib.jepa_set_profiling(enc.ctx, 0xFFFFFFFF)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    _lib.jepa_reset_kernel_stats(enc.ctx)
+    step()
+    torch.cuda.synchronize()
+    prof = _lib.jepa_kernel_stats(enc.ctx)
+    dominant = max(prof, key=lambda k: prof[k]["total_ms"])
+    if args.breakdown:
+        tot = sum(v["total_ms"] for v in prof.values())
+        for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["total_ms"]):
+            if v["launches"]:
+                print(f"[bench]   {k:12s} {v['launches']:4d} launches {v['total_ms']:8.3f} ms "
+                      f"({100 * v['total_ms'] / tot:5.1f} %)", file=sys.stderr)
+    print(f"[bench] dominant kernel class: {dominant}", file=sys.stderr, flush=True)
+
+    # the timed region: events only around the dominant class's launches
+    _lib.jepa_reset_kernel_stats(enc.ctx)
+    _lib.jepa_set_profiling(enc.ctx, 1 << classes.index(dominant))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.jepa_reset_kernel_stats(enc.ctx)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    st = _lib.jepa_kernel_stats(enc.ctx)[dominant]
+    _lib.jepa_set_profiling(enc.ctx, 0)
+
+    ms_per_step = 1e3 * wall / args.steps
+    tok_s = B * N * args.steps / wall
+    flops = forward_flops(dims, B)
+    peak = PEAK_TFLOPS[act]
+    util = flops / (ms_per_step * 1e-3) / (peak * 1e12)
+
+    avg_ms = st["total_ms"] / max(1, st["launches"])
+    cf, cb = class_flops(dims, B), class_bytes(dims, B)
+    if dominant in cf:
+        achieved = cf[dominant] / (avg_ms * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "work_per_launch": cf[dominant], "avg_launch_ms": round(avg_ms, 5),
+                "launches_timed": st["launches"]}
+    else:
+        achieved = cb[dominant] / (avg_ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "work_per_launch": cb[dominant], "avg_launch_ms": round(avg_ms, 5),
+                "launches_timed": st["launches"]}
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": act, "data": "synthetic (seeded uint8 frames, N(0,0.02) weights)",
+        "config": {"workload": args.workload, "batch": B, "tokens_per_clip": N,
+                   "frames": dims["frames"], "img": [dims["img_h"], dims["img_w"]],
+                   "tubelet": dims["tubelet"], "mask": dims["mask"], "weights": dims["mat_dtype"],
+                   "parallelism": "single GPU"},
+        "clips_per_s": round(B * args.steps / wall, 2),
+        "mfma_util_pct": round(100 * util, 2),
+        "forward_tflop": round(flops / 1e12, 4),
+        "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "roofline": roof,
+    }
+    enc.close()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(dims, stored, frames, args.cpu_sample_blocks)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

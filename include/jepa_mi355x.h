@@ -1,0 +1,188 @@
+/*
+ * jepa_mi355x.h -- C ABI of the MI355X (gfx950) JEPA ViT encoder forward pass.
+ *
+ * The operation: a clip of uint8 frames is normalised, cut into tubelet
+ * patches, embedded, run through pre-LN transformer blocks with bidirectional
+ * or block-causal multi-head attention, final-LayerNorm'ed into a token map,
+ * and optionally pooled (CLS or mean).
+ *   - LeVJEPA ViT-L/16 (VideoMix) model card, opening paragraph: tubelet 1,
+ *     block-causal mask (bidirectional inside a frame, causal across frames,
+ *     CLS read-only), the CLS token as the feature; "Run it": the pooling
+ *     modes and the single C header.
+ *   - V-JEPA 2 ViT-L/16 SSv2 card, opening paragraph: tubelet 2.
+ *   - jepa.cpp Quantization page, "The rule": the tensor names and which
+ *     tensors may be stored as q8_0 / q4_0 blocks; "File sizes": 8.5 / 4.5
+ *     bits per weight.
+ *   - jepa.cpp benchmarks page, "What the milliseconds are": the per-call
+ *     compute time and the resident model bytes the API reports.
+ *
+ * Conventions shared by every call:
+ *   - No call aborts, exits or throws.  Each returns a jepa_status; on a
+ *     negative status jepa_last_error() names the field or tensor at fault.
+ *     Arguments are validated before anything is enqueued.
+ *   - Device work is enqueued on the caller's HIP stream (a hipStream_t
+ *     passed as void*; NULL means the default stream) and the call returns
+ *     after enqueueing, except where noted.  Outputs are valid once the
+ *     caller synchronises that stream.  Device faults surface there.
+ *   - One context must not be used from two threads at once.
+ *   - The library needs a gfx950 device; it has no CPU fallback.
+ */
+#ifndef JEPA_MI355X_H
+#define JEPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct jepa_ctx jepa_ctx;
+
+typedef enum {
+    JEPA_OK = 0,
+    JEPA_E_INVALID_ARG = -1,     /* null pointer, bad enum, batch <= 0 */
+    JEPA_E_SHAPE = -2,           /* inconsistent dims or tensor shape */
+    JEPA_E_DTYPE = -3,           /* dtype not allowed for this tensor */
+    JEPA_E_MISSING_TENSOR = -4,  /* a required tensor is absent */
+    JEPA_E_OOM = -5,             /* device allocation failed or over the cap */
+    JEPA_E_HIP = -6,             /* a HIP runtime call or launch failed */
+    JEPA_E_UNSUPPORTED = -7,     /* valid but outside what this build runs */
+    JEPA_E_STATE = -8            /* e.g. pool before any encode */
+} jepa_status;
+
+/* Storage dtypes.  Q8_0: blocks of 32 weights along a row, each an f16
+ * scale d then 32 int8 codes (34 bytes), weight = d * q.  Q4_0: blocks of
+ * 32, an f16 scale d then 16 bytes whose byte j holds code j in the low
+ * nibble and code j + 16 in the high nibble (18 bytes), weight = d*(q-8). */
+typedef enum { JEPA_F32 = 0, JEPA_F16 = 1, JEPA_BF16 = 2, JEPA_Q8_0 = 3, JEPA_Q4_0 = 4 } jepa_dtype;
+
+typedef enum { JEPA_MASK_BIDIR = 0, JEPA_MASK_BLOCK_CAUSAL = 1 } jepa_mask;
+
+typedef enum { JEPA_POOL_NONE = 0, JEPA_POOL_CLS = 1, JEPA_POOL_MEAN = 2 } jepa_pool_mode;
+
+/* Model dimensions.  head_dim = dim / heads must be 64; dim and mlp_dim
+ * must be multiples of 64; img_h, img_w divisible by patch; frames divisible
+ * by tubelet.  Tokens per item: N = (frames/tubelet)*(img_h/patch)*(img_w/patch)
+ * + has_cls.  Pixels are normalised as (u/255 - mean[c]) / std[c].
+ * act_dtype (F32, F16 or BF16) is the precision of the GEMM and attention
+ * operands; accumulation, the residual stream, LayerNorm statistics and
+ * softmax are f32 throughout.  Under JEPA_MASK_BLOCK_CAUSAL a patch token of
+ * temporal slot t attends to the patch tokens of slots <= t and not to CLS;
+ * CLS attends to every token. */
+typedef struct {
+    int32_t dim, depth, heads, mlp_dim;
+    int32_t patch, tubelet, img_h, img_w, frames;
+    int32_t has_cls;    /* 1: token 0 of each item is a learned CLS token */
+    int32_t mask;       /* jepa_mask */
+    int32_t act_dtype;  /* jepa_dtype: JEPA_F32, JEPA_F16 or JEPA_BF16 */
+    float ln_eps;
+    float mean[3];
+    float std[3];
+} jepa_dims;
+
+/* One stored tensor, host memory.  ne0 = row length (in-features), ne1 =
+ * rows (out-features; 1 for vectors).  nbytes must equal the storage size
+ * of ne0*ne1 elements of dtype.  Names and shapes (D = dim, F = mlp_dim,
+ * P = tubelet*patch*patch*3, N = tokens per item):
+ *   enc.patch_embed.weight [ne0 P, ne1 D]   enc.patch_embed.bias [D]
+ *   enc.cls_token [D] (only if has_cls)     enc.pos_embed [ne0 D, ne1 N]
+ *   enc.blk.{i}.ln1.weight/.bias [D]        enc.blk.{i}.ln2.weight/.bias [D]
+ *   enc.blk.{i}.attn_qkv.weight [D, 3D] .bias [3D]   (columns [q | k | v],
+ *       head a owns features a*64..a*64+63 of each third)
+ *   enc.blk.{i}.attn_out.weight [D, D] .bias [D]
+ *   enc.blk.{i}.ffn_up.weight [D, F] .bias [F]
+ *   enc.blk.{i}.ffn_down.weight [F, D] .bias [D]
+ *   enc.norm.weight/.bias [D]
+ * A patch vector lists (dt, dy, dx, c) with c fastest; tokens are ordered
+ * slot-major then raster; CLS is token 0 and owns pos row 0.
+ * Only the four attn_qkv/attn_out/ffn_up/ffn_down weights may be Q8_0/Q4_0
+ * (ne0 % 32 == 0); the rest are F32, F16 or BF16. */
+typedef struct {
+    const char *name;
+    int32_t dtype;      /* jepa_dtype */
+    int64_t ne0;
+    int64_t ne1;
+    const void *data;   /* host pointer */
+    size_t nbytes;
+} jepa_tensor;
+
+/* Per-kernel-class timing record (see jepa_set_profiling). */
+typedef struct {
+    const char *name;   /* static string owned by the library */
+    int64_t launches;
+    double total_ms;
+} jepa_kernel_stat;
+
+/* Validate dims and tensors, allocate device memory on the current device,
+ * copy every tensor there (the caller may free its buffers on return) and
+ * return a context in *out.  Blocks until the copies are done.  Every name
+ * in the schema above must be present exactly once; unknown names are an
+ * error (JEPA_E_INVALID_ARG). */
+jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n_tensors,
+                        jepa_ctx **out);
+
+/* Encode a batch.  frames: uint8 [batch, frames, img_h, img_w, 3], HWC,
+ * contiguous; device memory if frames_on_device, else host memory (copied
+ * synchronously before the launches).  tokens_out: device f32
+ * [batch, N, dim] that receives the final-LayerNorm token map, or NULL to
+ * keep it in a context-owned buffer.  The token map stays readable by
+ * jepa_pool until the next encode on this context. */
+jepa_status jepa_encode(jepa_ctx *ctx, const uint8_t *frames, int batch, int frames_on_device,
+                        float *tokens_out, void *hip_stream);
+
+/* Pool the token map of the last encode.  out: device f32 [batch, dim] for
+ * CLS (token 0; needs has_cls) and MEAN (mean of the patch tokens, CLS
+ * excluded), [batch, N, dim] for NONE (a copy of the token map).
+ * JEPA_E_STATE if nothing was encoded yet. */
+jepa_status jepa_pool(jepa_ctx *ctx, int mode, float *out, void *hip_stream);
+
+/* Release everything the context owns.  NULL is ignored. */
+void jepa_free(jepa_ctx *ctx);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *jepa_last_error(void);
+
+/* Device milliseconds between the start and the end of the last encode
+ * (HIP events on the encode's stream); waits for that encode to finish.
+ * Negative if there was none. */
+float jepa_last_compute_ms(jepa_ctx *ctx);
+
+/* Bytes of tensor data as stored (the size the weight file's tensors would
+ * take: blocks for Q8_0/Q4_0, 2 or 4 bytes per element otherwise). */
+size_t jepa_model_n_bytes(const jepa_ctx *ctx);
+
+/* Bytes of device memory the context holds for weights. */
+size_t jepa_device_weight_bytes(const jepa_ctx *ctx);
+
+/* Bytes of device workspace an encode of `batch` items needs. */
+size_t jepa_workspace_bytes(const jepa_ctx *ctx, int batch);
+
+/* Write the f32 value of every element of the named tensor, as the GEMMs
+ * see it before rounding to act_dtype, into device memory out_dev
+ * ([ne1, ne0] row-major).  For Q8_0/Q4_0 this is f32(d) * code, exact. */
+jepa_status jepa_dequant_tensor(jepa_ctx *ctx, const char *name, float *out_dev, void *hip_stream);
+
+/* Host quantizer: f32 [rows, cols] -> Q8_0 or Q4_0 blocks [rows, cols/32]
+ * (dst holds rows*cols/32*34 or *18 bytes).  Scale d computed in f32 and
+ * stored as f16 (round to nearest even); Q8_0: d = max|x|/127, codes
+ * round-half-away(x * (1/d)); Q4_0: d = m / -8 with m the first element of
+ * largest magnitude, codes min(15, floor(x * (1/d) + 8.5)); zero blocks get
+ * d = 0.  cols % 32 == 0. */
+jepa_status jepa_quantize(int dtype, const float *src, int64_t rows, int64_t cols, uint8_t *dst);
+
+/* Kernel timing: every launch whose class bit is set in class_mask (bit i
+ * = record i of jepa_kernel_stats; 0 = off, 0xffffffff = all) is bracketed
+ * by HIP events on its stream.  jepa_kernel_stats waits for the recorded
+ * launches, adds them into per-class totals and copies up to `cap` records
+ * into out; it returns the number of classes (or a negative status).
+ * jepa_reset_kernel_stats clears the totals. */
+jepa_status jepa_set_profiling(jepa_ctx *ctx, uint32_t class_mask);
+int jepa_kernel_stats(jepa_ctx *ctx, jepa_kernel_stat *out, int cap);
+void jepa_reset_kernel_stats(jepa_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JEPA_MI355X_H */

@@ -1,0 +1,70 @@
+/*
+ * jepa_mi355x_ops.h -- the encoder's individual kernels, on caller-owned
+ * device buffers.  The same kernels jepa_encode launches, exposed one by one
+ * for kernel-level tests and measurements.  Conventions as in jepa_mi355x.h:
+ * a jepa_status return, arguments validated before anything is enqueued,
+ * work enqueued on the given HIP stream (NULL = default stream).
+ */
+#ifndef JEPA_MI355X_OPS_H
+#define JEPA_MI355X_OPS_H
+
+#include "jepa_mi355x.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JEPA_EPI_STORE = 0,   /* out[m, n] = act(acc + bias[n]) */
+    JEPA_EPI_GELU = 1,    /* out[m, n] = act(gelu_erf(acc + bias[n])) */
+    JEPA_EPI_RESID = 2    /* out[m, n] += acc + bias[n], out f32 */
+} jepa_epilogue;
+
+/* Pixel ingest (pages: a seeded uint8 stream through the model's own
+ * normalisation -- benchmarks page, "Box and build"; tubelet tokens -- V-JEPA 2
+ * card, opening paragraph).  frames uint8 [batch, frames, img_h, img_w, 3]
+ * -> out act [batch*Np, ld], row = slot-major raster token, columns
+ * (dt, dy, dx, c) with c fastest, value (u/255 - mean[c])/std[c]; columns
+ * P..ld-1 zero.  ld >= P. */
+jepa_status jepa_op_patchify(int act_dtype, const uint8_t *frames, int batch, int frames_per_item,
+                             int img_h, int img_w, int tubelet, int patch, const float mean[3],
+                             const float std[3], void *out, int64_t ld, void *hip_stream);
+
+/* LayerNorm (pre-LN blocks and the final norm; the Quantization page names
+ * ln1 / ln2 / norm): y = (x - mean)/sqrt(var + eps)*gamma + beta per row,
+ * biased variance.  x, gamma, beta f32 device; y dtype y_dtype (F32, F16,
+ * BF16), [rows, dim]. */
+jepa_status jepa_op_layernorm(const float *x, int64_t rows, int dim, const float *gamma,
+                              const float *beta, float eps, void *y, int y_dtype, void *hip_stream);
+
+/* Linear layer (attn_qkv / attn_out / ffn_up / ffn_down, Quantization page
+ * "The rule"): acc = a[M, K] * w[N, K]^T in f32, then the epilogue.  a is
+ * act_dtype; w is act_dtype (dense) or packed Q8_0 / Q4_0 (see
+ * jepa_pack_blocks) with w_scale its f16 scales [N, K/32].  bias f32 [N].
+ * out: act_dtype for STORE / GELU, f32 for RESID; row pitch ldo >= N.
+ * K % (128 / element size) == 0, N % 64 == 0. */
+jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
+                         int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
+                         int epilogue, void *out, int64_t ldo, void *hip_stream);
+
+/* Multi-head attention, head_dim 64 (LeVJEPA card, opening paragraph, for
+ * the block-causal mask).  qkv act [batch*n_tokens, 3*heads*64], columns
+ * [q | k | v] head-major -> out act [batch*n_tokens, heads*64].  mask
+ * JEPA_MASK_BLOCK_CAUSAL groups the patch tokens (after the optional CLS
+ * token 0) in consecutive runs of tokens_per_slot. */
+jepa_status jepa_op_attention(int act_dtype, const void *qkv, int batch, int n_tokens, int heads,
+                              int has_cls, int mask, int tokens_per_slot, void *out,
+                              void *hip_stream);
+
+/* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
+ * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2
+ * bytes of 16-byte nibble blocks for Q4_0) and scales (rows*cols/32 f16).
+ * A copy only: no value changes. */
+jepa_status jepa_pack_blocks(int dtype, const uint8_t *blocks, int64_t rows, int64_t cols,
+                             uint8_t *codes, uint16_t *scales);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JEPA_MI355X_OPS_H */

@@ -1,0 +1,134 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and its host-side logic (validation, the quantizer, block packing) is right.
+Nothing here launches a GPU kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import quant as Q
+from vision_transformer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"\b(jepa_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vision_transformer_amd import _lib
+    return _lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 19
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_binding_covers_every_entry_point(lib):
+    for n in declared_functions():
+        assert callable(getattr(lib, n)), n
+
+
+@pytest.mark.parametrize("dt", ["q8_0", "q4_0"])
+def test_host_quantizer_matches_oracle_bit_exact(lib, dt):
+    rng = np.random.default_rng(30)
+    x = (rng.standard_normal((257, 1024)) * 0.02).astype(np.float32)
+    x[5, 64:96] = 0.0                                    # a zero block
+    x[6, :32] = np.linspace(-1, 1, 32, dtype=np.float32)  # exact ties of magnitude
+    x[7, :32] = np.float32(3.0)                          # a constant block
+    x[8, 32:64] = (np.arange(32) - 16).astype(np.float32)
+    np.testing.assert_array_equal(lib.jepa_quantize(dt, x), Q.quantize(dt, x))
+
+
+@pytest.mark.parametrize("dt", ["q8_0", "q4_0"])
+def test_pack_blocks_is_a_pure_split(lib, dt):
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((3, 128)) * 0.02).astype(np.float32)
+    raw = Q.quantize(dt, x)
+    codes, scales = lib.jepa_pack_blocks(dt, raw, 3, 128)
+    bb = Q.block_bytes(dt)
+    blk = raw.reshape(-1, bb)
+    np.testing.assert_array_equal(scales.view(np.uint8).reshape(-1, 2), blk[:, :2])
+    np.testing.assert_array_equal(codes.reshape(-1, bb - 2), blk[:, 2:])
+
+
+def _small():
+    wl = synth.workload("small_bidir_cls_bf16")
+    dims = wl["dims"]
+    w32 = synth.make_f32_weights(dims, 1)
+    return dims, synth.stored_weights(dims, w32)
+
+
+def _expect_error(lib, status_name, dims, stored):
+    with pytest.raises(lib.JepaError) as e:
+        lib.jepa_create(dims, stored)
+    assert status_name in str(e.value), str(e.value)
+    return str(e.value)
+
+
+def test_create_rejects_a_missing_tensor(lib):
+    dims, stored = _small()
+    msg = _expect_error(lib, "JEPA_E_MISSING_TENSOR", dims,
+                        [t for t in stored if t["name"] != "enc.blk.1.ffn_up.bias"])
+    assert "enc.blk.1.ffn_up.bias" in msg
+
+
+def test_create_rejects_wrong_shape_and_size(lib):
+    dims, stored = _small()
+    bad = [dict(t) for t in stored]
+    bad[0]["ne1"] += 1
+    _expect_error(lib, "JEPA_E_SHAPE", dims, bad)
+    bad = [dict(t) for t in stored]
+    bad[0]["data"] = bad[0]["data"][:-1]
+    _expect_error(lib, "JEPA_E_SHAPE", dims, bad)
+
+
+def test_create_rejects_block_format_outside_the_rule(lib):
+    dims, stored = _small()
+    bad = [dict(t) for t in stored]
+    for t in bad:
+        if t["name"] == "enc.blk.0.ln1.weight":
+            t["dtype"] = "q8_0"
+            t["data"] = Q.quantize("q8_0", np.ones((1, t["ne0"]), np.float32))
+    _expect_error(lib, "JEPA_E_DTYPE", dims, bad)
+
+
+def test_create_rejects_unknown_and_duplicate_names(lib):
+    dims, stored = _small()
+    _expect_error(lib, "JEPA_E_INVALID_ARG", dims, stored + [dict(stored[0], name="enc.bogus")])
+    _expect_error(lib, "JEPA_E_INVALID_ARG", dims, stored + [stored[0]])
+
+
+def test_create_rejects_bad_dims(lib):
+    dims, stored = _small()
+    for change, status in [(dict(heads=2), "JEPA_E_UNSUPPORTED"),      # head_dim 96
+                           (dict(img_w=100), "JEPA_E_SHAPE"),          # not a multiple of patch
+                           (dict(frames=3, tubelet=2), "JEPA_E_SHAPE"),
+                           (dict(ln_eps=0.0), "JEPA_E_INVALID_ARG"),
+                           (dict(act_dtype="q8_0"), "JEPA_E_DTYPE")]:
+        d = dict(dims, **change)
+        _expect_error(lib, status, d, stored)
+
+
+def test_null_context_calls_fail_cleanly(lib):
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_encode(None, np.zeros((1, 1, 16, 16, 3), np.uint8), 1)
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_pool(None, "cls", np.zeros(4, np.float32))
+    assert lib.jepa_last_compute_ms(None) < 0
+    assert lib.jepa_model_n_bytes(None) == 0
+    lib.jepa_free(None)

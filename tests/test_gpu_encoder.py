@@ -1,0 +1,211 @@
+"""The whole encoder through the C ABI against the oracle.
+
+* Small workloads (the oracle runs in seconds): every token of the token map,
+  and the CLS / mean pools, against the oracle computed live.
+* The ViT-Ti/14 f32 image workload at its full size, live.
+* The four ViT-L workloads at full size, in the launch configuration the
+  benchmark times: sampled token rows and the pooled features against the
+  oracle's stored outputs (tests/golden/make_golden.py).
+* Invariants that must hold bit for bit: block-causal causality, the CLS
+  token being read-only, batch items being independent.
+* Dequantised weights bit-exact against the oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import encoder as E
+from oracle import quant as Q
+from tests import helpers as H
+from vision_transformer_amd import synth
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def Encoder():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from vision_transformer_amd.encoder import Encoder
+    return Encoder
+
+
+def _run(enc, frames):
+    y = enc.encode(torch.from_numpy(frames).cuda())
+    torch.cuda.synchronize()
+    return y
+
+
+def _check_pools(enc, dims, y_ref, B):
+    act = dims["act_dtype"]
+    if dims["has_cls"]:
+        cls = enc.pool("cls", B).cpu().numpy()
+        H.check_rows(act, cls, E.pool(y_ref, "cls", True), "cls")
+    mean = enc.pool("mean", B).cpu().numpy()
+    H.check_rows(act, mean, E.pool(y_ref, "mean", bool(dims["has_cls"])), "mean")
+
+
+@pytest.mark.parametrize("name", list(synth.SMALL_WORKLOADS))
+def test_small_workload_every_token(Encoder, name):
+    H.say(f"encoder {name}")
+    wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
+    enc = Encoder(dims, stored)
+    y = _run(enc, frames).cpu().numpy()
+    ref = H.oracle_tokens(dims, stored, frames)
+    H.check_rows(dims["act_dtype"], y, ref, "tokens")
+    _check_pools(enc, dims, ref, wl["batch"])
+    none = enc.pool("none", wl["batch"]).cpu().numpy()
+    assert np.array_equal(none, y)
+    enc.close()
+
+
+def test_vit_ti14_image_f32_full(Encoder):
+    H.say("encoder vit_ti14_image_f32")
+    wl, dims, frames, stored = H.workload_inputs("vit_ti14_image_f32")
+    enc = Encoder(dims, stored)
+    y = _run(enc, frames).cpu().numpy()
+    ref = H.oracle_tokens(dims, stored, frames)
+    r = H.check_rows("f32", y, ref, "tokens")
+    assert r["cos_worst"] >= H.F32_COS
+    _check_pools(enc, dims, ref, wl["batch"])
+    assert enc.last_compute_ms() > 0
+    enc.close()
+
+
+FULL = ["vit_l16_image_bf16_b32", "levjepa_vit_l16_16f_bf16_b4",
+        "vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_f16",
+        "vjepa2_vit_l16_64f256_q4_0"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_against_stored_oracle(Encoder, name):
+    path = os.path.join(H.GOLDEN, f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path, allow_pickle=False)
+    H.say(f"encoder {name} (full size)")
+    wl, dims, frames, stored = H.workload_inputs(name)
+    import hashlib
+    assert hashlib.sha256(frames.tobytes()).hexdigest() == str(g["frames_sha256"])
+    assert H.digest_weights(stored) == str(g["weights_sha256"])
+    enc = Encoder(dims, stored)
+    del stored
+    y = _run(enc, frames)
+    rows = g["rows"]
+    got = y[torch.from_numpy(rows[:, 0]).cuda(), torch.from_numpy(rows[:, 1]).cuda()].cpu().numpy()
+    act = dims["act_dtype"]
+    H.check_rows(act, got, g["sampled"], f"{len(rows)} sampled tokens")
+    B = wl["batch"]
+    if dims["has_cls"]:
+        H.check_rows(act, enc.pool("cls", B).cpu().numpy(), g["cls"], "cls")
+    H.check_rows(act, enc.pool("mean", B).cpu().numpy(), g["mean"], "mean")
+    enc.close()
+
+
+# ---------------------------------------------------------------------------
+# invariants, bit for bit
+# ---------------------------------------------------------------------------
+
+def test_block_causal_causality_bit_exact(Encoder):
+    wl, dims, frames, stored = H.workload_inputs("small_blockcausal_bf16")
+    enc = Encoder(dims, stored)
+    y0 = _run(enc, frames).cpu()
+    f2 = frames.copy()
+    t = 5
+    f2[:, t] = 255 - f2[:, t]
+    y1 = _run(enc, f2).cpu()
+    per = synth.grid(dims)[1] * synth.grid(dims)[2]
+    keep = 1 + t * per
+    assert torch.equal(y0[:, 1:keep], y1[:, 1:keep])
+    assert not torch.equal(y0[:, keep:], y1[:, keep:])
+    enc.close()
+
+
+def test_cls_token_is_read_only_bit_exact(Encoder):
+    wl, dims, frames, stored = H.workload_inputs("small_blockcausal_bf16")
+    enc = Encoder(dims, stored)
+    y0 = _run(enc, frames).cpu()
+    enc.close()
+    s2 = [dict(t) for t in stored]
+    for t in s2:
+        if t["name"] == "enc.cls_token":
+            t["data"] = synth.to_bfloat16_bits(np.full(dims["dim"], 0.5, np.float32))
+    enc = Encoder(dims, s2)
+    y1 = _run(enc, frames).cpu()
+    assert torch.equal(y0[:, 1:], y1[:, 1:])
+    assert not torch.equal(y0[:, 0], y1[:, 0])
+    enc.close()
+
+
+@pytest.mark.parametrize("name", ["small_blockcausal_bf16", "small_tubelet2_q8_0"])
+def test_batch_items_independent_bit_exact(Encoder, name):
+    wl, dims, frames, stored = H.workload_inputs(name)
+    enc = Encoder(dims, stored)
+    y = _run(enc, frames).cpu()
+    for b in range(frames.shape[0]):
+        yb = _run(enc, np.ascontiguousarray(frames[b:b + 1])).cpu()
+        assert torch.equal(y[b:b + 1], yb)
+    enc.close()
+
+
+def test_host_frames_match_device_frames(Encoder):
+    wl, dims, frames, stored = H.workload_inputs("small_bidir_cls_bf16")
+    enc = Encoder(dims, stored)
+    y_dev = _run(enc, frames).cpu()
+    y_host = enc.encode(frames)
+    torch.cuda.synchronize()
+    assert torch.equal(y_dev, y_host.cpu())
+    enc.close()
+
+
+# ---------------------------------------------------------------------------
+# weights as the GEMMs see them
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["small_tubelet2_q8_0", "small_tubelet2_q4_0", "small_bidir_f32",
+                                  "small_blockcausal_bf16"])
+def test_dequantised_weights_bit_exact(Encoder, name):
+    wl, dims, frames, stored = H.workload_inputs(name)
+    enc = Encoder(dims, stored)
+    for t in stored:
+        shape = (t["ne1"], t["ne0"]) if t["ne1"] > 1 else (t["ne0"],)
+        got = enc.dequant(t["name"], shape).cpu().numpy()
+        want = Q.stored_to_f64(t).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), t["name"]
+    enc.close()
+
+
+def test_model_bytes_of_a_levjepa_shaped_q8_0_set(Encoder):
+    """jepa_model_n_bytes of the LeVJEPA ViT-L/16 shape at q8_0 with an f32
+    remainder, minus the pos table the published file does not carry, is the
+    LeVJEPA card's 310.3 MiB (within the 0.1 MiB the page rounds to)."""
+    import json
+    pages = json.load(open(os.path.join(H.GOLDEN, "page_file_sizes.json")))
+    from vision_transformer_amd import _lib
+    dims = dict(synth.workload("levjepa_vit_l16_16f_bf16_b4")["dims"], act_dtype="f16",
+                mat_dtype="q8_0", rest_dtype="f32")
+    stored = []
+    for name, ne0, ne1 in synth.tensor_specs(dims):
+        dt = synth.storage_dtype(dims, name)
+        if dt == "q8_0":
+            data = np.zeros((ne1, ne0 // 32 * 34), np.uint8)
+        else:
+            data = np.zeros(ne0 * ne1, np.float32)
+        stored.append(dict(name=name, dtype=dt, ne0=ne0, ne1=ne1, data=data))
+    enc = Encoder(dims, stored)
+    pos = synth.n_tokens(dims) * dims["dim"] * 4
+    mib = (_lib.jepa_model_n_bytes(enc.ctx) - pos) / 2 ** 20
+    H.say(f"  LeVJEPA-shaped q8_0 model bytes without pos: {mib:.2f} MiB")
+    assert abs(mib - pages["levjepa_vitl16_mib"]["q8_0"]) <= pages["tolerance_mib"]
+    enc.close()
+
+
+def test_pool_before_encode_is_a_state_error(Encoder):
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs("small_bidir_f32")
+    enc = Encoder(dims, stored)
+    with pytest.raises(_lib.JepaError, match="JEPA_E_STATE"):
+        enc.pool("cls", 1)
+    enc.close()

@@ -1,0 +1,210 @@
+"""Each HIP kernel, through the C ABI, against the oracle's definition of its
+step, on seeded inputs that span several tiles with ragged tails.
+
+The operands are rounded to the activation dtype once, on the host, and the
+oracle sees exactly those rounded values, so what is measured is the
+kernel's own arithmetic: f32 accumulation order, and the roundings the kernel
+makes (its output, the probabilities fed to the PV product, dequantised
+weights)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import encoder as E
+from oracle import quant as Q
+from tests.helpers import rounded, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vision_transformer_amd import _lib
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return _lib
+
+
+# bound on |gpu - oracle| for one output rounded to act dtype from an f32 value
+OUT_REL = {"f32": 1e-6, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", [(1, 2, 32, 48, 1, 16), (2, 4, 64, 80, 2, 16), (1, 1, 56, 42, 1, 14)])
+def test_patchify(lib, act, shape):
+    B, T, H, W, kt, p = shape
+    say(f"patchify {act} {shape}")
+    frames = np.random.default_rng(40).integers(0, 256, (B, T, H, W, 3), dtype=np.uint8)
+    mean, std = (0.485, 0.456, 0.406), (0.229, 0.224, 0.225)
+    P = kt * p * p * 3
+    ld = -(-P // 64) * 64
+    np_ = (T // kt) * (H // p) * (W // p)
+    out = torch.full((B * np_, ld), 7.0, dtype=torch.float32, device="cuda").to(
+        {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[act])
+    lib.jepa_op_patchify(act, torch.from_numpy(frames).cuda(), kt, p, mean, std, out, ld)
+    got = out.double().cpu().numpy()
+    ref = E.patchify(E.normalize(frames, mean, std), kt, p).reshape(B * np_, P)
+    assert np.all(got[:, P:] == 0)
+    err = np.abs(got[:, :P] - ref)
+    assert np.all(err <= OUT_REL[act] * np.abs(ref) + 1e-6), err.max()
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dim", [128, 192, 1024])
+def test_layernorm(lib, act, dim):
+    say(f"layernorm {act} {dim}")
+    rng = np.random.default_rng(41)
+    rows = 301
+    x = (rng.standard_normal((rows, dim)) * 2 + 0.5).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(dim)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(dim)).astype(np.float32)
+    y = torch.empty((rows, dim), dtype={"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[act],
+                    device="cuda")
+    lib.jepa_op_layernorm(torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(),
+                          1e-6, y, act)
+    got = y.double().cpu().numpy()
+    ref = E.layer_norm(x.astype(np.float64), g.astype(np.float64), b.astype(np.float64), 1e-6)
+    err = np.abs(got - ref)
+    assert np.all(err <= OUT_REL[act] * np.abs(ref) + 2e-5), err.max()
+
+
+def _gemm_case(lib, act, wfmt, epi, M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    a_dev, a = rounded(act, rng.standard_normal((M, K)))
+    w32 = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    bias = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    scale = None
+    if wfmt in ("q8_0", "q4_0"):
+        raw = Q.quantize(wfmt, w32)
+        w = Q.stored_to_f64(dict(dtype=wfmt, ne0=K, ne1=N, data=raw))
+        codes, scales = lib.jepa_pack_blocks(wfmt, raw, N, K)
+        w_dev = torch.from_numpy(codes).cuda()
+        scale = torch.from_numpy(scales.view(np.int16)).cuda()
+    else:
+        w_dev, w = rounded(act, w32)
+    ref = E.linear(a, w, bias.astype(np.float64))
+    b_dev = torch.from_numpy(bias).cuda()
+    if epi == "resid":
+        x0 = rng.standard_normal((M, N)).astype(np.float32)
+        out = torch.from_numpy(x0.copy()).cuda()
+        ref = ref + x0
+    else:
+        out = torch.empty((M, N), dtype={"f32": torch.float32, "bf16": torch.bfloat16,
+                                         "f16": torch.float16}[act], device="cuda")
+        if epi == "gelu":
+            ref = E.gelu(ref)
+    lib.jepa_op_gemm(act, a_dev, w_dev, wfmt if wfmt != "dense" else act, N, b_dev, epi, out,
+                     w_scale=scale)
+    got = out.double().cpu().numpy()
+    return got, ref, a, w
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("epi", ["store", "gelu", "resid"])
+@pytest.mark.parametrize("mnk", [(300, 192, 256), (129, 320, 512), (1000, 3072, 1024)])
+def test_gemm_dense(lib, act, epi, mnk):
+    M, N, K = mnk
+    if act == "f32" and M * N * K > 1e9:
+        pytest.skip("the f32 path only serves small models")
+    say(f"gemm dense {act} {epi} {mnk}")
+    got, ref, a, w = _gemm_case(lib, act, "dense", epi, M, N, K, 42)
+    # accumulation error of an f32 dot product of length K, plus the output rounding
+    acc = 4 * K * 2.0 ** -24 * (np.abs(a) @ np.abs(w).T)
+    out_r = 0.0 if epi == "resid" else OUT_REL[act]
+    err = np.abs(got - ref)
+    assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
+
+
+@pytest.mark.parametrize("wfmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("epi", ["store", "resid"])
+def test_gemm_block_formats(lib, wfmt, act, epi):
+    M, N, K = 333, 256, 1024
+    say(f"gemm {wfmt} {act} {epi}")
+    got, ref, a, w = _gemm_case(lib, act, wfmt, epi, M, N, K, 43)
+    # the kernel rounds each dequantised weight to act dtype (relative 2^-11 f16,
+    # 2^-8 bf16), an error the oracle's exact weights do not have
+    wr = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}[act]
+    bound = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T)
+    out_r = 0.0 if epi == "resid" else OUT_REL[act]
+    err = np.abs(got - ref)
+    assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
+
+
+def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed):
+    rng = np.random.default_rng(seed)
+    D = heads * 64
+    qkv_dev, qkv = rounded(act, rng.standard_normal((B * N, 3 * D)))
+    out = torch.empty((B * N, D), dtype=qkv_dev.dtype, device="cuda")
+    lib.jepa_op_attention(act, qkv_dev, B, N, heads, has_cls, mask, per_slot, out)
+    got = out.double().cpu().numpy().reshape(B, N, D)
+    if mask == "bidir":
+        allowed = None
+    else:
+        allowed = E.block_causal_allowed((N - int(has_cls)) // per_slot, per_slot, has_cls)
+    ref = np.stack([E.attention(qkv.reshape(B, N, 3 * D)[b], heads, allowed) for b in range(B)])
+    return got, ref
+
+
+ATTN_CASES = [
+    # B, N, heads, has_cls, mask, per_slot
+    (2, 289, 2, True, "block_causal", 36),     # 8 slots of 6x6 + CLS
+    (1, 3137, 1, True, "block_causal", 196),   # the LeVJEPA shape, one head
+    (2, 197, 3, True, "bidir", 1),
+    (1, 300, 2, False, "bidir", 1),
+    (2, 96, 2, False, "block_causal", 24),      # tubelet slots, no CLS
+    (1, 1, 1, True, "bidir", 1),               # a single token
+]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[f"{c[1]}tok-{c[4]}-cls{int(c[3])}" for c in ATTN_CASES])
+def test_attention(lib, act, case):
+    say(f"attention {act} {case}")
+    got, ref = _attn_case(lib, act, *case, seed=44)
+    D = case[2] * 64
+    g = got.reshape(-1, D)
+    r = ref.reshape(-1, D)
+    if act == "f32":
+        assert np.max(np.abs(g - r)) <= 2e-5 * np.max(np.abs(r)) + 1e-6
+    else:
+        # probabilities and output rounded to act dtype: per-row relative error
+        # a small multiple of the dtype's half-ulp
+        err = np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)
+        assert err.max() <= {"bf16": 2e-2, "f16": 3e-3}[act], err.max()
+
+
+def test_attention_block_causal_rows_ignore_future_slots(lib):
+    """Changing the keys and values of the last slot leaves every earlier
+    patch row bit-identical (whole future tiles and masked elements alike)."""
+    B, N, heads, per = 1, 1 + 6 * 100, 2, 100
+    D = heads * 64
+    rng = np.random.default_rng(45)
+    qkv = rng.standard_normal((N, 3 * D)).astype(np.float32)
+    a_dev, _ = rounded("bf16", qkv)
+    qkv2 = qkv.copy()
+    qkv2[1 + 5 * per:, D:] = rng.standard_normal((per, 2 * D))
+    b_dev, _ = rounded("bf16", qkv2)
+    outs = []
+    for x in (a_dev, b_dev):
+        o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+        lib.jepa_op_attention("bf16", x, B, N, heads, True, "block_causal", per, o)
+        outs.append(o.cpu())
+    assert torch.equal(outs[0][1:1 + 5 * per], outs[1][1:1 + 5 * per])
+    assert not torch.equal(outs[0][0], outs[1][0])          # CLS reads the last slot
+
+
+def test_kernels_reject_out_of_contract_shapes(lib):
+    x = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 100), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, device="cuda")
+    out = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
+        lib.jepa_op_gemm("bf16", x, w, "bf16", 64, b, "store", out)      # K % 64 != 0
+    q = torch.zeros((10, 3 * 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((10, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
+        lib.jepa_op_attention("bf16", q, 1, 10, 1, True, "block_causal", 4, o)   # 9 % 4 != 0

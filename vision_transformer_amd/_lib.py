@@ -1,0 +1,247 @@
+"""ctypes binding of libjepa_mi355x.so: one Python function per C entry point
+of include/jepa_mi355x.h, with the same name.  Argument marshalling only:
+every step of the encoder runs in the library's HIP kernels.  torch supplies
+device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjepa_mi355x.so")
+
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+DTYPE = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0}
+MASK = {"bidir": 0, "block_causal": 1}
+POOL = {"none": 0, "cls": 1, "mean": 2}
+STATUS = {0: "JEPA_OK", -1: "JEPA_E_INVALID_ARG", -2: "JEPA_E_SHAPE", -3: "JEPA_E_DTYPE",
+          -4: "JEPA_E_MISSING_TENSOR", -5: "JEPA_E_OOM", -6: "JEPA_E_HIP",
+          -7: "JEPA_E_UNSUPPORTED", -8: "JEPA_E_STATE"}
+
+
+class JepaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class jepa_dims(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("depth", C.c_int32), ("heads", C.c_int32),
+                ("mlp_dim", C.c_int32), ("patch", C.c_int32), ("tubelet", C.c_int32),
+                ("img_h", C.c_int32), ("img_w", C.c_int32), ("frames", C.c_int32),
+                ("has_cls", C.c_int32), ("mask", C.c_int32), ("act_dtype", C.c_int32),
+                ("ln_eps", C.c_float), ("mean", C.c_float * 3), ("std", C.c_float * 3)]
+
+
+class jepa_tensor(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("dtype", C.c_int32), ("ne0", C.c_int64),
+                ("ne1", C.c_int64), ("data", C.c_void_p), ("nbytes", C.c_size_t)]
+
+
+class jepa_kernel_stat(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m vision_transformer_amd.build` "
+                          "(there is no CPU fallback)")
+    lib = C.CDLL(LIB_PATH)
+    P, I, I64, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    sig = {
+        "jepa_create": (I, [C.POINTER(jepa_dims), C.POINTER(jepa_tensor), I, C.POINTER(P)]),
+        "jepa_encode": (I, [P, P, I, I, P, P]),
+        "jepa_pool": (I, [P, I, P, P]),
+        "jepa_free": (None, [P]),
+        "jepa_last_error": (C.c_char_p, []),
+        "jepa_last_compute_ms": (C.c_float, [P]),
+        "jepa_model_n_bytes": (SZ, [P]),
+        "jepa_device_weight_bytes": (SZ, [P]),
+        "jepa_workspace_bytes": (SZ, [P, I]),
+        "jepa_dequant_tensor": (I, [P, C.c_char_p, P, P]),
+        "jepa_quantize": (I, [I, P, I64, I64, P]),
+        "jepa_set_profiling": (I, [P, C.c_uint32]),
+        "jepa_kernel_stats": (I, [P, C.POINTER(jepa_kernel_stat), I]),
+        "jepa_reset_kernel_stats": (None, [P]),
+        "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
+        "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
+        "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
+        "jepa_op_attention": (I, [I, P, I, I, I, I, I, I, P, P]),
+        "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise JepaError(status, _lib.jepa_last_error().decode())
+
+
+def _ptr(x) -> int | None:
+    """Device (torch) or host (numpy / torch cpu) buffer -> address."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
+        return x.ctypes.data
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_dims(d: dict) -> jepa_dims:
+    return jepa_dims(d["dim"], d["depth"], d["heads"], d["mlp_dim"], d["patch"], d["tubelet"],
+                     d["img_h"], d["img_w"], d["frames"], int(d["has_cls"]), MASK[d["mask"]],
+                     DTYPE[d["act_dtype"]], float(d["ln_eps"]), (C.c_float * 3)(*d["mean"]),
+                     (C.c_float * 3)(*d["std"]))
+
+
+def jepa_create(dims: dict, tensors: list[dict]) -> int:
+    """dims: mapping of jepa_dims fields (mask / act_dtype by name); tensors:
+    dicts with name, dtype (name), ne0, ne1 and data (a C-contiguous numpy
+    array of the raw storage).  Returns the context handle."""
+    arr = (jepa_tensor * len(tensors))()
+    keep = []
+    for i, t in enumerate(tensors):
+        data = np.ascontiguousarray(t["data"])
+        keep.append(data)
+        name = t["name"].encode()
+        keep.append(name)
+        arr[i] = jepa_tensor(name, DTYPE[t["dtype"]], t["ne0"], t["ne1"], data.ctypes.data, data.nbytes)
+    ctx = C.c_void_p()
+    d = make_dims(dims)
+    _check(_lib.jepa_create(C.byref(d), arr, len(tensors), C.byref(ctx)))
+    return ctx.value
+
+
+def jepa_encode(ctx: int, frames, batch: int, tokens_out=None, stream=None) -> None:
+    """frames: uint8 [batch, T, H, W, 3], a CUDA tensor (device) or a numpy
+    array / CPU tensor (host).  tokens_out: f32 CUDA tensor [batch, N, D] or None."""
+    on_dev = int(hasattr(frames, "is_cuda") and frames.is_cuda)
+    _check(_lib.jepa_encode(ctx, _ptr(frames), batch, on_dev, _ptr(tokens_out), _stream(stream)))
+
+
+def jepa_pool(ctx: int, mode: str | int, out, stream=None) -> None:
+    m = POOL[mode] if isinstance(mode, str) else mode
+    _check(_lib.jepa_pool(ctx, m, _ptr(out), _stream(stream)))
+
+
+def jepa_free(ctx: int) -> None:
+    _lib.jepa_free(ctx)
+
+
+def jepa_last_error() -> str:
+    return _lib.jepa_last_error().decode()
+
+
+def jepa_last_compute_ms(ctx: int) -> float:
+    return float(_lib.jepa_last_compute_ms(ctx))
+
+
+def jepa_model_n_bytes(ctx: int) -> int:
+    return int(_lib.jepa_model_n_bytes(ctx))
+
+
+def jepa_device_weight_bytes(ctx: int) -> int:
+    return int(_lib.jepa_device_weight_bytes(ctx))
+
+
+def jepa_workspace_bytes(ctx: int, batch: int) -> int:
+    return int(_lib.jepa_workspace_bytes(ctx, batch))
+
+
+def jepa_dequant_tensor(ctx: int, name: str, out, stream=None) -> None:
+    _check(_lib.jepa_dequant_tensor(ctx, name.encode(), _ptr(out), _stream(stream)))
+
+
+def jepa_quantize(dtype: str, x: np.ndarray) -> np.ndarray:
+    """Host quantizer: f32 [rows, cols] -> uint8 blocks [rows, cols/32*(34|18)]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    bb = {"q8_0": 34, "q4_0": 18}[dtype]
+    out = np.empty((rows, cols // 32 * bb), np.uint8)
+    _check(_lib.jepa_quantize(DTYPE[dtype], x.ctypes.data, rows, cols, out.ctypes.data))
+    return out
+
+
+def jepa_set_profiling(ctx: int, class_mask: int) -> None:
+    """class_mask: bit i times kernel class i (0 = off, 0xffffffff = all)."""
+    _check(_lib.jepa_set_profiling(ctx, class_mask & 0xFFFFFFFF))
+
+
+def jepa_kernel_stats(ctx: int) -> dict:
+    cap = 64
+    buf = (jepa_kernel_stat * cap)()
+    n = _lib.jepa_kernel_stats(ctx, buf, cap)
+    if n < 0:
+        _check(n)
+    return {buf[i].name.decode(): dict(launches=buf[i].launches, total_ms=buf[i].total_ms)
+            for i in range(min(n, cap))}
+
+
+def jepa_reset_kernel_stats(ctx: int) -> None:
+    _lib.jepa_reset_kernel_stats(ctx)
+
+
+# ---------------------------------------------------------------------------
+# single kernels (include/jepa_mi355x_ops.h)
+# ---------------------------------------------------------------------------
+EPI = {"store": 0, "gelu": 1, "resid": 2}
+
+
+def jepa_op_patchify(act_dtype: str, frames, tubelet: int, patch: int, mean, std, out, ld: int,
+                     stream=None) -> None:
+    B, T, H, W, _ = frames.shape
+    m = (C.c_float * 3)(*mean)
+    sd = (C.c_float * 3)(*std)
+    _check(_lib.jepa_op_patchify(DTYPE[act_dtype], _ptr(frames), B, T, H, W, tubelet, patch, m, sd,
+                                 _ptr(out), ld, _stream(stream)))
+
+
+def jepa_op_layernorm(x, gamma, beta, eps: float, y, y_dtype: str, stream=None) -> None:
+    rows, dim = x.shape
+    _check(_lib.jepa_op_layernorm(_ptr(x), rows, dim, _ptr(gamma), _ptr(beta), eps, _ptr(y),
+                                  DTYPE[y_dtype], _stream(stream)))
+
+
+def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str, out,
+                 w_scale=None, stream=None) -> None:
+    M, K = a.shape
+    _check(_lib.jepa_op_gemm(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
+                             n, _ptr(bias), EPI[epilogue], _ptr(out), out.shape[1], _stream(stream)))
+
+
+def jepa_op_attention(act_dtype: str, qkv, batch: int, n_tokens: int, heads: int, has_cls: bool,
+                      mask: str, tokens_per_slot: int, out, stream=None) -> None:
+    _check(_lib.jepa_op_attention(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, int(has_cls),
+                                  MASK[mask], tokens_per_slot, _ptr(out), _stream(stream)))
+
+
+def jepa_pack_blocks(dtype: str, blocks: np.ndarray, rows: int, cols: int):
+    """Host: blocks -> (codes uint8, scales uint16) in the GEMM's device layout."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    ncode = rows * cols if dtype == "q8_0" else rows * cols // 2
+    codes = np.empty(ncode, np.uint8)
+    scales = np.empty(rows * cols // 32, np.uint16)
+    _check(_lib.jepa_pack_blocks(DTYPE[dtype], blocks.ctypes.data, rows, cols, codes.ctypes.data,
+                                 scales.ctypes.data))
+    return codes, scales

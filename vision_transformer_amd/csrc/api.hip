@@ -1,0 +1,772 @@
+// The C ABI of include/jepa_mi355x.h: weight upload, workspace, the launch
+// sequence of one encoder forward, pooling, timing and the host quantizer.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/jepa_mi355x.h"
+#include "../../include/jepa_mi355x_ops.h"
+#include "kernels.hpp"
+
+using namespace jepa;
+
+namespace {
+
+thread_local std::string g_err;
+
+jepa_status fail(jepa_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define HIP_TRY(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(JEPA_E_HIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                        __LINE__);                                                         \
+    } while (0)
+
+// ---- host-side number formats ---------------------------------------------
+uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+float bf16_bits_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+// f32 -> IEEE half, round to nearest even.  Normal results round the
+// mantissa with the usual add-half-minus-one-plus-odd-bit trick; results
+// below the smallest normal half are produced by one f32 addition of a
+// magic constant whose ulp is the half subnormal step, so the FPU's own
+// round-to-nearest-even does the rounding.
+uint16_t f32_to_f16_bits(float f) {
+    uint32_t x = f32_bits(f);
+    const uint32_t sign = x & 0x80000000u;
+    x ^= sign;
+    uint16_t o;
+    if (x >= (143u << 23)) {                       // >= 65536, inf or nan
+        o = x > (255u << 23) ? 0x7e00 : 0x7c00;
+    } else if (x < (113u << 23)) {                 // below 2^-14
+        const uint32_t magic = 126u << 23;         // 0.5: ulp 2^-24
+        o = (uint16_t)(f32_bits(bits_f32(x) + bits_f32(magic)) - magic);
+    } else {
+        const uint32_t odd = (x >> 13) & 1u;
+        x += 0xc8000fffu + odd;                    // rebias exponent (-112 << 23) and round
+        o = (uint16_t)(x >> 13);
+    }
+    return (uint16_t)(o | (sign >> 16));
+}
+float f16_bits_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    if (e == 0) {
+        const float v = (float)m * 5.9604644775390625e-08f;   // m * 2^-24, exact
+        return sign ? -v : v;
+    }
+    if (e == 31) return bits_f32(sign | 0x7f800000u | (m << 13));
+    return bits_f32(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+size_t storage_bytes(int dt, int64_t n) {
+    switch (dt) {
+        case JEPA_F32: return (size_t)n * 4;
+        case JEPA_F16:
+        case JEPA_BF16: return (size_t)n * 2;
+        case JEPA_Q8_0: return (size_t)(n / 32) * 34;
+        case JEPA_Q4_0: return (size_t)(n / 32) * 18;
+    }
+    return 0;
+}
+
+float stored_to_f32(int dt, const void *data, int64_t i) {
+    switch (dt) {
+        case JEPA_F32: return ((const float *)data)[i];
+        case JEPA_F16: return f16_bits_to_f32(((const uint16_t *)data)[i]);
+        case JEPA_BF16: return bf16_bits_to_f32(((const uint16_t *)data)[i]);
+    }
+    return NAN;
+}
+
+const char *kClassNames[] = {"patchify",   "gemm_patch", "cls_rows",  "layernorm",
+                             "gemm_qkv",   "attention",  "gemm_out",  "gemm_fc1",
+                             "gemm_fc2",   "final_ln",   "pool"};
+enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_ATTN, K_GEMM_OUT,
+              K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_COUNT };
+
+struct DevTensor {
+    void *ptr = nullptr;        // device data
+    uint16_t *scale = nullptr;  // q formats: f16 scales
+    int dev_dt = 0;             // device dtype
+    int64_t ne0 = 0, ne1 = 0;
+};
+
+struct Layer {
+    DevTensor qkv, out, up, down;
+    float *ln1g, *ln1b, *ln2g, *ln2b, *bqkv, *bout, *bup, *bdown;
+};
+
+struct ProfRec {
+    int cls;
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct jepa_ctx {
+    jepa_dims d;
+    int D, H, F, L, P, Kp, Np, N, per_slot, act, es;
+    void *arena = nullptr;
+    size_t arena_bytes = 0, model_bytes = 0;
+    DevTensor wpe;
+    float *bpe = nullptr, *cls = nullptr, *pos = nullptr, *normg = nullptr, *normb = nullptr;
+    std::vector<Layer> layers;
+    std::map<std::string, DevTensor> by_name;
+    // workspace
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    int ws_batch = 0;
+    uint8_t *w_frames = nullptr;
+    void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_u = nullptr;
+    float *w_x = nullptr, *w_y = nullptr;
+    // last encode
+    const float *last_tokens = nullptr;
+    int last_batch = 0;
+    bool have_events = false, encoded = false;
+    hipEvent_t ev0, ev1;
+    // profiling
+    uint32_t prof = 0;          // class bitmask
+    std::vector<ProfRec> pending;
+    std::vector<hipEvent_t> event_pool;
+    int64_t stat_launches[K_COUNT] = {};
+    double stat_ms[K_COUNT] = {};
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t frames, patch, x, hn, qkv, o, u, y, total;
+};
+
+WsLayout ws_layout(const jepa_ctx *c, int B) {
+    WsLayout w;
+    const size_t M = (size_t)B * c->N;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    w.frames = take((size_t)B * c->d.frames * c->d.img_h * c->d.img_w * 3);
+    w.patch = take((size_t)B * c->Np * c->Kp * c->es);
+    w.x = take(M * c->D * 4);
+    w.hn = take(M * c->D * c->es);
+    w.qkv = take(M * 3 * c->D * c->es);
+    w.o = take(M * c->D * c->es);
+    w.u = take(M * c->F * c->es);
+    w.y = take(M * c->D * 4);
+    w.total = off;
+    return w;
+}
+
+jepa_status ensure_workspace(jepa_ctx *c, int B) {
+    if (B <= c->ws_batch) return JEPA_OK;
+    WsLayout w = ws_layout(c, B);
+    const char *cap = getenv("JEPA_MAX_WORKSPACE");
+    if (cap && (double)w.total > atof(cap))
+        return fail(JEPA_E_OOM, "workspace of %zu bytes for batch %d exceeds JEPA_MAX_WORKSPACE=%s",
+                    w.total, B, cap);
+    if (c->ws) {
+        HIP_TRY(hipDeviceSynchronize());
+        HIP_TRY(hipFree(c->ws));
+        c->ws = nullptr;
+        c->ws_batch = 0;
+    }
+    if (hipMalloc(&c->ws, w.total) != hipSuccess) {
+        c->ws = nullptr;
+        (void)hipGetLastError();
+        return fail(JEPA_E_OOM, "hipMalloc of %zu workspace bytes failed", w.total);
+    }
+    unsigned char *base = (unsigned char *)c->ws;
+    c->w_frames = base + w.frames;
+    c->w_patch = base + w.patch;
+    c->w_x = (float *)(base + w.x);
+    c->w_hn = base + w.hn;
+    c->w_qkv = base + w.qkv;
+    c->w_o = base + w.o;
+    c->w_u = base + w.u;
+    c->w_y = (float *)(base + w.y);
+    c->ws_bytes = w.total;
+    c->ws_batch = B;
+    return JEPA_OK;
+}
+
+hipEvent_t get_event(jepa_ctx *c) {
+    if (!c->event_pool.empty()) {
+        hipEvent_t e = c->event_pool.back();
+        c->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch wrapper: brackets the launch with events when profiling is on.
+template <typename F>
+jepa_status launch(jepa_ctx *c, int cls, hipStream_t s, F &&fn) {
+    ProfRec r{cls, nullptr, nullptr};
+    const bool on = (c->prof >> cls) & 1u;
+    if (on) {
+        r.a = get_event(c);
+        r.b = get_event(c);
+        if (r.a) HIP_TRY(hipEventRecord(r.a, s));
+    }
+    hipError_t e = fn();
+    if (e != hipSuccess) return fail(JEPA_E_HIP, "%s launch failed: %s", kClassNames[cls], hipGetErrorString(e));
+    if (on && r.a && r.b) {
+        HIP_TRY(hipEventRecord(r.b, s));
+        c->pending.push_back(r);
+    }
+    return JEPA_OK;
+}
+
+#define TRY(expr)                       \
+    do {                                \
+        jepa_status st_ = (expr);       \
+        if (st_ != JEPA_OK) return st_; \
+    } while (0)
+
+jepa_status check_dims(const jepa_dims *d) {
+    if (d->dim <= 0 || d->depth <= 0 || d->heads <= 0 || d->mlp_dim <= 0 || d->patch <= 0 ||
+        d->tubelet <= 0 || d->img_h <= 0 || d->img_w <= 0 || d->frames <= 0)
+        return fail(JEPA_E_SHAPE, "dims: every size must be positive");
+    if (d->dim % d->heads || d->dim / d->heads != 64)
+        return fail(JEPA_E_UNSUPPORTED, "dims: head_dim = dim/heads must be 64 (dim %d, heads %d)", d->dim, d->heads);
+    if (d->dim % 64 || d->mlp_dim % 64)
+        return fail(JEPA_E_UNSUPPORTED, "dims: dim and mlp_dim must be multiples of 64");
+    const int e = d->dim / 64;
+    if (!(e == 2 || e == 3 || e == 4 || e == 6 || e == 8 || e == 12 || e == 16 || e == 20 || e == 24 || e == 32))
+        return fail(JEPA_E_UNSUPPORTED, "dims: dim %d not among the LayerNorm widths built", d->dim);
+    if (d->img_h % d->patch || d->img_w % d->patch)
+        return fail(JEPA_E_SHAPE, "dims: img_h, img_w must be multiples of patch");
+    if (d->frames % d->tubelet) return fail(JEPA_E_SHAPE, "dims: frames %% tubelet != 0");
+    if (d->has_cls != 0 && d->has_cls != 1) return fail(JEPA_E_INVALID_ARG, "dims: has_cls must be 0 or 1");
+    if (d->mask != JEPA_MASK_BIDIR && d->mask != JEPA_MASK_BLOCK_CAUSAL)
+        return fail(JEPA_E_INVALID_ARG, "dims: unknown mask %d", d->mask);
+    if (d->act_dtype != JEPA_F32 && d->act_dtype != JEPA_F16 && d->act_dtype != JEPA_BF16)
+        return fail(JEPA_E_DTYPE, "dims: act_dtype must be F32, F16 or BF16");
+    if (!(d->ln_eps > 0.f)) return fail(JEPA_E_INVALID_ARG, "dims: ln_eps must be > 0");
+    for (int c = 0; c < 3; ++c)
+        if (!(d->std[c] != 0.f)) return fail(JEPA_E_INVALID_ARG, "dims: std[%d] is 0", c);
+    return JEPA_OK;
+}
+
+// [blocks](f16 scale, payload) -> payloads then scales
+void pack_blocks(int dt, const unsigned char *src, int64_t nb, unsigned char *codes, uint16_t *scales) {
+    const int bb = dt == JEPA_Q8_0 ? 34 : 18, pl = bb - 2;
+    for (int64_t ib = 0; ib < nb; ++ib) {
+        memcpy(codes + ib * pl, src + ib * bb + 2, pl);
+        memcpy(scales + ib, src + ib * bb, 2);
+    }
+}
+
+struct Expect {
+    int64_t ne0, ne1;
+    bool matrix;      // may be re-typed to a block format
+    bool present = false;
+    const jepa_tensor *t = nullptr;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *jepa_last_error(void) { return g_err.c_str(); }
+
+jepa_status jepa_quantize(int dtype, const float *src, int64_t rows, int64_t cols, uint8_t *dst) {
+#pragma clang fp contract(off)
+    if (!src || !dst || rows <= 0 || cols <= 0) return fail(JEPA_E_INVALID_ARG, "quantize: bad arguments");
+    if (cols % 32) return fail(JEPA_E_SHAPE, "quantize: cols %lld not a multiple of 32", (long long)cols);
+    if (dtype != JEPA_Q8_0 && dtype != JEPA_Q4_0) return fail(JEPA_E_DTYPE, "quantize: dtype must be Q8_0 or Q4_0");
+    const int64_t nb = rows * (cols / 32);
+    for (int64_t ib = 0; ib < nb; ++ib) {
+        const float *x = src + ib * 32;
+        float d;
+        uint8_t *o;
+        if (dtype == JEPA_Q8_0) {
+            float amax = 0.f;
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+            d = amax / 127.f;
+            const float id = d != 0.f ? 1.f / d : 0.f;
+            o = dst + ib * 34;
+            for (int j = 0; j < 32; ++j) ((int8_t *)o)[2 + j] = (int8_t)roundf(x[j] * id);
+        } else {
+            float amax = 0.f, m = 0.f;
+            for (int j = 0; j < 32; ++j)
+                if (amax < fabsf(x[j])) { amax = fabsf(x[j]); m = x[j]; }
+            d = m / -8.f;
+            const float id = d != 0.f ? 1.f / d : 0.f;
+            o = dst + ib * 18;
+            for (int j = 0; j < 16; ++j) {
+                int q0 = (int)(x[j] * id + 8.5f), q1 = (int)(x[j + 16] * id + 8.5f);
+                q0 = q0 < 15 ? q0 : 15;
+                q1 = q1 < 15 ? q1 : 15;
+                o[2 + j] = (uint8_t)(q0 | (q1 << 4));
+            }
+        }
+        const uint16_t h = f32_to_f16_bits(d);
+        memcpy(o, &h, 2);
+    }
+    return JEPA_OK;
+}
+
+jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n_tensors, jepa_ctx **out) {
+    if (!dims || !out || (!tensors && n_tensors > 0) || n_tensors < 0)
+        return fail(JEPA_E_INVALID_ARG, "create: null argument");
+    *out = nullptr;
+    TRY(check_dims(dims));
+    const jepa_dims &d = *dims;
+    const int D = d.dim, F = d.mlp_dim;
+    const int Tt = d.frames / d.tubelet, Hp = d.img_h / d.patch, Wp = d.img_w / d.patch;
+    const int Np = Tt * Hp * Wp, N = Np + d.has_cls, P = d.tubelet * d.patch * d.patch * 3;
+    if (d.mask == JEPA_MASK_BLOCK_CAUSAL && d.has_cls && N > 15360)
+        return fail(JEPA_E_UNSUPPORTED, "create: block-causal with CLS supports N <= 15360 (N = %d)", N);
+
+    // expected schema
+    std::map<std::string, Expect> want;
+    want["enc.patch_embed.weight"] = {P, D, false};
+    want["enc.patch_embed.bias"] = {D, 1, false};
+    if (d.has_cls) want["enc.cls_token"] = {D, 1, false};
+    want["enc.pos_embed"] = {D, N, false};
+    want["enc.norm.weight"] = {D, 1, false};
+    want["enc.norm.bias"] = {D, 1, false};
+    for (int i = 0; i < d.depth; ++i) {
+        const std::string p = "enc.blk." + std::to_string(i) + ".";
+        want[p + "ln1.weight"] = {D, 1, false};
+        want[p + "ln1.bias"] = {D, 1, false};
+        want[p + "ln2.weight"] = {D, 1, false};
+        want[p + "ln2.bias"] = {D, 1, false};
+        want[p + "attn_qkv.weight"] = {D, 3 * D, true};
+        want[p + "attn_qkv.bias"] = {3 * D, 1, false};
+        want[p + "attn_out.weight"] = {D, D, true};
+        want[p + "attn_out.bias"] = {D, 1, false};
+        want[p + "ffn_up.weight"] = {D, F, true};
+        want[p + "ffn_up.bias"] = {F, 1, false};
+        want[p + "ffn_down.weight"] = {F, D, true};
+        want[p + "ffn_down.bias"] = {D, 1, false};
+    }
+    size_t model_bytes = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        const jepa_tensor &t = tensors[i];
+        if (!t.name) return fail(JEPA_E_INVALID_ARG, "create: tensor %d has no name", i);
+        auto it = want.find(t.name);
+        if (it == want.end()) return fail(JEPA_E_INVALID_ARG, "create: unknown tensor '%s'", t.name);
+        Expect &e = it->second;
+        if (e.present) return fail(JEPA_E_INVALID_ARG, "create: tensor '%s' given twice", t.name);
+        if (t.ne0 != e.ne0 || t.ne1 != e.ne1)
+            return fail(JEPA_E_SHAPE, "create: '%s' is [%lld, %lld], expected [%lld, %lld]", t.name,
+                        (long long)t.ne0, (long long)t.ne1, (long long)e.ne0, (long long)e.ne1);
+        if (t.dtype < JEPA_F32 || t.dtype > JEPA_Q4_0)
+            return fail(JEPA_E_DTYPE, "create: '%s' has unknown dtype %d", t.name, t.dtype);
+        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && !e.matrix)
+            return fail(JEPA_E_DTYPE, "create: '%s' must keep a dense dtype (only the block matrices may be re-typed)", t.name);
+        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && (t.ne0 % 64))
+            return fail(JEPA_E_SHAPE, "create: '%s' row length %lld not a multiple of 64 for block formats", t.name, (long long)t.ne0);
+        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && d.act_dtype == JEPA_F32)
+            return fail(JEPA_E_UNSUPPORTED, "create: block-format '%s' needs act_dtype F16 or BF16", t.name);
+        const size_t nb = storage_bytes(t.dtype, t.ne0 * t.ne1);
+        if (t.nbytes != nb)
+            return fail(JEPA_E_SHAPE, "create: '%s' has %zu bytes, its dtype and shape need %zu", t.name, t.nbytes, nb);
+        if (!t.data) return fail(JEPA_E_INVALID_ARG, "create: '%s' has no data", t.name);
+        e.present = true;
+        e.t = &t;
+        model_bytes += nb;
+    }
+    for (auto &kv : want)
+        if (!kv.second.present) return fail(JEPA_E_MISSING_TENSOR, "create: tensor '%s' is missing", kv.first.c_str());
+
+    jepa_ctx *c = new jepa_ctx();
+    c->d = d;
+    c->D = D; c->H = d.heads; c->F = F; c->L = d.depth; c->P = P;
+    c->act = d.act_dtype;
+    c->es = d.act_dtype == JEPA_F32 ? 4 : 2;
+    const int bk = 128 / c->es;
+    c->Kp = (P + bk - 1) / bk * bk;
+    c->Np = Np; c->N = N; c->per_slot = Hp * Wp;
+    c->model_bytes = model_bytes;
+
+    // device layout of every tensor: block matrices keep their format (codes
+    // then scales); other matrices take the act dtype; vectors become f32.
+    struct Plan { std::string name; const jepa_tensor *t; int dev_dt; size_t off, scale_off, bytes; };
+    std::vector<Plan> plan;
+    size_t off = 0;
+    for (auto &kv : want) {
+        const jepa_tensor *t = kv.second.t;
+        Plan p{kv.first, t, 0, 0, 0, 0};
+        // vectors and the pos table are consumed in f32 by the epilogues
+        const bool vec = t->ne1 == 1 || kv.first == "enc.pos_embed";
+        if (t->dtype == JEPA_Q8_0 || t->dtype == JEPA_Q4_0) {
+            p.dev_dt = t->dtype;
+            p.off = off;
+            const size_t codes = t->dtype == JEPA_Q8_0 ? (size_t)t->ne0 * t->ne1 : (size_t)t->ne0 * t->ne1 / 2;
+            off += align256(codes);
+            p.scale_off = off;
+            off += align256((size_t)t->ne0 * t->ne1 / 32 * 2);
+            p.bytes = codes;
+        } else if (vec) {
+            p.dev_dt = JEPA_F32;
+            p.off = off;
+            p.bytes = (size_t)t->ne0 * t->ne1 * 4;
+            off += align256(p.bytes);
+        } else {
+            p.dev_dt = c->act;
+            p.off = off;
+            const int64_t rowlen = kv.first == "enc.patch_embed.weight" ? c->Kp : t->ne0;
+            p.bytes = (size_t)rowlen * t->ne1 * c->es;
+            off += align256(p.bytes);
+        }
+        plan.push_back(p);
+    }
+    if (hipMalloc(&c->arena, off) != hipSuccess) {
+        (void)hipGetLastError();
+        delete c;
+        return fail(JEPA_E_OOM, "create: hipMalloc of %zu weight bytes failed", off);
+    }
+    c->arena_bytes = off;
+    unsigned char *arena = (unsigned char *)c->arena;
+
+    std::vector<unsigned char> host;
+    for (auto &p : plan) {
+        const jepa_tensor *t = p.t;
+        DevTensor dt;
+        dt.dev_dt = p.dev_dt;
+        dt.ne0 = t->ne0;
+        dt.ne1 = t->ne1;
+        dt.ptr = arena + p.off;
+        const int64_t n = t->ne0 * t->ne1;
+        if (p.dev_dt == JEPA_Q8_0 || p.dev_dt == JEPA_Q4_0) {
+            // repack [rows][blocks](scale, payload) into codes then scales
+            const int64_t nb = n / 32;
+            host.assign(p.bytes + nb * 2, 0);
+            pack_blocks(p.dev_dt, (const unsigned char *)t->data, nb, host.data(),
+                        (uint16_t *)(host.data() + p.bytes));
+            dt.scale = (uint16_t *)(arena + p.scale_off);
+            if (hipMemcpy(dt.ptr, host.data(), p.bytes, hipMemcpyHostToDevice) != hipSuccess ||
+                hipMemcpy(dt.scale, host.data() + p.bytes, nb * 2, hipMemcpyHostToDevice) != hipSuccess) {
+                jepa_free(c);
+                return fail(JEPA_E_HIP, "create: upload of '%s' failed", p.name.c_str());
+            }
+        } else {
+            host.assign(p.bytes, 0);
+            const int64_t rowlen = p.name == "enc.patch_embed.weight" ? c->Kp : t->ne0;
+            const int es = p.dev_dt == JEPA_F32 ? 4 : 2;
+            if (p.dev_dt == t->dtype) {   // same format: copy rows (padded for patch-embed)
+                for (int64_t r = 0; r < t->ne1; ++r)
+                    memcpy(&host[r * rowlen * es], (const unsigned char *)t->data + r * t->ne0 * es, t->ne0 * es);
+            } else {                      // widen exactly, or round to nearest even
+                for (int64_t r = 0; r < t->ne1; ++r)
+                    for (int64_t k = 0; k < t->ne0; ++k) {
+                        const int64_t i = r * t->ne0 + k, o = r * rowlen + k;
+                        const float v = stored_to_f32(t->dtype, t->data, i);
+                        if (p.dev_dt == JEPA_F32) {
+                            memcpy(&host[o * 4], &v, 4);
+                        } else {
+                            const uint16_t h = p.dev_dt == JEPA_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+                            memcpy(&host[o * 2], &h, 2);
+                        }
+                    }
+            }
+            if (hipMemcpy(dt.ptr, host.data(), p.bytes, hipMemcpyHostToDevice) != hipSuccess) {
+                jepa_free(c);
+                return fail(JEPA_E_HIP, "create: upload of '%s' failed", p.name.c_str());
+            }
+        }
+        c->by_name[p.name] = dt;
+    }
+    auto vecp = [&](const std::string &n) { return (float *)c->by_name[n].ptr; };
+    c->wpe = c->by_name["enc.patch_embed.weight"];
+    c->bpe = vecp("enc.patch_embed.bias");
+    c->cls = d.has_cls ? vecp("enc.cls_token") : nullptr;
+    c->pos = vecp("enc.pos_embed");
+    c->normg = vecp("enc.norm.weight");
+    c->normb = vecp("enc.norm.bias");
+    c->layers.resize(d.depth);
+    for (int i = 0; i < d.depth; ++i) {
+        const std::string p = "enc.blk." + std::to_string(i) + ".";
+        Layer &L = c->layers[i];
+        L.qkv = c->by_name[p + "attn_qkv.weight"];
+        L.out = c->by_name[p + "attn_out.weight"];
+        L.up = c->by_name[p + "ffn_up.weight"];
+        L.down = c->by_name[p + "ffn_down.weight"];
+        L.ln1g = vecp(p + "ln1.weight"); L.ln1b = vecp(p + "ln1.bias");
+        L.ln2g = vecp(p + "ln2.weight"); L.ln2b = vecp(p + "ln2.bias");
+        L.bqkv = vecp(p + "attn_qkv.bias"); L.bout = vecp(p + "attn_out.bias");
+        L.bup = vecp(p + "ffn_up.bias"); L.bdown = vecp(p + "ffn_down.bias");
+    }
+    if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
+        jepa_free(c);
+        return fail(JEPA_E_HIP, "create: hipEventCreate failed");
+    }
+    c->have_events = true;
+    *out = c;
+    return JEPA_OK;
+}
+
+static jepa_status gemm(jepa_ctx *c, int cls, hipStream_t s, const void *a, int64_t M, int64_t K,
+                        const DevTensor &w, const float *bias, int epi, void *out, int64_t ldo) {
+    GemmArgs g{};
+    g.a = a; g.w = w.ptr; g.wscale = w.scale; g.bias = bias; g.out = out;
+    g.M = M; g.N = w.ne1; g.K = K; g.lda = K; g.ldo = ldo;
+    return launch(c, cls, s, [&] { return launch_gemm(c->act, w.dev_dt, epi, g, s); });
+}
+
+jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frames_on_device,
+                        float *tokens_out, void *hip_stream) {
+    if (!c || !frames) return fail(JEPA_E_INVALID_ARG, "encode: null argument");
+    if (batch <= 0) return fail(JEPA_E_INVALID_ARG, "encode: batch must be > 0 (got %d)", batch);
+    if ((int64_t)batch * c->N > (int64_t)65535 * 128)
+        return fail(JEPA_E_UNSUPPORTED, "encode: batch*tokens %lld too large", (long long)batch * c->N);
+    TRY(ensure_workspace(c, batch));
+    hipStream_t s = (hipStream_t)hip_stream;
+    const jepa_dims &d = c->d;
+    const int64_t M = (int64_t)batch * c->N;
+    const uint8_t *fr = frames;
+    if (!frames_on_device) {
+        const size_t nbytes = (size_t)batch * d.frames * d.img_h * d.img_w * 3;
+        HIP_TRY(hipMemcpyAsync(c->w_frames, frames, nbytes, hipMemcpyHostToDevice, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        fr = c->w_frames;
+    }
+    float *Y = tokens_out ? tokens_out : c->w_y;
+    HIP_TRY(hipEventRecord(c->ev0, s));
+
+    PatchifyArgs pa{};
+    pa.frames = fr; pa.B = batch; pa.T = d.frames; pa.H = d.img_h; pa.W = d.img_w;
+    pa.tubelet = d.tubelet; pa.patch = d.patch;
+    for (int i = 0; i < 3; ++i) { pa.mean[i] = d.mean[i]; pa.std[i] = d.std[i]; }
+    pa.out = c->w_patch; pa.ld = c->Kp;
+    TRY(launch(c, K_PATCHIFY, s, [&] { return launch_patchify(c->act, pa, s); }));
+
+    GemmArgs g{};
+    g.a = c->w_patch; g.w = c->wpe.ptr; g.bias = c->bpe; g.out = c->w_x;
+    g.M = (int64_t)batch * c->Np; g.N = c->D; g.K = c->Kp; g.lda = c->Kp; g.ldo = c->D;
+    g.pos = c->pos; g.np = c->Np; g.ntok = c->N; g.has_cls = d.has_cls;
+    TRY(launch(c, K_GEMM_PATCH, s, [&] { return launch_gemm(c->act, c->act, EPI_PATCH, g, s); }));
+    if (d.has_cls)
+        TRY(launch(c, K_CLS_ROWS, s, [&] { return launch_cls_rows(c->w_x, c->cls, c->pos, batch, c->N, c->D, s); }));
+
+    AttnArgs aa{};
+    aa.qkv = c->w_qkv; aa.out = c->w_o; aa.B = batch; aa.N = c->N; aa.heads = c->H;
+    aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
+    const int D = c->D;
+    for (int i = 0; i < c->L; ++i) {
+        const Layer &L = c->layers[i];
+        TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, L.ln1g, L.ln1b, d.ln_eps, c->w_hn, c->act, s); }));
+        TRY(gemm(c, K_GEMM_QKV, s, c->w_hn, M, D, L.qkv, L.bqkv, EPI_STORE, c->w_qkv, 3 * D));
+        TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
+        TRY(gemm(c, K_GEMM_OUT, s, c->w_o, M, D, L.out, L.bout, EPI_RESID, c->w_x, D));
+        TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, L.ln2g, L.ln2b, d.ln_eps, c->w_hn, c->act, s); }));
+        TRY(gemm(c, K_GEMM_FC1, s, c->w_hn, M, D, L.up, L.bup, EPI_GELU, c->w_u, c->F));
+        TRY(gemm(c, K_GEMM_FC2, s, c->w_u, M, c->F, L.down, L.bdown, EPI_RESID, c->w_x, D));
+    }
+    TRY(launch(c, K_FINAL_LN, s, [&] { return launch_layernorm(c->w_x, M, D, c->normg, c->normb, d.ln_eps, Y, JEPA_F32, s); }));
+    HIP_TRY(hipEventRecord(c->ev1, s));
+    c->last_tokens = Y;
+    c->last_batch = batch;
+    c->encoded = true;
+    return JEPA_OK;
+}
+
+jepa_status jepa_pool(jepa_ctx *c, int mode, float *out, void *hip_stream) {
+    if (!c || !out) return fail(JEPA_E_INVALID_ARG, "pool: null argument");
+    if (!c->encoded) return fail(JEPA_E_STATE, "pool: nothing encoded yet");
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int B = c->last_batch;
+    switch (mode) {
+        case JEPA_POOL_CLS:
+            if (!c->d.has_cls) return fail(JEPA_E_STATE, "pool: the model has no CLS token");
+            return launch(c, K_POOL, s, [&] { return launch_pool_cls(c->last_tokens, B, c->N, c->D, out, s); });
+        case JEPA_POOL_MEAN:
+            return launch(c, K_POOL, s, [&] { return launch_pool_mean(c->last_tokens, B, c->N, c->D, c->d.has_cls, out, s); });
+        case JEPA_POOL_NONE:
+            HIP_TRY(hipMemcpyAsync(out, c->last_tokens, (size_t)B * c->N * c->D * 4, hipMemcpyDeviceToDevice, s));
+            return JEPA_OK;
+    }
+    return fail(JEPA_E_INVALID_ARG, "pool: unknown mode %d", mode);
+}
+
+void jepa_free(jepa_ctx *c) {
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    if (c->arena) (void)hipFree(c->arena);
+    if (c->ws) (void)hipFree(c->ws);
+    if (c->have_events) {
+        (void)hipEventDestroy(c->ev0);
+        (void)hipEventDestroy(c->ev1);
+    }
+    for (auto &r : c->pending) {
+        if (r.a) (void)hipEventDestroy(r.a);
+        if (r.b) (void)hipEventDestroy(r.b);
+    }
+    for (auto e : c->event_pool) (void)hipEventDestroy(e);
+    delete c;
+}
+
+float jepa_last_compute_ms(jepa_ctx *c) {
+    if (!c || !c->encoded) return -1.f;
+    if (hipEventSynchronize(c->ev1) != hipSuccess) return -1.f;
+    float ms = -1.f;
+    if (hipEventElapsedTime(&ms, c->ev0, c->ev1) != hipSuccess) return -1.f;
+    return ms;
+}
+
+size_t jepa_model_n_bytes(const jepa_ctx *c) { return c ? c->model_bytes : 0; }
+size_t jepa_device_weight_bytes(const jepa_ctx *c) { return c ? c->arena_bytes : 0; }
+size_t jepa_workspace_bytes(const jepa_ctx *c, int batch) {
+    return (c && batch > 0) ? ws_layout(c, batch).total : 0;
+}
+
+jepa_status jepa_dequant_tensor(jepa_ctx *c, const char *name, float *out_dev, void *hip_stream) {
+    if (!c || !name || !out_dev) return fail(JEPA_E_INVALID_ARG, "dequant: null argument");
+    auto it = c->by_name.find(name);
+    if (it == c->by_name.end()) return fail(JEPA_E_MISSING_TENSOR, "dequant: no tensor '%s'", name);
+    const DevTensor &t = it->second;
+    hipStream_t s = (hipStream_t)hip_stream;
+    // the patch-embed matrix is stored with padded rows; copy row by row
+    if (std::string(name) == "enc.patch_embed.weight" && c->Kp != t.ne0) {
+        for (int64_t r = 0; r < t.ne1; ++r) {
+            hipError_t e = launch_dequant(t.dev_dt, (const unsigned char *)t.ptr + r * c->Kp * c->es,
+                                          nullptr, 1, t.ne0, out_dev + r * t.ne0, s);
+            if (e != hipSuccess) return fail(JEPA_E_HIP, "dequant: %s", hipGetErrorString(e));
+        }
+        return JEPA_OK;
+    }
+    hipError_t e = launch_dequant(t.dev_dt, t.ptr, t.scale, t.ne1, t.ne0, out_dev, s);
+    if (e != hipSuccess) return fail(JEPA_E_HIP, "dequant: %s", hipGetErrorString(e));
+    return JEPA_OK;
+}
+
+jepa_status jepa_set_profiling(jepa_ctx *c, uint32_t class_mask) {
+    if (!c) return fail(JEPA_E_INVALID_ARG, "set_profiling: null context");
+    c->prof = class_mask;
+    return JEPA_OK;
+}
+
+int jepa_kernel_stats(jepa_ctx *c, jepa_kernel_stat *out, int cap) {
+    if (!c) return fail(JEPA_E_INVALID_ARG, "kernel_stats: null context");
+    for (auto &r : c->pending) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return fail(JEPA_E_HIP, "kernel_stats: event sync failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(JEPA_E_HIP, "kernel_stats: elapsed failed");
+        c->stat_launches[r.cls] += 1;
+        c->stat_ms[r.cls] += ms;
+        c->event_pool.push_back(r.a);
+        c->event_pool.push_back(r.b);
+    }
+    c->pending.clear();
+    for (int i = 0; i < K_COUNT && i < cap; ++i) {
+        out[i].name = kClassNames[i];
+        out[i].launches = c->stat_launches[i];
+        out[i].total_ms = c->stat_ms[i];
+    }
+    return K_COUNT;
+}
+
+void jepa_reset_kernel_stats(jepa_ctx *c) {
+    if (!c) return;
+    jepa_kernel_stat tmp[K_COUNT];
+    (void)jepa_kernel_stats(c, tmp, K_COUNT);
+    for (int i = 0; i < K_COUNT; ++i) { c->stat_launches[i] = 0; c->stat_ms[i] = 0.0; }
+}
+
+// ---------------------------------------------------------------------------
+// single kernels (include/jepa_mi355x_ops.h)
+// ---------------------------------------------------------------------------
+
+static jepa_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return JEPA_OK;
+    if (e == hipErrorInvalidValue) return fail(JEPA_E_SHAPE, "%s: shape or argument outside the kernel's contract", what);
+    return fail(JEPA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool act_ok(int dt) { return dt == JEPA_F32 || dt == JEPA_F16 || dt == JEPA_BF16; }
+
+jepa_status jepa_op_patchify(int act_dtype, const uint8_t *frames, int batch, int frames_per_item,
+                             int img_h, int img_w, int tubelet, int patch, const float mean[3],
+                             const float std[3], void *out, int64_t ld, void *hip_stream) {
+    if (!frames || !out || !mean || !std) return fail(JEPA_E_INVALID_ARG, "op_patchify: null argument");
+    if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_patchify: bad act dtype");
+    PatchifyArgs a{};
+    a.frames = frames; a.B = batch; a.T = frames_per_item; a.H = img_h; a.W = img_w;
+    a.tubelet = tubelet; a.patch = patch; a.out = out; a.ld = ld;
+    for (int i = 0; i < 3; ++i) { a.mean[i] = mean[i]; a.std[i] = std[i]; }
+    return hip_status(launch_patchify(act_dtype, a, (hipStream_t)hip_stream), "op_patchify");
+}
+
+jepa_status jepa_op_layernorm(const float *x, int64_t rows, int dim, const float *gamma,
+                              const float *beta, float eps, void *y, int y_dtype, void *hip_stream) {
+    if (!x || !gamma || !beta || !y) return fail(JEPA_E_INVALID_ARG, "op_layernorm: null argument");
+    if (!act_ok(y_dtype)) return fail(JEPA_E_DTYPE, "op_layernorm: bad output dtype");
+    return hip_status(launch_layernorm(x, rows, dim, gamma, beta, eps, y, y_dtype, (hipStream_t)hip_stream),
+                      "op_layernorm");
+}
+
+jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
+                         int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
+                         int epilogue, void *out, int64_t ldo, void *hip_stream) {
+    if (!a || !w || !bias || !out) return fail(JEPA_E_INVALID_ARG, "op_gemm: null argument");
+    if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_gemm: bad act dtype");
+    if (epilogue < JEPA_EPI_STORE || epilogue > JEPA_EPI_RESID)
+        return fail(JEPA_E_INVALID_ARG, "op_gemm: unknown epilogue %d", epilogue);
+    GemmArgs g{};
+    g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = out;
+    g.M = M; g.N = N; g.K = K; g.lda = K; g.ldo = ldo;
+    return hip_status(launch_gemm(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm");
+}
+
+jepa_status jepa_op_attention(int act_dtype, const void *qkv, int batch, int n_tokens, int heads,
+                              int has_cls, int mask, int tokens_per_slot, void *out,
+                              void *hip_stream) {
+    if (!qkv || !out) return fail(JEPA_E_INVALID_ARG, "op_attention: null argument");
+    if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_attention: bad act dtype");
+    if (mask != JEPA_MASK_BIDIR && mask != JEPA_MASK_BLOCK_CAUSAL)
+        return fail(JEPA_E_INVALID_ARG, "op_attention: unknown mask %d", mask);
+    AttnArgs a{};
+    a.qkv = qkv; a.out = out; a.B = batch; a.N = n_tokens; a.heads = heads;
+    a.has_cls = has_cls ? 1 : 0; a.block_causal = mask == JEPA_MASK_BLOCK_CAUSAL;
+    a.per_slot = tokens_per_slot;
+    return hip_status(launch_attention(act_dtype, a, (hipStream_t)hip_stream), "op_attention");
+}
+
+jepa_status jepa_pack_blocks(int dtype, const uint8_t *blocks, int64_t rows, int64_t cols,
+                             uint8_t *codes, uint16_t *scales) {
+    if (!blocks || !codes || !scales || rows <= 0 || cols <= 0)
+        return fail(JEPA_E_INVALID_ARG, "pack_blocks: bad arguments");
+    if (dtype != JEPA_Q8_0 && dtype != JEPA_Q4_0) return fail(JEPA_E_DTYPE, "pack_blocks: dtype must be Q8_0 or Q4_0");
+    if (cols % 32) return fail(JEPA_E_SHAPE, "pack_blocks: cols not a multiple of 32");
+    pack_blocks(dtype, blocks, rows * (cols / 32), codes, scales);
+    return JEPA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher checks that the
+// shapes fit what its kernel and grid assume and returns hipErrorInvalidValue
+// otherwise; it never launches an out-of-contract grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jepa {
+
+// ---- patchify: uint8 frames -> normalised patch matrix ---------------------
+struct PatchifyArgs {
+    const uint8_t *frames;   // [B, T, H, W, 3]
+    int B, T, H, W, tubelet, patch;
+    float mean[3], std[3];
+    void *out;               // act dtype [B*Np, ld]; columns >= P are zero
+    int64_t ld;              // row pitch in elements (>= P, multiple of 64)
+};
+hipError_t launch_patchify(int act_dt, const PatchifyArgs &a, hipStream_t s);
+
+// ---- LayerNorm: f32 rows -> y in f32 / f16 / bf16 ----------------------------
+hipError_t launch_layernorm(const float *x, int64_t rows, int dim, const float *gamma,
+                            const float *beta, float eps, void *y, int y_dt, hipStream_t s);
+
+// ---- GEMM: out = epilogue(A[M, K] * W[N, K]^T + bias) -----------------------
+enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_PATCH = 3 };
+struct GemmArgs {
+    const void *a;           // act dtype [M, K] row-major, pitch lda elements
+    const void *w;           // dense: act dtype [N, K]; q8_0: int8 codes [N, K];
+                             // q4_0: nibble blocks [N, K/2]
+    const uint16_t *wscale;  // q formats: f16 scales [N, K/32]
+    const float *bias;       // [N]
+    void *out;               // STORE/GELU: act dtype [M, ldo]; RESID/PATCH: f32
+    int64_t M, N, K, lda, ldo;
+    // EPI_PATCH: row r = b*np + n goes to output row b*ntok + has_cls + n and
+    // adds pos[has_cls + n]
+    const float *pos;
+    int np, ntok, has_cls;
+};
+hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
+
+// ---- attention --------------------------------------------------------------
+struct AttnArgs {
+    const void *qkv;         // act dtype [B*N, 3D], columns [q | k | v]
+    void *out;               // act dtype [B*N, D]
+    int B, N, heads, has_cls, block_causal, per_slot;
+};
+hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
+
+// ---- small helpers ----------------------------------------------------------
+// X[b*N + 0] = cls + pos[0] for every item
+hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
+                           hipStream_t s);
+// pooling of a token map y [B, N, D]
+hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipStream_t s);
+hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
+                            hipStream_t s);
+// dequantise packed blocks, or widen f16 / bf16 / f32 storage, into f32 [rows, cols]
+hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
+                          int64_t cols, float *out, hipStream_t s);
+
+}  // namespace jepa

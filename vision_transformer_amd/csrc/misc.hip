@@ -1,0 +1,216 @@
+// The bandwidth-bound kernels of the encoder: patchify (pixel ingest and
+// normalisation), LayerNorm, CLS rows, pooling and dequantisation.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace jepa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// patchify: uint8 frames [B, T, H, W, 3] -> act [B*Np, ld].  Pixel u of
+// channel c becomes (u/255 - mean_c)/std_c; a patch vector lists
+// (dt, dy, dx, c) with c fastest; tokens are slot-major then raster.
+// Columns P..ld-1 are zero (K padding for the patch-embed GEMM).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const PatchifyArgs a, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int p = a.patch, kt = a.tubelet;
+    const int P = kt * p * p * 3;
+    const int64_t row = idx / a.ld;
+    const int k = (int)(idx - row * a.ld);
+    float val = 0.f;
+    if (k < P) {
+        const int Hp = a.H / p, Wp = a.W / p, Tt = a.T / kt;
+        const int64_t np = (int64_t)Tt * Hp * Wp;
+        const int64_t b = row / np;
+        const int n = (int)(row - b * np);
+        const int tt = n / (Hp * Wp), r = n - tt * (Hp * Wp);
+        const int i = r / Wp, j = r - i * Wp;
+        const int c = k % 3;
+        int t2 = k / 3;
+        const int dx = t2 % p;
+        t2 /= p;
+        const int dy = t2 % p, dt = t2 / p;
+        const int64_t pix = ((b * a.T + tt * kt + dt) * a.H + i * p + dy) * (int64_t)a.W + j * p + dx;
+        const float u = (float)a.frames[pix * 3 + c];
+        val = (u / 255.f - a.mean[c]) / a.std[c];
+    }
+    ((T *)a.out)[idx] = from_f32<T>(val);
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm over D = 64*EPL features, one wavefront per row: biased
+// variance, eps inside the square root, f32 statistics.
+// ---------------------------------------------------------------------------
+template <int EPL, typename TO>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x, int64_t rows,
+                                                        const float *__restrict__ gam,
+                                                        const float *__restrict__ bet, float eps,
+                                                        TO *__restrict__ y) {
+    constexpr int D = 64 * EPL;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *xr = x + row * D;
+    float v[EPL];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        v[i] = xr[lane + 64 * i];
+        s += v[i];
+    }
+    const float mean = wave_sum(s) * (1.f / D);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const float c = v[i] - mean;
+        q = fmaf(c, c, q);
+    }
+    const float rs = rsqrtf(wave_sum(q) * (1.f / D) + eps);
+    TO *yr = y + row * D;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int d = lane + 64 * i;
+        yr[d] = from_f32<TO>((v[i] - mean) * rs * gam[d] + bet[d]);
+    }
+}
+
+template <typename TO>
+hipError_t ln_dispatch(const float *x, int64_t rows, int dim, const float *g, const float *b,
+                       float eps, void *y, hipStream_t s) {
+    dim3 grid((unsigned)cdiv(rows, 4));
+#define LN_CASE(E)                                                                         \
+    case E:                                                                                \
+        hipLaunchKernelGGL((layernorm_kernel<E, TO>), grid, dim3(256), 0, s, x, rows, g, b, \
+                           eps, (TO *)y);                                                  \
+        return hipGetLastError();
+    switch (dim / 64) {
+        LN_CASE(2) LN_CASE(3) LN_CASE(4) LN_CASE(6) LN_CASE(8) LN_CASE(12) LN_CASE(16)
+        LN_CASE(20) LN_CASE(24) LN_CASE(32)
+    }
+#undef LN_CASE
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// CLS rows and pooling
+// ---------------------------------------------------------------------------
+__global__ void cls_rows_kernel(float *x, const float *cls, const float *pos, int N, int D) {
+    const int b = blockIdx.x;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) x[(int64_t)b * N * D + d] = cls[d] + pos[d];
+}
+
+__global__ void pool_cls_kernel(const float *y, int N, int D, float *out) {
+    const int b = blockIdx.x;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) out[(int64_t)b * D + d] = y[(int64_t)b * N * D + d];
+}
+
+// Mean over rows first..N-1 of item b; 64 columns x 4 row-phases per block.
+__global__ __launch_bounds__(256) void pool_mean_kernel(const float *y, int N, int D, int first, float *out) {
+    __shared__ float red[256];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int d = blockIdx.y * 64 + (tid & 63), part = tid >> 6;
+    const float *yb = y + (int64_t)b * N * D;
+    float s = 0.f;
+    for (int r = first + part; r < N; r += 4) s += yb[(int64_t)r * D + d];
+    red[tid] = s;
+    __syncthreads();
+    if (tid < 64)
+        out[(int64_t)b * D + d] = (red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]) / (float)(N - first);
+}
+
+// ---------------------------------------------------------------------------
+// dequantisation to f32 (exact: f32(d) * integer code)
+//   q8_0 packed: codes int8 [rows, cols], scales f16 [rows, cols/32]
+//   q4_0 packed: blocks of 16 bytes [rows, cols/32], byte j = code j (low
+//                nibble) | code j+16 (high nibble); scales as q8_0
+// ---------------------------------------------------------------------------
+__global__ void dequant_kernel(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
+                               int64_t cols, float *out) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * cols) return;
+    const int64_t r = idx / cols, c = idx - r * cols;
+    float v;
+    if (w_dt == DT_Q8_0 || w_dt == DT_Q4_0) {
+        const float d = (float)__builtin_bit_cast(_Float16, scale[r * (cols / 32) + c / 32]);
+        int q;
+        if (w_dt == DT_Q8_0) {
+            q = ((const int8_t *)w)[idx];
+        } else {
+            const int e = (int)(c & 31);
+            const uint8_t byte = ((const uint8_t *)w)[r * (cols / 2) + (c / 32) * 16 + (e & 15)];
+            q = (e < 16 ? (byte & 15) : (byte >> 4)) - 8;
+        }
+        v = d * (float)q;
+    } else if (w_dt == DT_F16) {
+        v = to_f32(((const f16_t *)w)[idx]);
+    } else if (w_dt == DT_BF16) {
+        v = to_f32(((const bf16_t *)w)[idx]);
+    } else {
+        v = ((const float *)w)[idx];
+    }
+    out[idx] = v;
+}
+
+}  // namespace
+
+hipError_t launch_patchify(int act_dt, const PatchifyArgs &a, hipStream_t s) {
+    const int P = a.tubelet * a.patch * a.patch * 3;
+    if (a.B <= 0 || a.patch <= 0 || a.tubelet <= 0 || a.H % a.patch || a.W % a.patch ||
+        a.T % a.tubelet || a.ld < P)
+        return hipErrorInvalidValue;
+    const int64_t np = (int64_t)(a.T / a.tubelet) * (a.H / a.patch) * (a.W / a.patch);
+    const int64_t total = (int64_t)a.B * np * a.ld;
+    const dim3 grid((unsigned)cdiv(total, 256));
+    switch (act_dt) {
+        case DT_F32: hipLaunchKernelGGL(patchify_kernel<float>, grid, dim3(256), 0, s, a, total); break;
+        case DT_BF16: hipLaunchKernelGGL(patchify_kernel<bf16_t>, grid, dim3(256), 0, s, a, total); break;
+        case DT_F16: hipLaunchKernelGGL(patchify_kernel<f16_t>, grid, dim3(256), 0, s, a, total); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float *x, int64_t rows, int dim, const float *gamma,
+                            const float *beta, float eps, void *y, int y_dt, hipStream_t s) {
+    if (rows <= 0 || dim % 64) return hipErrorInvalidValue;
+    switch (y_dt) {
+        case DT_F32: return ln_dispatch<float>(x, rows, dim, gamma, beta, eps, y, s);
+        case DT_BF16: return ln_dispatch<bf16_t>(x, rows, dim, gamma, beta, eps, y, s);
+        case DT_F16: return ln_dispatch<f16_t>(x, rows, dim, gamma, beta, eps, y, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
+                           hipStream_t s) {
+    if (B <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cls_rows_kernel, dim3(B), dim3(256), 0, s, x, cls, pos, N, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipStream_t s) {
+    if (B <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pool_cls_kernel, dim3(B), dim3(256), 0, s, y, N, D, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
+                            hipStream_t s) {
+    if (B <= 0 || D % 64 || first >= N) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pool_mean_kernel, dim3(B, D / 64), dim3(256), 0, s, y, N, D, first, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
+                          int64_t cols, float *out, hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return hipErrorInvalidValue;
+    if ((w_dt == DT_Q8_0 || w_dt == DT_Q4_0) && (cols % 32 || !scale)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)cdiv(rows * cols, 256)), dim3(256), 0, s,
+                       w_dt, w, scale, rows, cols, out);
+    return hipGetLastError();
+}
+
+}  // namespace jepa
