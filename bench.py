@@ -74,7 +74,9 @@ def class_bytes(dims: dict, B: int) -> dict:
     D = dims["dim"]
     M = B * synth.n_tokens(dims)
     es = 4 if dims["act_dtype"] == "f32" else 2
-    return {"layernorm": M * D * (4 + es), "final_ln": M * D * 8}
+    npad = -(-synth.n_tokens(dims) // 64) * 64
+    return {"layernorm": M * D * (4 + es), "final_ln": M * D * 8,
+            "transpose_v": M * D * es + B * D * npad * es}
 
 
 # ---------------------------------------------------------------------------
@@ -99,8 +101,10 @@ def cpu_baseline(dims: dict, stored: list, frames: np.ndarray, sample_blocks: in
     per_clip = dt * dims["depth"] / sample_blocks
     N = synth.n_tokens(dims)
     return {"value": N / per_clip, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 clip, {sample_blocks} of {dims['depth']} blocks (float64 numpy oracle), "
-                      f"{dt:.1f} s, scaled x{dims['depth'] / sample_blocks:g} to a whole clip",
+            "sample": (f"1 clip of the batch of {len(frames)}, {sample_blocks} of {dims['depth']} blocks "
+                       f"(float64 numpy oracle), {dt:.1f} s"
+                       + (f", scaled x{dims['depth'] / sample_blocks:g} to a whole clip"
+                          if sample_blocks != dims["depth"] else "")),
             "clips_per_s": 1.0 / per_clip, "load_avg_1min_before": load0,
             "load_avg_1min_after": os.getloadavg()[0]}
 
@@ -118,7 +122,7 @@ def main() -> int:
                     choices=sorted(synth.WORKLOADS))
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=2)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=24)
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel-class times to stderr")
     args = ap.parse_args()
 

@@ -47,14 +47,23 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
                          int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
                          int epilogue, void *out, int64_t ldo, void *hip_stream);
 
+/* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
+ * per head into vt act [batch, heads, 64, npad] (columns >= n_tokens not
+ * written). */
+jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n_tokens,
+                                int heads, void *vt, int64_t npad, void *hip_stream);
+
 /* Multi-head attention, head_dim 64 (LeVJEPA card, opening paragraph, for
- * the block-causal mask).  qkv act [batch*n_tokens, 3*heads*64], columns
- * [q | k | v] head-major -> out act [batch*n_tokens, heads*64].  mask
- * JEPA_MASK_BLOCK_CAUSAL groups the patch tokens (after the optional CLS
- * token 0) in consecutive runs of tokens_per_slot. */
-jepa_status jepa_op_attention(int act_dtype, const void *qkv, int batch, int n_tokens, int heads,
-                              int has_cls, int mask, int tokens_per_slot, void *out,
-                              void *hip_stream);
+ * the block-causal mask).  q and k: act rows of pitch ld_qk elements (token
+ * item*n_tokens + n), q of head h at column h*64, k at column heads*64 +
+ * h*64; v: vt act [batch, heads, 64, npad] as written by jepa_op_transpose_v,
+ * npad = n_tokens rounded up to 64, columns n_tokens..npad-1 finite (zero).
+ * -> out act [batch*n_tokens, heads*64].  mask JEPA_MASK_BLOCK_CAUSAL groups
+ * the patch tokens (after the optional CLS token 0) in consecutive runs of
+ * tokens_per_slot. */
+jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
+                              int64_t npad, int batch, int n_tokens, int heads, int has_cls,
+                              int mask, int tokens_per_slot, void *out, void *hip_stream);
 
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
  * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2

@@ -134,12 +134,25 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
 
 
+def _vt_of(lib, act, qkv_dev, B, N, heads):
+    npad = -(-N // 64) * 64
+    vt = torch.zeros((B, heads, 64, npad), dtype=qkv_dev.dtype, device="cuda")
+    lib.jepa_op_transpose_v(act, qkv_dev, B, N, heads, vt)
+    return vt
+
+
+def _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot):
+    vt = _vt_of(lib, act, qkv_dev, B, N, heads)
+    out = torch.empty((B * N, heads * 64), dtype=qkv_dev.dtype, device="cuda")
+    lib.jepa_op_attention(act, qkv_dev, vt, B, N, heads, has_cls, mask, per_slot, out)
+    return out
+
+
 def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed):
     rng = np.random.default_rng(seed)
     D = heads * 64
     qkv_dev, qkv = rounded(act, rng.standard_normal((B * N, 3 * D)))
-    out = torch.empty((B * N, D), dtype=qkv_dev.dtype, device="cuda")
-    lib.jepa_op_attention(act, qkv_dev, B, N, heads, has_cls, mask, per_slot, out)
+    out = _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot)
     got = out.double().cpu().numpy().reshape(B, N, D)
     if mask == "bidir":
         allowed = None
@@ -188,11 +201,7 @@ def test_attention_block_causal_rows_ignore_future_slots(lib):
     qkv2 = qkv.copy()
     qkv2[1 + 5 * per:, D:] = rng.standard_normal((per, 2 * D))
     b_dev, _ = rounded("bf16", qkv2)
-    outs = []
-    for x in (a_dev, b_dev):
-        o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
-        lib.jepa_op_attention("bf16", x, B, N, heads, True, "block_causal", per, o)
-        outs.append(o.cpu())
+    outs = [_attend(lib, "bf16", x, B, N, heads, True, "block_causal", per).cpu() for x in (a_dev, b_dev)]
     assert torch.equal(outs[0][1:1 + 5 * per], outs[1][1:1 + 5 * per])
     assert not torch.equal(outs[0][0], outs[1][0])          # CLS reads the last slot
 
@@ -205,6 +214,25 @@ def test_kernels_reject_out_of_contract_shapes(lib):
     with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
         lib.jepa_op_gemm("bf16", x, w, "bf16", 64, b, "store", out)      # K % 64 != 0
     q = torch.zeros((10, 3 * 64), dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
     o = torch.zeros((10, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
-        lib.jepa_op_attention("bf16", q, 1, 10, 1, True, "block_causal", 4, o)   # 9 % 4 != 0
+        lib.jepa_op_attention("bf16", q, vt, 1, 10, 1, True, "block_causal", 4, o)   # 9 % 4 != 0
+    vt_short = torch.zeros((1, 1, 64, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
+        lib.jepa_op_attention("bf16", q, vt_short, 1, 10, 1, True, "bidir", 1, o)   # npad < 64
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("B,N,heads", [(2, 3137, 16), (3, 289, 2), (1, 1, 1)])
+def test_transpose_v(lib, act, B, N, heads):
+    if act == "f32" and B * N * heads > 10000:
+        pytest.skip("the f32 path only serves small models")
+    rng = np.random.default_rng(46)
+    D = heads * 64
+    qkv_dev, _ = rounded(act, rng.standard_normal((B * N, 3 * D)))
+    vt = _vt_of(lib, act, qkv_dev, B, N, heads)
+    v = qkv_dev[:, 2 * D:].float().cpu().numpy().reshape(B, N, heads, 64)
+    got = vt.float().cpu().numpy()
+    assert np.array_equal(got[..., :N], v.transpose(0, 2, 3, 1))
+    assert np.all(got[..., N:] == 0)

@@ -71,7 +71,8 @@ def _load():
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
-        "jepa_op_attention": (I, [I, P, I, I, I, I, I, I, P, P]),
+        "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, P, P]),
+        "jepa_op_transpose_v": (I, [I, P, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -230,10 +231,18 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
                              n, _ptr(bias), EPI[epilogue], _ptr(out), out.shape[1], _stream(stream)))
 
 
-def jepa_op_attention(act_dtype: str, qkv, batch: int, n_tokens: int, heads: int, has_cls: bool,
+def jepa_op_attention(act_dtype: str, qk, vt, batch: int, n_tokens: int, heads: int, has_cls: bool,
                       mask: str, tokens_per_slot: int, out, stream=None) -> None:
-    _check(_lib.jepa_op_attention(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, int(has_cls),
-                                  MASK[mask], tokens_per_slot, _ptr(out), _stream(stream)))
+    """qk: [batch*n_tokens, ld] (q | k columns first); vt: [batch, heads, 64, npad]."""
+    _check(_lib.jepa_op_attention(DTYPE[act_dtype], _ptr(qk), qk.shape[1], _ptr(vt), vt.shape[-1],
+                                  batch, n_tokens, heads, int(has_cls), MASK[mask], tokens_per_slot,
+                                  _ptr(out), _stream(stream)))
+
+
+def jepa_op_transpose_v(act_dtype: str, qkv, batch: int, n_tokens: int, heads: int, vt,
+                        stream=None) -> None:
+    _check(_lib.jepa_op_transpose_v(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, _ptr(vt),
+                                    vt.shape[-1], _stream(stream)))
 
 
 def jepa_pack_blocks(dtype: str, blocks: np.ndarray, rows: int, cols: int):

@@ -110,11 +110,11 @@ float stored_to_f32(int dt, const void *data, int64_t i) {
     return NAN;
 }
 
-const char *kClassNames[] = {"patchify",   "gemm_patch", "cls_rows",  "layernorm",
-                             "gemm_qkv",   "attention",  "gemm_out",  "gemm_fc1",
-                             "gemm_fc2",   "final_ln",   "pool"};
-enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_ATTN, K_GEMM_OUT,
-              K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_COUNT };
+const char *kClassNames[] = {"patchify", "gemm_patch", "cls_rows", "layernorm", "gemm_qkv",
+                             "transpose_v", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
+                             "final_ln", "pool"};
+enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_TRANSPOSE_V, K_ATTN,
+              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_COUNT };
 
 struct DevTensor {
     void *ptr = nullptr;        // device data
@@ -138,6 +138,7 @@ struct ProfRec {
 struct jepa_ctx {
     jepa_dims d;
     int D, H, F, L, P, Kp, Np, N, per_slot, act, es;
+    int64_t npad;               // V^T row length: N rounded up to 64
     void *arena = nullptr;
     size_t arena_bytes = 0, model_bytes = 0;
     DevTensor wpe;
@@ -149,7 +150,7 @@ struct jepa_ctx {
     size_t ws_bytes = 0;
     int ws_batch = 0;
     uint8_t *w_frames = nullptr;
-    void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_u = nullptr;
+    void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_vt = nullptr, *w_o = nullptr, *w_u = nullptr;
     float *w_x = nullptr, *w_y = nullptr;
     // last encode
     const float *last_tokens = nullptr;
@@ -169,7 +170,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t frames, patch, x, hn, qkv, o, u, y, total;
+    size_t frames, patch, x, hn, qkv, vt, o, u, y, total;
 };
 
 WsLayout ws_layout(const jepa_ctx *c, int B) {
@@ -182,6 +183,7 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
     w.x = take(M * c->D * 4);
     w.hn = take(M * c->D * c->es);
     w.qkv = take(M * 3 * c->D * c->es);
+    w.vt = take((size_t)B * c->D * c->npad * c->es);
     w.o = take(M * c->D * c->es);
     w.u = take(M * c->F * c->es);
     w.y = take(M * c->D * 4);
@@ -213,6 +215,10 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
     c->w_x = (float *)(base + w.x);
     c->w_hn = base + w.hn;
     c->w_qkv = base + w.qkv;
+    c->w_vt = base + w.vt;
+    // columns N..npad-1 of V^T are read (and multiplied by zero weights) by
+    // the last key tile of each head: keep them finite
+    HIP_TRY(hipMemset(c->w_vt, 0, (size_t)B * c->D * c->npad * c->es));
     c->w_o = base + w.o;
     c->w_u = base + w.u;
     c->w_y = (float *)(base + w.y);
@@ -350,8 +356,6 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     const int D = d.dim, F = d.mlp_dim;
     const int Tt = d.frames / d.tubelet, Hp = d.img_h / d.patch, Wp = d.img_w / d.patch;
     const int Np = Tt * Hp * Wp, N = Np + d.has_cls, P = d.tubelet * d.patch * d.patch * 3;
-    if (d.mask == JEPA_MASK_BLOCK_CAUSAL && d.has_cls && N > 15360)
-        return fail(JEPA_E_UNSUPPORTED, "create: block-causal with CLS supports N <= 15360 (N = %d)", N);
 
     // expected schema
     std::map<std::string, Expect> want;
@@ -414,6 +418,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     const int bk = 128 / c->es;
     c->Kp = (P + bk - 1) / bk * bk;
     c->Np = Np; c->N = N; c->per_slot = Hp * Wp;
+    c->npad = (N + 63) / 64 * 64;
     c->model_bytes = model_bytes;
 
     // device layout of every tensor: block matrices keep their format (codes
@@ -577,13 +582,17 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
         TRY(launch(c, K_CLS_ROWS, s, [&] { return launch_cls_rows(c->w_x, c->cls, c->pos, batch, c->N, c->D, s); }));
 
     AttnArgs aa{};
-    aa.qkv = c->w_qkv; aa.out = c->w_o; aa.B = batch; aa.N = c->N; aa.heads = c->H;
+    aa.qk = c->w_qkv; aa.ld_qk = 3 * c->D; aa.vt = c->w_vt; aa.npad = c->npad;
+    aa.out = c->w_o; aa.B = batch; aa.N = c->N; aa.heads = c->H;
     aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
     const int D = c->D;
     for (int i = 0; i < c->L; ++i) {
         const Layer &L = c->layers[i];
         TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, L.ln1g, L.ln1b, d.ln_eps, c->w_hn, c->act, s); }));
         TRY(gemm(c, K_GEMM_QKV, s, c->w_hn, M, D, L.qkv, L.bqkv, EPI_STORE, c->w_qkv, 3 * D));
+        TRY(launch(c, K_TRANSPOSE_V, s, [&] {
+            return launch_transpose_v(c->act, c->w_qkv, batch, c->N, c->H, c->w_vt, c->npad, s);
+        }));
         TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
         TRY(gemm(c, K_GEMM_OUT, s, c->w_o, M, D, L.out, L.bout, EPI_RESID, c->w_x, D));
         TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, L.ln2g, L.ln2b, d.ln_eps, c->w_hn, c->act, s); }));
@@ -745,18 +754,27 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
     return hip_status(launch_gemm(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm");
 }
 
-jepa_status jepa_op_attention(int act_dtype, const void *qkv, int batch, int n_tokens, int heads,
-                              int has_cls, int mask, int tokens_per_slot, void *out,
-                              void *hip_stream) {
-    if (!qkv || !out) return fail(JEPA_E_INVALID_ARG, "op_attention: null argument");
+jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
+                              int64_t npad, int batch, int n_tokens, int heads, int has_cls,
+                              int mask, int tokens_per_slot, void *out, void *hip_stream) {
+    if (!qk || !vt || !out) return fail(JEPA_E_INVALID_ARG, "op_attention: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_attention: bad act dtype");
     if (mask != JEPA_MASK_BIDIR && mask != JEPA_MASK_BLOCK_CAUSAL)
         return fail(JEPA_E_INVALID_ARG, "op_attention: unknown mask %d", mask);
     AttnArgs a{};
-    a.qkv = qkv; a.out = out; a.B = batch; a.N = n_tokens; a.heads = heads;
+    a.qk = qk; a.ld_qk = ld_qk; a.vt = vt; a.npad = npad;
+    a.out = out; a.B = batch; a.N = n_tokens; a.heads = heads;
     a.has_cls = has_cls ? 1 : 0; a.block_causal = mask == JEPA_MASK_BLOCK_CAUSAL;
     a.per_slot = tokens_per_slot;
     return hip_status(launch_attention(act_dtype, a, (hipStream_t)hip_stream), "op_attention");
+}
+
+jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n_tokens,
+                                int heads, void *vt, int64_t npad, void *hip_stream) {
+    if (!qkv || !vt) return fail(JEPA_E_INVALID_ARG, "op_transpose_v: null argument");
+    if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_transpose_v: bad act dtype");
+    return hip_status(launch_transpose_v(act_dtype, qkv, batch, n_tokens, heads, vt, npad,
+                                         (hipStream_t)hip_stream), "op_transpose_v");
 }
 
 jepa_status jepa_pack_blocks(int dtype, const uint8_t *blocks, int64_t rows, int64_t cols,

@@ -1,23 +1,26 @@
 // Multi-head attention, head_dim 64, bidirectional or block-causal, as a
 // flash-attention forward on MFMA: K and V tiles of 64 keys are staged in
-// LDS, scores and probabilities stay in registers, softmax is online.
+// LDS (double buffered, the next tile's loads in flight during the current
+// tile's MFMAs), scores and probabilities stay in registers, softmax is
+// online.
 //
 // Mask (LeVJEPA ViT-L/16 card, opening paragraph): under block-causal a
 // patch token of temporal slot t attends to the patch tokens of slots <= t
 // and not to CLS; CLS attends to every token.  With CLS as token 0 and
 // tokens ordered slot by slot, every query's allowed keys form one range
 // [lo, hi): lo = 1 (skip CLS) and hi = end of the query's slot.  Key tiles
-// past the largest hi of a query tile are never visited (whole future-frame
-// tiles skipped); a tile that straddles some query's hi masks elementwise.
-// The CLS query of a block-causal item reads all N keys, so it runs in a
-// separate small kernel rather than stretching the first query tile.
+// (aligned to multiples of 64) past the largest hi of a query tile are never
+// visited, i.e. whole future-frame tiles are skipped; tiles that straddle a
+// query's lo or hi mask elementwise.  The CLS query of a block-causal item
+// reads all N keys: it rides along as an extra query slot (index N) of the
+// last query tile, which visits every key anyway, with range [0, N).
 //
-// Layout trick: each wave computes S^T = K Q^T (32 keys x 32 queries per
-// MFMA), so lane l owns query l % 32 and holds 16 of its scores.  Those
-// scores, exponentiated, are exactly the B operand of O^T = V^T P^T, so P
-// never leaves registers.  V is written to LDS transposed, with the keys of
-// each 32-key block permuted so that every lane's A operand is one
-// contiguous LDS read.
+// Layout: each wave computes S^T = K Q^T (32 keys x 32 queries per MFMA), so
+// lane l owns query l % 32 and holds 16 of its scores; exponentiated, they
+// are exactly the B operand of O^T = V^T P^T, so P never leaves registers.
+// The A operand of that product is V^T, which the qkv GEMM writes once per
+// head ([B, H, 64, npad]); a lane's 8 keys of one operand are two runs of 4
+// consecutive keys, i.e. two 8-byte LDS reads.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,41 +31,36 @@ constexpr int DH = 64;      // head dim
 constexpr int QT = 128;     // queries per workgroup (4 waves x 32)
 constexpr int KT = 64;      // keys per step
 
-// LDS column of key r (0..63 within a tile) in the transposed V tile: the
-// k-slot that the P^T operand gives to that key.  Accumulator element v of
-// lane group g holds key 8*(v/4) + 4*g + v%4 of its 32-key block; operand
-// chunk c, slot j of group g takes element v = c*VEC + j.
-template <int VEC, int KC>
-__device__ __forceinline__ int vt_col(int r) {
-    const int sb = r >> 5, kap = r & 31;
-    const int g = (kap >> 2) & 1;
-    const int v = 4 * (kap >> 3) + (kap & 3);
-    return sb * 32 + (v / VEC) * KC + g * VEC + (v % VEC);
-}
-
 template <typename T>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     constexpr int ES = sizeof(T);
     constexpr int VEC = MM::VEC, KC = MM::KC;
     constexpr int CE = 16 / ES;                 // elements per 16-byte chunk
-    constexpr int KROWB = DH * ES + 16;         // K tile row bytes (padded)
-    constexpr int VROWB = KT * ES + 16;         // V^T tile row bytes (padded)
-    __shared__ __attribute__((aligned(16))) unsigned char sK[KT * KROWB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[DH * VROWB];
+    constexpr int ROWB = 64 * ES + 16;          // LDS row bytes (64 elements + pad)
+    constexpr int TILEB = 64 * ROWB;
+    constexpr int CHUNKS = 64 * 64 / CE / 256;  // 16-byte chunks per thread per operand
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][TILEB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-    const int b = blockIdx.z, h = blockIdx.y;
-    const int tile = a.block_causal ? (n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    // grid (head, item, query tile): with the head fastest, all query tiles of
+    // one (item, head) land on the same XCD under round-robin dispatch (when
+    // heads is a multiple of 8) and share its L2; block-causal tiles go
+    // heaviest (latest slot) first
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tile = a.block_causal ? (n_qtiles - 1 - (int)blockIdx.z) : (int)blockIdx.z;
     const int N = a.N, D = a.heads * DH;
-    const int64_t ld = 3 * (int64_t)D;
-    const T *base = (const T *)a.qkv + (int64_t)b * N * ld;
+    const T *qk = (const T *)a.qk + (int64_t)b * N * a.ld_qk;
+    const T *vt = (const T *)a.vt + ((int64_t)b * a.heads + h) * DH * a.npad;
     const int q0 = q_start + tile * QT;
     const int qi = q0 + wave * 32 + (lane & 31);
-    const bool qvalid = qi < N;
-
-    // allowed key range of a query (see header)
+    // allowed key range of a query (see header); slot N is the CLS query
     const int lo = (a.block_causal && a.has_cls) ? 1 : 0;
+    const bool cls_lane = lo && qi == N;
+    const bool qvalid = qi < N || cls_lane;
+    const int qrow = cls_lane ? 0 : qi;
+    const int my_lo = cls_lane ? 0 : lo;
     auto hi_of = [&](int q) -> int {
         if (!a.block_causal || q >= N) return N;
         const int h_ = a.has_cls + a.per_slot * ((q - a.has_cls) / a.per_slot + 1);
@@ -78,10 +76,34 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 #pragma unroll
     for (int c = 0; c < DH / KC; ++c) {
         if (qvalid)
-            qv[c] = MM::load(base + (int64_t)qi * ld + h * DH + c * KC + g * VEC);
+            qv[c] = MM::load(qk + (int64_t)qrow * a.ld_qk + h * DH + c * KC + g * VEC);
         else
             qv[c] = typename MM::vec{};
     }
+
+    // ---- K / V^T tile staging: registers -> LDS ----
+    uint4 kreg[CHUNKS], vreg[CHUNKS];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int ci = tid + 256 * i;
+            const int r = ci / (64 / CE), c = ci % (64 / CE);
+            const int key = k0 + r;
+            kreg[i] = make_uint4(0, 0, 0, 0);
+            if (key < N) kreg[i] = *(const uint4 *)(qk + (int64_t)key * a.ld_qk + D + h * DH + c * CE);
+            // V^T row r (= dim d), keys k0 + c*CE .. ; npad covers the tile
+            vreg[i] = *(const uint4 *)(vt + (int64_t)r * a.npad + k0 + c * CE);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int ci = tid + 256 * i;
+            const int r = ci / (64 / CE), c = ci % (64 / CE);
+            *(uint4 *)(sK[buf] + r * ROWB + c * 16) = kreg[i];
+            *(uint4 *)(sV[buf] + r * ROWB + c * 16) = vreg[i];
+        }
+    };
 
     const float sl2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
     float m = -INFINITY, l = 0.f;
@@ -89,28 +111,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
 
-    for (int k0 = lo; k0 < kend; k0 += KT) {
-        __syncthreads();
-        // stage K (row-major) and V (transposed, permuted) for keys k0..k0+63
-        constexpr int CHUNKS = KT * DH / CE / 256;
-#pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
-            const int ci = tid + 256 * i;
-            const int r = ci / (DH / CE), c = ci % (DH / CE);
-            const int key = k0 + r;
-            uint4 kc = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
-            if (key < N) {
-                const T *row = base + (int64_t)key * ld + h * DH + c * CE;
-                kc = *(const uint4 *)(row + D);
-                vc = *(const uint4 *)(row + 2 * D);
-            }
-            *(uint4 *)(sK + r * KROWB + c * 16) = kc;
-            const T *ve = (const T *)&vc;
-            const int col = vt_col<VEC, KC>(r);
-#pragma unroll
-            for (int e = 0; e < CE; ++e) *(T *)(sV + (c * CE + e) * VROWB + col * ES) = ve[e];
-        }
-        __syncthreads();
+    const int kbeg = lo & ~(KT - 1);
+    load_tile(kbeg);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += KT, buf ^= 1) {
+        const bool more = k0 + KT < kend;
+        if (more) load_tile(k0 + KT);
+        const unsigned char *kb = sK[buf];
+        const unsigned char *vb = sV[buf];
 
         // S^T for the two 32-key blocks
         f32x16 s[2];
@@ -120,17 +130,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
             for (int c = 0; c < DH / KC; ++c) {
-                typename MM::vec kv = MM::load(sK + (sb * 32 + (lane & 31)) * KROWB + (c * KC + g * VEC) * ES);
+                typename MM::vec kv = MM::load(kb + (sb * 32 + (lane & 31)) * ROWB + (c * KC + g * VEC) * ES);
                 s[sb] = MM::mma(kv, qv[c], s[sb]);
             }
         }
-        if (k0 + KT > hi_min) {
+        if (k0 < lo || k0 + KT > hi_min) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = k0 + sb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-                    if (key >= my_hi) s[sb][v] = -INFINITY;
+                    if (key < my_lo || key >= my_hi) s[sb][v] = -INFINITY;
                 }
         }
         // online softmax (row = this lane's query; its other half is lane ^ 32)
@@ -141,21 +151,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
             for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[sb][v]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float mn = fmaxf(m, mt);
-        const float alpha = exp2f((m - mn) * sl2);
-        const float mb = mn * sl2;
-        m = mn;
-        l *= alpha;
+        if (__any(mn > m)) {          // rescale only when some running max grew
+            const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
+            l *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+            for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+            m = mn;
+        }
+        const float mb = m * sl2;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(fmaf(s[sb][v], sl2, -mb));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
                 s[sb][v] = p;
                 l += p;
             }
-        // O^T += V^T P^T
+        // O^T += V^T P^T: operand chunk cc, slot j of lane group g is key
+        // 8*(v/4) + 4*g + v%4 of the 32-key block, v = cc*VEC + j
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
@@ -166,18 +179,29 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
                 typename MM::vec pb = pack_operand<T>(pv);
 #pragma unroll
                 for (int db = 0; db < 2; ++db) {
-                    typename MM::vec va = MM::load(sV + (db * 32 + (lane & 31)) * VROWB +
-                                                   (sb * 32 + cc * KC + g * VEC) * ES);
+                    const unsigned char *row = vb + (db * 32 + (lane & 31)) * ROWB;
+                    typename MM::vec va;
+                    if constexpr (VEC == 8) {
+                        const int k = sb * 32 + 16 * cc + 4 * g;
+                        const uint2 lo4 = *(const uint2 *)(row + k * ES);
+                        const uint2 hi4 = *(const uint2 *)(row + (k + 8) * ES);
+                        va = __builtin_bit_cast(typename MM::vec, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                    } else {
+                        const int k = sb * 32 + 8 * (cc >> 2) + 4 * g + (cc & 3);
+                        va = MM::load(row + k * ES);
+                    }
                     o[db] = MM::mma(va, pb, o[db]);
                 }
             }
         }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
     l += __shfl_xor(l, 32, 64);
     if (!qvalid) return;
     const float inv = 1.f / l;
-    T *out = (T *)a.out + ((int64_t)b * N + qi) * D + h * DH;
+    T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -185,77 +209,214 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
 }
 
-// The CLS query of a block-causal item: one workgroup per (head, item),
-// scores for all N keys in LDS, then the weighted sum of V.
+// 16-bit variant: K and V^T tiles go global -> LDS directly
+// (global_load_lds_dwordx4, lane i of a wave instruction lands at base + 16 i)
+// into unpadded 128-byte rows whose 16-byte chunks are XOR-swizzled (chunk c
+// of row r in slot c ^ swz(r)), two stages.  Each step reads all of its
+// tile's MFMA operands out of LDS into registers first and only then issues
+// the next tile's loads, so no LDS read follows a load in flight: the loads
+// overlap the step's whole MFMA + softmax time.  No staging registers for
+// the loads, no LDS write instructions.
+__device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
+
 template <typename T>
-__global__ __launch_bounds__(256) void attn_cls_kernel(const AttnArgs a) {
-    extern __shared__ float sc[];                 // [N] scores, then probabilities
-    __shared__ float qs[DH];
-    __shared__ float red[256];
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
+    typedef Mfma<T> MM;
+    typedef typename MM::vec vec;
+    static_assert(sizeof(T) == 2, "16-bit operands");
+    constexpr int TB = 64 * 128;                 // bytes of one 64 x 64 tile
+    __shared__ __attribute__((aligned(1024))) unsigned char sK[2][TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV[2][TB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int h = blockIdx.x, b = blockIdx.y;
+    const int tile = a.block_causal ? (n_qtiles - 1 - (int)blockIdx.z) : (int)blockIdx.z;
     const int N = a.N, D = a.heads * DH;
-    const int64_t ld = 3 * (int64_t)D;
-    const T *base = (const T *)a.qkv + (int64_t)b * N * ld;
-    if (tid < DH) qs[tid] = to_f32(base[h * DH + tid]);
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int j = tid; j < N; j += 256) {
-        const T *k = base + (int64_t)j * ld + D + h * DH;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < DH; ++d) acc = fmaf(qs[d], to_f32(k[d]), acc);
-        acc *= 0.125f;
-        sc[j] = acc;
-        mx = fmaxf(mx, acc);
+    const T *qk = (const T *)a.qk + (int64_t)b * N * a.ld_qk;
+    const T *vt = (const T *)a.vt + ((int64_t)b * a.heads + h) * DH * a.npad;
+    const int q0 = q_start + tile * QT;
+    const int qi = q0 + wave * 32 + (lane & 31);
+    // allowed key range of a query (see header); slot N is the CLS query
+    const int lo = (a.block_causal && a.has_cls) ? 1 : 0;
+    const bool cls_lane = lo && qi == N;
+    const bool qvalid = qi < N || cls_lane;
+    const int qrow = cls_lane ? 0 : qi;
+    const int my_lo = cls_lane ? 0 : lo;
+    auto hi_of = [&](int q) -> int {
+        if (!a.block_causal || q >= N) return N;
+        const int h_ = a.has_cls + a.per_slot * ((q - a.has_cls) / a.per_slot + 1);
+        return h_ < N ? h_ : N;
+    };
+    const int my_hi = hi_of(qi);
+    const int tile_last = (q0 + QT - 1 < N - 1) ? q0 + QT - 1 : N - 1;
+    const int kend = hi_of(tile_last);
+    const int hi_min = hi_of(q0);
+    const int kbeg = lo & ~(KT - 1);
+    const int ntiles = (kend - kbeg + KT - 1) / KT;
+
+    vec qv[DH / 16];
+#pragma unroll
+    for (int c = 0; c < DH / 16; ++c)
+        qv[c] = qvalid ? MM::load(qk + (int64_t)qrow * a.ld_qk + h * DH + c * 16 + g * 8) : vec{};
+
+    // this thread's two chunks of each tile: chunk id ci = i*256 + tid, row
+    // ci >> 3, slot ci & 7 holding global chunk slot ^ swz(row)
+    int krow[2], kcol[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ci = i * 256 + tid, r = ci >> 3;
+        krow[i] = r;
+        kcol[i] = ((ci & 7) ^ aswz(r)) * 8;      // element offset of the chunk
     }
-    red[tid] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-        __syncthreads();
+    auto issue = [&](int t, int st) {
+        const int k0 = kbeg + t * KT;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int base = (i * 256 + wave * 64) * 16;  // LDS byte offset of lane 0
+            int key = k0 + krow[i];
+            key = key < N ? key : N - 1;                  // past N: a valid row, masked later
+            __builtin_amdgcn_global_load_lds((const void *)(qk + (int64_t)key * a.ld_qk + D + h * DH + kcol[i]),
+                (__attribute__((address_space(3))) void *)(sK[st] + base), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vt + (int64_t)krow[i] * a.npad + k0 + kcol[i]),
+                (__attribute__((address_space(3))) void *)(sV[st] + base), 16, 0, 0);
+        }
+    };
+
+    const float sl2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
+
+    const int r0 = lane & 31;
+    const int sw[2] = {aswz(r0), aswz(32 + r0)};
+
+    issue(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int st = t & 1;
+        __builtin_amdgcn_s_waitcnt(0xF70);     // vmcnt(0): this wave's loads of tile t landed
+        __builtin_amdgcn_s_barrier();           // everyone's did; everyone is done with stage st^1
+        // all MFMA operands of tile t, LDS -> registers
+        vec kf[2][DH / 16], vf[2][2][2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int c = 0; c < DH / 16; ++c)
+                kf[sb][c] = MM::load(sK[st] + (sb * 32 + r0) * 128 + (((2 * c + g) ^ sw[sb]) << 4));
+        // V^T operand chunk cc of key block sb, dim block db: keys 16*cc +
+        // 8*(j/4) + 4*g + j%4 of the block, i.e. two 8-byte reads
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int ch = 4 * sb + 2 * cc;
+                    const unsigned char *rp = sV[st] + (db * 32 + r0) * 128 + 8 * g;
+                    const uint2 lo4 = *(const uint2 *)(rp + ((ch ^ sw[db]) << 4));
+                    const uint2 hi4 = *(const uint2 *)(rp + (((ch + 1) ^ sw[db]) << 4));
+                    vf[db][sb][cc] = __builtin_bit_cast(vec, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                }
+        if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+
+        const int k0 = kbeg + t * KT;
+        f32x16 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
+#pragma unroll
+            for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[sb][c], qv[c], s[sb]);
+        }
+        if (k0 < lo || k0 + KT > hi_min) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = k0 + sb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+                    if (key < my_lo || key >= my_hi) s[sb][v] = -INFINITY;
+                }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[sb][v]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m, mt);
+        if (__any(mn > m)) {                 // rescale only when some running max grew
+            const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
+            l *= alpha;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+            m = mn;
+        }
+        const float mb = m * sl2;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
+                s[sb][v] = p;
+                l += p;
+            }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                float pv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pv[j] = s[sb][cc * 8 + j];
+                const vec pb = pack_operand<T>(pv);
+#pragma unroll
+                for (int db = 0; db < 2; ++db) o[db] = MM::mma(vf[db][sb][cc], pb, o[db]);
+            }
     }
-    mx = red[0];
-    __syncthreads();
-    float sum = 0.f;
-    for (int j = tid; j < N; j += 256) {
-        const float p = expf(sc[j] - mx);
-        sc[j] = p;
-        sum += p;
+
+    l += __shfl_xor(l, 32, 64);
+    if (!qvalid) return;
+    const float inv = 1.f / l;
+    T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
+}
+
+// v columns of qkv [B*N, 3D] -> vt [B, H, 64, npad] (columns >= N untouched)
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T *qkv, int N, int heads, T *vt,
+                                                          int64_t npad) {
+    __shared__ T tile[64][65];
+    const int b = blockIdx.z, h = blockIdx.y, n0 = blockIdx.x * 64;
+    const int D = heads * DH;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) {
+        const int n = n0 + r;
+        if (n < N) tile[r][tx] = qkv[((int64_t)b * N + n) * 3 * D + 2 * D + h * DH + tx];
     }
-    red[tid] = sum;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] += red[tid + s];
-        __syncthreads();
-    }
-    sum = red[0];
-    __syncthreads();
-    const int d = tid & 63, part = tid >> 6;
-    float acc = 0.f;
-    for (int j = part; j < N; j += 4) acc = fmaf(sc[j], to_f32(base[(int64_t)j * ld + 2 * D + h * DH + d]), acc);
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < DH) {
-        const float o = (red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]) / sum;
-        ((T *)a.out)[(int64_t)b * N * D + h * DH + tid] = from_f32<T>(o);
+    for (int d = ty; d < 64; d += 4) {
+        const int n = n0 + tx;
+        if (n < N) vt[(((int64_t)b * heads + h) * DH + d) * npad + n] = tile[tx][d];
     }
 }
 
 template <typename T>
 hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+    // block-causal with CLS: query tiles cover tokens 1..N-1 plus the CLS
+    // slot N, i.e. N slots from 1; otherwise tokens 0..N-1
     const int q_start = (a.block_causal && a.has_cls) ? 1 : 0;
-    const int n_q = a.N - q_start;
-    const int n_qtiles = (int)cdiv(n_q, QT);
+    const int n_qtiles = (int)cdiv(a.N, QT);
     if (n_qtiles > 0) {
-        hipLaunchKernelGGL((attn_kernel<T>), dim3(n_qtiles, a.heads, a.B), dim3(256), 0, s, a,
-                           q_start, n_qtiles);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (q_start) {
-        hipLaunchKernelGGL((attn_cls_kernel<T>), dim3(a.heads, a.B), dim3(256),
-                           (size_t)a.N * sizeof(float), s, a);
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((attn16_kernel<T>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
+                               q_start, n_qtiles);
+        else
+            hipLaunchKernelGGL((attn_kernel<T>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
+                               q_start, n_qtiles);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -263,20 +424,38 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Largest N whose scores fit the CLS kernel's dynamic LDS (kept under 64 KB).
-constexpr int kMaxClsTokens = 15360;
-
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
-    if (a.B <= 0 || a.N <= 0 || a.heads <= 0 || a.heads > 65535 || a.B > 65535)
+    if (a.B <= 0 || a.N <= 0 || a.heads <= 0 || a.heads > 65535 || a.B > 65535 || a.N / QT >= 65535)
         return hipErrorInvalidValue;
+    if (a.npad < cdiv(a.N, 64) * 64 || a.npad % 64) return hipErrorInvalidValue;
+    if (a.ld_qk < 2 * (int64_t)a.heads * DH || a.ld_qk % 8) return hipErrorInvalidValue;
+    if (((uintptr_t)a.qk | (uintptr_t)a.vt) % 16) return hipErrorInvalidValue;
     if (a.block_causal && (a.per_slot <= 0 || (a.N - a.has_cls) % a.per_slot)) return hipErrorInvalidValue;
-    if (a.block_causal && a.has_cls && a.N > kMaxClsTokens) return hipErrorInvalidValue;
     switch (act_dt) {
         case DT_F32: return launch_t<float>(a, s);
         case DT_BF16: return launch_t<bf16_t>(a, s);
         case DT_F16: return launch_t<f16_t>(a, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
+                              int64_t npad, hipStream_t s) {
+    if (B <= 0 || N <= 0 || heads <= 0 || npad < N) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cdiv(N, 64), heads, B);
+    switch (act_dt) {
+        case DT_F32:
+            hipLaunchKernelGGL(transpose_v_kernel<float>, grid, dim3(256), 0, s, (const float *)qkv, N, heads, (float *)vt, npad);
+            break;
+        case DT_BF16:
+            hipLaunchKernelGGL(transpose_v_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)qkv, N, heads, (bf16_t *)vt, npad);
+            break;
+        case DT_F16:
+            hipLaunchKernelGGL(transpose_v_kernel<f16_t>, grid, dim3(256), 0, s, (const f16_t *)qkv, N, heads, (f16_t *)vt, npad);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace jepa

@@ -40,12 +40,21 @@ struct GemmArgs {
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
 // ---- attention --------------------------------------------------------------
+// Q and K: act dtype rows of pitch ld_qk, q of head h at column h*64, k at
+// column D + h*64.  V transposed: vt [B, H, 64, npad], npad = N rounded up to
+// 64, columns N..npad-1 finite (zero).
 struct AttnArgs {
-    const void *qkv;         // act dtype [B*N, 3D], columns [q | k | v]
+    const void *qk;
+    int64_t ld_qk;
+    const void *vt;
+    int64_t npad;
     void *out;               // act dtype [B*N, D]
     int B, N, heads, has_cls, block_causal, per_slot;
 };
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
+// vt <- the v columns of a [B*N, 3D] qkv matrix, transposed per head
+hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
+                              int64_t npad, hipStream_t s);
 
 // ---- small helpers ----------------------------------------------------------
 // X[b*N + 0] = cls + pos[0] for every item
