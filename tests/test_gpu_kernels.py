@@ -118,6 +118,22 @@ def test_gemm_dense(lib, act, epi, mnk):
     assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
 
 
+@pytest.mark.parametrize("variant,N", [("big128", 384), ("big256", 512)])
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 1024])
+@pytest.mark.parametrize("epi", ["store", "gelu", "resid"])
+def test_gemm_large_tile(lib, monkeypatch, variant, N, K, epi):
+    """The 256-row tile kernel pinned by name: K steps of 32 from 2 (shorter
+    than its 4-stage ring) to 32, M = 1300 ending in a ragged tile."""
+    monkeypatch.setenv("JEPA_GEMM_VARIANT", variant)
+    M = 1300
+    say(f"gemm {variant} bf16 {epi} M={M} N={N} K={K}")
+    got, ref, a, w = _gemm_case(lib, "bf16", "dense", epi, M, N, K, 44)
+    acc = 4 * K * 2.0 ** -24 * (np.abs(a) @ np.abs(w).T)
+    out_r = 0.0 if epi == "resid" else OUT_REL["bf16"]
+    err = np.abs(got - ref)
+    assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
+
+
 @pytest.mark.parametrize("wfmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("epi", ["store", "resid"])

@@ -22,6 +22,7 @@
 
 #include <string>
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -95,39 +96,98 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, int64_t row, int64_t
     }
 }
 
-// One 32 x 32 accumulator block of a lane, accumulated transposed (the
-// weights are the MFMA's A operand, the activations its B operand): the lane
-// owns output row `row` and, for v = 4q + r, column col0 + 8q + r.  Each
-// group of 4 consecutive columns is one 8-byte (16-bit out) or 16-byte (f32)
-// access, with the 4 biases from one 16-byte load.  STORE / GELU / RESID.
-template <typename T, int EPI>
-__device__ __forceinline__ void epilogue_block_t(const GemmArgs &g, const f32x16 &acc, int64_t row,
-                                                 int64_t col0) {
-    if (row >= g.M) return;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int64_t col = col0 + 8 * q;
-        if (col >= g.N) continue;
-        const float4 b4 = *(const float4 *)(g.bias + col);
-        float z[4] = {acc[4 * q] + b4.x, acc[4 * q + 1] + b4.y, acc[4 * q + 2] + b4.z, acc[4 * q + 3] + b4.w};
+// Raw buffer resource over the first nbytes at p (gfx9 descriptor word 3):
+// loads past the end return 0 and stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)nbytes, 0x00020000);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// The output stage of one wave's MB_ x NB_ accumulator blocks (STORE / GELU
+// / RESID).  The blocks are accumulated transposed (the weights are the
+// MFMA's A operand): element 4q + r of block (i, j) of lane l is output row
+// 32 i + l % 32, column 32 j + 8 q + 4 (l / 32) + r of the wave's tile.  Each
+// 32-row block is finished in registers (bias, GELU, rounding), written to
+// the wave's LDS scratch, and read back so that consecutive lanes hold
+// consecutive 16 bytes of a row: every global access then covers whole
+// 128-byte lines (32 partial-line writes per row, the register layout's
+// pattern, cost more than the rows' bandwidth).  Scratch rows hold 16-byte
+// chunk c at c ^ (row % min(16, chunks per row)), which spreads the column
+// writes over the banks and keeps the row reads conflict-free.  Outputs go through a buffer resource sized to M rows, so
+// rows past M need no branch.  RESID reads X one block ahead of its writes
+// (issued after the block's staging, to keep one buffer live there), and each
+// element is read and written by one lane only.
+template <typename T, int EPI, int MB_, int NB_>
+__device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
+                                              const float *sb, unsigned char *ls, int64_t row0,
+                                              int64_t col0, int lane) {
+    constexpr int OES = EPI == EPI_RESID ? 4 : (int)sizeof(T);
+    constexpr int RB = 32 * NB_ * OES;           // bytes of one scratch row
+    constexpr int CH = RB / 16;                  // 16-byte chunks per row = lanes per row
+    constexpr int RPI = 64 / CH;                 // rows per read instruction
+    constexpr int NRD = 32 / RPI;                // read instructions per 32-row block
+    constexpr int SWM = (CH < 16 ? CH : 16) - 1; // chunk swizzle mask
+    static_assert(CH <= 64 && 64 % CH == 0, "scratch row shape");
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g.out, (uint32_t)(g.M * g.ldo * OES));
+    const int rl = lane & 31, g32 = lane >> 5;
+    const int rr = lane / CH, rc = lane % CH;     // read side: row in instruction, chunk
+    const uint32_t rowb = (uint32_t)(g.ldo * OES);
+    // global byte offset of (row0 + 32 i + t*RPI + rr, col0 + 16 rc / OES)
+    const uint32_t gbase = (uint32_t)(row0 * g.ldo * OES + col0 * OES) + rr * rowb + rc * 16;
+
+    float4 xv[2][NRD];
+    auto load_x = [&](int i, int bf) {
         if constexpr (EPI == EPI_RESID) {
-            float4 *x = (float4 *)((float *)g.out + row * g.ldo + col);
-            float4 v = *x;
-            v.x += z[0]; v.y += z[1]; v.z += z[2]; v.w += z[3];
-            *x = v;
-        } else {
-            if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) z[r] = gelu_erf<T>(z[r]);
+            for (int t = 0; t < NRD; ++t)
+                xv[bf][t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, gbase + (32 * i + t * RPI) * rowb, 0, 0));
+        }
+    };
+    load_x(0, 0);
+#pragma unroll
+    for (int i = 0; i < MB_; ++i) {
+        __builtin_amdgcn_sched_barrier(0);       // keep the loads where they are issued
+        // stage block row i
+#pragma unroll
+        for (int j = 0; j < NB_; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = 32 * j + 8 * q + 4 * g32;
+                const float4 b = *(const float4 *)(sb + col);
+                float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
+                              acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
+                if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[r] = gelu_erf<T>(z[r]);
+                }
+                const int cb = col * OES;
+                unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
+                if constexpr (OES == 2) {
+                    uint2 pk;
+                    pk.x = (uint32_t)from_f32<T>(z[0]).v | ((uint32_t)from_f32<T>(z[1]).v << 16);
+                    pk.y = (uint32_t)from_f32<T>(z[2]).v | ((uint32_t)from_f32<T>(z[3]).v << 16);
+                    *(uint2 *)dst = pk;
+                } else {
+                    *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
+                }
             }
-            if constexpr (sizeof(T) == 2) {
-                uint2 pk;
-                pk.x = (uint32_t)from_f32<T>(z[0]).v | ((uint32_t)from_f32<T>(z[1]).v << 16);
-                pk.y = (uint32_t)from_f32<T>(z[2]).v | ((uint32_t)from_f32<T>(z[3]).v << 16);
-                *(uint2 *)((T *)g.out + row * g.ldo + col) = pk;
-            } else {
-                *(float4 *)((float *)g.out + row * g.ldo + col) = make_float4(z[0], z[1], z[2], z[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < MB_) load_x(i + 1, (i + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // read back by rows and write whole lines
+#pragma unroll
+        for (int t = 0; t < NRD; ++t) {
+            const int r = t * RPI + rr;
+            float4 v = *(const float4 *)(ls + r * RB + ((rc ^ (r & SWM)) << 4));
+            if constexpr (EPI == EPI_RESID) {
+                const float4 x = xv[i & 1][t];
+                v.x = x.x + v.x; v.y = x.y + v.y; v.z = x.z + v.z; v.w = x.w + v.w;
             }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                   gbase + (32 * i + t * RPI) * rowb, 0, 0);
         }
     }
 }
@@ -141,11 +201,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     constexpr bool DENSE = (WF == DT_F32);  // DT_F32 here tags "dense, act dtype"
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TILEB];
+    __shared__ __attribute__((aligned(16))) float sbias[BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int nk = (int)(g.K / BK);
+
+    // the tile's biases (N is a multiple of 64; columns past N read as 0)
+    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < BN / 4 && n0 + 4 * tid < g.N) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
 
     const unsigned char *A = (const unsigned char *)g.a;
     const unsigned char *W = (const unsigned char *)g.w;
@@ -248,6 +313,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 
     load_global(0);
     store_lds(0);
+    if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
@@ -273,23 +339,25 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     // ---- epilogue: block (i, j) holds rows m0 + wm*64 + i*32 + lane%32 and
     // columns n0 + wn*64 + j*32 + 8*(v/4) + 4*g + v%4 ----
     const int g32 = lane >> 5;
+    if constexpr (EPI == EPI_PATCH) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t row = m0 + wm * 64 + i * 32 + (lane & 31);
+        for (int i = 0; i < 2; ++i) {
+            const int64_t row = m0 + wm * 64 + i * 32 + (lane & 31);
+            if (row >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col0 = n0 + wn * 64 + j * 32 + 4 * g32;
-            if constexpr (EPI == EPI_PATCH) {
-                if (row >= g.M) continue;
+            for (int j = 0; j < 2; ++j) {
+                const int64_t col0 = n0 + wn * 64 + j * 32 + 4 * g32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t col = col0 + 8 * (v >> 2) + (v & 3);
                     if (col < g.N) epilogue<T, EPI>(g, row, col, acc[i][j][v] + g.bias[col]);
                 }
-            } else {
-                epilogue_block_t<T, EPI>(g, acc[i][j], row, col0);
             }
         }
+    } else if (n0 + wn * 64 < g.N) {   // a wave's 64 columns are all in or all out
+        // the loop's last barrier has freed the operand tiles: 8 KB of scratch per wave
+        epilogue_wave<T, EPI, 2, 2>(g, acc, sbias + wn * 64, &smem[0][0][0] + wave * 8192,
+                                    m0 + wm * 64, n0 + wn * 64, lane);
     }
 }
 
@@ -298,33 +366,57 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 // workgroup of 4 waves (2 x 2), each wave 128 x BN/2 (4 x BN/64 blocks of
 // 32 x 32 accumulators, held in AGPRs), one workgroup per CU.
 //
-// K steps of 32 elements flow through a 4-stage LDS ring, filled by direct
-// global -> LDS loads (global_load_lds_dwordx4: lane i of a wave instruction
-// lands at base + 16 i) issued three steps ahead, so memory latency hides
-// behind three steps of MFMAs.  Each step waits for its own stage only
-// (vmcnt), reads all of its MFMA operands into registers, and only then issues
-// the next stage's loads: no LDS read ever follows a load in flight.
+// K steps of 64 elements (128 bytes of every operand row) flow through a
+// ring of NS LDS stages, filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: lane i of a wave instruction lands at base +
+// 16 i) issued NS - 1 steps ahead.  Eight lanes cover one row's 128 bytes, so
+// every L2 request is a whole line: with 64-byte row pieces the L2 request
+// rate, not its bandwidth, capped the loads (measured on MI355X: half the
+// requests at the same bytes and misses as a vendor GEMM).  A step waits for
+// its own stage only, and a stage is refilled only after the barrier that
+// follows every wave's last read of it.
 //
-// LDS rows are 64 bytes with no padding; chunk c (16 bytes) of row r lives in
-// slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3, so the rows one
-// operand read touches per LDS cycle fall in distinct banks.
+// LDS rows are 128 bytes with no padding; 16-byte chunk c of row r lives in
+// slot c ^ swz(r), swz(r) = (r ^ ((r >> 3) & 3)) & 7, so the rows one operand
+// read touches per LDS cycle fall in distinct banks.
 //
 // Tile order: workgroups go to the 8 XCDs round-robin, so ids are remapped to
 // give each XCD a contiguous range of tiles, and within that range GROUP_M
 // M-tiles are swept together across N, for L2 reuse of both operands.
 // ---------------------------------------------------------------------------
 constexpr int BIG_BM = 256;
-constexpr int BIG_BK = 32;               // elements per K step (64 bytes of a row)
-constexpr int BIG_NS = 4;                // LDS stages
+constexpr int BIG_BK = 64;               // elements per K step (128 bytes of a row)
 constexpr int GROUP_M = 4;
 constexpr int N_XCD = 8;
 
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// depends on row bits 0-4 only, so a 32-row MFMA block shares one swizzle
+__device__ __forceinline__ int swz8(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 __device__ __forceinline__ int xcd_remap(int w, int T) {
     const int q = T / N_XCD, r = T % N_XCD;
     const int x = w % N_XCD, local = w / N_XCD;
     return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
+// Instruction order inside one K chunk of MBNB MFMAs: NDS LDS reads, two per
+// slot, behind the first MFMAs, and NVM global -> LDS loads spread evenly over
+// the chunk (one slot = one MFMA and what is issued after it).
+template <int ID, int MBNB, int NDS, int NVM, int I>
+__device__ __forceinline__ void sched_slot() {
+    constexpr int ds = I < NDS / 2 ? 2 : 0;
+    constexpr int vm = (I + 1) * NVM / MBNB - I * NVM / MBNB;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, ID);
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, ID);
+}
+template <int ID, int MBNB, int NDS, int NVM, int... I>
+__device__ __forceinline__ void sched_chunk_seq(std::integer_sequence<int, I...>) {
+    (sched_slot<ID, MBNB, NDS, NVM, I>(), ...);
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <int ID, int MBNB, int NDS, int NVM>
+__device__ __forceinline__ void sched_chunk() {
+    sched_chunk_seq<ID, MBNB, NDS, NVM>(std::make_integer_sequence<int, MBNB>{});
 }
 
 template <typename T, int EPI, int BN>
@@ -333,11 +425,31 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     typedef typename MM::vec vec;
     static_assert(sizeof(T) == 2, "16-bit operands only");
     constexpr int MB = 4, NB = BN / 64;              // 32x32 blocks per wave
-    constexpr int A_BYTES = BIG_BM * 64, B_BYTES = BN * 64, ST = A_BYTES + B_BYTES;
-    constexpr int A_CH = BIG_BM * 4 / 256, B_CH = BN * 4 / 256;   // 16-byte chunks per thread
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[BIG_NS * ST];
+    constexpr int NS = BN == 256 ? 2 : 3;            // stages: 64 KB or 48 KB each
+    constexpr int A_BYTES = BIG_BM * 128, B_BYTES = BN * 128, ST = A_BYTES + B_BYTES;
+    constexpr int A_CH = BIG_BM * 8 / 256, B_CH = BN * 8 / 256;   // 16-byte chunks per thread
+    constexpr int LPS = A_CH + B_CH;                 // loads per thread per stage
+    constexpr int HALF = LPS / 2;
+    constexpr int MBNB = MB * NB, NRD = MB + NB;     // MFMAs and LDS reads per K chunk
+    static_assert(LPS % 2 == 0 && NS * ST + 1024 <= 160 * 1024 - BN * 4, "LDS");
+    static_assert((NS - 1) * LPS < 64, "vmcnt range");
+    static_assert(NRD % 2 == 0 && NRD / 2 <= MBNB && HALF <= MBNB, "chunk schedule");
+    // One array per stage: the compiler gives each its own alias scope, so a
+    // read of one stage needs no wait for loads still landing in another (a
+    // single indexed array makes it wait for every load in flight).
+    __shared__ __attribute__((aligned(1024))) unsigned char lds0[ST];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds1[ST];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds2[NS == 3 ? ST : 1024];
+    __shared__ __attribute__((aligned(16))) float sbias[BN];
+    auto stage = [&](auto S) -> unsigned char * __attribute__((always_inline)) {
+        if constexpr (decltype(S)::value == 0) return lds0;
+        else if constexpr (decltype(S)::value == 1) return lds1;
+        else return lds2;
+    };
+    auto stage_rt = [&](int s) -> unsigned char * __attribute__((always_inline)) { return s == 0 ? lds0 : s == 1 ? lds1 : lds2; };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g32 = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-load bases in SGPRs
     const int wm = wave >> 1, wn = wave & 1;
 
     const int ntiles = tiles_m * tiles_n;
@@ -354,34 +466,37 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     const unsigned char *W = (const unsigned char *)g.w;
 
     // 32-bit byte offsets of this thread's chunks (a K step is a uniform
-    // 64-byte advance).  Chunk id ci = i*256 + tid -> row ci >> 2, slot ci & 3,
-    // which holds global chunk slot ^ swz(row).  Rows past M / N read a
-    // clamped valid row: they only feed outputs that are never stored.
-    uint32_t aoff[A_CH], woff[B_CH];
+    // 128-byte advance).  Load l < A_CH is A chunk ci = l*256 + tid, load
+    // l >= A_CH is W chunk ci = (l - A_CH)*256 + tid; chunk ci -> row ci >> 3,
+    // slot ci & 7, which holds global chunk slot ^ swz(row).  Rows past M / N
+    // read a clamped valid row: they only feed outputs that are never stored.
+    uint32_t off[LPS];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int ci = i * 256 + tid, r = ci >> 2, c = (ci & 3) ^ swz4(r);
-        int64_t m = m0 + r;
-        if (m >= g.M) m = g.M - 1;
-        aoff[i] = (uint32_t)(m * g.lda * 2 + c * 16);
+    for (int l = 0; l < LPS; ++l) {
+        const bool is_a = l < A_CH;
+        const int ci = (is_a ? l : l - A_CH) * 256 + tid, r = ci >> 3, c = (ci & 7) ^ swz8(r);
+        if (is_a) {
+            int64_t m = m0 + r;
+            if (m >= g.M) m = g.M - 1;
+            off[l] = (uint32_t)(m * g.lda * 2 + c * 16);
+        } else {
+            int64_t n = n0 + r;
+            if (n >= g.N) n = g.N - 1;
+            off[l] = (uint32_t)(n * g.K * 2 + c * 16);
+        }
     }
+    // half h of the loads of step kt into stage memory st; a stage's loads go
+    // out in two halves, so that the CU's address unit is never handed more
+    // than it drains while the MFMAs around them run
+    auto issue_half = [&](unsigned char *st, int kt, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int ci = i * 256 + tid, r = ci >> 2, c = (ci & 3) ^ swz4(r);
-        int64_t n = n0 + r;
-        if (n >= g.N) n = g.N - 1;
-        woff[i] = (uint32_t)(n * g.K * 2 + c * 16);
-    }
-    auto issue = [&](int kt) {
-        unsigned char *st = smem + (kt % BIG_NS) * ST;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            __builtin_amdgcn_global_load_lds((const void *)(A + (size_t)kt * 64 + aoff[i]),
-                (__attribute__((address_space(3))) void *)(st + (i * 256 + wave * 64) * 16), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            __builtin_amdgcn_global_load_lds((const void *)(W + (size_t)kt * 64 + woff[i]),
-                (__attribute__((address_space(3))) void *)(st + A_BYTES + (i * 256 + wave * 64) * 16), 16, 0, 0);
+        for (int l = h * HALF; l < (h + 1) * HALF; ++l) {
+            const bool is_a = l < A_CH;
+            __builtin_amdgcn_global_load_lds((const void *)((is_a ? A : W) + (size_t)kt * 128 + off[l]),
+                (__attribute__((address_space(3))) void *)(st + (is_a ? 0 : A_BYTES) +
+                                                           ((is_a ? l : l - A_CH) * 256 + wave * 64) * 16),
+                16, 0, 0);
+        }
     };
 
     f32x16 acc[MB][NB];
@@ -393,74 +508,126 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     // operand rows of this lane (same swizzle for every row of a 32-row block)
-    const int rl = lane & 31, sw = swz4(rl);
+    const int rl = lane & 31, sw = swz8(rl);
     int arow[MB], brow[NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) arow[i] = (wm * 128 + i * 32 + rl) * 64;
+    for (int i = 0; i < MB; ++i) arow[i] = (wm * 128 + i * 32 + rl) * 128;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) brow[j] = A_BYTES + (wn * (BN / 2) + j * 32 + rl) * 64;
+    for (int j = 0; j < NB; ++j) brow[j] = A_BYTES + (wn * (BN / 2) + j * 32 + rl) * 128;
 
-    // Operands move LDS -> registers one K half (16 elements) at a time, two
-    // halves in flight: step kt reads its second half while the MFMAs of its
-    // first half run, then (after one barrier) the first half of step kt+1
-    // while the MFMAs of its second half run.  Before that barrier every wave
-    // has finished reading stage kt and step kt+1 has landed, so the barrier
-    // both publishes stage kt+1 and frees stage kt for the loads of step
-    // kt+NS.
-    vec a[2][MB], b[2][NB];                       // [half buffer][block]
-    auto read_half = [&](int kt, int c, int buf) {
-        const unsigned char *sm = smem + (kt % BIG_NS) * ST;
+    // Operands move LDS -> registers one 16-element K chunk (of 4 per step)
+    // ahead of the MFMAs that use them, in two register sets; the first chunk
+    // of step kt+1 is read, after the step's barrier, while the MFMAs of the
+    // last chunk of step kt run.
+    vec a[2][MB], b[2][NB];                       // [register set][block]
+    auto read_chunk = [&](const unsigned char *sm, int c, int buf) __attribute__((always_inline)) {
         const int slot = ((2 * c + g32) ^ sw) << 4;
 #pragma unroll
         for (int i = 0; i < MB; ++i) a[buf][i] = MM::load(sm + arow[i] + slot);
 #pragma unroll
         for (int j = 0; j < NB; ++j) b[buf][j] = MM::load(sm + brow[j] + slot);
     };
-    auto mma_half = [&](int buf) {
+    auto mma_chunk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 acc[i][j] = MM::mma(b[buf][j], a[buf][i], acc[i][j]);   // transposed
     };
-    // s_waitcnt lgkmcnt(0) with at most n stages of loads still in flight
-    constexpr int LPS = A_CH + B_CH;              // loads per thread per stage
-    auto wait_stages = [&](int n) {
+    // s_waitcnt lgkmcnt(0) with at most n of this thread's loads in flight
+    auto wait_loads = [&](int n) __attribute__((always_inline)) {
         switch (n) {
             case 0: __builtin_amdgcn_s_waitcnt(0x070); break;
-            case 1: __builtin_amdgcn_s_waitcnt(0x070 | (LPS & 15) | ((LPS >> 4) << 14)); break;
-            case 2: __builtin_amdgcn_s_waitcnt(0x070 | ((2 * LPS) & 15) | (((2 * LPS) >> 4) << 14)); break;
-            default: __builtin_amdgcn_s_waitcnt(0x070 | ((3 * LPS) & 15) | (((3 * LPS) >> 4) << 14)); break;
+            case HALF: __builtin_amdgcn_s_waitcnt(0x070 | (HALF & 15) | ((HALF >> 4) << 14)); break;
+            case LPS: __builtin_amdgcn_s_waitcnt(0x070 | (LPS & 15) | ((LPS >> 4) << 14)); break;
+            default: __builtin_amdgcn_s_waitcnt(0x070 | ((LPS + HALF) & 15) | (((LPS + HALF) >> 4) << 14)); break;
         }
     };
-    static_assert(BIG_NS <= 4 && 3 * (A_CH + B_CH) < 64, "wait_stages encodings");
 
+    // Step kt (stage S = kt % NS, a compile-time constant): chunk 0 carries the
+    // second half of step kt+NS-1's loads, chunk 3 (after the barrier that
+    // frees stage S) the first half of step kt+NS's.  At the barrier the loads
+    // allowed in flight are those of the steps after kt+1.
+    auto steady_step = [&](auto S, int kt) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value;
+        unsigned char *cur = stage(S);
+        unsigned char *nxt = stage(std::integral_constant<int, (s + 1) % NS>{});
+        unsigned char *prv = stage(std::integral_constant<int, (s + NS - 1) % NS>{});
+        read_chunk(cur, 1, 1);
+        issue_half(prv, kt + NS - 1, 1);
+        mma_chunk(0);
+        sched_chunk<0, MBNB, NRD, HALF>();
+        read_chunk(cur, 2, 0);
+        mma_chunk(1);
+        sched_chunk<1, MBNB, NRD, 0>();
+        read_chunk(cur, 3, 1);
+        mma_chunk(0);
+        sched_chunk<2, MBNB, NRD, 0>();
+        wait_loads((NS - 2) * LPS);               // step kt+1 landed
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_chunk(nxt, 0, 0);
+        issue_half(cur, kt + NS, 0);
+        mma_chunk(1);
+        sched_chunk<3, MBNB, NRD, HALF>();
+    };
+
+    // the tile's biases, to LDS behind the first stages' loads (N % BN == 0)
+    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < BN / 4) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
+    // prologue: stages 0 .. NS-2 whole, the first half of stage NS-1
 #pragma unroll
-    for (int s0 = 0; s0 < BIG_NS; ++s0)
-        if (s0 < nk) issue(s0);
-    wait_stages(min(BIG_NS - 1, nk - 1));         // step 0 landed
+    for (int s0 = 0; s0 < NS - 1; ++s0)
+        if (s0 < nk) { issue_half(stage_rt(s0), s0, 0); issue_half(stage_rt(s0), s0, 1); }
+    if (NS - 1 < nk) issue_half(stage_rt(NS - 1), NS - 1, 0);
+    if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
+    wait_loads(min(NS - 2, nk - 1) * LPS + (NS - 1 < nk ? HALF : 0));   // step 0 landed
     __builtin_amdgcn_s_barrier();
-    read_half(0, 0, 0);
+    read_chunk(lds0, 0, 0);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        read_half(kt, 1, 1);
-        mma_half(0);
-        if (kt + 1 < nk) {
-            // issued so far: steps <= min(kt+NS-1, nk-1); step kt+1 must land
-            wait_stages(min(BIG_NS - 2, nk - 2 - kt));
-            __builtin_amdgcn_s_barrier();
-            if (kt + BIG_NS < nk) issue(kt + BIG_NS);
-            read_half(kt + 1, 0, 0);
-        }
-        mma_half(1);
+    // Steady steps (a stage to start) in groups of NS, so that every stage is
+    // named at compile time; the loop bodies have no branch around their
+    // operand reads (a join with a path that skipped them makes the compiler
+    // wait for all of them).
+    int kt = 0;
+    for (; kt + 2 * NS - 1 < nk; kt += NS) {
+        steady_step(std::integral_constant<int, 0>{}, kt);
+        steady_step(std::integral_constant<int, 1>{}, kt + 1);
+        if constexpr (NS == 3) steady_step(std::integral_constant<int, 2>{}, kt + 2);
+    }
+    // the remaining steps but the last, with run-time stages (a second set of
+    // compile-time bodies here would exhaust the registers)
+    for (; kt < nk - 1; ++kt) {
+        unsigned char *cur = stage_rt(kt % NS);
+        read_chunk(cur, 1, 1);
+        if (kt + NS - 1 < nk) issue_half(stage_rt((kt + NS - 1) % NS), kt + NS - 1, 1);
+        mma_chunk(0);
+        read_chunk(cur, 2, 0);
+        mma_chunk(1);
+        read_chunk(cur, 3, 1);
+        mma_chunk(0);
+        wait_loads(min(NS - 2, nk - 2 - kt) * LPS);   // step kt+1 landed
+        __builtin_amdgcn_s_barrier();
+        read_chunk(stage_rt((kt + 1) % NS), 0, 0);
+        if (kt + NS < nk) issue_half(cur, kt + NS, 0);
+        mma_chunk(1);
+    }
+    {
+        const unsigned char *cur = stage_rt((nk - 1) % NS);
+        read_chunk(cur, 1, 1);
+        mma_chunk(0);
+        read_chunk(cur, 2, 0);
+        mma_chunk(1);
+        read_chunk(cur, 3, 1);
+        mma_chunk(0);
+        mma_chunk(1);
     }
 
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-            epilogue_block_t<T, EPI>(g, acc[i][j], m0 + wm * 128 + i * 32 + rl,
-                                     n0 + wn * (BN / 2) + j * 32 + 4 * g32);
+    // every wave has read its last operands: stage 0 becomes output scratch
+    static_assert(4 * 64 * BN <= ST, "epilogue scratch");
+    __builtin_amdgcn_s_barrier();
+    epilogue_wave<T, EPI, MB, NB>(g, acc, sbias + wn * (BN / 2), lds0 + wave * (64 * BN), m0 + wm * 128,
+                                  n0 + wn * (BN / 2), lane);
 }
 
 // Variant choice (below); JEPA_GEMM_VARIANT (small | big256 | big128) pins it.
@@ -482,11 +649,10 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
                             g.N * g.K * 2 < (1ll << 32) && cdiv(g.M, BIG_BM) * cdiv(g.N, 128) < (1ll << 31);
         if (big_ok && var == "big256" && g.N % 256 == 0) return launch_big<T, EPI, 256>(g, s);
         if (big_ok && var == "big128") return launch_big<T, EPI, 128>(g, s);
-        // measured on MI355X at the ViT-L shapes (M = 12548): the large tile
-        // wins when K is long (fc2) or N small (out-proj); for K = 1024 with
-        // wide N (qkv, fc1) two 128 x 128 workgroups per CU hide each other's
-        // tile prologue and epilogue better
-        if (big_ok && var.empty() && g.M >= 1024 && (g.K >= 2048 || g.N <= 1024)) {
+        // measured on MI355X at the ViT-L shapes (M = 12548): the 256 x 256
+        // tile is fastest for all four linear layers; below ~1024 rows the
+        // 128 x 128 tile's larger grid fills the chip better
+        if (big_ok && var.empty() && g.M >= 1024) {
             if (g.N % 256 == 0) return launch_big<T, EPI, 256>(g, s);
             return launch_big<T, EPI, 128>(g, s);
         }
@@ -518,7 +684,13 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (g.lda < g.K || (epi != EPI_PATCH && g.ldo < g.N)) return hipErrorInvalidValue;
     if (g.M / BM >= 65535) return hipErrorInvalidValue;
     if (epi == EPI_PATCH && (g.np <= 0 || g.M % g.np || !g.pos)) return hipErrorInvalidValue;
+    // the epilogue addresses the output through a buffer resource with 32-bit
+    // byte offsets (rows up to M + 255 are formed, those past M dropped)
+    if (epi != EPI_PATCH && (g.M + 256) * g.ldo * (epi == EPI_RESID ? 4 : es) >= (1ll << 31))
+        return hipErrorInvalidValue;
     if (32 * g.ldo >= (1ll << 31)) return hipErrorInvalidValue;   // in-block row offsets are 32-bit
+    if (((uintptr_t)g.bias | (uintptr_t)g.out) & 15) return hipErrorInvalidValue;   // 16-byte vectors
+    if (epi != EPI_PATCH && (g.ldo * (epi == EPI_RESID ? 4 : es)) % 16) return hipErrorInvalidValue;
     const bool dense = (w_dt == act_dt);
     if (!dense && (act_dt == DT_F32 || (w_dt != DT_Q8_0 && w_dt != DT_Q4_0) || !g.wscale))
         return hipErrorInvalidValue;
