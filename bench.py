@@ -8,11 +8,18 @@ clip), synthetic seeded frames and N(0, 0.02) weights.
 
 Prints one JSON line: tokens/s (whole job), clips/s, MFMA utilisation of the
 whole forward against the dense bf16/f16 peak, the roofline of the dominant
-kernel (algorithmic work per launch / its HIP-event-timed average duration
-inside the timed region), and the CPU oracle timed on a bounded sample.
+kernel, and the CPU oracle timed on a bounded sample.
+
+Two timed regions of K steps each.  The first gives `value`: the encoder as
+it runs by default (the batch split into concurrent parts, one HIP stream
+each), with no timing events between kernels.  The second gives the
+roofline: the same steps with the batch as one part, HIP events around each
+launch of the dominant kernel class on its stream, so that a launch's
+duration is its own and not shared with another part's kernels; achieved =
+algorithmic work per launch / average launch duration.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--breakdown]
+                       [--parts P] [--no-cpu-baseline] [--breakdown]
 """
 from __future__ import annotations
 
@@ -79,6 +86,31 @@ def class_bytes(dims: dict, B: int) -> dict:
             "transpose_v": M * D * es + B * D * npad * es}
 
 
+def measured_traffic(workload: str, cls: str):
+    """HBM-side bytes per launch of kernel class `cls` from the FETCH_SIZE /
+    WRITE_SIZE summaries under profiles/ (copy-calibrated), or None when none
+    exists or the kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "vision_transformer_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+        for line in open(path):
+            f = line.split()
+            if len(f) != 6 or f[0] != "traffic" or f[1] != workload or f[2] != cls:
+                continue
+            kv = dict(x.split("=", 1) for x in f[3:])
+            h = hashlib.sha256()
+            try:
+                for name in kv["sources"].split(","):
+                    h.update(open(os.path.join(csrc, name), "rb").read())
+            except OSError:
+                return None
+            if h.hexdigest() == kv["sha256"]:
+                return int(kv["bytes"]), os.path.relpath(path, ROOT)
+            return None
+    return None
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle on a bounded sample
 # ---------------------------------------------------------------------------
@@ -113,6 +145,27 @@ def cpu_baseline(dims: dict, stored: list, frames: np.ndarray, sample_blocks: in
 # main
 # ---------------------------------------------------------------------------
 
+def copy_probe(mib: int) -> int:
+    """A plain device-to-device copy of known size: it reads and writes
+    exactly mib MiB per launch, which calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    print(json.dumps({"copy_probe_bytes": n, "ms": round(ms, 4), "GB_per_s_read_plus_write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,10 +174,17 @@ def main() -> int:
     ap.add_argument("--workload", default="levjepa_vit_l16_16f_bf16_b4",
                     choices=sorted(synth.WORKLOADS))
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--parts", type=int, default=0,
+                    help="concurrent batch parts of the throughput region (0 = the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=24)
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel-class times to stderr")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device 5 times (the reference kernel of known "
+                         "traffic that scales the HBM counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the encoder path is built and measured on a single "
@@ -157,8 +217,20 @@ def main() -> int:
         enc.encode(fr, tokens)
         enc.pool(pool_mode, B, pooled)
 
-    # a short profiled pass (not timed) finds the dominant kernel class
+    def timed(nsteps):
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(nsteps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+    # a short profiled pass (not timed), batch as one part, finds the dominant class
     classes = list(_lib.jepa_kernel_stats(enc.ctx).keys())
+    _lib.jepa_set_batch_parts(enc.ctx, 1)
     _lib.jepa_set_profiling(enc.ctx, 0xFFFFFFFF)
     for _ in range(max(1, args.warmup)):
         step()
@@ -175,26 +247,28 @@ def main() -> int:
                 print(f"[bench]   {k:12s} {v['launches']:4d} launches {v['total_ms']:8.3f} ms "
                       f"({100 * v['total_ms'] / tot:5.1f} %)", file=sys.stderr)
     print(f"[bench] dominant kernel class: {dominant}", file=sys.stderr, flush=True)
+    _lib.jepa_set_profiling(enc.ctx, 0)
 
-    # the timed region: events only around the dominant class's launches
-    _lib.jepa_reset_kernel_stats(enc.ctx)
+    # timed region 1: throughput, default concurrency, no events between kernels
+    _lib.jepa_set_batch_parts(enc.ctx, args.parts)
+    for _ in range(args.warmup):
+        step()
+    wall, dev_ms = timed(args.steps)
+    print(f"[bench] throughput region: {1e3 * wall / args.steps:.3f} ms per step", file=sys.stderr, flush=True)
+
+    # timed region 2: roofline of the dominant class, batch as one part
+    _lib.jepa_set_batch_parts(enc.ctx, 1)
     _lib.jepa_set_profiling(enc.ctx, 1 << classes.index(dominant))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     _lib.jepa_reset_kernel_stats(enc.ctx)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dev_ms = ev0.elapsed_time(ev1)
+    wall1, _ = timed(args.steps)
     st = _lib.jepa_kernel_stats(enc.ctx)[dominant]
     _lib.jepa_set_profiling(enc.ctx, 0)
+    _lib.jepa_set_batch_parts(enc.ctx, 0)
+    print(f"[bench] roofline region (one part): {1e3 * wall1 / args.steps:.3f} ms per step", file=sys.stderr,
+          flush=True)
 
     ms_per_step = 1e3 * wall / args.steps
     tok_s = B * N * args.steps / wall
@@ -216,6 +290,12 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                 "work_per_launch": cb[dominant], "avg_launch_ms": round(avg_ms, 5),
                 "launches_timed": st["launches"]}
+    parts = min(args.parts or 4, B)
+    tr = measured_traffic(args.workload, dominant) if B == wl["batch"] else None
+    if tr:
+        roof["traffic"], roof["traffic_source"] = tr
+    roof["batch_parts"] = 1
+    roof["region_ms_per_step"] = round(1e3 * wall1 / args.steps, 4)
 
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -225,7 +305,7 @@ def main() -> int:
         "config": {"workload": args.workload, "batch": B, "tokens_per_clip": N,
                    "frames": dims["frames"], "img": [dims["img_h"], dims["img_w"]],
                    "tubelet": dims["tubelet"], "mask": dims["mask"], "weights": dims["mat_dtype"],
-                   "parallelism": "single GPU"},
+                   "parallelism": f"single GPU, batch in {parts} concurrent parts"},
         "clips_per_s": round(B * args.steps / wall, 2),
         "mfma_util_pct": round(100 * util, 2),
         "forward_tflop": round(flops / 1e12, 4),

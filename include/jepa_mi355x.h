@@ -131,6 +131,18 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
 jepa_status jepa_encode(jepa_ctx *ctx, const uint8_t *frames, int batch, int frames_on_device,
                         float *tokens_out, void *hip_stream);
 
+/* Concurrency of jepa_encode: the batch is split into `parts` contiguous
+ * groups of items, encoded concurrently on the caller's stream and parts-1
+ * internal non-blocking HIP streams (default priority) forked from and
+ * joined back onto the caller's stream, so that the work still starts and
+ * ends in the caller's stream order.  Items never interact, so the
+ * result does not depend on parts; only the overlap of kernels does (one
+ * part's last, partial round of workgroups runs beside another part's
+ * kernels).  parts = 0 restores the default (4, or the JEPA_STREAMS
+ * environment variable); the effective count is min(parts, batch).
+ * JEPA_E_INVALID_ARG unless 0 <= parts <= 4. */
+jepa_status jepa_set_batch_parts(jepa_ctx *ctx, int parts);
+
 /* Pool the token map of the last encode.  out: device f32 [batch, dim] for
  * CLS (token 0; needs has_cls) and MEAN (mean of the patch tokens, CLS
  * excluded), [batch, N, dim] for NONE (a copy of the token map).

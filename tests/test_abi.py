@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) >= 19
+    assert len(names) >= 20
     so = ctypes.CDLL(lib.LIB_PATH)
     for n in names:
         assert hasattr(so, n), n
@@ -129,6 +129,8 @@ def test_null_context_calls_fail_cleanly(lib):
         lib.jepa_encode(None, np.zeros((1, 1, 16, 16, 3), np.uint8), 1)
     with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
         lib.jepa_pool(None, "cls", np.zeros(4, np.float32))
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_set_batch_parts(None, 2)
     assert lib.jepa_last_compute_ms(None) < 0
     assert lib.jepa_model_n_bytes(None) == 0
     lib.jepa_free(None)

@@ -150,6 +150,27 @@ def test_batch_items_independent_bit_exact(Encoder, name):
     enc.close()
 
 
+@pytest.mark.parametrize("name", ["small_blockcausal_bf16", "small_tubelet2_q4_0"])
+def test_batch_parts_do_not_change_tokens(Encoder, name):
+    """The batch runs as concurrent parts (one HIP stream each); items never
+    interact, so 1 to 4 parts give bit-identical tokens (batch 5: ragged
+    parts of 3+2, 2+2+1 and 2+1+1+1 items)."""
+    from vision_transformer_amd import _lib
+    wl, dims, _, stored = H.workload_inputs(name)
+    frames = synth.make_frames(dims, 5, 77)
+    enc = Encoder(dims, stored)
+    ys = []
+    for parts in (1, 2, 3, 4):
+        H.say(f"encoder {name} batch 5 in {parts} parts")
+        _lib.jepa_set_batch_parts(enc.ctx, parts)
+        ys.append(_run(enc, frames).cpu().clone())
+    for y in ys[1:]:
+        assert torch.equal(ys[0], y)
+    with pytest.raises(_lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        _lib.jepa_set_batch_parts(enc.ctx, 5)
+    enc.close()
+
+
 def test_host_frames_match_device_frames(Encoder):
     wl, dims, frames, stored = H.workload_inputs("small_bidir_cls_bf16")
     enc = Encoder(dims, stored)

@@ -66,6 +66,7 @@ def _load():
         "jepa_dequant_tensor": (I, [P, C.c_char_p, P, P]),
         "jepa_quantize": (I, [I, P, I64, I64, P]),
         "jepa_set_profiling": (I, [P, C.c_uint32]),
+        "jepa_set_batch_parts": (I, [P, I]),
         "jepa_kernel_stats": (I, [P, C.POINTER(jepa_kernel_stat), I]),
         "jepa_reset_kernel_stats": (None, [P]),
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
@@ -182,6 +183,11 @@ def jepa_quantize(dtype: str, x: np.ndarray) -> np.ndarray:
     out = np.empty((rows, cols // 32 * bb), np.uint8)
     _check(_lib.jepa_quantize(DTYPE[dtype], x.ctypes.data, rows, cols, out.ctypes.data))
     return out
+
+
+def jepa_set_batch_parts(ctx: int, parts: int) -> None:
+    """Encode the batch as `parts` concurrent groups of items (0 = default)."""
+    _check(_lib.jepa_set_batch_parts(ctx, parts))
 
 
 def jepa_set_profiling(ctx: int, class_mask: int) -> None:

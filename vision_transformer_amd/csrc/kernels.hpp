@@ -61,6 +61,7 @@ hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int hea
 hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
                            hipStream_t s);
 // pooling of a token map y [B, N, D]
+hipError_t launch_copy_f32(const float *y, int64_t n, float *out, hipStream_t s);
 hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipStream_t s);
 hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
                             hipStream_t s);

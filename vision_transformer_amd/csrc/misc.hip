@@ -1,5 +1,7 @@
 // The bandwidth-bound kernels of the encoder: patchify (pixel ingest and
 // normalisation), LayerNorm, CLS rows, pooling and dequantisation.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -188,6 +190,23 @@ hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, 
                            hipStream_t s) {
     if (B <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(cls_rows_kernel, dim3(B), dim3(256), 0, s, x, cls, pos, N, D);
+    return hipGetLastError();
+}
+
+// out[i] = y[i] for n f32 values, 16 bytes per thread where both are aligned
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float *y, int64_t n, float *out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        ((float4 *)out)[i] = ((const float4 *)y)[i];
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = y[i];
+}
+
+hipError_t launch_copy_f32(const float *y, int64_t n, float *out, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (((uintptr_t)y | (uintptr_t)out) & 15) return hipErrorInvalidValue;
+    const int64_t blocks = std::min<int64_t>(cdiv(n / 4 + 1, 256), 4096);
+    hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, y, n, out);
     return hipGetLastError();
 }
 
