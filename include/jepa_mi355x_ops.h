@@ -47,6 +47,19 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
                          int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
                          int epilogue, void *out, int64_t ldo, void *hip_stream);
 
+/* The qkv linear layer (attn_qkv, Quantization page "The rule") with V
+ * written transposed for attention: acc = a[M, K] * w[N, K]^T + bias in
+ * f32, N = 3*heads*64, weights as in jepa_op_gemm.  Columns [0, 2*heads*64)
+ * (q and k) -> qk_out act [M, ld_qk] (ld_qk >= N; columns N - heads*64 .. N-1
+ * of qk_out are not written); columns [2*heads*64, N) (v) -> vt act
+ * [M / n_tokens, heads, 64, npad], row b*n_tokens + n being token n of item
+ * b, each value rounded once to the act dtype.  vt columns n_tokens..npad-1
+ * are not written.  M % n_tokens == 0, npad >= n_tokens. */
+jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
+                             int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
+                             int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
+                             void *hip_stream);
+
 /* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
  * per head into vt act [batch, heads, 64, npad] (columns >= n_tokens not
  * written). */

@@ -122,8 +122,8 @@ def test_gemm_dense(lib, act, epi, mnk):
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 1024])
 @pytest.mark.parametrize("epi", ["store", "gelu", "resid"])
 def test_gemm_large_tile(lib, monkeypatch, variant, N, K, epi):
-    """The 256-row tile kernel pinned by name: K steps of 32 from 2 (shorter
-    than its 4-stage ring) to 32, M = 1300 ending in a ragged tile."""
+    """The 256-row tile kernel pinned by name: K steps of 64 from 1 (fewer
+    than its LDS stages) to 16, M = 1300 ending in a ragged tile."""
     monkeypatch.setenv("JEPA_GEMM_VARIANT", variant)
     M = 1300
     say(f"gemm {variant} bf16 {epi} M={M} N={N} K={K}")
@@ -148,6 +148,51 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     out_r = 0.0 if epi == "resid" else OUT_REL[act]
     err = np.abs(got - ref)
     assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
+
+
+@pytest.mark.parametrize("act,wfmt,B,N,heads,K", [
+    ("bf16", "dense", 7, 197, 4, 256),      # M = 1379: 256-row tiles, items straddling 32-row blocks
+    ("bf16", "dense", 2, 289, 2, 128),      # M = 578: 128-row tiles
+    ("f16", "q8_0", 3, 106, 2, 256),
+    ("bf16", "q4_0", 2, 126, 2, 128),
+    ("f32", "dense", 2, 85, 2, 64),
+    ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
+])
+def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K):
+    """q and k columns as a plain linear layer; v columns straight into V^T
+    [B, heads, 64, npad] (the attention kernel's layout), padding untouched."""
+    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K}")
+    rng = np.random.default_rng(47)
+    M, D = B * N, heads * 64
+    a_dev, a = rounded(act, rng.standard_normal((M, K)))
+    w32 = (rng.standard_normal((3 * D, K)) * 0.05).astype(np.float32)
+    bias = (rng.standard_normal(3 * D) * 0.1).astype(np.float32)
+    scale, wr = None, 0.0
+    if wfmt in ("q8_0", "q4_0"):
+        raw = Q.quantize(wfmt, w32)
+        w = Q.stored_to_f64(dict(dtype=wfmt, ne0=K, ne1=3 * D, data=raw))
+        codes, scales = lib.jepa_pack_blocks(wfmt, raw, 3 * D, K)
+        w_dev = torch.from_numpy(codes).cuda()
+        scale = torch.from_numpy(scales.view(np.int16)).cuda()
+        wr = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}[act]
+    else:
+        w_dev, w = rounded(act, w32)
+    ref = E.linear(a, w, bias.astype(np.float64))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[act]
+    npad = -(-N // 64) * 64
+    qk = torch.zeros((M, 3 * D), dtype=tdt, device="cuda")
+    vt = torch.full((B, heads, 64, npad), 7.0, dtype=tdt, device="cuda")
+    lib.jepa_op_gemm_qkv(act, a_dev, w_dev, wfmt if wfmt != "dense" else act, heads,
+                         torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale)
+    bound = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T) + OUT_REL[act] * np.abs(ref) + 1e-6
+    got_qk = qk.double().cpu().numpy()
+    assert np.all(np.abs(got_qk[:, :2 * D] - ref[:, :2 * D]) <= bound[:, :2 * D])
+    assert np.all(got_qk[:, 2 * D:] == 0)                       # v columns not written
+    got_vt = vt.double().cpu().numpy()
+    want = ref[:, 2 * D:].reshape(B, N, heads, 64).transpose(0, 2, 3, 1)
+    bnd = bound[:, 2 * D:].reshape(B, N, heads, 64).transpose(0, 2, 3, 1)
+    assert np.all(np.abs(got_vt[..., :N] - want) <= bnd)
+    assert np.all(got_vt[..., N:] == 7.0)                        # padding columns untouched
 
 
 def _vt_of(lib, act, qkv_dev, B, N, heads):

@@ -72,6 +72,7 @@ def _load():
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
+        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, P]),
         "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, P, P]),
         "jepa_op_transpose_v": (I, [I, P, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
@@ -235,6 +236,15 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
     M, K = a.shape
     _check(_lib.jepa_op_gemm(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
                              n, _ptr(bias), EPI[epilogue], _ptr(out), out.shape[1], _stream(stream)))
+
+
+def jepa_op_gemm_qkv(act_dtype: str, a, w, w_dtype: str, heads: int, bias, n_tokens: int, qk_out, vt,
+                     w_scale=None, stream=None) -> None:
+    """q, k columns -> qk_out [M, ld]; v columns transposed -> vt [M/n_tokens, heads, 64, npad]."""
+    M, K = a.shape
+    _check(_lib.jepa_op_gemm_qkv(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
+                                 heads, _ptr(bias), n_tokens, _ptr(qk_out), qk_out.shape[1], _ptr(vt),
+                                 vt.shape[-1], _stream(stream)))
 
 
 def jepa_op_attention(act_dtype: str, qk, vt, batch: int, n_tokens: int, heads: int, has_cls: bool,

@@ -659,10 +659,13 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             aa.out = o; aa.B = q.nb; aa.N = c->N; aa.heads = c->H;
             aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
-            TRY(gemm(c, K_GEMM_QKV, s, hn, M, D, L.qkv, L.bqkv, EPI_STORE, qkv, 3 * D));
-            TRY(launch(c, K_TRANSPOSE_V, s, [&] {
-                return launch_transpose_v(c->act, qkv, q.nb, c->N, c->H, vt, c->npad, s);
-            }));
+            {   // q, k to qkv; v transposed straight into V^T
+                GemmArgs g{};
+                g.a = hn; g.w = L.qkv.ptr; g.wscale = L.qkv.scale; g.bias = L.bqkv; g.out = qkv;
+                g.M = M; g.N = L.qkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
+                g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
+                TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, L.qkv.dev_dt, EPI_QKV, g, s); }));
+            }
             TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
             TRY(gemm(c, K_GEMM_OUT, s, o, M, D, L.out, L.bout, EPI_RESID, x, D));
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
@@ -847,6 +850,20 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = out;
     g.M = M; g.N = N; g.K = K; g.lda = K; g.ldo = ldo;
     return hip_status(launch_gemm(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm");
+}
+
+jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
+                             int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
+                             int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
+                             void *hip_stream) {
+    if (!a || !w || !bias || !qk_out || !vt) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: null argument");
+    if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_gemm_qkv: bad act dtype");
+    if (heads <= 0 || n_tokens <= 0) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: heads and n_tokens must be > 0");
+    GemmArgs g{};
+    g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = qk_out;
+    g.M = M; g.N = 3 * (int64_t)heads * 64; g.K = K; g.lda = K; g.ldo = ld_qk;
+    g.ntok = n_tokens; g.vt = vt; g.npad = npad; g.vcol0 = 2 * (int64_t)heads * 64;
+    return hip_status(launch_gemm(act_dtype, w_dtype, EPI_QKV, g, (hipStream_t)hip_stream), "op_gemm_qkv");
 }
 
 jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,

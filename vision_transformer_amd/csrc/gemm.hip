@@ -18,6 +18,7 @@
 //   GELU   out = act(gelu_erf(acc + b))          (fc1)
 //   RESID  X  += acc + b   (f32 residual)        (out-proj, fc2)
 //   PATCH  X[token] = acc + b + pos[token]       (patch-embed, CLS offset)
+//   QKV    q, k columns as STORE; v columns transposed per head into V^T
 #include <stdlib.h>
 
 #include <string>
@@ -105,6 +106,67 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uin
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// The v columns of the qkv product, written transposed: V^T [B, heads, 64,
+// npad] holds, for every head and dim, the item's tokens in a row.  Each
+// 32-row block (32 consecutive tokens, possibly of two items) is finished in
+// registers (bias, rounding) and staged in LDS as in the STORE case, then read
+// back by column: a wave store writes two columns of 32 tokens, i.e. two runs
+// of 64 (2-byte types) or 128 bytes of V^T, one element per lane.  Rows past
+// M fall past the end of V^T, where the buffer resource drops them.
+template <typename T, int MB_, int NB_>
+__device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
+                                                 const float *sb, unsigned char *ls, int64_t row0,
+                                                 int64_t col0, int lane) {
+    constexpr int OES = (int)sizeof(T);
+    constexpr int RB = 32 * NB_ * OES;
+    constexpr int CH = RB / 16;
+    constexpr int SWM = (CH < 16 ? CH : 16) - 1;
+    const int heads = (int)((g.N - g.vcol0) / 64);
+    const int64_t nitems = g.M / g.ntok;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g.vt, (uint32_t)(nitems * heads * 64 * g.npad * OES));
+    const int rl = lane & 31, g32 = lane >> 5;
+    const int64_t dcol0 = col0 - g.vcol0;        // first v column of the wave (multiple of 64)
+#pragma unroll
+    for (int i = 0; i < MB_; ++i) {
+        // stage block row i (bias, rounding), row-major with swizzled chunks
+#pragma unroll
+        for (int j = 0; j < NB_; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = 32 * j + 8 * q + 4 * g32;
+                const float4 b = *(const float4 *)(sb + col);
+                const float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
+                                    acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
+                const int cb = col * OES;
+                unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
+                if constexpr (OES == 2) {
+                    uint2 pk;
+                    pk.x = (uint32_t)from_f32<T>(z[0]).v | ((uint32_t)from_f32<T>(z[1]).v << 16);
+                    pk.y = (uint32_t)from_f32<T>(z[2]).v | ((uint32_t)from_f32<T>(z[3]).v << 16);
+                    *(uint2 *)dst = pk;
+                } else {
+                    *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
+                }
+            }
+        // this lane's token: row row0 + 32 i + rl
+        const uint32_t m = (uint32_t)(row0 + 32 * i + rl);
+        const uint32_t b = m / (uint32_t)g.ntok, n = m - b * (uint32_t)g.ntok;
+        const uint32_t tok = b * (uint32_t)(heads * 64 * g.npad) + n;       // element offset of (b, h=0, d=0, n)
+#pragma unroll
+        for (int t = 0; t < NB_ * 16; ++t) {
+            const int c = 2 * t + g32;                           // column of the wave
+            const int cb = c * OES;
+            const unsigned char *src = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
+            const int64_t dc = dcol0 + c;                        // v column: head dc / 64, dim dc % 64
+            const uint32_t off = (tok + (uint32_t)dc * (uint32_t)g.npad) * OES;
+            if constexpr (OES == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(*(const unsigned short *)src, rs, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(*(const unsigned int *)src, rs, off, 0, 0);
+        }
+    }
+}
+
 // The output stage of one wave's MB_ x NB_ accumulator blocks (STORE / GELU
 // / RESID).  The blocks are accumulated transposed (the weights are the
 // MFMA's A operand): element 4q + r of block (i, j) of lane l is output row
@@ -123,6 +185,13 @@ template <typename T, int EPI, int MB_, int NB_>
 __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
                                               const float *sb, unsigned char *ls, int64_t row0,
                                               int64_t col0, int lane) {
+    if constexpr (EPI == EPI_QKV) {
+        // a wave's columns are all q/k or all v (v starts at a multiple of 128)
+        if (col0 >= g.vcol0) {
+            epilogue_wave_vt<T, MB_, NB_>(g, acc, sb, ls, row0, col0, lane);
+            return;
+        }
+    }
     constexpr int OES = EPI == EPI_RESID ? 4 : (int)sizeof(T);
     constexpr int RB = 32 * NB_ * OES;           // bytes of one scratch row
     constexpr int CH = RB / 16;                  // 16-byte chunks per row = lanes per row
@@ -668,6 +737,7 @@ hipError_t launch_epi(int epi, const GemmArgs &g, hipStream_t s) {
         case EPI_STORE: return launch_t<T, WF, EPI_STORE>(g, s);
         case EPI_GELU: return launch_t<T, WF, EPI_GELU>(g, s);
         case EPI_RESID: return launch_t<T, WF, EPI_RESID>(g, s);
+        case EPI_QKV: return launch_t<T, WF, EPI_QKV>(g, s);
         case EPI_PATCH:
             if constexpr (WF == DT_F32) return launch_t<T, WF, EPI_PATCH>(g, s);
             return hipErrorInvalidValue;
@@ -684,6 +754,13 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (g.lda < g.K || (epi != EPI_PATCH && g.ldo < g.N)) return hipErrorInvalidValue;
     if (g.M / BM >= 65535) return hipErrorInvalidValue;
     if (epi == EPI_PATCH && (g.np <= 0 || g.M % g.np || !g.pos)) return hipErrorInvalidValue;
+    if (epi == EPI_QKV) {
+        // v starts at a multiple of 128 columns, so no wave straddles q/k and v
+        if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
+            g.vcol0 % 128 || g.npad < g.ntok)
+            return hipErrorInvalidValue;
+        if ((g.M / g.ntok) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
+    }
     // the epilogue addresses the output through a buffer resource with 32-bit
     // byte offsets (rows up to M + 255 are formed, those past M dropped)
     if (epi != EPI_PATCH && (g.M + 256) * g.ldo * (epi == EPI_RESID ? 4 : es) >= (1ll << 31))

@@ -23,7 +23,7 @@ hipError_t launch_layernorm(const float *x, int64_t rows, int dim, const float *
                             const float *beta, float eps, void *y, int y_dt, hipStream_t s);
 
 // ---- GEMM: out = epilogue(A[M, K] * W[N, K]^T + bias) -----------------------
-enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_PATCH = 3 };
+enum Epi { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_PATCH = 3, EPI_QKV = 4 };
 struct GemmArgs {
     const void *a;           // act dtype [M, K] row-major, pitch lda elements
     const void *w;           // dense: act dtype [N, K]; q8_0: int8 codes [N, K];
@@ -36,6 +36,11 @@ struct GemmArgs {
     // adds pos[has_cls + n]
     const float *pos;
     int np, ntok, has_cls;
+    // EPI_QKV: columns < vcol0 as EPI_STORE; columns >= vcol0 (the v part,
+    // heads of 64) go transposed to vt [M / ntok, (N - vcol0) / 64, 64, npad],
+    // row r = b*ntok + n being token n of item b
+    void *vt;
+    int64_t npad, vcol0;
 };
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
