@@ -21,6 +21,8 @@
 // The A operand of that product is V^T, which the qkv GEMM writes once per
 // head ([B, H, 64, npad]); a lane's 8 keys of one operand are two runs of 4
 // consecutive keys, i.e. two 8-byte LDS reads.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -283,17 +285,61 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
     };
 
     const float sl2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
-    float m = -INFINITY, l = 0.f;
+    // The running max m is a reference, not the exact max: it is raised only
+    // when a score exceeds it by TH (2^8 in p), so p <= 2^8 and the rescale of
+    // O and l runs a few times per query instead of at most tiles.  Any
+    // reference gives the same softmax once O is divided by l.
+    const float TH = 8.f / sl2;
+    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
     f32x16 o[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
 
     const int r0 = lane & 31;
     const int sw[2] = {aswz(r0), aswz(32 + r0)};
+    // this lane's LDS byte offsets of the tile's operands; a stage adds a
+    // constant (the tile loop is unrolled over the two stages)
+    int koff[2][DH / 16], voff[2][2][2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int c = 0; c < DH / 16; ++c) koff[sb][c] = (sb * 32 + r0) * 128 + (((2 * c + g) ^ sw[sb]) << 4);
+    // V^T operand chunk cc of key block sb, dim block db: keys 16*cc +
+    // 8*(j/4) + 4*g + j%4 of the block, i.e. two 8-byte reads
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int ch = 4 * sb + 2 * cc, base = (db * 32 + r0) * 128 + 8 * g;
+                voff[db][sb][cc][0] = base + ((ch ^ sw[db]) << 4);
+                voff[db][sb][cc][1] = base + (((ch + 1) ^ sw[db]) << 4);
+            }
+    // row sums from the packed P operand (the values PV multiplies): two
+    // products of (p, 1) per instruction, two chains
+    const uint32_t ones = sizeof(T) == 2 && std::is_same<T, bf16_t>::value ? 0x3f803f80u : 0x3c003c00u;
+    auto rowsum = [&](const vec &pb) __attribute__((always_inline)) {
+        const uint4 w = __builtin_bit_cast(uint4, pb);
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 one = __builtin_bit_cast(b2, ones);
+            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.x), one, l0, false);
+            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.y), one, l1, false);
+            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.z), one, l0, false);
+            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.w), one, l1, false);
+        } else {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const h2 one = __builtin_bit_cast(h2, ones);
+            l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.x), one, l0, false);
+            l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.y), one, l1, false);
+            l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.z), one, l0, false);
+            l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.w), one, l1, false);
+        }
+    };
 
-    issue(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int st = t & 1;
+    auto step = [&](auto ST, int t) __attribute__((always_inline)) {
+        constexpr int st = decltype(ST)::value;
         __builtin_amdgcn_s_waitcnt(0xF70);     // vmcnt(0): this wave's loads of tile t landed
         __builtin_amdgcn_s_barrier();           // everyone's did; everyone is done with stage st^1
         // all MFMA operands of tile t, LDS -> registers
@@ -301,20 +347,15 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int c = 0; c < DH / 16; ++c)
-                kf[sb][c] = MM::load(sK[st] + (sb * 32 + r0) * 128 + (((2 * c + g) ^ sw[sb]) << 4));
-        // V^T operand chunk cc of key block sb, dim block db: keys 16*cc +
-        // 8*(j/4) + 4*g + j%4 of the block, i.e. two 8-byte reads
+            for (int c = 0; c < DH / 16; ++c) kf[sb][c] = MM::load(sK[st] + koff[sb][c]);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    const int ch = 4 * sb + 2 * cc;
-                    const unsigned char *rp = sV[st] + (db * 32 + r0) * 128 + 8 * g;
-                    const uint2 lo4 = *(const uint2 *)(rp + ((ch ^ sw[db]) << 4));
-                    const uint2 hi4 = *(const uint2 *)(rp + (((ch + 1) ^ sw[db]) << 4));
+                    const uint2 lo4 = *(const uint2 *)(sV[st] + voff[db][sb][cc][0]);
+                    const uint2 hi4 = *(const uint2 *)(sV[st] + voff[db][sb][cc][1]);
                     vf[db][sb][cc] = __builtin_bit_cast(vec, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
                 }
         if (t + 1 < ntiles) issue(t + 1, st ^ 1);
@@ -343,10 +384,11 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[sb][v]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(m, mt);
-        if (__any(mn > m)) {                 // rescale only when some running max grew
+        if (__any(mt > m + TH)) {
+            const float mn = fmaxf(m, mt);
             const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-            l *= alpha;
+            l0 *= alpha;
+            l1 *= alpha;
 #pragma unroll
             for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
             m = mn;
@@ -355,11 +397,7 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
-                s[sb][v] = p;
-                l += p;
-            }
+            for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
         // O^T += V^T P^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -369,11 +407,21 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
 #pragma unroll
                 for (int j = 0; j < 8; ++j) pv[j] = s[sb][cc * 8 + j];
                 const vec pb = pack_operand<T>(pv);
+                rowsum(pb);
 #pragma unroll
                 for (int db = 0; db < 2; ++db) o[db] = MM::mma(vf[db][sb][cc], pb, o[db]);
             }
-    }
+    };
 
+    issue(0, 0);
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        step(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t < ntiles) step(std::integral_constant<int, 0>{}, t);
+
+    float l = l0 + l1;
     l += __shfl_xor(l, 32, 64);
     if (!qvalid) return;
     const float inv = 1.f / l;
