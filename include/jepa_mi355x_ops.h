@@ -10,6 +10,12 @@
 
 #include "jepa_mi355x.h"
 
+/* Position of token n within a row of the transposed-V layout (vt) that
+ * jepa_op_gemm_qkv and jepa_op_transpose_v write and jepa_op_attention reads:
+ * bits 2 and 3 of n swapped, i.e. each aligned run of 16 tokens in the order
+ * 0-3, 8-11, 4-7, 12-15. */
+#define JEPA_VT_POS(n) (((n) & ~(int64_t)12) | (((n) & 4) << 1) | (((n) & 8) >> 1))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -53,24 +59,28 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
  * (q and k) -> qk_out act [M, ld_qk] (ld_qk >= N; columns N - heads*64 .. N-1
  * of qk_out are not written); columns [2*heads*64, N) (v) -> vt act
  * [M / n_tokens, heads, 64, npad], row b*n_tokens + n being token n of item
- * b, each value rounded once to the act dtype.  vt columns n_tokens..npad-1
- * are not written.  M % n_tokens == 0, npad >= n_tokens. */
+ * b, each value rounded once to the act dtype.  Within a vt row, token n is
+ * at position JEPA_VT_POS(n): each aligned run of 16 tokens is stored in the
+ * order 0-3, 8-11, 4-7, 12-15, the order the attention kernel's operands
+ * read.  Positions holding no token are not written.  M % n_tokens == 0,
+ * npad >= n_tokens rounded up to 16. */
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
                              int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
                              int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
                              void *hip_stream);
 
 /* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
- * per head into vt act [batch, heads, 64, npad] (columns >= n_tokens not
- * written). */
+ * per head into vt act [batch, heads, 64, npad], token n at position
+ * JEPA_VT_POS(n) of its row (positions holding no token not written). */
 jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n_tokens,
                                 int heads, void *vt, int64_t npad, void *hip_stream);
 
 /* Multi-head attention, head_dim 64 (LeVJEPA card, opening paragraph, for
  * the block-causal mask).  q and k: act rows of pitch ld_qk elements (token
  * item*n_tokens + n), q of head h at column h*64, k at column heads*64 +
- * h*64; v: vt act [batch, heads, 64, npad] as written by jepa_op_transpose_v,
- * npad = n_tokens rounded up to 64, columns n_tokens..npad-1 finite (zero).
+ * h*64; v: vt act [batch, heads, 64, npad] as written by jepa_op_transpose_v
+ * (token n at JEPA_VT_POS(n)), npad = n_tokens rounded up to 64, positions
+ * holding no token finite (zero).
  * -> out act [batch*n_tokens, heads*64].  mask JEPA_MASK_BLOCK_CAUSAL groups
  * the patch tokens (after the optional CLS token 0) in consecutive runs of
  * tokens_per_slot. */

@@ -70,3 +70,10 @@ def rounded(act: str, x: np.ndarray):
 
 def oracle_tokens(dims, stored, frames):
     return E.encode(dims, E.weights_f64(stored), frames)
+
+
+def vt_pos(n):
+    """Position of token n in a transposed-V row: bits 2 and 3 swapped (each
+    aligned run of 16 tokens stored as 0-3, 8-11, 4-7, 12-15)."""
+    n = np.asarray(n, dtype=np.int64)
+    return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1)

@@ -20,7 +20,8 @@
 // are exactly the B operand of O^T = V^T P^T, so P never leaves registers.
 // The A operand of that product is V^T, which the qkv GEMM writes once per
 // head ([B, H, 64, npad]); a lane's 8 keys of one operand are two runs of 4
-// consecutive keys, i.e. two 8-byte LDS reads.
+// keys (4g..4g+3 and 8+4g..8+4g+3 of a 16-key group), which V^T stores
+// side by side (vt_pos), so the operand is one 16-byte LDS read.
 #include <type_traits>
 
 #include "common.hpp"
@@ -184,13 +185,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
                     const unsigned char *row = vb + (db * 32 + (lane & 31)) * ROWB;
                     typename MM::vec va;
                     if constexpr (VEC == 8) {
-                        const int k = sb * 32 + 16 * cc + 4 * g;
-                        const uint2 lo4 = *(const uint2 *)(row + k * ES);
-                        const uint2 hi4 = *(const uint2 *)(row + (k + 8) * ES);
-                        va = __builtin_bit_cast(typename MM::vec, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                        // keys 16*cc + 4*g + {0-3, 8-11}: 16 contiguous bytes at their V^T position
+                        va = MM::load(row + (sb * 32 + 16 * cc + 8 * g) * ES);
                     } else {
                         const int k = sb * 32 + 8 * (cc >> 2) + 4 * g + (cc & 3);
-                        va = MM::load(row + k * ES);
+                        va = MM::load(row + vt_pos(k) * ES);
                     }
                     o[db] = MM::mma(va, pb, o[db]);
                 }
@@ -222,13 +221,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 __device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 template <typename T>
-__global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
+__global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
     static_assert(sizeof(T) == 2, "16-bit operands");
     constexpr int TB = 64 * 128;                 // bytes of one 64 x 64 tile
-    __shared__ __attribute__((aligned(1024))) unsigned char sK[2][TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV[2][TB];
+    // one array per stage: the compiler gives each its own alias scope, so
+    // reads of one stage need not wait for loads landing in the other
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int h = blockIdx.x, b = blockIdx.y;
@@ -270,7 +273,9 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
         krow[i] = r;
         kcol[i] = ((ci & 7) ^ aswz(r)) * 8;      // element offset of the chunk
     }
-    auto issue = [&](int t, int st) {
+    auto issue = [&](int t, auto ST) __attribute__((always_inline)) {
+        unsigned char *sk = decltype(ST)::value ? sK1 : sK0;
+        unsigned char *sv = decltype(ST)::value ? sV1 : sV0;
         const int k0 = kbeg + t * KT;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -278,9 +283,9 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
             int key = k0 + krow[i];
             key = key < N ? key : N - 1;                  // past N: a valid row, masked later
             __builtin_amdgcn_global_load_lds((const void *)(qk + (int64_t)key * a.ld_qk + D + h * DH + kcol[i]),
-                (__attribute__((address_space(3))) void *)(sK[st] + base), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(sk + base), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void *)(vt + (int64_t)krow[i] * a.npad + k0 + kcol[i]),
-                (__attribute__((address_space(3))) void *)(sV[st] + base), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(sv + base), 16, 0, 0);
         }
     };
 
@@ -299,23 +304,17 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
     const int sw[2] = {aswz(r0), aswz(32 + r0)};
     // this lane's LDS byte offsets of the tile's operands; a stage adds a
     // constant (the tile loop is unrolled over the two stages)
-    int koff[2][DH / 16], voff[2][2][2][2];
+    int koff[2][DH / 16], voff[2][4];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int c = 0; c < DH / 16; ++c) koff[sb][c] = (sb * 32 + r0) * 128 + (((2 * c + g) ^ sw[sb]) << 4);
-    // V^T operand chunk cc of key block sb, dim block db: keys 16*cc +
-    // 8*(j/4) + 4*g + j%4 of the block, i.e. two 8-byte reads
+    // V^T operand of dim block db and 16-key group kg: keys 16*kg + 8*(j/4) +
+    // 4*g + j%4, stored contiguously as chunk 2*kg + g of the row
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int ch = 4 * sb + 2 * cc, base = (db * 32 + r0) * 128 + 8 * g;
-                voff[db][sb][cc][0] = base + ((ch ^ sw[db]) << 4);
-                voff[db][sb][cc][1] = base + (((ch + 1) ^ sw[db]) << 4);
-            }
+        for (int kg = 0; kg < 4; ++kg) voff[db][kg] = (db * 32 + r0) * 128 + (((2 * kg + g) ^ sw[db]) << 4);
     // row sums from the packed P operand (the values PV multiplies): two
     // products of (p, 1) per instruction, two chains
     const uint32_t ones = sizeof(T) == 2 && std::is_same<T, bf16_t>::value ? 0x3f803f80u : 0x3c003c00u;
@@ -338,36 +337,30 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
         }
     };
 
+    // Tile t in stage ST: the next tile's loads issued into the other stage,
+    // S = K Q^T from K operands read block by block, the softmax, then the V
+    // operands (read only now, so K's and V's registers are never live
+    // together) and O^T += V^T P^T.
     auto step = [&](auto ST, int t) __attribute__((always_inline)) {
         constexpr int st = decltype(ST)::value;
+        const unsigned char *sk = st ? sK1 : sK0;
+        const unsigned char *sv = st ? sV1 : sV0;
         __builtin_amdgcn_s_waitcnt(0xF70);     // vmcnt(0): this wave's loads of tile t landed
-        __builtin_amdgcn_s_barrier();           // everyone's did; everyone is done with stage st^1
-        // all MFMA operands of tile t, LDS -> registers
-        vec kf[2][DH / 16], vf[2][2][2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int c = 0; c < DH / 16; ++c) kf[sb][c] = MM::load(sK[st] + koff[sb][c]);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const uint2 lo4 = *(const uint2 *)(sV[st] + voff[db][sb][cc][0]);
-                    const uint2 hi4 = *(const uint2 *)(sV[st] + voff[db][sb][cc][1]);
-                    vf[db][sb][cc] = __builtin_bit_cast(vec, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-                }
-        if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+        __builtin_amdgcn_s_barrier();           // everyone's did; everyone is done with the other stage
+        if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, st ^ 1>{});
 
+        // S^T = K Q^T, one 32-key block at a time
         const int k0 = kbeg + t * KT;
         f32x16 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
+            vec kf[DH / 16];
+#pragma unroll
+            for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + koff[sb][c]);
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
-            for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[sb][c], qv[c], s[sb]);
+            for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[c], qv[c], s[sb]);
         }
         if (k0 < lo || k0 + KT > hi_min) {
 #pragma unroll
@@ -409,11 +402,11 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
                 const vec pb = pack_operand<T>(pv);
                 rowsum(pb);
 #pragma unroll
-                for (int db = 0; db < 2; ++db) o[db] = MM::mma(vf[db][sb][cc], pb, o[db]);
+                for (int db = 0; db < 2; ++db) o[db] = MM::mma(MM::load(sv + voff[db][2 * sb + cc]), pb, o[db]);
             }
     };
 
-    issue(0, 0);
+    issue(0, std::integral_constant<int, 0>{});
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
         step(std::integral_constant<int, 0>{}, t);
@@ -433,7 +426,8 @@ __global__ __launch_bounds__(256, 2) void attn16_kernel(const AttnArgs a, int q_
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
 }
 
-// v columns of qkv [B*N, 3D] -> vt [B, H, 64, npad] (columns >= N untouched)
+// v columns of qkv [B*N, 3D] -> vt [B, H, 64, npad], token n at vt_pos(n)
+// (positions of no token untouched)
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T *qkv, int N, int heads, T *vt,
                                                           int64_t npad) {
@@ -448,7 +442,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T *qkv, int N, i
     __syncthreads();
     for (int d = ty; d < 64; d += 4) {
         const int n = n0 + tx;
-        if (n < N) vt[(((int64_t)b * heads + h) * DH + d) * npad + n] = tile[tx][d];
+        if (n < N) vt[(((int64_t)b * heads + h) * DH + d) * npad + vt_pos(n)] = tile[tx][d];
     }
 }
 
@@ -489,7 +483,7 @@ hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
                               int64_t npad, hipStream_t s) {
-    if (B <= 0 || N <= 0 || heads <= 0 || npad < N) return hipErrorInvalidValue;
+    if (B <= 0 || N <= 0 || heads <= 0 || npad < cdiv(N, 16) * 16) return hipErrorInvalidValue;
     const dim3 grid((unsigned)cdiv(N, 64), heads, B);
     switch (act_dt) {
         case DT_F32:

@@ -107,7 +107,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // The v columns of the qkv product, written transposed: V^T [B, heads, 64,
-// npad] holds, for every head and dim, the item's tokens in a row.  Each
+// npad] holds, for every head and dim, the item's tokens in a row (token n at
+// vt_pos(n)).  Each
 // 32-row block (32 consecutive tokens, possibly of two items) is finished in
 // registers (bias, rounding) and staged in LDS as in the STORE case, then read
 // back by column: a wave store writes two columns of 32 tokens, i.e. two runs
@@ -148,10 +149,10 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
                     *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
                 }
             }
-        // this lane's token: row row0 + 32 i + rl
+        // this lane's token: row row0 + 32 i + rl, at its V^T position
         const uint32_t m = (uint32_t)(row0 + 32 * i + rl);
         const uint32_t b = m / (uint32_t)g.ntok, n = m - b * (uint32_t)g.ntok;
-        const uint32_t tok = b * (uint32_t)(heads * 64 * g.npad) + n;       // element offset of (b, h=0, d=0, n)
+        const uint32_t tok = b * (uint32_t)(heads * 64 * g.npad) + (uint32_t)vt_pos(n);   // (b, h=0, d=0, n)
 #pragma unroll
         for (int t = 0; t < NB_ * 16; ++t) {
             const int c = 2 * t + g32;                           // column of the wave
@@ -757,7 +758,7 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (epi == EPI_QKV) {
         // v starts at a multiple of 128 columns, so no wave straddles q/k and v
         if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
-            g.vcol0 % 128 || g.npad < g.ntok)
+            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16)
             return hipErrorInvalidValue;
         if ((g.M / g.ntok) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
     }

@@ -44,6 +44,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
+// Position of token n in a V^T row: each aligned run of 16 tokens is stored
+// in the order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 swapped), so the eight
+// keys one lane of the PV MFMA operand needs are 16 contiguous bytes.
+__host__ __device__ __forceinline__ int64_t vt_pos(int64_t n) {
+    return (n & ~(int64_t)12) | ((n & 4) << 1) | ((n & 8) >> 1);
+}
+
 // ---- attention --------------------------------------------------------------
 // Q and K: act dtype rows of pitch ld_qk, q of head h at column h*64, k at
 // column D + h*64.  V transposed: vt [B, H, 64, npad], npad = N rounded up to
