@@ -16,6 +16,11 @@
  * 0-3, 8-11, 4-7, 12-15. */
 #define JEPA_VT_POS(n) (((n) & ~(int64_t)12) | (((n) & 4) << 1) | (((n) & 8) >> 1))
 
+/* log2(e) / sqrt(64).  q multiplied by it turns q.k into the base-2 exponent
+ * of the softmax (scale 1/sqrt(head_dim), base e); jepa_encode folds it into
+ * the qkv layer's q columns (q_scale) and runs attention with q_prescaled. */
+#define JEPA_ATTN_Q_SCALE 0.18033688011112042f
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -62,12 +67,14 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
  * b, each value rounded once to the act dtype.  Within a vt row, token n is
  * at position JEPA_VT_POS(n): each aligned run of 16 tokens is stored in the
  * order 0-3, 8-11, 4-7, 12-15, the order the attention kernel's operands
- * read.  Positions holding no token are not written.  M % n_tokens == 0,
+ * read.  Positions holding no token are not written.  q_scale (0 or 1:
+ * none) multiplies the q columns before their rounding, e.g.
+ * JEPA_ATTN_Q_SCALE for jepa_op_attention's q_prescaled.  M % n_tokens == 0,
  * npad >= n_tokens rounded up to 16. */
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
                              int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
                              int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             void *hip_stream);
+                             float q_scale, void *hip_stream);
 
 /* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
  * per head into vt act [batch, heads, 64, npad], token n at position
@@ -83,10 +90,13 @@ jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n
  * holding no token finite (zero).
  * -> out act [batch*n_tokens, heads*64].  mask JEPA_MASK_BLOCK_CAUSAL groups
  * the patch tokens (after the optional CLS token 0) in consecutive runs of
- * tokens_per_slot. */
+ * tokens_per_slot.  q_prescaled: the q columns hold q * JEPA_ATTN_Q_SCALE
+ * (as jepa_op_gemm_qkv writes them with that q_scale), so q.k is already the
+ * base-2 softmax exponent; otherwise q is the plain projection. */
 jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
                               int64_t npad, int batch, int n_tokens, int heads, int has_cls,
-                              int mask, int tokens_per_slot, void *out, void *hip_stream);
+                              int mask, int tokens_per_slot, int q_prescaled, void *out,
+                              void *hip_stream);
 
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
  * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2

@@ -150,6 +150,7 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("q_scale", [0.0, 0.18033688011112042], ids=["q", "qscaled"])
 @pytest.mark.parametrize("act,wfmt,B,N,heads,K", [
     ("bf16", "dense", 7, 197, 4, 256),      # M = 1379: 256-row tiles, items straddling 32-row blocks
     ("bf16", "dense", 2, 289, 2, 128),      # M = 578: 128-row tiles
@@ -158,10 +159,11 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     ("f32", "dense", 2, 85, 2, 64),
     ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
 ])
-def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K):
-    """q and k columns as a plain linear layer; v columns straight into V^T
-    [B, heads, 64, npad] (the attention kernel's layout), padding untouched."""
-    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K}")
+def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale):
+    """q and k columns as a plain linear layer (q times q_scale before its one
+    rounding); v columns straight into V^T [B, heads, 64, npad] (the
+    attention kernel's layout), padding untouched."""
+    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K} q_scale={q_scale}")
     rng = np.random.default_rng(47)
     M, D = B * N, heads * 64
     a_dev, a = rounded(act, rng.standard_normal((M, K)))
@@ -183,8 +185,12 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K):
     qk = torch.zeros((M, 3 * D), dtype=tdt, device="cuda")
     vt = torch.full((B, heads, 64, npad), 7.0, dtype=tdt, device="cuda")
     lib.jepa_op_gemm_qkv(act, a_dev, w_dev, wfmt if wfmt != "dense" else act, heads,
-                         torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale)
+                         torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale, q_scale=q_scale)
     bound = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T) + OUT_REL[act] * np.abs(ref) + 1e-6
+    if q_scale:
+        ref = ref.copy()
+        ref[:, :D] *= q_scale
+        bound[:, :D] = bound[:, :D] * q_scale + OUT_REL[act] * np.abs(ref[:, :D])
     got_qk = qk.double().cpu().numpy()
     assert np.all(np.abs(got_qk[:, :2 * D] - ref[:, :2 * D]) <= bound[:, :2 * D])
     assert np.all(got_qk[:, 2 * D:] == 0)                       # v columns not written
@@ -204,18 +210,27 @@ def _vt_of(lib, act, qkv_dev, B, N, heads):
     return vt
 
 
-def _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot):
+def _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled=False):
     vt = _vt_of(lib, act, qkv_dev, B, N, heads)
     out = torch.empty((B * N, heads * 64), dtype=qkv_dev.dtype, device="cuda")
-    lib.jepa_op_attention(act, qkv_dev, vt, B, N, heads, has_cls, mask, per_slot, out)
+    lib.jepa_op_attention(act, qkv_dev, vt, B, N, heads, has_cls, mask, per_slot, out, q_prescaled=prescaled)
     return out
 
 
-def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed):
+def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed, prescaled=False, mag=1.0):
+    """GPU attention vs the oracle on seeded q, k, v.  prescaled: the device q
+    columns hold q * log2(e)/8 rounded to act (as the qkv layer writes them);
+    the oracle gets the q those rounded values stand for."""
     rng = np.random.default_rng(seed)
     D = heads * 64
-    qkv_dev, qkv = rounded(act, rng.standard_normal((B * N, 3 * D)))
-    out = _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot)
+    x = rng.standard_normal((B * N, 3 * D)) * mag
+    if prescaled:
+        x[:, :D] *= lib.ATTN_Q_SCALE
+    qkv_dev, qkv = rounded(act, x)
+    if prescaled:
+        qkv = qkv.copy()
+        qkv[:, :D] /= lib.ATTN_Q_SCALE
+    out = _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled)
     got = out.double().cpu().numpy().reshape(B, N, D)
     if mask == "bidir":
         allowed = None
@@ -236,11 +251,12 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("prescaled", [False, True], ids=["q", "qscaled"])
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"{c[1]}tok-{c[4]}-cls{int(c[3])}" for c in ATTN_CASES])
-def test_attention(lib, act, case):
-    say(f"attention {act} {case}")
-    got, ref = _attn_case(lib, act, *case, seed=44)
+def test_attention(lib, act, case, prescaled):
+    say(f"attention {act} {case} prescaled={prescaled}")
+    got, ref = _attn_case(lib, act, *case, seed=44, prescaled=prescaled)
     D = case[2] * 64
     g = got.reshape(-1, D)
     r = ref.reshape(-1, D)
@@ -251,6 +267,22 @@ def test_attention(lib, act, case):
         # a small multiple of the dtype's half-ulp
         err = np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)
         assert err.max() <= {"bf16": 2e-2, "f16": 3e-3}[act], err.max()
+
+
+@pytest.mark.parametrize("prescaled", [False, True], ids=["q", "qscaled"])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("mag", [0.05, 3.0])
+def test_attention_score_range(lib, act, mag, prescaled):
+    """Scores far from O(1): nearly flat (0.05) and very peaked (3.0: score
+    spread of hundreds in the base-2 exponent), so the softmax reference is
+    set low on the first key tile and raised several times later."""
+    case = (2, 289, 2, True, "block_causal", 36)
+    say(f"attention score range {act} mag={mag} prescaled={prescaled}")
+    got, ref = _attn_case(lib, act, *case, seed=48, prescaled=prescaled, mag=mag)
+    g = got.reshape(-1, 128)
+    r = ref.reshape(-1, 128)
+    err = np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)
+    assert err.max() <= {"bf16": 2e-2, "f16": 3e-3}[act], err.max()
 
 
 def test_attention_block_causal_rows_ignore_future_slots(lib):

@@ -72,8 +72,8 @@ def _load():
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
-        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, P]),
-        "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, P, P]),
+        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, C.c_float, P]),
+        "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, I, P, P]),
         "jepa_op_transpose_v": (I, [I, P, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
     }
@@ -239,20 +239,26 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
 
 
 def jepa_op_gemm_qkv(act_dtype: str, a, w, w_dtype: str, heads: int, bias, n_tokens: int, qk_out, vt,
-                     w_scale=None, stream=None) -> None:
-    """q, k columns -> qk_out [M, ld]; v columns transposed -> vt [M/n_tokens, heads, 64, npad]."""
+                     w_scale=None, q_scale: float = 0.0, stream=None) -> None:
+    """q, k columns -> qk_out [M, ld] (q times q_scale if nonzero); v columns
+    transposed -> vt [M/n_tokens, heads, 64, npad]."""
     M, K = a.shape
     _check(_lib.jepa_op_gemm_qkv(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
                                  heads, _ptr(bias), n_tokens, _ptr(qk_out), qk_out.shape[1], _ptr(vt),
-                                 vt.shape[-1], _stream(stream)))
+                                 vt.shape[-1], float(q_scale), _stream(stream)))
+
+
+# log2(e) / sqrt(64): JEPA_ATTN_Q_SCALE, the factor jepa_op_gemm_qkv folds into q
+ATTN_Q_SCALE = 0.18033688011112042
 
 
 def jepa_op_attention(act_dtype: str, qk, vt, batch: int, n_tokens: int, heads: int, has_cls: bool,
-                      mask: str, tokens_per_slot: int, out, stream=None) -> None:
-    """qk: [batch*n_tokens, ld] (q | k columns first); vt: [batch, heads, 64, npad]."""
+                      mask: str, tokens_per_slot: int, out, q_prescaled: bool = False, stream=None) -> None:
+    """qk: [batch*n_tokens, ld] (q | k columns first; q times JEPA_ATTN_Q_SCALE
+    if q_prescaled); vt: [batch, heads, 64, npad]."""
     _check(_lib.jepa_op_attention(DTYPE[act_dtype], _ptr(qk), qk.shape[1], _ptr(vt), vt.shape[-1],
                                   batch, n_tokens, heads, int(has_cls), MASK[mask], tokens_per_slot,
-                                  _ptr(out), _stream(stream)))
+                                  int(q_prescaled), _ptr(out), _stream(stream)))
 
 
 def jepa_op_transpose_v(act_dtype: str, qkv, batch: int, n_tokens: int, heads: int, vt,

@@ -658,12 +658,14 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             aa.qk = qkv; aa.ld_qk = 3 * D; aa.vt = vt; aa.npad = c->npad;
             aa.out = o; aa.B = q.nb; aa.N = c->N; aa.heads = c->H;
             aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
+            aa.q_prescaled = 1;
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
             {   // q, k to qkv; v transposed straight into V^T
                 GemmArgs g{};
                 g.a = hn; g.w = L.qkv.ptr; g.wscale = L.qkv.scale; g.bias = L.bqkv; g.out = qkv;
                 g.M = M; g.N = L.qkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
                 g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
+                g.qscale = ATTN_Q_SCALE;   // the softmax scale and base change, folded into q
                 TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, L.qkv.dev_dt, EPI_QKV, g, s); }));
             }
             TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
@@ -855,7 +857,7 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
                              int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
                              int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             void *hip_stream) {
+                             float q_scale, void *hip_stream) {
     if (!a || !w || !bias || !qk_out || !vt) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_gemm_qkv: bad act dtype");
     if (heads <= 0 || n_tokens <= 0) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: heads and n_tokens must be > 0");
@@ -863,12 +865,14 @@ jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K,
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = qk_out;
     g.M = M; g.N = 3 * (int64_t)heads * 64; g.K = K; g.lda = K; g.ldo = ld_qk;
     g.ntok = n_tokens; g.vt = vt; g.npad = npad; g.vcol0 = 2 * (int64_t)heads * 64;
+    g.qscale = q_scale == 1.f ? 0.f : q_scale;
     return hip_status(launch_gemm(act_dtype, w_dtype, EPI_QKV, g, (hipStream_t)hip_stream), "op_gemm_qkv");
 }
 
 jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
                               int64_t npad, int batch, int n_tokens, int heads, int has_cls,
-                              int mask, int tokens_per_slot, void *out, void *hip_stream) {
+                              int mask, int tokens_per_slot, int q_prescaled, void *out,
+                              void *hip_stream) {
     if (!qk || !vt || !out) return fail(JEPA_E_INVALID_ARG, "op_attention: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_attention: bad act dtype");
     if (mask != JEPA_MASK_BIDIR && mask != JEPA_MASK_BLOCK_CAUSAL)
@@ -878,6 +882,7 @@ jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, cons
     a.out = out; a.B = batch; a.N = n_tokens; a.heads = heads;
     a.has_cls = has_cls ? 1 : 0; a.block_causal = mask == JEPA_MASK_BLOCK_CAUSAL;
     a.per_slot = tokens_per_slot;
+    a.q_prescaled = q_prescaled ? 1 : 0;
     return hip_status(launch_attention(act_dtype, a, (hipStream_t)hip_stream), "op_attention");
 }
 

@@ -23,6 +23,7 @@
 // keys (4g..4g+3 and 8+4g..8+4g+3 of a 16-key group), which V^T stores
 // side by side (vt_pos), so the operand is one 16-byte LDS read.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
         }
     };
 
-    const float sl2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+    const float sl2 = a.q_prescaled ? 1.f : ATTN_Q_SCALE;   // score -> base-2 exponent
     float m = -INFINITY, l = 0.f;
     f32x16 o[2];
 #pragma unroll
@@ -220,7 +221,29 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 // the loads, no LDS write instructions.
 __device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <typename T>
+// The smallest value of the 16-bit type T that is >= x (x finite).
+template <typename T> __device__ __forceinline__ float round_up_t(float x);
+template <> __device__ __forceinline__ float round_up_t<bf16_t>(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = (int32_t)u >= 0 ? (u + 0xFFFFu) & 0xFFFF0000u : u & 0xFFFF0000u;   // magnitude up if x >= 0, else down
+    return __uint_as_float(u);
+}
+template <> __device__ __forceinline__ float round_up_t<f16_t>(float x) {
+    _Float16 h = (_Float16)x;
+    if ((float)h < x) {
+        uint16_t b = __builtin_bit_cast(uint16_t, h);
+        b = (b & 0x8000) ? b - 1 : b + 1;                                       // one step up
+        h = __builtin_bit_cast(_Float16, b);
+    }
+    return (float)h;
+}
+
+// QS: the q columns hold q * ATTN_Q_SCALE, so q.k is the base-2 exponent,
+// and the reference max m enters S through the MFMA itself: a fifth 16-deep
+// k chunk where K contributes 1 at dimension 64 and Q contributes -m (m kept
+// exactly representable in T).  S then comes out as the exponent s - m and
+// p = exp2(S) needs no VALU arithmetic before the exponential.
+template <typename T, bool QS>
 __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
@@ -233,7 +256,8 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-load bases in SGPRs
     const int h = blockIdx.x, b = blockIdx.y;
     const int tile = a.block_causal ? (n_qtiles - 1 - (int)blockIdx.z) : (int)blockIdx.z;
     const int N = a.N, D = a.heads * DH;
@@ -264,38 +288,50 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     for (int c = 0; c < DH / 16; ++c)
         qv[c] = qvalid ? MM::load(qk + (int64_t)qrow * a.ld_qk + h * DH + c * 16 + g * 8) : vec{};
 
-    // this thread's two chunks of each tile: chunk id ci = i*256 + tid, row
-    // ci >> 3, slot ci & 7 holding global chunk slot ^ swz(row)
-    int krow[2], kcol[2];
+    // This thread's two chunks of each tile: chunk id ci = i*256 + tid, row
+    // ci >> 3, slot ci & 7 holding global chunk slot ^ swz(row).  Loads go
+    // through buffer resources over the item's K rows and the (item, head)'s
+    // V^T rows: the thread's byte offsets are fixed and a tile adds a uniform
+    // one; key rows past the item's N read as 0 (masked keys).
+    uint32_t koffg[2], voffg[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int ci = i * 256 + tid, r = ci >> 3;
-        krow[i] = r;
-        kcol[i] = ((ci & 7) ^ aswz(r)) * 8;      // element offset of the chunk
+        const int col = ((ci & 7) ^ aswz(r)) * 8;     // element offset of the chunk
+        koffg[i] = (uint32_t)((r * a.ld_qk + col) * (int64_t)sizeof(T));
+        voffg[i] = (uint32_t)((r * a.npad + col) * (int64_t)sizeof(T));
     }
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(qk + D + h * DH), 0, (int)(((int64_t)N * a.ld_qk - D - h * DH) * (int64_t)sizeof(T)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)vt, 0, (int)((int64_t)DH * a.npad * (int64_t)sizeof(T)), 0x00020000);
     auto issue = [&](int t, auto ST) __attribute__((always_inline)) {
         unsigned char *sk = decltype(ST)::value ? sK1 : sK0;
         unsigned char *sv = decltype(ST)::value ? sV1 : sV0;
         const int k0 = kbeg + t * KT;
+        const uint32_t ks = (uint32_t)(k0 * a.ld_qk * (int64_t)sizeof(T)), vs = (uint32_t)(k0 * sizeof(T));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int base = (i * 256 + wave * 64) * 16;  // LDS byte offset of lane 0
-            int key = k0 + krow[i];
-            key = key < N ? key : N - 1;                  // past N: a valid row, masked later
-            __builtin_amdgcn_global_load_lds((const void *)(qk + (int64_t)key * a.ld_qk + D + h * DH + kcol[i]),
-                (__attribute__((address_space(3))) void *)(sk + base), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vt + (int64_t)krow[i] * a.npad + k0 + kcol[i]),
-                (__attribute__((address_space(3))) void *)(sv + base), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(sk + base),
+                                                     16, koffg[i], ks, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(sv + base),
+                                                     16, voffg[i], vs, 0, 0);
         }
     };
 
-    const float sl2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+    const float sl2 = QS ? 1.f : ATTN_Q_SCALE;       // score -> base-2 exponent
     // The running max m is a reference, not the exact max: it is raised only
     // when a score exceeds it by TH (2^8 in p), so p <= 2^8 and the rescale of
     // O and l runs a few times per query instead of at most tiles.  Any
     // reference gives the same softmax once O is divided by l.
     const float TH = 8.f / sl2;
-    float m = -INFINITY, l0 = 0.f, l1 = 0.f;
+    float m = QS ? 0.f : -INFINITY, l0 = 0.f, l1 = 0.f;
+    bool first = true;
+    // QS: the fifth k chunk's operands (dimension 64 of K is 1, of Q is -m)
+    typedef typename std::conditional<std::is_same<T, bf16_t>::value, __bf16, _Float16>::type elem_t;
+    vec kx{}, qx{};
+    kx[0] = g == 0 ? (elem_t)1.f : (elem_t)0.f;
     f32x16 o[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
@@ -361,6 +397,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
             for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[c], qv[c], s[sb]);
+            if constexpr (QS) s[sb] = MM::mma(kx, qx, s[sb]);   // - m
         }
         if (k0 < lo || k0 + KT > hi_min) {
 #pragma unroll
@@ -377,20 +414,47 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[sb][v]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        if (__any(mt > m + TH)) {
-            const float mn = fmaxf(m, mt);
-            const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-            l0 *= alpha;
-            l1 *= alpha;
+        if constexpr (QS) {
+            // s already holds the exponent relative to m; the first tile sets
+            // m (its max rounded up to T), later ones raise it past TH
+            if (first || __any(mt > TH)) {
+                const float mn = (first || mt > 0.f) ? round_up_t<T>(m + mt) : m;
+                const float d = mn - m;
+                if (!first) {
+                    const float alpha = __builtin_amdgcn_exp2f(-d);
+                    l0 *= alpha;
+                    l1 *= alpha;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
-            m = mn;
+                    for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+                }
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) s[sb][v] -= d;
+                m = mn;
+                qx[0] = g == 0 ? (elem_t)(-m) : (elem_t)0.f;
+                first = false;
+            }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(s[sb][v]);
+        } else {
+            if (__any(mt > m + TH)) {
+                const float mn = fmaxf(m, mt);
+                const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
+                l0 *= alpha;
+                l1 *= alpha;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+                m = mn;
+            }
+            const float mb = m * sl2;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
         }
-        const float mb = m * sl2;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
         // O^T += V^T P^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -453,10 +517,14 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     const int q_start = (a.block_causal && a.has_cls) ? 1 : 0;
     const int n_qtiles = (int)cdiv(a.N, QT);
     if (n_qtiles > 0) {
-        if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((attn16_kernel<T>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
-                               q_start, n_qtiles);
-        else
+        if constexpr (sizeof(T) == 2) {
+            if (a.q_prescaled)
+                hipLaunchKernelGGL((attn16_kernel<T, true>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
+                                   q_start, n_qtiles);
+            else
+                hipLaunchKernelGGL((attn16_kernel<T, false>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
+                                   q_start, n_qtiles);
+        } else
             hipLaunchKernelGGL((attn_kernel<T>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
                                q_start, n_qtiles);
         return hipGetLastError();
@@ -470,6 +538,9 @@ hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.N <= 0 || a.heads <= 0 || a.heads > 65535 || a.B > 65535 || a.N / QT >= 65535)
         return hipErrorInvalidValue;
     if (a.npad < cdiv(a.N, 64) * 64 || a.npad % 64) return hipErrorInvalidValue;
+    // the 16-bit kernel addresses one item's rows with 32-bit byte offsets
+    if ((int64_t)(a.N + 64) * a.ld_qk * 2 >= (1ll << 31) || (int64_t)DH * a.npad * 2 >= (1ll << 31))
+        return hipErrorInvalidValue;
     if (a.ld_qk < 2 * (int64_t)a.heads * DH || a.ld_qk % 8) return hipErrorInvalidValue;
     if (((uintptr_t)a.qk | (uintptr_t)a.vt) % 16) return hipErrorInvalidValue;
     if (a.block_causal && (a.per_slot <= 0 || (a.N - a.has_cls) % a.per_slot)) return hipErrorInvalidValue;

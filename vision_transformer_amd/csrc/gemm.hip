@@ -18,7 +18,8 @@
 //   GELU   out = act(gelu_erf(acc + b))          (fc1)
 //   RESID  X  += acc + b   (f32 residual)        (out-proj, fc2)
 //   PATCH  X[token] = acc + b + pos[token]       (patch-embed, CLS offset)
-//   QKV    q, k columns as STORE; v columns transposed per head into V^T
+//   QKV    q, k columns as STORE (q optionally scaled first); v columns
+//          transposed per head into V^T
 #include <stdlib.h>
 
 #include <string>
@@ -207,6 +208,13 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
     // global byte offset of (row0 + 32 i + t*RPI + rr, col0 + 16 rc / OES)
     const uint32_t gbase = (uint32_t)(row0 * g.ldo * OES + col0 * OES) + rr * rowb + rc * 16;
 
+    // EPI_QKV: the q columns' scale, per 4-column group (D is a multiple of 64)
+    auto col_scale = [&](int col) -> float {
+        if constexpr (EPI == EPI_QKV) {
+            if (g.qscale != 0.f && col0 + col < g.vcol0 / 2) return g.qscale;
+        }
+        return 1.f;
+    };
     float4 xv[2][NRD];
     auto load_x = [&](int i, int bf) {
         if constexpr (EPI == EPI_RESID) {
@@ -229,6 +237,11 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 const float4 b = *(const float4 *)(sb + col);
                 float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
                               acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
+                if constexpr (EPI == EPI_QKV) {
+                    const float cs = col_scale(col);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[r] *= cs;
+                }
                 if constexpr (EPI == EPI_GELU) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) z[r] = gelu_erf<T>(z[r]);

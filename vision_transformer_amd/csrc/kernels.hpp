@@ -41,6 +41,9 @@ struct GemmArgs {
     // row r = b*ntok + n being token n of item b
     void *vt;
     int64_t npad, vcol0;
+    // EPI_QKV: the q columns [0, vcol0 / 2) are multiplied by qscale before
+    // rounding (0: left as they are)
+    float qscale;
 };
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
@@ -62,7 +65,11 @@ struct AttnArgs {
     int64_t npad;
     void *out;               // act dtype [B*N, D]
     int B, N, heads, has_cls, block_causal, per_slot;
+    int q_prescaled;         // q already multiplied by ATTN_Q_SCALE
 };
+// log2(e) / sqrt(64): with q multiplied by it, q.k is the exponent of the
+// softmax in base 2
+constexpr float ATTN_Q_SCALE = 0.18033688011112042f;
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
 // vt <- the v columns of a [B*N, 3D] qkv matrix, transposed per head
 hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
