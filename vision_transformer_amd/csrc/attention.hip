@@ -219,7 +219,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 // the next tile's loads, so no LDS read follows a load in flight: the loads
 // overlap the step's whole MFMA + softmax time.  No staging registers for
 // the loads, no LDS write instructions.
-__device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
+// depends on row bits 0-4 only, so rows r and r + 32 share it
+__device__ __forceinline__ int aswz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 // The smallest value of the 16-bit type T that is >= x (x finite).
 template <typename T> __device__ __forceinline__ float round_up_t(float x);
@@ -239,7 +240,7 @@ template <> __device__ __forceinline__ float round_up_t<f16_t>(float x) {
 }
 
 // QS: the q columns hold q * ATTN_Q_SCALE, so q.k is the base-2 exponent,
-// and the reference max m enters S through the MFMA itself: a fifth 16-deep
+// and the reference max m enters S through the MFMA itself: an extra 8-deep
 // k chunk where K contributes 1 at dimension 64 and Q contributes -m (m kept
 // exactly representable in T).  S then comes out as the exponent s - m and
 // p = exp2(S) needs no VALU arithmetic before the exponential.
@@ -293,14 +294,15 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     // through buffer resources over the item's K rows and the (item, head)'s
     // V^T rows: the thread's byte offsets are fixed and a tile adds a uniform
     // one; key rows past the item's N read as 0 (masked keys).
-    uint32_t koffg[2], voffg[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ci = i * 256 + tid, r = ci >> 3;
-        const int col = ((ci & 7) ^ aswz(r)) * 8;     // element offset of the chunk
-        koffg[i] = (uint32_t)((r * a.ld_qk + col) * (int64_t)sizeof(T));
-        voffg[i] = (uint32_t)((r * a.npad + col) * (int64_t)sizeof(T));
+    // chunk i = 1 is chunk 0's, 32 rows on (same swizzle): a uniform offset
+    uint32_t koffg, voffg;
+    {
+        const int r = tid >> 3;
+        const int col = ((tid & 7) ^ aswz(r)) * 8;    // element offset of the chunk
+        koffg = (uint32_t)((r * a.ld_qk + col) * (int64_t)sizeof(T));
+        voffg = (uint32_t)((r * a.npad + col) * (int64_t)sizeof(T));
     }
+    const uint32_t k32 = (uint32_t)(32 * a.ld_qk * (int64_t)sizeof(T)), v32 = (uint32_t)(32 * a.npad * (int64_t)sizeof(T));
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(qk + D + h * DH), 0, (int)(((int64_t)N * a.ld_qk - D - h * DH) * (int64_t)sizeof(T)), 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -314,9 +316,9 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         for (int i = 0; i < 2; ++i) {
             const int base = (i * 256 + wave * 64) * 16;  // LDS byte offset of lane 0
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(sk + base),
-                                                     16, koffg[i], ks, 0, 0);
+                                                     16, koffg, ks + i * k32, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void *)(sv + base),
-                                                     16, voffg[i], vs, 0, 0);
+                                                     16, voffg, vs + i * v32, 0, 0);
         }
     };
 
@@ -328,29 +330,35 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     const float TH = 8.f / sl2;
     float m = QS ? 0.f : -INFINITY, l0 = 0.f, l1 = 0.f;
     bool first = true;
-    // QS: the fifth k chunk's operands (dimension 64 of K is 1, of Q is -m)
+    // QS: the extra k chunk's operands (dimension 64 of K is 1, of Q is -m),
+    // for the 8-deep MFMA (4 elements per lane: half the registers and cycles
+    // of a 16-deep chunk)
     typedef typename std::conditional<std::is_same<T, bf16_t>::value, __bf16, _Float16>::type elem_t;
-    vec kx{}, qx{};
+    typedef elem_t x4 __attribute__((ext_vector_type(4)));
+    x4 kx{}, qx{};
     kx[0] = g == 0 ? (elem_t)1.f : (elem_t)0.f;
+    auto mma_x = [&](const f32x16 &c) __attribute__((always_inline)) -> f32x16 {
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            typedef short s4 __attribute__((ext_vector_type(4)));
+            return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, kx), __builtin_bit_cast(s4, qx), c, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x8f16(kx, qx, c, 0, 0, 0);
+        }
+    };
     f32x16 o[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
 
-    const int r0 = lane & 31;
-    const int sw[2] = {aswz(r0), aswz(32 + r0)};
-    // this lane's LDS byte offsets of the tile's operands; a stage adds a
-    // constant (the tile loop is unrolled over the two stages)
-    int koff[2][DH / 16], voff[2][4];
+    const int r0 = lane & 31, sw = aswz(r0);
+    // this lane's LDS byte offsets of the tile's operands in rows 0..31; the
+    // second 32-row block (same swizzle) and the stage add constants
+    int koff[DH / 16], voff[4];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int c = 0; c < DH / 16; ++c) koff[c] = r0 * 128 + (((2 * c + g) ^ sw) << 4);
+    // V^T operand of 16-key group kg: keys 16*kg + 8*(j/4) + 4*g + j%4,
+    // stored contiguously as chunk 2*kg + g of the row
 #pragma unroll
-        for (int c = 0; c < DH / 16; ++c) koff[sb][c] = (sb * 32 + r0) * 128 + (((2 * c + g) ^ sw[sb]) << 4);
-    // V^T operand of dim block db and 16-key group kg: keys 16*kg + 8*(j/4) +
-    // 4*g + j%4, stored contiguously as chunk 2*kg + g of the row
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg) voff[db][kg] = (db * 32 + r0) * 128 + (((2 * kg + g) ^ sw[db]) << 4);
+    for (int kg = 0; kg < 4; ++kg) voff[kg] = r0 * 128 + (((2 * kg + g) ^ sw) << 4);
     // row sums from the packed P operand (the values PV multiplies): two
     // products of (p, 1) per instruction, two chains
     const uint32_t ones = sizeof(T) == 2 && std::is_same<T, bf16_t>::value ? 0x3f803f80u : 0x3c003c00u;
@@ -392,12 +400,12 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         for (int sb = 0; sb < 2; ++sb) {
             vec kf[DH / 16];
 #pragma unroll
-            for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + koff[sb][c]);
+            for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + sb * 4096 + koff[c]);
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
             for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[c], qv[c], s[sb]);
-            if constexpr (QS) s[sb] = MM::mma(kx, qx, s[sb]);   // - m
+            if constexpr (QS) s[sb] = mma_x(s[sb]);             // - m
         }
         if (k0 < lo || k0 + KT > hi_min) {
 #pragma unroll
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                 const vec pb = pack_operand<T>(pv);
                 rowsum(pb);
 #pragma unroll
-                for (int db = 0; db < 2; ++db) o[db] = MM::mma(MM::load(sv + voff[db][2 * sb + cc]), pb, o[db]);
+                for (int db = 0; db < 2; ++db) o[db] = MM::mma(MM::load(sv + db * 4096 + voff[2 * sb + cc]), pb, o[db]);
             }
     };
 

@@ -37,6 +37,19 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) {
     return f16_t{__builtin_bit_cast(uint16_t, (_Float16)x)};
 }
+// two values rounded to a 16-bit type, a in the low half (one packed
+// conversion instruction for bf16)
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float a, float b) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
 
 // ---------------------------------------------------------------------------
 // MFMA 32x32 tiles.  Operand lane layout, for lane l, g = l / 32:

@@ -36,29 +36,30 @@ constexpr int BM = 128, BN = 128;
 constexpr int ROWB = 144;                 // LDS bytes per tile row (128 + pad)
 constexpr int TILEB = 128 * ROWB;         // LDS bytes per 128-row tile
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26
-// (Hastings' rational approximation): |error| <= 1.5e-7 for all x.  One
-// reciprocal and one exponential instead of a library erf; used where the
-// result is rounded to a 16-bit type anyway.
-__device__ __forceinline__ float erf_as7126(float x) {
-    const float ax = fabsf(x);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-    float p = fmaf(1.061405429f, t, -1.453152027f);
-    p = fmaf(p, t, 1.421413741f);
-    p = fmaf(p, t, -0.284496736f);
-    p = fmaf(p, t, 0.254829592f);
-    p *= t;
-    const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-    const float y = fmaf(-p, e, 1.0f);
-    return copysignf(y, x);
+// GELU, erf form: 0.5 z (1 + erf(z / sqrt 2)) = z Phi(z).  The f32 path
+// keeps the library erf.  For 16-bit outputs it is written as
+//   GELU(z) = max(z, 0) - |z| erfc(|z| / sqrt 2) / 2,
+// the same function without the cancellation in 1 + erf for z < 0, with
+// erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x) from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, 7.1.26 (Hastings): |error| <= 1.5e-7 for x >= 0.  One
+// reciprocal, one exponential and ten other operations per value.
+__device__ __forceinline__ float gelu_as7126(float z) {
+    constexpr float P = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2: t in terms of |z|
+    const float t = __builtin_amdgcn_rcpf(fmaf(P, fabsf(z), 1.0f));
+    float q = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);   // coefficients halved
+    q = fmaf(q, t, 0.5f * 1.421413741f);
+    q = fmaf(q, t, 0.5f * -0.284496736f);
+    q = fmaf(q, t, 0.5f * 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(z * z * (-0.5f * 1.4426950408889634f));   // exp(-z^2 / 2)
+    const float h = (z * q) * (t * e);                                             // z erfc(|z|/sqrt2) / 2
+    return fmaxf(z, 0.f) - fabsf(h);
 }
 
-// GELU, erf form: 0.5 z (1 + erf(z / sqrt 2)).  The f32 path keeps the
-// library erf; 16-bit outputs use the 7.1.26 approximation.
 template <typename T>
 __device__ __forceinline__ float gelu_erf(float z) {
     if constexpr (sizeof(T) == 4) return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-    else return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752f));
+    else return gelu_as7126(z);
 }
 
 // Registers that carry one K step of the W tile from global memory to LDS.
@@ -70,15 +71,8 @@ template <> struct BRegs<DT_Q4_0> { uint4 q; float d; };
 template <typename T>
 __device__ __forceinline__ void store_f16x8(unsigned char *dst, const float *x) {
     // x holds 8 f32 values, stored as 8 act-dtype values (16 bytes)
-    uint4 r;
-    uint16_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = from_f32<T>(x[j]).v;
-    r.x = h[0] | ((uint32_t)h[1] << 16);
-    r.y = h[2] | ((uint32_t)h[3] << 16);
-    r.z = h[4] | ((uint32_t)h[5] << 16);
-    r.w = h[6] | ((uint32_t)h[7] << 16);
-    *(uint4 *)dst = r;
+    *(uint4 *)dst = make_uint4(pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]), pack2<T>(x[4], x[5]),
+                               pack2<T>(x[6], x[7]));
 }
 
 // One output element: z = acc + bias, applied per the epilogue.
@@ -142,10 +136,7 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
                 const int cb = col * OES;
                 unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
                 if constexpr (OES == 2) {
-                    uint2 pk;
-                    pk.x = (uint32_t)from_f32<T>(z[0]).v | ((uint32_t)from_f32<T>(z[1]).v << 16);
-                    pk.y = (uint32_t)from_f32<T>(z[2]).v | ((uint32_t)from_f32<T>(z[3]).v << 16);
-                    *(uint2 *)dst = pk;
+                    *(uint2 *)dst = make_uint2(pack2<T>(z[0], z[1]), pack2<T>(z[2], z[3]));
                 } else {
                     *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
                 }
@@ -224,6 +215,16 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                     rs, gbase + (32 * i + t * RPI) * rowb, 0, 0));
         }
     };
+    // this lane's biases, once for all block rows (the qkv epilogue, whose v
+    // branch needs the registers, reads them per block row)
+    constexpr bool HOIST = EPI != EPI_QKV;
+    float4 bias[HOIST ? NB_ : 1][4];
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int j = 0; j < NB_; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bias[j][q] = *(const float4 *)(sb + 32 * j + 8 * q + 4 * g32);
+    }
     load_x(0, 0);
 #pragma unroll
     for (int i = 0; i < MB_; ++i) {
@@ -234,7 +235,7 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * j + 8 * q + 4 * g32;
-                const float4 b = *(const float4 *)(sb + col);
+                const float4 b = HOIST ? bias[HOIST ? j : 0][q] : *(const float4 *)(sb + col);
                 float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
                               acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
                 if constexpr (EPI == EPI_QKV) {
@@ -249,10 +250,7 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 const int cb = col * OES;
                 unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
                 if constexpr (OES == 2) {
-                    uint2 pk;
-                    pk.x = (uint32_t)from_f32<T>(z[0]).v | ((uint32_t)from_f32<T>(z[1]).v << 16);
-                    pk.y = (uint32_t)from_f32<T>(z[2]).v | ((uint32_t)from_f32<T>(z[3]).v << 16);
-                    *(uint2 *)dst = pk;
+                    *(uint2 *)dst = make_uint2(pack2<T>(z[0], z[1]), pack2<T>(z[2], z[3]));
                 } else {
                     *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
                 }
