@@ -270,6 +270,40 @@ def main() -> int:
     print(f"[bench] roofline region (one part): {1e3 * wall1 / args.steps:.3f} ms per step", file=sys.stderr,
           flush=True)
 
+    # one step captured into a HIP graph and replayed (the pages' CUDA-graph
+    # replay row), and the API wall time with host frames in and the token
+    # map copied back to the host (the pages' wall_ms row; never the value)
+    graph_ms = None
+    try:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+        del graph
+    except Exception as e:  # capture is an extra row: report, do not fail the bench
+        print(f"[bench] graph replay not measured: {e}", file=sys.stderr, flush=True)
+    host_tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, pin_memory=True)
+    api_steps = max(1, min(args.steps, 5))
+    enc.encode(frames, tokens)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(api_steps):
+        enc.encode(frames, tokens)          # host frames: staged by the library
+        host_tokens.copy_(tokens)
+    torch.cuda.synchronize()
+    api_ms = 1e3 * (time.perf_counter() - t0) / api_steps
+    print(f"[bench] graph replay: {graph_ms if graph_ms is None else round(graph_ms, 3)} ms per step, "
+          f"API wall with host frames and host tokens: {api_ms:.3f} ms per step", file=sys.stderr, flush=True)
+
     ms_per_step = 1e3 * wall / args.steps
     tok_s = B * N * args.steps / wall
     flops = forward_flops(dims, B)
@@ -310,6 +344,8 @@ def main() -> int:
         "mfma_util_pct": round(100 * util, 2),
         "forward_tflop": round(flops / 1e12, 4),
         "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "api_wall_ms_per_step_host_io": round(api_ms, 4),
         "roofline": roof,
     }
     enc.close()

@@ -52,7 +52,8 @@ def test_small_workload_every_token(Encoder, name):
     H.say(f"encoder {name}")
     wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
     enc = Encoder(dims, stored)
-    y = _run(enc, frames).cpu().numpy()
+    y_dev = _run(enc, frames)        # kept alive: pool() reads the last encode's token map
+    y = y_dev.cpu().numpy()
     ref = H.oracle_tokens(dims, stored, frames)
     H.check_rows(dims["act_dtype"], y, ref, "tokens")
     _check_pools(enc, dims, ref, wl["batch"])
@@ -65,7 +66,8 @@ def test_vit_ti14_image_f32_full(Encoder):
     H.say("encoder vit_ti14_image_f32")
     wl, dims, frames, stored = H.workload_inputs("vit_ti14_image_f32")
     enc = Encoder(dims, stored)
-    y = _run(enc, frames).cpu().numpy()
+    y_dev = _run(enc, frames)        # kept alive: pool() reads the last encode's token map
+    y = y_dev.cpu().numpy()
     ref = H.oracle_tokens(dims, stored, frames)
     r = H.check_rows("f32", y, ref, "tokens")
     assert r["cos_worst"] >= H.F32_COS
@@ -168,6 +170,42 @@ def test_batch_parts_do_not_change_tokens(Encoder, name):
         assert torch.equal(ys[0], y)
     with pytest.raises(_lib.JepaError, match="JEPA_E_INVALID_ARG"):
         _lib.jepa_set_batch_parts(enc.ctx, 5)
+    enc.close()
+
+
+@pytest.mark.parametrize("parts", [1, 3])
+def test_graph_replay_matches_eager(Encoder, parts):
+    """encode + pool captured into one HIP graph (with the batch in concurrent
+    parts: the fork / join events become graph edges).  Every replay, with
+    eager work and synchronisations in between, equals the eager result bit
+    for bit."""
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs("small_blockcausal_bf16")
+    enc = Encoder(dims, stored)
+    _lib.jepa_set_batch_parts(enc.ctx, parts)
+    fr = torch.from_numpy(frames).cuda()
+    B = frames.shape[0]
+    tokens = torch.empty((B, enc.n_tokens, dims["dim"]), dtype=torch.float32, device="cuda")
+    pooled = torch.empty((B, dims["dim"]), dtype=torch.float32, device="cuda")
+    enc.encode(fr, tokens)
+    enc.pool("cls", B, pooled)
+    torch.cuda.synchronize()
+    want_t, want_p = tokens.clone(), pooled.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enc.encode(fr, tokens)
+        enc.pool("cls", B, pooled)
+    for r in range(3):
+        H.say(f"graph replay {r}, parts {parts}")
+        tokens.zero_()
+        pooled.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, want_t) and torch.equal(pooled, want_p)
+        enc.encode(fr, tokens)              # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, want_t)
+    del graph
     enc.close()
 
 

@@ -546,11 +546,12 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     return JEPA_OK;
 }
 
-static jepa_status gemm(jepa_ctx *c, int cls, hipStream_t s, const void *a, int64_t M, int64_t K,
+static jepa_status gemm(jepa_ctx *c, int cls, hipStream_t s, int conc, const void *a, int64_t M, int64_t K,
                         const DevTensor &w, const float *bias, int epi, void *out, int64_t ldo) {
     GemmArgs g{};
     g.a = a; g.w = w.ptr; g.wscale = w.scale; g.bias = bias; g.out = out;
     g.M = M; g.N = w.ne1; g.K = K; g.lda = K; g.ldo = ldo;
+    g.conc = conc;
     return launch(c, cls, s, [&] { return launch_gemm(c->act, w.dev_dt, epi, g, s); });
 }
 
@@ -666,13 +667,14 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
                 g.M = M; g.N = L.qkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
                 g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
                 g.qscale = ATTN_Q_SCALE;   // the softmax scale and base change, folded into q
+                g.conc = parts;
                 TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, L.qkv.dev_dt, EPI_QKV, g, s); }));
             }
             TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
-            TRY(gemm(c, K_GEMM_OUT, s, o, M, D, L.out, L.bout, EPI_RESID, x, D));
+            TRY(gemm(c, K_GEMM_OUT, s, parts, o, M, D, L.out, L.bout, EPI_RESID, x, D));
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
-            TRY(gemm(c, K_GEMM_FC1, s, hn, M, D, L.up, L.bup, EPI_GELU, u, F));
-            TRY(gemm(c, K_GEMM_FC2, s, u, M, F, L.down, L.bdown, EPI_RESID, x, D));
+            TRY(gemm(c, K_GEMM_FC1, s, parts, hn, M, D, L.up, L.bup, EPI_GELU, u, F));
+            TRY(gemm(c, K_GEMM_FC2, s, parts, u, M, F, L.down, L.bdown, EPI_RESID, x, D));
         }
     }
     for (int p = 0; p < parts; ++p) {

@@ -713,6 +713,18 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
 
 // Variant choice (below); JEPA_GEMM_VARIANT (small | big256 | big128) pins it.
 
+int cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <typename T, int EPI, int BN>
 hipError_t launch_big(const GemmArgs &g, hipStream_t s) {
     const int tm = (int)cdiv(g.M, BIG_BM), tn = (int)cdiv(g.N, BN);
@@ -730,11 +742,21 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
                             g.N * g.K * 2 < (1ll << 32) && cdiv(g.M, BIG_BM) * cdiv(g.N, 128) < (1ll << 31);
         if (big_ok && var == "big256" && g.N % 256 == 0) return launch_big<T, EPI, 256>(g, s);
         if (big_ok && var == "big128") return launch_big<T, EPI, 128>(g, s);
-        // measured on MI355X at the ViT-L shapes (M = 12548): the 256 x 256
-        // tile is fastest for all four linear layers; below ~1024 rows the
-        // 128 x 128 tile's larger grid fills the chip better
+        // Below ~1024 rows the 128 x 128 tile's larger grid fills the chip
+        // better.  Above, the 256-row tiles, 256 or 128 columns wide: by the
+        // rounds of workgroups each needs (counting the tiles of the launches
+        // expected to run beside this one) times its tile time, a 256 x 128
+        // tile taking 0.6 of a 256 x 256 one (measured on MI355X at the ViT-L
+        // shapes, epilogues aside).  The wide tile wins whenever the tiles
+        // fill several rounds; the narrow one when the wide tiles leave CUs
+        // idle (ViT-L/16 images, batch 32: fc2 and out-proj have 100 wide tiles).
         if (big_ok && var.empty() && g.M >= 1024) {
-            if (g.N % 256 == 0) return launch_big<T, EPI, 256>(g, s);
+            if (g.N % 256 == 0) {
+                const int64_t cus = cu_count(), conc = g.conc > 1 ? g.conc : 1;
+                const int64_t tm = cdiv(g.M, BIG_BM);
+                const int64_t r256 = cdiv(tm * (g.N / 256) * conc, cus), r128 = cdiv(tm * (g.N / 128) * conc, cus);
+                if (10 * r256 <= 6 * r128) return launch_big<T, EPI, 256>(g, s);
+            }
             return launch_big<T, EPI, 128>(g, s);
         }
     }

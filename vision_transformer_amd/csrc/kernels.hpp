@@ -44,6 +44,9 @@ struct GemmArgs {
     // EPI_QKV: the q columns [0, vcol0 / 2) are multiplied by qscale before
     // rounding (0: left as they are)
     float qscale;
+    // launches of this shape expected to run concurrently (batch parts on
+    // other streams; 0 or 1: none), a hint for the tile-shape choice
+    int conc;
 };
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
