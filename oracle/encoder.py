@@ -21,6 +21,15 @@ Where the pages are silent the readings are:
   R7  Pixels are normalised as (u / 255 - mean_c) / std_c.
   R8  Mean pooling averages the final-LayerNorm rows of the patch tokens
       only (CLS excluded).
+  R9  3-D rotary position (V-JEPA 2 encoders; the pages name "3-D RoPE" and
+      give no formula).  The plainest reading of the published technique
+      (RoFormer rotary embedding, one axis per third of the head): each
+      head's dimensions are cut into three segments of ds = 2*floor(dh/6)
+      (20 of 64), for the tubelet's temporal index t, patch row h and patch
+      column w; the dh - 3*ds left over are not rotated.  Pair (2i, 2i+1) of
+      a segment is rotated by pos_axis * 10000^(-2i/ds).  q and k are rotated
+      before the scores; v is not.  A CLS token has no position (angle 0),
+      and with rotary position the model has no additive table.
 """
 from __future__ import annotations
 
@@ -115,12 +124,39 @@ def attention_head(q, k, v, allowed):
     return softmax_masked(s, allowed) @ v
 
 
-def attention(qkv: np.ndarray, heads: int, allowed, threads: int = 8) -> np.ndarray:
+def rope_angles(dims: dict) -> np.ndarray:
+    """[N, dh/2] rotation angle of every token and dimension pair (R9)."""
+    dh = dims["dim"] // dims["heads"]
+    ds = 2 * (dh // 6)
+    Tt = dims["frames"] // dims["tubelet"]
+    Hp, Wp = dims["img_h"] // dims["patch"], dims["img_w"] // dims["patch"]
+    pn = np.arange(Tt * Hp * Wp)
+    axes = [pn // (Hp * Wp), (pn // Wp) % Hp, pn % Wp]        # t, h, w of each patch token
+    ang = np.zeros((pn.size, dh // 2))
+    for a, pos in enumerate(axes):
+        for i in range(ds // 2):
+            ang[:, a * ds // 2 + i] = pos * 10000.0 ** (-2.0 * i / ds)
+    if dims["has_cls"]:
+        ang = np.concatenate([np.zeros((1, dh // 2)), ang])  # CLS: no position
+    return ang
+
+
+def rope(x: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """x [N, dh] of one head: pair (2p, 2p+1) of token n rotated by ang[n, p] (R9)."""
+    c, s = np.cos(ang), np.sin(ang)
+    y = np.empty_like(x)
+    y[:, 0::2] = x[:, 0::2] * c - x[:, 1::2] * s
+    y[:, 1::2] = x[:, 0::2] * s + x[:, 1::2] * c
+    return y
+
+
+def attention(qkv: np.ndarray, heads: int, allowed, threads: int = 8, ang=None) -> np.ndarray:
     """Multi-head attention of one item.
 
     qkv [N, 3D] with columns [q | k | v] (R3) -> concat of head outputs [N, D].
-    Heads are independent, so they are evaluated on a thread pool; each is
-    the plain definition.
+    With ang (rope_angles), q and k are rotated per head first (R9).  Heads are
+    independent, so they are evaluated on a thread pool; each is the plain
+    definition.
     """
     N, threeD = qkv.shape
     D = threeD // 3
@@ -130,7 +166,10 @@ def attention(qkv: np.ndarray, heads: int, allowed, threads: int = 8) -> np.ndar
 
     def one(a):
         sl = slice(a * dh, (a + 1) * dh)
-        out[:, sl] = attention_head(q[:, sl], k[:, sl], v[:, sl], allowed)
+        qa, ka = q[:, sl], k[:, sl]
+        if ang is not None:
+            qa, ka = rope(qa, ang), rope(ka, ang)
+        out[:, sl] = attention_head(qa, ka, v[:, sl], allowed)
 
     with ThreadPoolExecutor(max_workers=max(1, min(threads, heads))) as ex:
         list(ex.map(one, range(heads)))
@@ -163,7 +202,7 @@ def embed(dims: dict, w: dict, frames: np.ndarray) -> np.ndarray:
     if dims["has_cls"]:
         cls = np.broadcast_to(w["enc.cls_token"], (e.shape[0], 1, e.shape[2]))
         e = np.concatenate([cls, e], axis=1)
-    return e + w["enc.pos_embed"]
+    return e + w["enc.pos_embed"] if "enc.pos_embed" in w else e     # none with rotary position (R9)
 
 
 def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed) -> np.ndarray:
@@ -172,7 +211,8 @@ def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed) -> np.ndarray:
     eps = dims["ln_eps"]
     h = layer_norm(x, w[p + "ln1.weight"], w[p + "ln1.bias"], eps)
     qkv = linear(h, w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"])
-    o = np.stack([attention(qkv[b], dims["heads"], allowed) for b in range(x.shape[0])])
+    ang = rope_angles(dims) if dims.get("rope") else None
+    o = np.stack([attention(qkv[b], dims["heads"], allowed, ang=ang) for b in range(x.shape[0])])
     x = x + linear(o, w[p + "attn_out.weight"], w[p + "attn_out.bias"])
     h = layer_norm(x, w[p + "ln2.weight"], w[p + "ln2.bias"], eps)
     u = gelu(linear(h, w[p + "ffn_up.weight"], w[p + "ffn_up.bias"]))

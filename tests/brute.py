@@ -7,6 +7,7 @@ oracle's pin tests; never by the HIP path.
 """
 from __future__ import annotations
 
+import cmath
 import math
 
 
@@ -14,7 +15,7 @@ def _embed(dims, w, frames):
     B, T, H, W, _ = frames.shape
     kt, p, D = dims["tubelet"], dims["patch"], dims["dim"]
     Tt, Hp, Wp = T // kt, H // p, W // p
-    Wpe, bpe, pos = w["enc.patch_embed.weight"], w["enc.patch_embed.bias"], w["enc.pos_embed"]
+    Wpe, bpe, pos = w["enc.patch_embed.weight"], w["enc.patch_embed.bias"], w.get("enc.pos_embed")
     out = []
     for b in range(B):
         toks = []
@@ -32,7 +33,8 @@ def _embed(dims, w, frames):
                                     v.append((u / 255.0 - dims["mean"][c]) / dims["std"][c])
                     toks.append([float(bpe[d]) + sum(float(Wpe[d, k]) * v[k] for k in range(len(v)))
                                  for d in range(D)])
-        out.append([[toks[n][d] + float(pos[n, d]) for d in range(D)] for n in range(len(toks))])
+        out.append([[toks[n][d] + (float(pos[n, d]) if pos is not None else 0.0) for d in range(D)]
+                    for n in range(len(toks))])
     return out
 
 
@@ -60,6 +62,35 @@ def _may_attend(dims, i, j):
     return (j - c) // per_slot <= (i - c) // per_slot
 
 
+def _rotary(dims, vec):
+    """3-D rotary position of q or k: vec[N][dh] of one head -> rotated copy.
+
+    Each dimension pair is read as one complex number and multiplied by the
+    unit complex number of angle position * frequency; the head is split into
+    a t, an h and a w segment of 2*floor(dh/6) dimensions each, the rest is
+    left alone, and a CLS token (no position) is not rotated."""
+    dh = len(vec[0])
+    seg = 2 * (dh // 6)
+    c = int(dims["has_cls"])
+    Hp, Wp = dims["img_h"] // dims["patch"], dims["img_w"] // dims["patch"]
+    pos = [None] * c
+    for tt in range(dims["frames"] // dims["tubelet"]):
+        for i in range(Hp):
+            for j in range(Wp):
+                pos.append((tt, i, j))
+    out = []
+    for n, row in enumerate(vec):
+        r = list(row)
+        if pos[n] is not None:
+            for axis in range(3):
+                for k in range(seg // 2):
+                    d = axis * seg + 2 * k
+                    z = complex(row[d], row[d + 1]) * cmath.exp(1j * pos[n][axis] / 10000.0 ** (2.0 * k / seg))
+                    r[d], r[d + 1] = z.real, z.imag
+        out.append(r)
+    return out
+
+
 def encode(dims, w, frames):
     """frames uint8 [B, T, H, W, 3] -> list [B][N][D] of floats."""
     D, H = dims["dim"], dims["heads"]
@@ -75,10 +106,13 @@ def encode(dims, w, frames):
                         w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"]) for n in range(N)]
             o = [[0.0] * D for _ in range(N)]
             for a in range(H):
+                qa = [qkv[n][a * dh:(a + 1) * dh] for n in range(N)]
+                ka = [qkv[n][D + a * dh:D + (a + 1) * dh] for n in range(N)]
+                if dims.get("rope"):
+                    qa, ka = _rotary(dims, qa), _rotary(dims, ka)
                 for i in range(N):
                     js = [j for j in range(N) if _may_attend(dims, i, j)]
-                    s = [sum(qkv[i][a * dh + t] * qkv[j][D + a * dh + t] for t in range(dh))
-                         / math.sqrt(dh) for j in js]
+                    s = [sum(qa[i][t] * ka[j][t] for t in range(dh)) / math.sqrt(dh) for j in js]
                     m = max(s)
                     e = [math.exp(v - m) for v in s]
                     z = sum(e)

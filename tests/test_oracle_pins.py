@@ -324,6 +324,90 @@ def test_pool_modes():
 
 
 # ---------------------------------------------------------------------------
+# 3-D rotary position (V-JEPA 2 card: the encoder's "3-D RoPE"; RoFormer's
+# rotation, one third of each head per axis)
+# ---------------------------------------------------------------------------
+
+_VJ2_16F = dict(dim=1024, heads=16, patch=16, tubelet=2, img_h=256, img_w=256, frames=16,
+                has_cls=0)
+
+
+def test_rope_angles_hand_values():
+    """dh 64: segments of 20 dims for t, h, w, dims 60-63 unrotated; the
+    frequency of pair i of a segment is 10000^(-i/10)."""
+    ang = E.rope_angles(_VJ2_16F)
+    assert ang.shape == (8 * 16 * 16, 32)
+    tok = lambda t, h, w: (t * 16 + h) * 16 + w
+    f = 10000.0 ** (-np.arange(10) / 10.0)
+    np.testing.assert_array_equal(ang[tok(0, 0, 0)], 0.0)
+    np.testing.assert_allclose(ang[tok(3, 0, 0)], np.r_[3 * f, np.zeros(22)], rtol=1e-15)
+    np.testing.assert_allclose(ang[tok(0, 5, 0)], np.r_[np.zeros(10), 5 * f, np.zeros(12)], rtol=1e-15)
+    np.testing.assert_allclose(ang[tok(7, 15, 11)], np.r_[7 * f, 15 * f, 11 * f, 0, 0], rtol=1e-15)
+    assert ang[tok(1, 0, 0), 1] == pytest.approx(10 ** -0.4, rel=1e-15)
+    # a CLS token (no position) is token 0 and is never rotated
+    ac = E.rope_angles(dict(_VJ2_16F, has_cls=1))
+    np.testing.assert_array_equal(ac[0], 0.0)
+    np.testing.assert_array_equal(ac[1:], ang)
+
+
+def test_rope_rotates_pairs_by_hand():
+    """e_0 at t = 1 -> (cos 1, sin 1) in dims 0, 1; e_41 at w = 1 -> (-sin 1,
+    cos 1) in dims 40, 41; dims 60-63 pass through."""
+    ang = E.rope_angles(_VJ2_16F)
+    x = np.zeros((ang.shape[0], 64))
+    t1, w1 = 16 * 16, 1
+    x[t1, 0] = 1.0
+    x[w1, 41] = 1.0
+    x[:, 60:] = 2.5
+    y = E.rope(x, ang)
+    np.testing.assert_allclose(y[t1, :2], [math.cos(1), math.sin(1)], rtol=1e-15)
+    np.testing.assert_allclose(y[w1, 40:42], [-math.sin(1), math.cos(1)], rtol=1e-15)
+    np.testing.assert_array_equal(np.delete(y[t1], [0, 1]), np.delete(x[t1], [0, 1]))
+    np.testing.assert_array_equal(y[:, 60:], 2.5)
+
+
+def test_rope_is_a_rotation_and_relative():
+    """Rotation keeps every pair's length; q.k after rotation depends only on
+    the difference of the two tokens' (t, h, w) positions."""
+    rng = np.random.default_rng(30)
+    ang = E.rope_angles(_VJ2_16F)
+    x = rng.standard_normal((ang.shape[0], 64))
+    y = E.rope(x, ang)
+    np.testing.assert_allclose((y ** 2).reshape(-1, 32, 2).sum(-1), (x ** 2).reshape(-1, 32, 2).sum(-1),
+                               rtol=1e-13)
+    q, k = rng.standard_normal((2, 1, 64))
+    tok = lambda t, h, w: (t * 16 + h) * 16 + w
+    dot = lambda a, b: float((E.rope(q, ang[[a]]) @ E.rope(k, ang[[b]]).T)[0, 0])
+    for (p0, p1), s in [(((0, 0, 0), (2, 3, 5)), (4, 7, 1)), (((5, 9, 2), (1, 0, 14)), (2, 6, 1))]:
+        moved = [tuple(a + b for a, b in zip(p, s)) for p in (p0, p1)]
+        assert dot(tok(*moved[0]), tok(*moved[1])) == pytest.approx(dot(tok(*p0), tok(*p1)), rel=1e-12)
+    # and it does depend on the difference: a shift of one token only changes it
+    assert abs(dot(tok(0, 0, 0), tok(0, 0, 1)) - dot(tok(0, 0, 0), tok(0, 0, 0))) > 1e-3
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mask="bidir"),                                      # CLS, not rotated
+    dict(has_cls=0, tubelet=2, frames=4, mask="bidir"),      # V-JEPA 2 shape
+    dict(),                                                  # block-causal, CLS
+])
+def test_rope_encoder_matches_brute_force(kw):
+    """dh 14: segments of 4 dims per axis and 2 left over, on a 2x3 patch
+    grid, against the scalar-loop encoder whose rotation is a complex
+    multiplication."""
+    dims = _tiny_dims(dim=28, heads=2, mlp_dim=32, img_h=4, img_w=6, rope=1, **kw)
+    w = _tiny_weights(dims, 31)
+    assert "enc.pos_embed" not in w
+    frames = synth.make_frames(dims, 2, 32)
+    y = E.encode(dims, w, frames)
+    ref = np.array(brute.encode(dims, w, frames))
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-11)
+    # and the rotation is not a no-op
+    y0 = E.encode(dict(dims, rope=0), dict(w, **{"enc.pos_embed": np.zeros((synth.n_tokens(dims), 28))}),
+                  frames)
+    assert np.abs(y - y0).max() > 1e-4
+
+
+# ---------------------------------------------------------------------------
 # block formats
 # ---------------------------------------------------------------------------
 

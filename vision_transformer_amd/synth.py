@@ -33,7 +33,7 @@ def _dims(**kw):
     d = dict(dim=192, depth=12, heads=3, mlp_dim=768, patch=14, tubelet=1,
              img_h=224, img_w=224, frames=1, has_cls=1, mask="bidir",
              ln_eps=1e-6, mean=(0.5, 0.5, 0.5), std=(0.5, 0.5, 0.5),
-             act_dtype="f32", mat_dtype="f32", rest_dtype="f32")
+             act_dtype="f32", mat_dtype="f32", rest_dtype="f32", rope=0)
     d.update(kw)
     return d
 
@@ -101,6 +101,28 @@ SMALL_WORKLOADS = {
                    img_h=64, img_w=96, frames=8, has_cls=0, mask="block_causal",
                    act_dtype="f16", mat_dtype="f16", rest_dtype="f16"),
         batch=2, frame_seed=15, weight_seed=25),
+    # 3-D rotary position instead of the additive table (V-JEPA 2 card: the
+    # encoder's "3-D RoPE"); with and without a CLS token
+    "small_rope_tubelet2_f16": dict(
+        dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
+                   img_h=96, img_w=112, frames=6, has_cls=0, act_dtype="f16",
+                   mat_dtype="f16", rest_dtype="f16", rope=1),
+        batch=2, frame_seed=16, weight_seed=26),
+    "small_rope_cls_blockcausal_bf16": dict(
+        dims=_dims(dim=192, depth=2, heads=3, mlp_dim=768, patch=16, img_h=64,
+                   img_w=80, frames=5, mask="block_causal", act_dtype="bf16",
+                   mat_dtype="bf16", rest_dtype="bf16", rope=1),
+        batch=2, frame_seed=17, weight_seed=27),
+    "small_rope_f32": dict(
+        dims=_dims(dim=128, depth=2, heads=2, mlp_dim=256, patch=14, img_h=84,
+                   img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
+                   rest_dtype="f32", rope=1),
+        batch=2, frame_seed=18, weight_seed=28),
+    "small_rope_q4_0": dict(
+        dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
+                   img_h=96, img_w=112, frames=6, has_cls=0, act_dtype="f16",
+                   mat_dtype="q4_0", rest_dtype="f16", rope=1),
+        batch=2, frame_seed=19, weight_seed=29),
 }
 
 
@@ -144,7 +166,8 @@ def tensor_specs(dims: dict) -> list[tuple[str, int, int]]:
     s = [("enc.patch_embed.weight", P, D), ("enc.patch_embed.bias", D, 1)]
     if dims["has_cls"]:
         s.append(("enc.cls_token", D, 1))
-    s.append(("enc.pos_embed", D, N))
+    if not dims.get("rope"):
+        s.append(("enc.pos_embed", D, N))
     for i in range(dims["depth"]):
         p = f"enc.blk.{i}."
         s += [(p + "ln1.weight", D, 1), (p + "ln1.bias", D, 1),
