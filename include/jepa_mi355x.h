@@ -69,7 +69,14 @@ typedef enum { JEPA_POOL_NONE = 0, JEPA_POOL_CLS = 1, JEPA_POOL_MEAN = 2 } jepa_
  * operands; accumulation, the residual stream, LayerNorm statistics and
  * softmax are f32 throughout.  Under JEPA_MASK_BLOCK_CAUSAL a patch token of
  * temporal slot t attends to the patch tokens of slots <= t and not to CLS;
- * CLS attends to every token. */
+ * CLS attends to every token.
+ * rope = 1 selects 3-D rotary position (V-JEPA 2 card, opening paragraph:
+ * the encoder uses "3-D RoPE"; the rotation is RoFormer's) instead of the
+ * additive table enc.pos_embed, which is then not part of the schema: in
+ * every block, before the scores, each head's q and k are rotated pairwise,
+ * dims (2i, 2i+1) of segment a (a = 0, 1, 2: temporal slot, patch row, patch
+ * column, 20 dims each, dims 60-63 untouched) by pos_a * 10000^(-i/10)
+ * radians.  A CLS token has no position and is not rotated. */
 typedef struct {
     int32_t dim, depth, heads, mlp_dim;
     int32_t patch, tubelet, img_h, img_w, frames;
@@ -79,6 +86,7 @@ typedef struct {
     float ln_eps;
     float mean[3];
     float std[3];
+    int32_t rope;       /* 0: additive enc.pos_embed; 1: 3-D rotary position */
 } jepa_dims;
 
 /* One stored tensor, host memory.  ne0 = row length (in-features), ne1 =
@@ -86,7 +94,7 @@ typedef struct {
  * of ne0*ne1 elements of dtype.  Names and shapes (D = dim, F = mlp_dim,
  * P = tubelet*patch*patch*3, N = tokens per item):
  *   enc.patch_embed.weight [ne0 P, ne1 D]   enc.patch_embed.bias [D]
- *   enc.cls_token [D] (only if has_cls)     enc.pos_embed [ne0 D, ne1 N]
+ *   enc.cls_token [D] (only if has_cls)     enc.pos_embed [ne0 D, ne1 N] (not if rope)
  *   enc.blk.{i}.ln1.weight/.bias [D]        enc.blk.{i}.ln2.weight/.bias [D]
  *   enc.blk.{i}.attn_qkv.weight [D, 3D] .bias [3D]   (columns [q | k | v],
  *       head a owns features a*64..a*64+63 of each third)

@@ -67,14 +67,17 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
  * b, each value rounded once to the act dtype.  Within a vt row, token n is
  * at position JEPA_VT_POS(n): each aligned run of 16 tokens is stored in the
  * order 0-3, 8-11, 4-7, 12-15, the order the attention kernel's operands
- * read.  Positions holding no token are not written.  q_scale (0 or 1:
- * none) multiplies the q columns before their rounding, e.g.
- * JEPA_ATTN_Q_SCALE for jepa_op_attention's q_prescaled.  M % n_tokens == 0,
- * npad >= n_tokens rounded up to 16. */
+ * read.  Positions holding no token are not written.  rope (NULL: none),
+ * f32 device [n_tokens, 32, 2] as jepa_rope_table writes it: q and k of
+ * token n (row b*n_tokens + n), dims (2p, 2p+1) of every head, are rotated
+ * by the angle whose (cos, sin) is entry (n, p), in f32, before the scale.
+ * q_scale (0 or 1: none) then multiplies the q columns before their
+ * rounding, e.g. JEPA_ATTN_Q_SCALE for jepa_op_attention's q_prescaled.
+ * M % n_tokens == 0, npad >= n_tokens rounded up to 16. */
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
                              int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
                              int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             float q_scale, void *hip_stream);
+                             const float *rope, float q_scale, void *hip_stream);
 
 /* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
  * per head into vt act [batch, heads, 64, npad], token n at position
@@ -97,6 +100,16 @@ jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, cons
                               int64_t npad, int batch, int n_tokens, int heads, int has_cls,
                               int mask, int tokens_per_slot, int q_prescaled, void *out,
                               void *hip_stream);
+
+/* Host: the table of 3-D rotary position (see jepa_dims.rope; V-JEPA 2
+ * card, opening paragraph) for the token grid of dims: out f32 host
+ * [N, 32, 2], N = tokens per item, entry (n, p) = (cos, sin) of the angle of
+ * token n's dimension pair p: for a patch token at (slot t, row h, column w),
+ * pair 10a + i (a < 3, i < 10) has angle (t, h, w)[a] * 10000^(-i/10);
+ * pairs 30 and 31, and every pair of a CLS token, have angle 0.  Angles and
+ * their cos / sin are evaluated in double and rounded once to f32.  dims is
+ * validated as by jepa_create (rope itself may be 0 or 1). */
+jepa_status jepa_rope_table(const jepa_dims *dims, float *out);
 
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
  * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2

@@ -1,5 +1,6 @@
 """The C-ABI library on the CPU: it loads, exports every declared entry point,
-and its host-side logic (validation, the quantizer, block packing) is right.
+and its host-side logic (validation, the quantizer, block packing, the rotary
+table) is right.
 Nothing here launches a GPU kernel."""
 import ctypes
 import os
@@ -8,6 +9,7 @@ import re
 import numpy as np
 import pytest
 
+from oracle import encoder as E
 from oracle import quant as Q
 from vision_transformer_amd import synth
 
@@ -134,3 +136,32 @@ def test_null_context_calls_fail_cleanly(lib):
     assert lib.jepa_last_compute_ms(None) < 0
     assert lib.jepa_model_n_bytes(None) == 0
     lib.jepa_free(None)
+
+
+# ---------------------------------------------------------------------------
+# 3-D rotary position: the host table and the schema
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["vjepa2_vit_l16_64f256_f16", "small_rope_cls_blockcausal_bf16"])
+def test_rope_table_is_the_oracle_angles(lib, name):
+    """jepa_rope_table's (cos, sin) are the oracle's angles' cos / sin rounded
+    to f32 (to within the one ulp by which two libm's may differ)."""
+    dims = dict(synth.workload(name)["dims"], rope=1)
+    got = lib.jepa_rope_table(dims)
+    ang = E.rope_angles(dims)
+    assert got.shape == (synth.n_tokens(dims), 32, 2)
+    np.testing.assert_allclose(got[..., 0], np.cos(ang), rtol=0, atol=1.2e-7)
+    np.testing.assert_allclose(got[..., 1], np.sin(ang), rtol=0, atol=1.2e-7)
+    assert np.array_equal(got[:, 30:], np.tile(np.float32([1, 0]), (got.shape[0], 2, 1)))
+
+
+def test_create_with_rope_has_no_pos_table(lib):
+    wl = synth.workload("small_rope_tubelet2_f16")
+    dims = wl["dims"]
+    stored = synth.stored_weights(dims, synth.make_f32_weights(dims, 1))
+    extra = dict(name="enc.pos_embed", dtype="f16", ne0=dims["dim"], ne1=synth.n_tokens(dims),
+                 data=np.zeros(dims["dim"] * synth.n_tokens(dims), np.uint16))
+    msg = _expect_error(lib, "JEPA_E_INVALID_ARG", dims, stored + [extra])
+    assert "enc.pos_embed" in msg
+    _expect_error(lib, "JEPA_E_INVALID_ARG", dict(dims, rope=2), stored)
+    _expect_error(lib, "JEPA_E_MISSING_TENSOR", dict(dims, rope=0), stored)

@@ -3,9 +3,10 @@
 * Small workloads (the oracle runs in seconds): every token of the token map,
   and the CLS / mean pools, against the oracle computed live.
 * The ViT-Ti/14 f32 image workload at its full size, live.
-* The four ViT-L workloads at full size, in the launch configuration the
-  benchmark times: sampled token rows and the pooled features against the
-  oracle's stored outputs (tests/golden/make_golden.py).
+* The ViT-L workloads at full size (additive or 3-D rotary position), in
+  the launch configuration the benchmark times: sampled token rows and the
+  pooled features against the oracle's stored outputs
+  (tests/golden/make_golden.py).
 * Invariants that must hold bit for bit: block-causal causality, the CLS
   token being read-only, batch items being independent.
 * Dequantised weights bit-exact against the oracle.
@@ -78,7 +79,7 @@ def test_vit_ti14_image_f32_full(Encoder):
 
 FULL = ["vit_l16_image_bf16_b32", "levjepa_vit_l16_16f_bf16_b4",
         "vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_f16",
-        "vjepa2_vit_l16_64f256_q4_0"]
+        "vjepa2_vit_l16_64f256_q4_0", "vjepa2_rope_vit_l16_16f256_f16_b4"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -150,6 +150,7 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("rope", [False, True], ids=["norope", "rope"])
 @pytest.mark.parametrize("q_scale", [0.0, 0.18033688011112042], ids=["q", "qscaled"])
 @pytest.mark.parametrize("act,wfmt,B,N,heads,K", [
     ("bf16", "dense", 7, 197, 4, 256),      # M = 1379: 256-row tiles, items straddling 32-row blocks
@@ -159,11 +160,13 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     ("f32", "dense", 2, 85, 2, 64),
     ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
 ])
-def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale):
-    """q and k columns as a plain linear layer (q times q_scale before its one
-    rounding); v columns straight into V^T [B, heads, 64, npad] (the
-    attention kernel's layout), padding untouched."""
-    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K} q_scale={q_scale}")
+def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale, rope):
+    """q and k columns as a plain linear layer (rotated pairwise by a table of
+    per-token angles, then q times q_scale, before their one rounding); v
+    columns straight into V^T [B, heads, 64, npad] (the attention kernel's
+    layout), padding untouched.  The angles are seeded uniform in [-pi, pi]
+    for every token and pair, so every table entry is exercised."""
+    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K} q_scale={q_scale} rope={rope}")
     rng = np.random.default_rng(47)
     M, D = B * N, heads * 64
     a_dev, a = rounded(act, rng.standard_normal((M, K)))
@@ -184,9 +187,27 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale):
     npad = -(-N // 64) * 64
     qk = torch.zeros((M, 3 * D), dtype=tdt, device="cuda")
     vt = torch.full((B, heads, 64, npad), 7.0, dtype=tdt, device="cuda")
+    table = None
+    if rope:
+        ang = np.random.default_rng(48).uniform(-math.pi, math.pi, (N, 32))
+        table = torch.from_numpy(np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)).cuda()
     lib.jepa_op_gemm_qkv(act, a_dev, w_dev, wfmt if wfmt != "dense" else act, heads,
-                         torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale, q_scale=q_scale)
-    bound = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T) + OUT_REL[act] * np.abs(ref) + 1e-6
+                         torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale, q_scale=q_scale,
+                         rope=table)
+    pre = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T) + 1e-6
+    if rope:
+        # oracle rotation of every head's q and k; the f32 rotation adds at
+        # most e0 + e1 of the pair's errors plus a few f32 roundings of
+        # |z0| + |z1| (the table's cos / sin are rounded too)
+        ref = ref.copy()
+        ang_b = np.tile(ang, (B, 1))
+        for c0 in range(0, 2 * D, 64):
+            z = ref[:, c0:c0 + 64].copy()
+            ref[:, c0:c0 + 64] = E.rope(z, ang_b)
+            e = pre[:, c0:c0 + 64].reshape(M, 32, 2).sum(-1)
+            zz = np.abs(z).reshape(M, 32, 2).sum(-1)
+            pre[:, c0:c0 + 64] = np.repeat(e + 4 * 2.0 ** -24 * zz, 2, axis=1)
+    bound = pre + OUT_REL[act] * np.abs(ref)
     if q_scale:
         ref = ref.copy()
         ref[:, :D] *= q_scale

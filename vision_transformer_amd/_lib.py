@@ -35,7 +35,8 @@ class jepa_dims(C.Structure):
                 ("mlp_dim", C.c_int32), ("patch", C.c_int32), ("tubelet", C.c_int32),
                 ("img_h", C.c_int32), ("img_w", C.c_int32), ("frames", C.c_int32),
                 ("has_cls", C.c_int32), ("mask", C.c_int32), ("act_dtype", C.c_int32),
-                ("ln_eps", C.c_float), ("mean", C.c_float * 3), ("std", C.c_float * 3)]
+                ("ln_eps", C.c_float), ("mean", C.c_float * 3), ("std", C.c_float * 3),
+                ("rope", C.c_int32)]
 
 
 class jepa_tensor(C.Structure):
@@ -72,10 +73,11 @@ def _load():
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
-        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, C.c_float, P]),
+        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, P, C.c_float, P]),
         "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, I, P, P]),
         "jepa_op_transpose_v": (I, [I, P, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
+        "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -115,7 +117,7 @@ def make_dims(d: dict) -> jepa_dims:
     return jepa_dims(d["dim"], d["depth"], d["heads"], d["mlp_dim"], d["patch"], d["tubelet"],
                      d["img_h"], d["img_w"], d["frames"], int(d["has_cls"]), MASK[d["mask"]],
                      DTYPE[d["act_dtype"]], float(d["ln_eps"]), (C.c_float * 3)(*d["mean"]),
-                     (C.c_float * 3)(*d["std"]))
+                     (C.c_float * 3)(*d["std"]), int(d.get("rope", 0)))
 
 
 def jepa_create(dims: dict, tensors: list[dict]) -> int:
@@ -239,13 +241,24 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
 
 
 def jepa_op_gemm_qkv(act_dtype: str, a, w, w_dtype: str, heads: int, bias, n_tokens: int, qk_out, vt,
-                     w_scale=None, q_scale: float = 0.0, stream=None) -> None:
-    """q, k columns -> qk_out [M, ld] (q times q_scale if nonzero); v columns
-    transposed -> vt [M/n_tokens, heads, 64, npad]."""
+                     w_scale=None, q_scale: float = 0.0, rope=None, stream=None) -> None:
+    """q, k columns -> qk_out [M, ld] (rotated by the rope table [n_tokens,
+    32, 2] if given, then q times q_scale if nonzero); v columns transposed ->
+    vt [M/n_tokens, heads, 64, npad]."""
     M, K = a.shape
     _check(_lib.jepa_op_gemm_qkv(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
                                  heads, _ptr(bias), n_tokens, _ptr(qk_out), qk_out.shape[1], _ptr(vt),
-                                 vt.shape[-1], float(q_scale), _stream(stream)))
+                                 vt.shape[-1], _ptr(rope), float(q_scale), _stream(stream)))
+
+
+def jepa_rope_table(dims: dict) -> np.ndarray:
+    """Host: the 3-D rotary table of dims' token grid, f32 [N, 32, 2] (cos, sin)."""
+    d = make_dims(dims)
+    n = (dims["frames"] // dims["tubelet"]) * (dims["img_h"] // dims["patch"]) * \
+        (dims["img_w"] // dims["patch"]) + int(dims["has_cls"])
+    out = np.empty((n, 32, 2), np.float32)
+    _check(_lib.jepa_rope_table(C.byref(d), out.ctypes.data))
+    return out
 
 
 # log2(e) / sqrt(64): JEPA_ATTN_Q_SCALE, the factor jepa_op_gemm_qkv folds into q

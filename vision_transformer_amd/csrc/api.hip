@@ -144,6 +144,7 @@ struct jepa_ctx {
     size_t arena_bytes = 0, model_bytes = 0;
     DevTensor wpe;
     float *bpe = nullptr, *cls = nullptr, *pos = nullptr, *normg = nullptr, *normb = nullptr;
+    float *rope = nullptr;      // 3-D rotary table [N, 32] (cos, sin), or null
     std::vector<Layer> layers;
     std::map<std::string, DevTensor> by_name;
     // workspace
@@ -286,6 +287,7 @@ jepa_status check_dims(const jepa_dims *d) {
         return fail(JEPA_E_SHAPE, "dims: img_h, img_w must be multiples of patch");
     if (d->frames % d->tubelet) return fail(JEPA_E_SHAPE, "dims: frames %% tubelet != 0");
     if (d->has_cls != 0 && d->has_cls != 1) return fail(JEPA_E_INVALID_ARG, "dims: has_cls must be 0 or 1");
+    if (d->rope != 0 && d->rope != 1) return fail(JEPA_E_INVALID_ARG, "dims: rope must be 0 or 1");
     if (d->mask != JEPA_MASK_BIDIR && d->mask != JEPA_MASK_BLOCK_CAUSAL)
         return fail(JEPA_E_INVALID_ARG, "dims: unknown mask %d", d->mask);
     if (d->act_dtype != JEPA_F32 && d->act_dtype != JEPA_F16 && d->act_dtype != JEPA_BF16)
@@ -294,6 +296,28 @@ jepa_status check_dims(const jepa_dims *d) {
     for (int c = 0; c < 3; ++c)
         if (!(d->std[c] != 0.f)) return fail(JEPA_E_INVALID_ARG, "dims: std[%d] is 0", c);
     return JEPA_OK;
+}
+
+// 3-D rotary position (V-JEPA 2 card, opening paragraph; RoFormer's pairwise
+// rotation): [N, 32] (cos, sin) for head_dim 64, three 20-dim segments for
+// the temporal slot, patch row and patch column, pair i of a segment at
+// frequency 10000^(-i/10); pairs 30, 31 and a CLS token have angle 0.
+void rope_table(const jepa_dims &d, float *out) {
+    const int Hp = d.img_h / d.patch, Wp = d.img_w / d.patch;
+    const int Np = d.frames / d.tubelet * Hp * Wp, N = Np + d.has_cls;
+    for (int n = 0; n < N; ++n) {
+        float *row = out + (size_t)n * 64;
+        for (int p = 0; p < 32; ++p) { row[2 * p] = 1.f; row[2 * p + 1] = 0.f; }
+        if (d.has_cls && n == 0) continue;
+        const int pn = n - d.has_cls;
+        const int pos[3] = {pn / (Hp * Wp), pn / Wp % Hp, pn % Wp};
+        for (int a = 0; a < 3; ++a)
+            for (int i = 0; i < 10; ++i) {
+                const double ang = pos[a] * pow(10000.0, -i / 10.0);
+                row[2 * (10 * a + i)] = (float)cos(ang);
+                row[2 * (10 * a + i) + 1] = (float)sin(ang);
+            }
+    }
 }
 
 // [blocks](f16 scale, payload) -> payloads then scales
@@ -370,7 +394,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     want["enc.patch_embed.weight"] = {P, D, false};
     want["enc.patch_embed.bias"] = {D, 1, false};
     if (d.has_cls) want["enc.cls_token"] = {D, 1, false};
-    want["enc.pos_embed"] = {D, N, false};
+    if (!d.rope) want["enc.pos_embed"] = {D, N, false};
     want["enc.norm.weight"] = {D, 1, false};
     want["enc.norm.bias"] = {D, 1, false};
     for (int i = 0; i < d.depth; ++i) {
@@ -461,6 +485,14 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         }
         plan.push_back(p);
     }
+    // the rotary table follows the weights
+    const size_t rope_off = off;
+    std::vector<float> rope_host;
+    if (d.rope) {
+        rope_host.resize((size_t)N * 64);
+        rope_table(d, rope_host.data());
+        off += align256(rope_host.size() * 4);
+    }
     if (hipMalloc(&c->arena, off) != hipSuccess) {
         (void)hipGetLastError();
         delete c;
@@ -468,6 +500,10 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     }
     c->arena_bytes = off;
     unsigned char *arena = (unsigned char *)c->arena;
+    if (d.rope && hipMemcpy(arena + rope_off, rope_host.data(), rope_host.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        jepa_free(c);
+        return fail(JEPA_E_HIP, "create: upload of the rotary table failed");
+    }
 
     std::vector<unsigned char> host;
     for (auto &p : plan) {
@@ -521,7 +557,8 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     c->wpe = c->by_name["enc.patch_embed.weight"];
     c->bpe = vecp("enc.patch_embed.bias");
     c->cls = d.has_cls ? vecp("enc.cls_token") : nullptr;
-    c->pos = vecp("enc.pos_embed");
+    c->pos = d.rope ? nullptr : vecp("enc.pos_embed");
+    c->rope = d.rope ? (float *)(arena + rope_off) : nullptr;
     c->normg = vecp("enc.norm.weight");
     c->normb = vecp("enc.norm.bias");
     c->layers.resize(d.depth);
@@ -666,6 +703,7 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
                 g.a = hn; g.w = L.qkv.ptr; g.wscale = L.qkv.scale; g.bias = L.bqkv; g.out = qkv;
                 g.M = M; g.N = L.qkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
                 g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
+                g.rope = c->rope;
                 g.qscale = ATTN_Q_SCALE;   // the softmax scale and base change, folded into q
                 g.conc = parts;
                 TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, L.qkv.dev_dt, EPI_QKV, g, s); }));
@@ -859,7 +897,7 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
                              int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
                              int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             float q_scale, void *hip_stream) {
+                             const float *rope, float q_scale, void *hip_stream) {
     if (!a || !w || !bias || !qk_out || !vt) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_gemm_qkv: bad act dtype");
     if (heads <= 0 || n_tokens <= 0) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: heads and n_tokens must be > 0");
@@ -867,6 +905,7 @@ jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K,
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = qk_out;
     g.M = M; g.N = 3 * (int64_t)heads * 64; g.K = K; g.lda = K; g.ldo = ld_qk;
     g.ntok = n_tokens; g.vt = vt; g.npad = npad; g.vcol0 = 2 * (int64_t)heads * 64;
+    g.rope = rope;
     g.qscale = q_scale == 1.f ? 0.f : q_scale;
     return hip_status(launch_gemm(act_dtype, w_dtype, EPI_QKV, g, (hipStream_t)hip_stream), "op_gemm_qkv");
 }
@@ -903,6 +942,13 @@ jepa_status jepa_pack_blocks(int dtype, const uint8_t *blocks, int64_t rows, int
     if (dtype != JEPA_Q8_0 && dtype != JEPA_Q4_0) return fail(JEPA_E_DTYPE, "pack_blocks: dtype must be Q8_0 or Q4_0");
     if (cols % 32) return fail(JEPA_E_SHAPE, "pack_blocks: cols not a multiple of 32");
     pack_blocks(dtype, blocks, rows * (cols / 32), codes, scales);
+    return JEPA_OK;
+}
+
+jepa_status jepa_rope_table(const jepa_dims *dims, float *out) {
+    if (!dims || !out) return fail(JEPA_E_INVALID_ARG, "rope_table: null argument");
+    TRY(check_dims(dims));
+    rope_table(*dims, out);
     return JEPA_OK;
 }
 

@@ -88,7 +88,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, int64_t row, int64_t
     } else {  // EPI_PATCH
         const int64_t b = row / g.np, n = row - b * g.np;
         const int64_t t = g.has_cls + n;
-        ((float *)g.out)[(b * g.ntok + t) * g.ldo + col] = z + g.pos[t * g.ldo + col];
+        ((float *)g.out)[(b * g.ntok + t) * g.ldo + col] = g.pos ? z + g.pos[t * g.ldo + col] : z;
     }
 }
 
@@ -229,6 +229,10 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
 #pragma unroll
     for (int i = 0; i < MB_; ++i) {
         __builtin_amdgcn_sched_barrier(0);       // keep the loads where they are issued
+        // EPI_QKV with rotary position: this lane's token (rows past M wrap to
+        // a valid table row; they are dropped at the store)
+        uint32_t rn = 0;
+        if constexpr (EPI == EPI_QKV) rn = (uint32_t)(row0 + 32 * i + rl) % (uint32_t)g.ntok;
         // stage block row i
 #pragma unroll
         for (int j = 0; j < NB_; ++j)
@@ -239,6 +243,15 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
                               acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
                 if constexpr (EPI == EPI_QKV) {
+                    if (g.rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
+                        const uint32_t p = (uint32_t)((col0 + col) & 63) >> 1;
+                        const float4 r = *(const float4 *)(g.rope + 2 * (rn * 32 + p));
+                        const float z0 = z[0], z2 = z[2];
+                        z[0] = z0 * r.x - z[1] * r.y;
+                        z[1] = z0 * r.y + z[1] * r.x;
+                        z[2] = z2 * r.z - z[3] * r.w;
+                        z[3] = z2 * r.w + z[3] * r.z;
+                    }
                     const float cs = col_scale(col);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) z[r] *= cs;
@@ -787,11 +800,11 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % bk || g.N % 64) return hipErrorInvalidValue;
     if (g.lda < g.K || (epi != EPI_PATCH && g.ldo < g.N)) return hipErrorInvalidValue;
     if (g.M / BM >= 65535) return hipErrorInvalidValue;
-    if (epi == EPI_PATCH && (g.np <= 0 || g.M % g.np || !g.pos)) return hipErrorInvalidValue;
+    if (epi == EPI_PATCH && (g.np <= 0 || g.M % g.np)) return hipErrorInvalidValue;
     if (epi == EPI_QKV) {
         // v starts at a multiple of 128 columns, so no wave straddles q/k and v
         if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
-            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16)
+            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15))
             return hipErrorInvalidValue;
         if ((g.M / g.ntok) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
     }

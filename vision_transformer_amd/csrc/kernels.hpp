@@ -33,7 +33,7 @@ struct GemmArgs {
     void *out;               // STORE/GELU: act dtype [M, ldo]; RESID/PATCH: f32
     int64_t M, N, K, lda, ldo;
     // EPI_PATCH: row r = b*np + n goes to output row b*ntok + has_cls + n and
-    // adds pos[has_cls + n]
+    // adds pos[has_cls + n] (pos null: nothing)
     const float *pos;
     int np, ntok, has_cls;
     // EPI_QKV: columns < vcol0 as EPI_STORE; columns >= vcol0 (the v part,
@@ -41,8 +41,11 @@ struct GemmArgs {
     // row r = b*ntok + n being token n of item b
     void *vt;
     int64_t npad, vcol0;
-    // EPI_QKV: the q columns [0, vcol0 / 2) are multiplied by qscale before
-    // rounding (0: left as they are)
+    // EPI_QKV: with rope (else null), f32 [ntok, 32] (cos, sin) pairs, the
+    // q and k columns' dims (2p, 2p+1) of each head of token n = row % ntok
+    // are rotated by entry (n, p) first; then the q columns [0, vcol0 / 2) are
+    // multiplied by qscale before rounding (0: left as they are)
+    const float *rope;
     float qscale;
     // launches of this shape expected to run concurrently (batch parts on
     // other streams; 0 or 1: none), a hint for the tile-shape choice
@@ -79,7 +82,7 @@ hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int hea
                               int64_t npad, hipStream_t s);
 
 // ---- small helpers ----------------------------------------------------------
-// X[b*N + 0] = cls + pos[0] for every item
+// X[b*N + 0] = cls + pos[0] for every item (pos null: cls)
 hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
                            hipStream_t s);
 // pooling of a token map y [B, N, D]

@@ -101,7 +101,7 @@ hipError_t ln_dispatch(const float *x, int64_t rows, int dim, const float *g, co
 // ---------------------------------------------------------------------------
 __global__ void cls_rows_kernel(float *x, const float *cls, const float *pos, int N, int D) {
     const int b = blockIdx.x;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) x[(int64_t)b * N * D + d] = cls[d] + pos[d];
+    for (int d = threadIdx.x; d < D; d += blockDim.x) x[(int64_t)b * N * D + d] = pos ? cls[d] + pos[d] : cls[d];
 }
 
 __global__ void pool_cls_kernel(const float *y, int N, int D, float *out) {

@@ -40,7 +40,7 @@ def _dims(**kw):
 
 _VITL = dict(dim=1024, depth=24, heads=16, mlp_dim=4096, patch=16)
 
-# The five full-size workloads.  Each entry: dims, batch, frame seed, weight
+# The full-size workloads.  Each entry: dims, batch, frame seed, weight
 # seed, which pooled outputs the workload reports.
 WORKLOADS = {
     "vit_ti14_image_f32": dict(
@@ -65,6 +65,12 @@ WORKLOADS = {
         dims=_dims(**_VITL, frames=64, tubelet=2, img_h=256, img_w=256, has_cls=0,
                    act_dtype="f16", mat_dtype="q4_0", rest_dtype="f16"),
         batch=1, frame_seed=1004, weight_seed=2004, outputs=("tokens", "mean")),
+    # the V-JEPA 2 encoder with its 3-D rotary position instead of an
+    # additive table (V-JEPA 2 card, opening paragraph)
+    "vjepa2_rope_vit_l16_16f256_f16_b4": dict(
+        dims=_dims(**_VITL, frames=16, tubelet=2, img_h=256, img_w=256, has_cls=0,
+                   act_dtype="f16", mat_dtype="f16", rest_dtype="f16", rope=1),
+        batch=4, frame_seed=1005, weight_seed=2005, outputs=("mean",)),
 }
 
 # Small workloads the oracle finishes in seconds.  They keep the structure of
