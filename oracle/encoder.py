@@ -21,7 +21,7 @@ Where the pages are silent the readings are:
   R7  Pixels are normalised as (u / 255 - mean_c) / std_c.
   R8  Mean pooling averages the final-LayerNorm rows of the patch tokens
       only (CLS excluded).
-  R9  3-D rotary position (V-JEPA 2 encoders; the pages name "3-D RoPE" and
+  R12 3-D rotary position (V-JEPA 2 encoders; the pages name "3-D RoPE" and
       give no formula).  The plainest reading of the published technique
       (RoFormer rotary embedding, one axis per third of the head): each
       head's dimensions are cut into three segments of ds = 2*floor(dh/6)
@@ -125,7 +125,7 @@ def attention_head(q, k, v, allowed):
 
 
 def rope_angles(dims: dict) -> np.ndarray:
-    """[N, dh/2] rotation angle of every token and dimension pair (R9)."""
+    """[N, dh/2] rotation angle of every token and dimension pair (R12)."""
     dh = dims["dim"] // dims["heads"]
     ds = 2 * (dh // 6)
     Tt = dims["frames"] // dims["tubelet"]
@@ -142,7 +142,7 @@ def rope_angles(dims: dict) -> np.ndarray:
 
 
 def rope(x: np.ndarray, ang: np.ndarray) -> np.ndarray:
-    """x [N, dh] of one head: pair (2p, 2p+1) of token n rotated by ang[n, p] (R9)."""
+    """x [N, dh] of one head: pair (2p, 2p+1) of token n rotated by ang[n, p] (R12)."""
     c, s = np.cos(ang), np.sin(ang)
     y = np.empty_like(x)
     y[:, 0::2] = x[:, 0::2] * c - x[:, 1::2] * s
@@ -154,7 +154,7 @@ def attention(qkv: np.ndarray, heads: int, allowed, threads: int = 8, ang=None) 
     """Multi-head attention of one item.
 
     qkv [N, 3D] with columns [q | k | v] (R3) -> concat of head outputs [N, D].
-    With ang (rope_angles), q and k are rotated per head first (R9).  Heads are
+    With ang (rope_angles), q and k are rotated per head first (R12).  Heads are
     independent, so they are evaluated on a thread pool; each is the plain
     definition.
     """
@@ -202,7 +202,7 @@ def embed(dims: dict, w: dict, frames: np.ndarray) -> np.ndarray:
     if dims["has_cls"]:
         cls = np.broadcast_to(w["enc.cls_token"], (e.shape[0], 1, e.shape[2]))
         e = np.concatenate([cls, e], axis=1)
-    return e + w["enc.pos_embed"] if "enc.pos_embed" in w else e     # none with rotary position (R9)
+    return e + w["enc.pos_embed"] if "enc.pos_embed" in w else e     # none with rotary position (R12)
 
 
 def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed) -> np.ndarray:
