@@ -175,7 +175,13 @@ size_t jepa_model_n_bytes(const jepa_ctx *ctx);
 /* Bytes of device memory the context holds for weights. */
 size_t jepa_device_weight_bytes(const jepa_ctx *ctx);
 
-/* Bytes of device workspace an encode of `batch` items needs. */
+/* Bytes of device workspace an encode of `batch` items needs (with the
+ * current batch-part setting).  It includes, for a model with Q8_0 / Q4_0
+ * block matrices and batch parts of 1024 or more token rows, an
+ * activation-dtype copy of those matrices that each such encode rewrites
+ * from the blocks before its first layer (the GEMMs then run dense);
+ * smaller batches dequantise inside the GEMM and need no copy.  The
+ * environment variable JEPA_Q_EXPAND = 0 or 1 forces either way. */
 size_t jepa_workspace_bytes(const jepa_ctx *ctx, int batch);
 
 /* Write the f32 value of every element of the named tensor, as the GEMMs

@@ -210,6 +210,45 @@ def test_graph_replay_matches_eager(Encoder, parts):
     enc.close()
 
 
+@pytest.mark.parametrize("name", ["small_tubelet2_q8_0", "small_tubelet2_q4_0", "small_rope_q4_0"])
+def test_expanded_block_matrices_every_token(Encoder, name, monkeypatch):
+    """JEPA_Q_EXPAND=1: the q8_0 / q4_0 matrices are expanded to the act dtype
+    at the start of the encode and the GEMMs run dense; every token and the
+    mean pool against the oracle.  The workspace size counts the copy."""
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
+    enc = Encoder(dims, stored)
+    plain = _lib.jepa_workspace_bytes(enc.ctx, wl["batch"])
+    monkeypatch.setenv("JEPA_Q_EXPAND", "1")
+    H.say(f"encoder {name}, block matrices expanded")
+    assert _lib.jepa_workspace_bytes(enc.ctx, wl["batch"]) > plain
+    y_dev = _run(enc, frames)
+    ref = H.oracle_tokens(dims, stored, frames)
+    H.check_rows(dims["act_dtype"], y_dev.cpu().numpy(), ref, "tokens")
+    _check_pools(enc, dims, ref, wl["batch"])
+    enc.close()
+
+
+def test_expansion_chosen_by_rows_per_part(Encoder, monkeypatch):
+    """Without the override, 9 items of 126 tokens in one part (1134 rows)
+    take the expanded path and match the oracle; in 4 parts (at most 378
+    rows each) they do not expand."""
+    from vision_transformer_amd import _lib
+    monkeypatch.delenv("JEPA_Q_EXPAND", raising=False)
+    wl, dims, _, stored = H.workload_inputs("small_tubelet2_q8_0", ln_affine=True)
+    frames = synth.make_frames(dims, 9, 78)
+    enc = Encoder(dims, stored)
+    _lib.jepa_set_batch_parts(enc.ctx, 4)
+    small = _lib.jepa_workspace_bytes(enc.ctx, 9)
+    _lib.jepa_set_batch_parts(enc.ctx, 1)
+    assert _lib.jepa_workspace_bytes(enc.ctx, 9) > small
+    H.say("encoder small_tubelet2_q8_0, batch 9 in one part")
+    y_dev = _run(enc, frames)
+    ref = H.oracle_tokens(dims, stored, frames)
+    H.check_rows(dims["act_dtype"], y_dev.cpu().numpy(), ref, "tokens")
+    enc.close()
+
+
 def test_host_frames_match_device_frames(Encoder):
     wl, dims, frames, stored = H.workload_inputs("small_bidir_cls_bf16")
     enc = Encoder(dims, stored)

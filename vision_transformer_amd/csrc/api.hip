@@ -113,9 +113,9 @@ float stored_to_f32(int dt, const void *data, int64_t i) {
 
 const char *kClassNames[] = {"patchify", "gemm_patch", "cls_rows", "layernorm", "gemm_qkv",
                              "transpose_v", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                             "final_ln", "pool"};
+                             "final_ln", "pool", "expand_weights"};
 enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_TRANSPOSE_V, K_ATTN,
-              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_COUNT };
+              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_EXPAND, K_COUNT };
 
 struct DevTensor {
     void *ptr = nullptr;        // device data
@@ -126,6 +126,7 @@ struct DevTensor {
 
 struct Layer {
     DevTensor qkv, out, up, down;
+    DevTensor xqkv, xout, xup, xdown;   // q8_0 / q4_0 ones expanded to the act dtype (when in use)
     float *ln1g, *ln1b, *ln2g, *ln2b, *bqkv, *bout, *bup, *bdown;
 };
 
@@ -145,6 +146,13 @@ struct jepa_ctx {
     DevTensor wpe;
     float *bpe = nullptr, *cls = nullptr, *pos = nullptr, *normg = nullptr, *normb = nullptr;
     float *rope = nullptr;      // 3-D rotary table [N, 32] (cos, sin), or null
+    // q8_0 / q4_0 block matrices expanded to the act dtype for large batches
+    bool has_q = false;
+    void *xbuf = nullptr;       // expansion jobs, then the expanded matrices
+    size_t xbuf_bytes = 0;
+    const ExpandJob *xjobs = nullptr;
+    int n_xjobs = 0;
+    int64_t x_nblk = 0;
     std::vector<Layer> layers;
     std::map<std::string, DevTensor> by_name;
     // workspace
@@ -198,6 +206,82 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
     w.y = take(M * c->D * 4);
     w.total = off;
     return w;
+}
+
+// Large batches run the q8_0 / q4_0 layers as dense GEMMs on an act-dtype copy
+// of the block matrices, expanded once per encode (a bandwidth-bound pass:
+// 1 + 1/16 bytes read and 2 written per weight for q8_0).  Above ~1024 rows
+// per batch part the GEMMs take the 256-row MFMA tiles, whose operands flow
+// straight from memory into LDS; a dequantising load would put the
+// conversion on the VALU inside the K loop, and an int8 MFMA path with
+// per-block rescaling is VALU-bound on this chip.  Small batches keep the
+// dequantising 128 x 128 tile.  JEPA_Q_EXPAND = 0 / 1 forces either.
+std::vector<DevTensor *> q_matrices(jepa_ctx *c) {
+    std::vector<DevTensor *> v;
+    for (auto &L : c->layers)
+        for (DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
+            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) v.push_back(t);
+    return v;
+}
+
+size_t expand_bytes(const jepa_ctx *c) {
+    size_t n = 0, jobs = 0;
+    for (const auto &L : c->layers)
+        for (const DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
+            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) {
+                n += align256((size_t)t->ne0 * t->ne1 * c->es);
+                ++jobs;
+            }
+    return jobs ? align256(jobs * sizeof(ExpandJob)) + n : 0;
+}
+
+bool use_expand(const jepa_ctx *c, int batch, int parts) {
+    if (!c->has_q) return false;
+    if (const char *e = getenv("JEPA_Q_EXPAND")) {
+        if (!strcmp(e, "0")) return false;
+        if (!strcmp(e, "1")) return true;
+    }
+    return (int64_t)((batch + parts - 1) / parts) * c->N >= 1024;
+}
+
+jepa_status ensure_expanded(jepa_ctx *c) {
+    if (c->xbuf) return JEPA_OK;
+    const size_t bytes = expand_bytes(c);
+    if (hipMalloc(&c->xbuf, bytes) != hipSuccess) {
+        c->xbuf = nullptr;
+        (void)hipGetLastError();
+        return fail(JEPA_E_OOM, "hipMalloc of %zu bytes for the expanded block matrices failed", bytes);
+    }
+    auto mats = q_matrices(c);
+    unsigned char *base = (unsigned char *)c->xbuf;
+    size_t off = align256(mats.size() * sizeof(ExpandJob));
+    std::vector<ExpandJob> jobs;
+    int64_t blk = 0;
+    for (auto &L : c->layers) {
+        for (auto pr : {std::make_pair(&L.qkv, &L.xqkv), std::make_pair(&L.out, &L.xout),
+                        std::make_pair(&L.up, &L.xup), std::make_pair(&L.down, &L.xdown)}) {
+            const DevTensor &t = *pr.first;
+            DevTensor &x = *pr.second;
+            x = t;
+            if (t.dev_dt != JEPA_Q8_0 && t.dev_dt != JEPA_Q4_0) continue;
+            x.dev_dt = c->act;
+            x.scale = nullptr;
+            x.ptr = base + off;
+            jobs.push_back(ExpandJob{t.ptr, t.scale, x.ptr, blk, t.dev_dt});
+            blk += t.ne0 * t.ne1 / 32;
+            off += align256((size_t)t.ne0 * t.ne1 * c->es);
+        }
+    }
+    if (hipMemcpy(c->xbuf, jobs.data(), jobs.size() * sizeof(ExpandJob), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(c->xbuf);
+        c->xbuf = nullptr;
+        return fail(JEPA_E_HIP, "upload of the expansion jobs failed");
+    }
+    c->xbuf_bytes = bytes;
+    c->xjobs = (const ExpandJob *)c->xbuf;
+    c->n_xjobs = (int)jobs.size();
+    c->x_nblk = blk;
+    return JEPA_OK;
 }
 
 jepa_status ensure_workspace(jepa_ctx *c, int B) {
@@ -562,6 +646,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     c->normg = vecp("enc.norm.weight");
     c->normb = vecp("enc.norm.bias");
     c->layers.resize(d.depth);
+    c->has_q = false;
     for (int i = 0; i < d.depth; ++i) {
         const std::string p = "enc.blk." + std::to_string(i) + ".";
         Layer &L = c->layers[i];
@@ -573,6 +658,8 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         L.ln2g = vecp(p + "ln2.weight"); L.ln2b = vecp(p + "ln2.bias");
         L.bqkv = vecp(p + "attn_qkv.bias"); L.bout = vecp(p + "attn_out.bias");
         L.bup = vecp(p + "ffn_up.bias"); L.bdown = vecp(p + "ffn_down.bias");
+        for (const DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
+            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) c->has_q = true;
     }
     if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
         jepa_free(c);
@@ -640,6 +727,11 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     }
     float *Y = tokens_out ? tokens_out : c->w_y;
     HIP_TRY(hipEventRecord(c->ev0, s0));
+    const bool expand = use_expand(c, batch, parts);
+    if (expand) {
+        TRY(ensure_expanded(c));
+        TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
+    }
     if (parts > 1) {
         HIP_TRY(hipEventRecord(c->fork_ev, s0));
         for (int p = 1; p < parts; ++p) HIP_TRY(hipStreamWaitEvent(c->aux[p - 1], c->fork_ev, 0));
@@ -684,6 +776,8 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
 
     for (int i = 0; i < c->L; ++i) {
         const Layer &L = c->layers[i];
+        const DevTensor &Wqkv = expand ? L.xqkv : L.qkv, &Wout = expand ? L.xout : L.out;
+        const DevTensor &Wup = expand ? L.xup : L.up, &Wdown = expand ? L.xdown : L.down;
         for (int p = 0; p < parts; ++p) {
             const Part &q = P[p];
             const hipStream_t s = q.s;
@@ -700,19 +794,19 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
             {   // q, k to qkv; v transposed straight into V^T
                 GemmArgs g{};
-                g.a = hn; g.w = L.qkv.ptr; g.wscale = L.qkv.scale; g.bias = L.bqkv; g.out = qkv;
-                g.M = M; g.N = L.qkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
+                g.a = hn; g.w = Wqkv.ptr; g.wscale = Wqkv.scale; g.bias = L.bqkv; g.out = qkv;
+                g.M = M; g.N = Wqkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
                 g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
                 g.rope = c->rope;
                 g.qscale = ATTN_Q_SCALE;   // the softmax scale and base change, folded into q
                 g.conc = parts;
-                TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, L.qkv.dev_dt, EPI_QKV, g, s); }));
+                TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
             }
             TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
-            TRY(gemm(c, K_GEMM_OUT, s, parts, o, M, D, L.out, L.bout, EPI_RESID, x, D));
+            TRY(gemm(c, K_GEMM_OUT, s, parts, o, M, D, Wout, L.bout, EPI_RESID, x, D));
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
-            TRY(gemm(c, K_GEMM_FC1, s, parts, hn, M, D, L.up, L.bup, EPI_GELU, u, F));
-            TRY(gemm(c, K_GEMM_FC2, s, parts, u, M, F, L.down, L.bdown, EPI_RESID, x, D));
+            TRY(gemm(c, K_GEMM_FC1, s, parts, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
+            TRY(gemm(c, K_GEMM_FC2, s, parts, u, M, F, Wdown, L.bdown, EPI_RESID, x, D));
         }
     }
     for (int p = 0; p < parts; ++p) {
@@ -765,6 +859,7 @@ void jepa_free(jepa_ctx *c) {
     (void)hipDeviceSynchronize();
     if (c->arena) (void)hipFree(c->arena);
     if (c->ws) (void)hipFree(c->ws);
+    if (c->xbuf) (void)hipFree(c->xbuf);
     if (c->have_events) {
         (void)hipEventDestroy(c->ev0);
         (void)hipEventDestroy(c->ev1);
@@ -793,7 +888,8 @@ float jepa_last_compute_ms(jepa_ctx *c) {
 size_t jepa_model_n_bytes(const jepa_ctx *c) { return c ? c->model_bytes : 0; }
 size_t jepa_device_weight_bytes(const jepa_ctx *c) { return c ? c->arena_bytes : 0; }
 size_t jepa_workspace_bytes(const jepa_ctx *c, int batch) {
-    return (c && batch > 0) ? ws_layout(c, batch).total : 0;
+    if (!c || batch <= 0) return 0;
+    return ws_layout(c, batch).total + (use_expand(c, batch, n_parts(c, batch)) ? expand_bytes(c) : 0);
 }
 
 jepa_status jepa_dequant_tensor(jepa_ctx *c, const char *name, float *out_dev, void *hip_stream) {

@@ -90,6 +90,19 @@ hipError_t launch_copy_f32(const float *y, int64_t n, float *out, hipStream_t s)
 hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipStream_t s);
 hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
                             hipStream_t s);
+// q8_0 / q4_0 matrices expanded to the activation dtype, act(f32(d) * q), the
+// values the GEMM's own dequantising tile load makes.  Job j covers the
+// matrix's blocks of 32 weights [blk0_j, blk0_{j+1}) of the concatenated
+// range (blk0 ascending, blk0_0 = 0); codes and scales as the GEMM reads
+// them, dst the act-dtype matrix [rows, cols] (16-byte aligned).
+struct ExpandJob {
+    const void *codes;
+    const uint16_t *scale;
+    void *dst;
+    int64_t blk0;
+    int w_dt;
+};
+hipError_t launch_expand(int act_dt, const ExpandJob *jobs, int njobs, int64_t nblk, hipStream_t s);
 // dequantise packed blocks, or widen f16 / bf16 / f32 storage, into f32 [rows, cols]
 hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
                           int64_t cols, float *out, hipStream_t s);

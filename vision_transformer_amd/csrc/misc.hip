@@ -156,7 +156,58 @@ __global__ void dequant_kernel(int w_dt, const void *w, const uint16_t *scale, i
     out[idx] = v;
 }
 
+// One thread per block of 32 weights: 32 (q8_0) or 16 (q4_0) code bytes and
+// the f16 scale in, 64 bytes of act values out.  Neighbouring threads take
+// neighbouring blocks, so every wave reads and writes contiguous runs.
+template <typename T>
+__global__ __launch_bounds__(256) void expand_kernel(const ExpandJob *jobs, int njobs, int64_t nblk) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    int lo = 0, hi = njobs - 1;                  // the last job with blk0 <= b
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].blk0 <= b) lo = mid;
+        else hi = mid - 1;
+    }
+    const ExpandJob j = jobs[lo];
+    const int64_t k = b - j.blk0;
+    const float d = (float)__builtin_bit_cast(_Float16, j.scale[k]);
+    float x[32];
+    if (j.w_dt == DT_Q8_0) {
+        const uint4 *src = (const uint4 *)((const int8_t *)j.codes + k * 32);
+        const uint4 q0 = src[0], q1 = src[1];
+        const int8_t *c0 = (const int8_t *)&q0, *c1 = (const int8_t *)&q1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = d * (float)c0[i];
+            x[16 + i] = d * (float)c1[i];
+        }
+    } else {
+        const uint4 q = *(const uint4 *)((const uint8_t *)j.codes + k * 16);
+        const uint8_t *c = (const uint8_t *)&q;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = d * (float)((int)(c[i] & 15) - 8);
+            x[16 + i] = d * (float)((int)(c[i] >> 4) - 8);
+        }
+    }
+    uint4 *dst = (uint4 *)((T *)j.dst + k * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        dst[c] = make_uint4(pack2<T>(x[8 * c], x[8 * c + 1]), pack2<T>(x[8 * c + 2], x[8 * c + 3]),
+                            pack2<T>(x[8 * c + 4], x[8 * c + 5]), pack2<T>(x[8 * c + 6], x[8 * c + 7]));
+}
+
 }  // namespace
+
+hipError_t launch_expand(int act_dt, const ExpandJob *jobs, int njobs, int64_t nblk, hipStream_t s) {
+    if (!jobs || njobs <= 0 || nblk <= 0 || cdiv(nblk, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cdiv(nblk, 256));
+    if (act_dt == DT_BF16) hipLaunchKernelGGL(expand_kernel<bf16_t>, grid, dim3(256), 0, s, jobs, njobs, nblk);
+    else if (act_dt == DT_F16) hipLaunchKernelGGL(expand_kernel<f16_t>, grid, dim3(256), 0, s, jobs, njobs, nblk);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_patchify(int act_dt, const PatchifyArgs &a, hipStream_t s) {
     const int P = a.tubelet * a.patch * a.patch * 3;
