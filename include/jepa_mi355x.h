@@ -61,7 +61,7 @@ typedef enum { JEPA_MASK_BIDIR = 0, JEPA_MASK_BLOCK_CAUSAL = 1 } jepa_mask;
 
 typedef enum { JEPA_POOL_NONE = 0, JEPA_POOL_CLS = 1, JEPA_POOL_MEAN = 2 } jepa_pool_mode;
 
-/* Model dimensions.  head_dim = dim / heads must be 64; dim and mlp_dim
+/* Model dimensions.  head_dim = dim / heads must be 64 or 32; dim and mlp_dim
  * must be multiples of 64; img_h, img_w divisible by patch; frames divisible
  * by tubelet.  Tokens per item: N = (frames/tubelet)*(img_h/patch)*(img_w/patch)
  * + has_cls.  Pixels are normalised as (u/255 - mean[c]) / std[c].
@@ -75,8 +75,9 @@ typedef enum { JEPA_POOL_NONE = 0, JEPA_POOL_CLS = 1, JEPA_POOL_MEAN = 2 } jepa_
  * additive table enc.pos_embed, which is then not part of the schema: in
  * every block, before the scores, each head's q and k are rotated pairwise,
  * dims (2i, 2i+1) of segment a (a = 0, 1, 2: temporal slot, patch row, patch
- * column, 20 dims each, dims 60-63 untouched) by pos_a * 10000^(-i/10)
- * radians.  A CLS token has no position and is not rotated. */
+ * column, ds = 2*floor(head_dim/6) dims each: 20 of 64, 10 of 32; the dims
+ * after the three segments untouched) by pos_a * 10000^(-2i/ds) radians.  A
+ * CLS token has no position and is not rotated. */
 typedef struct {
     int32_t dim, depth, heads, mlp_dim;
     int32_t patch, tubelet, img_h, img_w, frames;
@@ -97,7 +98,7 @@ typedef struct {
  *   enc.cls_token [D] (only if has_cls)     enc.pos_embed [ne0 D, ne1 N] (not if rope)
  *   enc.blk.{i}.ln1.weight/.bias [D]        enc.blk.{i}.ln2.weight/.bias [D]
  *   enc.blk.{i}.attn_qkv.weight [D, 3D] .bias [3D]   (columns [q | k | v],
- *       head a owns features a*64..a*64+63 of each third)
+ *       head a owns features a*hd..a*hd+hd-1 of each third, hd = head_dim)
  *   enc.blk.{i}.attn_out.weight [D, D] .bias [D]
  *   enc.blk.{i}.ffn_up.weight [D, F] .bias [F]
  *   enc.blk.{i}.ffn_down.weight [F, D] .bias [D]

@@ -16,10 +16,12 @@
  * 0-3, 8-11, 4-7, 12-15. */
 #define JEPA_VT_POS(n) (((n) & ~(int64_t)12) | (((n) & 4) << 1) | (((n) & 8) >> 1))
 
-/* log2(e) / sqrt(64).  q multiplied by it turns q.k into the base-2 exponent
- * of the softmax (scale 1/sqrt(head_dim), base e); jepa_encode folds it into
- * the qkv layer's q columns (q_scale) and runs attention with q_prescaled. */
+/* log2(e) / sqrt(head_dim) for head_dim 64 and 32.  q multiplied by it
+ * turns q.k into the base-2 exponent of the softmax (scale 1/sqrt(head_dim),
+ * base e); jepa_encode folds it into the qkv layer's q columns (q_scale) and
+ * runs attention with q_prescaled. */
 #define JEPA_ATTN_Q_SCALE 0.18033688011112042f
+#define JEPA_ATTN_Q_SCALE_32 0.25503486164919736f
 
 #ifdef __cplusplus
 extern "C" {
@@ -60,55 +62,62 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
 
 /* The qkv linear layer (attn_qkv, Quantization page "The rule") with V
  * written transposed for attention: acc = a[M, K] * w[N, K]^T + bias in
- * f32, N = 3*heads*64, weights as in jepa_op_gemm.  Columns [0, 2*heads*64)
- * (q and k) -> qk_out act [M, ld_qk] (ld_qk >= N; columns N - heads*64 .. N-1
- * of qk_out are not written); columns [2*heads*64, N) (v) -> vt act
- * [M / n_tokens, heads, 64, npad], row b*n_tokens + n being token n of item
- * b, each value rounded once to the act dtype.  Within a vt row, token n is
- * at position JEPA_VT_POS(n): each aligned run of 16 tokens is stored in the
- * order 0-3, 8-11, 4-7, 12-15, the order the attention kernel's operands
- * read.  Positions holding no token are not written.  rope (NULL: none),
- * f32 device [n_tokens, 32, 2] as jepa_rope_table writes it: q and k of
- * token n (row b*n_tokens + n), dims (2p, 2p+1) of every head, are rotated
- * by the angle whose (cos, sin) is entry (n, p), in f32, before the scale.
- * q_scale (0 or 1: none) then multiplies the q columns before their
- * rounding, e.g. JEPA_ATTN_Q_SCALE for jepa_op_attention's q_prescaled.
+ * f32, D = heads*head_dim (head_dim 32 or 64), N = 3*D, weights as in
+ * jepa_op_gemm.  Columns [0, 2D) (q and k) -> qk_out act [M, ld_qk]
+ * (ld_qk >= N; columns 2D .. N-1 of qk_out are not written); columns
+ * [2D, N) (v) -> vt act [M / n_tokens, D, npad]: row b*D + c of vt holds v
+ * column c (head c / head_dim, dim c % head_dim) of item b's tokens, row
+ * b*n_tokens + n of a being token n of item b, each value rounded once to
+ * the act dtype.  Within a vt row, token n is at position JEPA_VT_POS(n):
+ * each aligned run of 16 tokens is stored in the order 0-3, 8-11, 4-7,
+ * 12-15, the order the attention kernel's operands read.  Positions holding
+ * no token are not written.  rope (NULL: none), f32 device
+ * [n_tokens, head_dim/2, 2] as jepa_rope_table writes it: q and k of token
+ * n, dims (2p, 2p+1) of every head, are rotated by the angle whose
+ * (cos, sin) is entry (n, p), in f32, before the scale.  q_scale (0 or 1:
+ * none) then multiplies the q columns before their rounding, e.g.
+ * JEPA_ATTN_Q_SCALE(_32) for jepa_op_attention's q_prescaled.
  * M % n_tokens == 0, npad >= n_tokens rounded up to 16. */
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
-                             int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
-                             int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             const float *rope, float q_scale, void *hip_stream);
+                             int w_dtype, const uint16_t *w_scale, int heads, int head_dim,
+                             const float *bias, int n_tokens, void *qk_out, int64_t ld_qk, void *vt,
+                             int64_t npad, const float *rope, float q_scale, void *hip_stream);
 
-/* The v columns of a qkv matrix act [batch*n_tokens, 3*heads*64] transposed
- * per head into vt act [batch, heads, 64, npad], token n at position
- * JEPA_VT_POS(n) of its row (positions holding no token not written). */
+/* The v columns of a qkv matrix act [batch*n_tokens, 3*D], D =
+ * heads*head_dim, transposed into vt act [batch, D, npad] (the layout
+ * jepa_op_gemm_qkv writes), token n at position JEPA_VT_POS(n) of its row
+ * (positions holding no token not written). */
 jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n_tokens,
-                                int heads, void *vt, int64_t npad, void *hip_stream);
+                                int heads, int head_dim, void *vt, int64_t npad, void *hip_stream);
 
-/* Multi-head attention, head_dim 64 (LeVJEPA card, opening paragraph, for
- * the block-causal mask).  q and k: act rows of pitch ld_qk elements (token
- * item*n_tokens + n), q of head h at column h*64, k at column heads*64 +
- * h*64; v: vt act [batch, heads, 64, npad] as written by jepa_op_transpose_v
- * (token n at JEPA_VT_POS(n)), npad = n_tokens rounded up to 64, positions
- * holding no token finite (zero).
- * -> out act [batch*n_tokens, heads*64].  mask JEPA_MASK_BLOCK_CAUSAL groups
- * the patch tokens (after the optional CLS token 0) in consecutive runs of
- * tokens_per_slot.  q_prescaled: the q columns hold q * JEPA_ATTN_Q_SCALE
- * (as jepa_op_gemm_qkv writes them with that q_scale), so q.k is already the
- * base-2 softmax exponent; otherwise q is the plain projection. */
+/* Multi-head attention, head_dim 64 or 32 (LeVJEPA card, opening paragraph,
+ * for the block-causal mask; head_dim 32 is the V-JEPA 2 predictor's width).
+ * q and k: act rows of pitch ld_qk elements (token item*n_tokens + n), q of
+ * head h at column h*head_dim, k at column D + h*head_dim, D =
+ * heads*head_dim; v: vt act [batch, D, npad] as written by
+ * jepa_op_transpose_v (token n at JEPA_VT_POS(n)), npad = n_tokens rounded
+ * up to 64, positions holding no token finite (zero).
+ * -> out act [batch*n_tokens, D].  mask JEPA_MASK_BLOCK_CAUSAL groups the
+ * patch tokens (after the optional CLS token 0) in consecutive runs of
+ * tokens_per_slot.  q_prescaled: the q columns hold q * log2(e) /
+ * sqrt(head_dim) (JEPA_ATTN_Q_SCALE or _32, as jepa_op_gemm_qkv writes them
+ * with that q_scale), so q.k is already the base-2 softmax exponent;
+ * otherwise q is the plain projection. */
 jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
-                              int64_t npad, int batch, int n_tokens, int heads, int has_cls,
-                              int mask, int tokens_per_slot, int q_prescaled, void *out,
-                              void *hip_stream);
+                              int64_t npad, int batch, int n_tokens, int heads, int head_dim,
+                              int has_cls, int mask, int tokens_per_slot, int q_prescaled,
+                              void *out, void *hip_stream);
 
 /* Host: the table of 3-D rotary position (see jepa_dims.rope; V-JEPA 2
  * card, opening paragraph) for the token grid of dims: out f32 host
- * [N, 32, 2], N = tokens per item, entry (n, p) = (cos, sin) of the angle of
- * token n's dimension pair p: for a patch token at (slot t, row h, column w),
- * pair 10a + i (a < 3, i < 10) has angle (t, h, w)[a] * 10000^(-i/10);
- * pairs 30 and 31, and every pair of a CLS token, have angle 0.  Angles and
- * their cos / sin are evaluated in double and rounded once to f32.  dims is
- * validated as by jepa_create (rope itself may be 0 or 1). */
+ * [N, dh/2, 2], N = tokens per item, dh = dim/heads, entry (n, p) =
+ * (cos, sin) of the angle of token n's dimension pair p.  With ds =
+ * 2*floor(dh/6) (20 for dh 64, 10 for 32), a patch token at (slot t, row h,
+ * column w) has, for pair a*ds/2 + i (a < 3, i < ds/2), the angle
+ * (t, h, w)[a] * 10000^(-2i/ds); the remaining pairs, and every pair of a
+ * CLS token, have angle 0.  Angles and their cos / sin are evaluated in
+ * double and rounded once to f32.  dims is validated as by jepa_create
+ * (rope itself may be 0 or 1). */
 jepa_status jepa_rope_table(const jepa_dims *dims, float *out);
 
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout

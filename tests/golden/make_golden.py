@@ -32,7 +32,8 @@ from vision_transformer_amd import synth  # noqa: E402
 
 FULL = ["vit_l16_image_bf16_b32", "levjepa_vit_l16_16f_bf16_b4",
         "vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_f16",
-        "vjepa2_vit_l16_64f256_q4_0", "vjepa2_rope_vit_l16_16f256_f16_b4"]
+        "vjepa2_vit_l16_64f256_q4_0", "vjepa2_rope_vit_l16_16f256_f16_b4",
+        "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4"]
 N_SAMPLE = 32
 
 

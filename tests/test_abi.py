@@ -142,17 +142,20 @@ def test_null_context_calls_fail_cleanly(lib):
 # 3-D rotary position: the host table and the schema
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["vjepa2_vit_l16_64f256_f16", "small_rope_cls_blockcausal_bf16"])
+@pytest.mark.parametrize("name", ["vjepa2_vit_l16_64f256_f16", "small_rope_cls_blockcausal_bf16",
+                                  "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4"])
 def test_rope_table_is_the_oracle_angles(lib, name):
     """jepa_rope_table's (cos, sin) are the oracle's angles' cos / sin rounded
     to f32 (to within the one ulp by which two libm's may differ)."""
     dims = dict(synth.workload(name)["dims"], rope=1)
     got = lib.jepa_rope_table(dims)
     ang = E.rope_angles(dims)
-    assert got.shape == (synth.n_tokens(dims), 32, 2)
+    dh = dims["dim"] // dims["heads"]
+    assert got.shape == (synth.n_tokens(dims), dh // 2, 2)
     np.testing.assert_allclose(got[..., 0], np.cos(ang), rtol=0, atol=1.2e-7)
     np.testing.assert_allclose(got[..., 1], np.sin(ang), rtol=0, atol=1.2e-7)
-    assert np.array_equal(got[:, 30:], np.tile(np.float32([1, 0]), (got.shape[0], 2, 1)))
+    rest = 3 * (dh // 6)                       # pairs past the three segments
+    assert np.array_equal(got[:, rest:], np.tile(np.float32([1, 0]), (got.shape[0], dh // 2 - rest, 1)))
 
 
 def test_create_with_rope_has_no_pos_table(lib):

@@ -150,8 +150,9 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     assert np.all(err <= bound + out_r * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("dh", [64, 32], ids=["dh64", "dh32"])
 @pytest.mark.parametrize("rope", [False, True], ids=["norope", "rope"])
-@pytest.mark.parametrize("q_scale", [0.0, 0.18033688011112042], ids=["q", "qscaled"])
+@pytest.mark.parametrize("qscaled", [False, True], ids=["q", "qscaled"])
 @pytest.mark.parametrize("act,wfmt,B,N,heads,K", [
     ("bf16", "dense", 7, 197, 4, 256),      # M = 1379: 256-row tiles, items straddling 32-row blocks
     ("bf16", "dense", 2, 289, 2, 128),      # M = 578: 128-row tiles
@@ -160,15 +161,18 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     ("f32", "dense", 2, 85, 2, 64),
     ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
 ])
-def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale, rope):
+def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, qscaled, rope, dh):
     """q and k columns as a plain linear layer (rotated pairwise by a table of
     per-token angles, then q times q_scale, before their one rounding); v
-    columns straight into V^T [B, heads, 64, npad] (the attention kernel's
-    layout), padding untouched.  The angles are seeded uniform in [-pi, pi]
-    for every token and pair, so every table entry is exercised."""
-    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads} K={K} q_scale={q_scale} rope={rope}")
+    columns straight into V^T [B, D, npad] (the attention kernel's layout),
+    padding untouched.  Heads of 64 and of 32 (the same widths).  The angles
+    are seeded uniform in [-pi, pi] for every token and pair, so every table
+    entry is exercised."""
+    heads = heads * 64 // dh                     # the same width in heads of dh
+    q_scale = lib.attn_q_scale(dh) if qscaled else 0.0
+    say(f"gemm qkv {act} {wfmt} B={B} N={N} heads={heads}x{dh} K={K} q_scale={q_scale} rope={rope}")
     rng = np.random.default_rng(47)
-    M, D = B * N, heads * 64
+    M, D = B * N, heads * dh
     a_dev, a = rounded(act, rng.standard_normal((M, K)))
     w32 = (rng.standard_normal((3 * D, K)) * 0.05).astype(np.float32)
     bias = (rng.standard_normal(3 * D) * 0.1).astype(np.float32)
@@ -186,14 +190,14 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale, r
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[act]
     npad = -(-N // 64) * 64
     qk = torch.zeros((M, 3 * D), dtype=tdt, device="cuda")
-    vt = torch.full((B, heads, 64, npad), 7.0, dtype=tdt, device="cuda")
+    vt = torch.full((B, D, npad), 7.0, dtype=tdt, device="cuda")
     table = None
     if rope:
-        ang = np.random.default_rng(48).uniform(-math.pi, math.pi, (N, 32))
+        ang = np.random.default_rng(48).uniform(-math.pi, math.pi, (N, dh // 2))
         table = torch.from_numpy(np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)).cuda()
     lib.jepa_op_gemm_qkv(act, a_dev, w_dev, wfmt if wfmt != "dense" else act, heads,
                          torch.from_numpy(bias).cuda(), N, qk, vt, w_scale=scale, q_scale=q_scale,
-                         rope=table)
+                         rope=table, head_dim=dh)
     pre = (wr + 4 * K * 2.0 ** -24) * (np.abs(a) @ np.abs(w).T) + 1e-6
     if rope:
         # oracle rotation of every head's q and k; the f32 rotation adds at
@@ -201,12 +205,12 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale, r
         # |z0| + |z1| (the table's cos / sin are rounded too)
         ref = ref.copy()
         ang_b = np.tile(ang, (B, 1))
-        for c0 in range(0, 2 * D, 64):
-            z = ref[:, c0:c0 + 64].copy()
-            ref[:, c0:c0 + 64] = E.rope(z, ang_b)
-            e = pre[:, c0:c0 + 64].reshape(M, 32, 2).sum(-1)
-            zz = np.abs(z).reshape(M, 32, 2).sum(-1)
-            pre[:, c0:c0 + 64] = np.repeat(e + 4 * 2.0 ** -24 * zz, 2, axis=1)
+        for c0 in range(0, 2 * D, dh):
+            z = ref[:, c0:c0 + dh].copy()
+            ref[:, c0:c0 + dh] = E.rope(z, ang_b)
+            e = pre[:, c0:c0 + dh].reshape(M, dh // 2, 2).sum(-1)
+            zz = np.abs(z).reshape(M, dh // 2, 2).sum(-1)
+            pre[:, c0:c0 + dh] = np.repeat(e + 4 * 2.0 ** -24 * zz, 2, axis=1)
     bound = pre + OUT_REL[act] * np.abs(ref)
     if q_scale:
         ref = ref.copy()
@@ -216,42 +220,44 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, q_scale, r
     assert np.all(np.abs(got_qk[:, :2 * D] - ref[:, :2 * D]) <= bound[:, :2 * D])
     assert np.all(got_qk[:, 2 * D:] == 0)                       # v columns not written
     got_vt = vt.double().cpu().numpy()
-    want = ref[:, 2 * D:].reshape(B, N, heads, 64).transpose(0, 2, 3, 1)
-    bnd = bound[:, 2 * D:].reshape(B, N, heads, 64).transpose(0, 2, 3, 1)
+    want = ref[:, 2 * D:].reshape(B, N, D).transpose(0, 2, 1)
+    bnd = bound[:, 2 * D:].reshape(B, N, D).transpose(0, 2, 1)
     pos = vt_pos(np.arange(N))
     assert np.all(np.abs(got_vt[..., pos] - want) <= bnd)
     free = np.setdiff1d(np.arange(npad), pos)
     assert np.all(got_vt[..., free] == 7.0)                      # positions of no token untouched
 
 
-def _vt_of(lib, act, qkv_dev, B, N, heads):
+def _vt_of(lib, act, qkv_dev, B, N, heads, dh=64):
     npad = -(-N // 64) * 64
-    vt = torch.zeros((B, heads, 64, npad), dtype=qkv_dev.dtype, device="cuda")
-    lib.jepa_op_transpose_v(act, qkv_dev, B, N, heads, vt)
+    vt = torch.zeros((B, heads * dh, npad), dtype=qkv_dev.dtype, device="cuda")
+    lib.jepa_op_transpose_v(act, qkv_dev, B, N, heads, vt, head_dim=dh)
     return vt
 
 
-def _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled=False):
-    vt = _vt_of(lib, act, qkv_dev, B, N, heads)
-    out = torch.empty((B * N, heads * 64), dtype=qkv_dev.dtype, device="cuda")
-    lib.jepa_op_attention(act, qkv_dev, vt, B, N, heads, has_cls, mask, per_slot, out, q_prescaled=prescaled)
+def _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled=False, dh=64):
+    vt = _vt_of(lib, act, qkv_dev, B, N, heads, dh)
+    out = torch.empty((B * N, heads * dh), dtype=qkv_dev.dtype, device="cuda")
+    lib.jepa_op_attention(act, qkv_dev, vt, B, N, heads, has_cls, mask, per_slot, out, q_prescaled=prescaled,
+                          head_dim=dh)
     return out
 
 
-def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed, prescaled=False, mag=1.0):
+def _attn_case(lib, act, B, N, heads, has_cls, mask, per_slot, seed, prescaled=False, mag=1.0, dh=64):
     """GPU attention vs the oracle on seeded q, k, v.  prescaled: the device q
-    columns hold q * log2(e)/8 rounded to act (as the qkv layer writes them);
-    the oracle gets the q those rounded values stand for."""
+    columns hold q * log2(e)/sqrt(dh) rounded to act (as the qkv layer writes
+    them); the oracle gets the q those rounded values stand for."""
     rng = np.random.default_rng(seed)
-    D = heads * 64
+    D = heads * dh
     x = rng.standard_normal((B * N, 3 * D)) * mag
+    qs = lib.attn_q_scale(dh)
     if prescaled:
-        x[:, :D] *= lib.ATTN_Q_SCALE
+        x[:, :D] *= qs
     qkv_dev, qkv = rounded(act, x)
     if prescaled:
         qkv = qkv.copy()
-        qkv[:, :D] /= lib.ATTN_Q_SCALE
-    out = _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled)
+        qkv[:, :D] /= qs
+    out = _attend(lib, act, qkv_dev, B, N, heads, has_cls, mask, per_slot, prescaled, dh)
     got = out.double().cpu().numpy().reshape(B, N, D)
     if mask == "bidir":
         allowed = None
@@ -272,13 +278,16 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("dh", [64, 32], ids=["dh64", "dh32"])
 @pytest.mark.parametrize("prescaled", [False, True], ids=["q", "qscaled"])
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[f"{c[1]}tok-{c[4]}-cls{int(c[3])}" for c in ATTN_CASES])
-def test_attention(lib, act, case, prescaled):
-    say(f"attention {act} {case} prescaled={prescaled}")
-    got, ref = _attn_case(lib, act, *case, seed=44, prescaled=prescaled)
-    D = case[2] * 64
+def test_attention(lib, act, case, prescaled, dh):
+    B, N, heads, has_cls, mask, per = case
+    heads = heads * 64 // dh                      # the same width in heads of dh
+    say(f"attention {act} {case} heads={heads}x{dh} prescaled={prescaled}")
+    got, ref = _attn_case(lib, act, B, N, heads, has_cls, mask, per, seed=44, prescaled=prescaled, dh=dh)
+    D = heads * dh
     g = got.reshape(-1, D)
     r = ref.reshape(-1, D)
     if act == "f32":
@@ -330,26 +339,28 @@ def test_kernels_reject_out_of_contract_shapes(lib):
     with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
         lib.jepa_op_gemm("bf16", x, w, "bf16", 64, b, "store", out)      # K % 64 != 0
     q = torch.zeros((10, 3 * 64), dtype=torch.bfloat16, device="cuda")
-    vt = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device="cuda")
     o = torch.zeros((10, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
         lib.jepa_op_attention("bf16", q, vt, 1, 10, 1, True, "block_causal", 4, o)   # 9 % 4 != 0
-    vt_short = torch.zeros((1, 1, 64, 8), dtype=torch.bfloat16, device="cuda")
+    vt_short = torch.zeros((1, 64, 8), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(lib.JepaError, match="JEPA_E_SHAPE"):
         lib.jepa_op_attention("bf16", q, vt_short, 1, 10, 1, True, "bidir", 1, o)   # npad < 64
+    with pytest.raises(lib.JepaError, match="JEPA_E_UNSUPPORTED"):
+        lib.jepa_op_attention("bf16", q, vt, 1, 10, 4, True, "bidir", 1, o, head_dim=16)
 
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])
-@pytest.mark.parametrize("B,N,heads", [(2, 3137, 16), (3, 289, 2), (1, 1, 1)])
-def test_transpose_v(lib, act, B, N, heads):
+@pytest.mark.parametrize("B,N,heads,dh", [(2, 3137, 16, 64), (3, 289, 2, 64), (1, 1, 1, 64), (2, 197, 6, 32)])
+def test_transpose_v(lib, act, B, N, heads, dh):
     if act == "f32" and B * N * heads > 10000:
         pytest.skip("the f32 path only serves small models")
     rng = np.random.default_rng(46)
-    D = heads * 64
+    D = heads * dh
     qkv_dev, _ = rounded(act, rng.standard_normal((B * N, 3 * D)))
-    vt = _vt_of(lib, act, qkv_dev, B, N, heads)
-    v = qkv_dev[:, 2 * D:].float().cpu().numpy().reshape(B, N, heads, 64)
+    vt = _vt_of(lib, act, qkv_dev, B, N, heads, dh)
+    v = qkv_dev[:, 2 * D:].float().cpu().numpy().reshape(B, N, D)
     got = vt.float().cpu().numpy()
     pos = vt_pos(np.arange(N))
-    assert np.array_equal(got[..., pos], v.transpose(0, 2, 3, 1))
+    assert np.array_equal(got[..., pos], v.transpose(0, 2, 1))
     assert np.all(got[..., np.setdiff1d(np.arange(got.shape[-1]), pos)] == 0)

@@ -344,6 +344,12 @@ def test_rope_angles_hand_values():
     np.testing.assert_allclose(ang[tok(0, 5, 0)], np.r_[np.zeros(10), 5 * f, np.zeros(12)], rtol=1e-15)
     np.testing.assert_allclose(ang[tok(7, 15, 11)], np.r_[7 * f, 15 * f, 11 * f, 0, 0], rtol=1e-15)
     assert ang[tok(1, 0, 0), 1] == pytest.approx(10 ** -0.4, rel=1e-15)
+    # heads of 32: segments of 10 dims, pair i of a segment at 10000^(-i/5),
+    # the last pair unrotated
+    a32 = E.rope_angles(dict(_VJ2_16F, dim=384, heads=12))
+    f5 = 10000.0 ** (-np.arange(5) / 5.0)
+    assert a32.shape == (8 * 16 * 16, 16)
+    np.testing.assert_allclose(a32[tok(2, 3, 4)], np.r_[2 * f5, 3 * f5, 4 * f5, 0], rtol=1e-15)
     # a CLS token (no position) is token 0 and is never rotated
     ac = E.rope_angles(dict(_VJ2_16F, has_cls=1))
     np.testing.assert_array_equal(ac[0], 0.0)

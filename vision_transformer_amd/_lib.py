@@ -73,9 +73,9 @@ def _load():
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
-        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, P, I, P, I64, P, I64, P, C.c_float, P]),
-        "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, I, P, P]),
-        "jepa_op_transpose_v": (I, [I, P, I, I, I, P, I64, P]),
+        "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, I, P, I, P, I64, P, I64, P, C.c_float, P]),
+        "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, I, I, P, P]),
+        "jepa_op_transpose_v": (I, [I, P, I, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
     }
@@ -241,43 +241,51 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
 
 
 def jepa_op_gemm_qkv(act_dtype: str, a, w, w_dtype: str, heads: int, bias, n_tokens: int, qk_out, vt,
-                     w_scale=None, q_scale: float = 0.0, rope=None, stream=None) -> None:
+                     w_scale=None, q_scale: float = 0.0, rope=None, head_dim: int = 64,
+                     stream=None) -> None:
     """q, k columns -> qk_out [M, ld] (rotated by the rope table [n_tokens,
-    32, 2] if given, then q times q_scale if nonzero); v columns transposed ->
-    vt [M/n_tokens, heads, 64, npad]."""
+    head_dim/2, 2] if given, then q times q_scale if nonzero); v columns
+    transposed -> vt [M/n_tokens, heads*head_dim, npad]."""
     M, K = a.shape
     _check(_lib.jepa_op_gemm_qkv(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
-                                 heads, _ptr(bias), n_tokens, _ptr(qk_out), qk_out.shape[1], _ptr(vt),
-                                 vt.shape[-1], _ptr(rope), float(q_scale), _stream(stream)))
+                                 heads, head_dim, _ptr(bias), n_tokens, _ptr(qk_out), qk_out.shape[1],
+                                 _ptr(vt), vt.shape[-1], _ptr(rope), float(q_scale), _stream(stream)))
 
 
 def jepa_rope_table(dims: dict) -> np.ndarray:
-    """Host: the 3-D rotary table of dims' token grid, f32 [N, 32, 2] (cos, sin)."""
+    """Host: the 3-D rotary table of dims' token grid, f32 [N, dh/2, 2] (cos, sin)."""
     d = make_dims(dims)
     n = (dims["frames"] // dims["tubelet"]) * (dims["img_h"] // dims["patch"]) * \
         (dims["img_w"] // dims["patch"]) + int(dims["has_cls"])
-    out = np.empty((n, 32, 2), np.float32)
+    out = np.empty((n, dims["dim"] // dims["heads"] // 2, 2), np.float32)
     _check(_lib.jepa_rope_table(C.byref(d), out.ctypes.data))
     return out
 
 
-# log2(e) / sqrt(64): JEPA_ATTN_Q_SCALE, the factor jepa_op_gemm_qkv folds into q
+# log2(e) / sqrt(head_dim): JEPA_ATTN_Q_SCALE and _32, the factor
+# jepa_op_gemm_qkv folds into q
 ATTN_Q_SCALE = 0.18033688011112042
+ATTN_Q_SCALE_32 = 0.25503486164919736
+
+
+def attn_q_scale(head_dim: int) -> float:
+    return ATTN_Q_SCALE_32 if head_dim == 32 else ATTN_Q_SCALE
 
 
 def jepa_op_attention(act_dtype: str, qk, vt, batch: int, n_tokens: int, heads: int, has_cls: bool,
-                      mask: str, tokens_per_slot: int, out, q_prescaled: bool = False, stream=None) -> None:
-    """qk: [batch*n_tokens, ld] (q | k columns first; q times JEPA_ATTN_Q_SCALE
-    if q_prescaled); vt: [batch, heads, 64, npad]."""
+                      mask: str, tokens_per_slot: int, out, q_prescaled: bool = False, head_dim: int = 64,
+                      stream=None) -> None:
+    """qk: [batch*n_tokens, ld] (q | k columns first; q times
+    attn_q_scale(head_dim) if q_prescaled); vt: [batch, heads*head_dim, npad]."""
     _check(_lib.jepa_op_attention(DTYPE[act_dtype], _ptr(qk), qk.shape[1], _ptr(vt), vt.shape[-1],
-                                  batch, n_tokens, heads, int(has_cls), MASK[mask], tokens_per_slot,
+                                  batch, n_tokens, heads, head_dim, int(has_cls), MASK[mask], tokens_per_slot,
                                   int(q_prescaled), _ptr(out), _stream(stream)))
 
 
 def jepa_op_transpose_v(act_dtype: str, qkv, batch: int, n_tokens: int, heads: int, vt,
-                        stream=None) -> None:
-    _check(_lib.jepa_op_transpose_v(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, _ptr(vt),
-                                    vt.shape[-1], _stream(stream)))
+                        head_dim: int = 64, stream=None) -> None:
+    _check(_lib.jepa_op_transpose_v(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, head_dim,
+                                    _ptr(vt), vt.shape[-1], _stream(stream)))
 
 
 def jepa_pack_blocks(dtype: str, blocks: np.ndarray, rows: int, cols: int):

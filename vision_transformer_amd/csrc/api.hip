@@ -161,7 +161,7 @@ struct jepa_ctx {
     int ws_batch = 0;
     uint8_t *w_frames = nullptr;
     void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_vt = nullptr, *w_o = nullptr, *w_u = nullptr;
-    float *w_x = nullptr, *w_y = nullptr;
+    float *w_x = nullptr, *w_y = nullptr, *w_pool = nullptr;
     // last encode
     const float *last_tokens = nullptr;
     int last_batch = 0;
@@ -187,7 +187,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t frames, patch, x, hn, qkv, vt, o, u, y, total;
+    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, total;
 };
 
 WsLayout ws_layout(const jepa_ctx *c, int B) {
@@ -204,6 +204,7 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
     w.o = take(M * c->D * c->es);
     w.u = take(M * c->F * c->es);
     w.y = take(M * c->D * 4);
+    w.pool = take((size_t)B * POOL_CHUNKS * c->D * 4);
     w.total = off;
     return w;
 }
@@ -315,6 +316,7 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
     c->w_o = base + w.o;
     c->w_u = base + w.u;
     c->w_y = (float *)(base + w.y);
+    c->w_pool = (float *)(base + w.pool);
     c->ws_bytes = w.total;
     c->ws_batch = B;
     return JEPA_OK;
@@ -360,8 +362,8 @@ jepa_status check_dims(const jepa_dims *d) {
     if (d->dim <= 0 || d->depth <= 0 || d->heads <= 0 || d->mlp_dim <= 0 || d->patch <= 0 ||
         d->tubelet <= 0 || d->img_h <= 0 || d->img_w <= 0 || d->frames <= 0)
         return fail(JEPA_E_SHAPE, "dims: every size must be positive");
-    if (d->dim % d->heads || d->dim / d->heads != 64)
-        return fail(JEPA_E_UNSUPPORTED, "dims: head_dim = dim/heads must be 64 (dim %d, heads %d)", d->dim, d->heads);
+    if (d->dim % d->heads || (d->dim / d->heads != 64 && d->dim / d->heads != 32))
+        return fail(JEPA_E_UNSUPPORTED, "dims: head_dim = dim/heads must be 32 or 64 (dim %d, heads %d)", d->dim, d->heads);
     if (d->dim % 64 || d->mlp_dim % 64)
         return fail(JEPA_E_UNSUPPORTED, "dims: dim and mlp_dim must be multiples of 64");
     const int e = d->dim / 64;
@@ -383,23 +385,25 @@ jepa_status check_dims(const jepa_dims *d) {
 }
 
 // 3-D rotary position (V-JEPA 2 card, opening paragraph; RoFormer's pairwise
-// rotation): [N, 32] (cos, sin) for head_dim 64, three 20-dim segments for
-// the temporal slot, patch row and patch column, pair i of a segment at
-// frequency 10000^(-i/10); pairs 30, 31 and a CLS token have angle 0.
+// rotation): [N, dh/2] (cos, sin) pairs, three segments of ds = 2*floor(dh/6)
+// dims (20 of 64, 10 of 32) for the temporal slot, patch row and patch
+// column, pair i of a segment at frequency 10000^(-2i/ds); the pairs past
+// the three segments and every pair of a CLS token have angle 0.
 void rope_table(const jepa_dims &d, float *out) {
+    const int dh = d.dim / d.heads, np = dh / 2, ds = 2 * (dh / 6);
     const int Hp = d.img_h / d.patch, Wp = d.img_w / d.patch;
     const int Np = d.frames / d.tubelet * Hp * Wp, N = Np + d.has_cls;
     for (int n = 0; n < N; ++n) {
-        float *row = out + (size_t)n * 64;
-        for (int p = 0; p < 32; ++p) { row[2 * p] = 1.f; row[2 * p + 1] = 0.f; }
+        float *row = out + (size_t)n * dh;
+        for (int p = 0; p < np; ++p) { row[2 * p] = 1.f; row[2 * p + 1] = 0.f; }
         if (d.has_cls && n == 0) continue;
         const int pn = n - d.has_cls;
         const int pos[3] = {pn / (Hp * Wp), pn / Wp % Hp, pn % Wp};
         for (int a = 0; a < 3; ++a)
-            for (int i = 0; i < 10; ++i) {
-                const double ang = pos[a] * pow(10000.0, -i / 10.0);
-                row[2 * (10 * a + i)] = (float)cos(ang);
-                row[2 * (10 * a + i) + 1] = (float)sin(ang);
+            for (int i = 0; i < ds / 2; ++i) {
+                const double ang = pos[a] * pow(10000.0, -2.0 * i / ds);
+                row[2 * (a * ds / 2 + i)] = (float)cos(ang);
+                row[2 * (a * ds / 2 + i) + 1] = (float)sin(ang);
             }
     }
 }
@@ -573,7 +577,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     const size_t rope_off = off;
     std::vector<float> rope_host;
     if (d.rope) {
-        rope_host.resize((size_t)N * 64);
+        rope_host.resize((size_t)N * (D / d.heads));
         rope_table(d, rope_host.data());
         off += align256(rope_host.size() * 4);
     }
@@ -791,14 +795,15 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             aa.out = o; aa.B = q.nb; aa.N = c->N; aa.heads = c->H;
             aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
             aa.q_prescaled = 1;
+            aa.dh = D / c->H;
             TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
             {   // q, k to qkv; v transposed straight into V^T
                 GemmArgs g{};
                 g.a = hn; g.w = Wqkv.ptr; g.wscale = Wqkv.scale; g.bias = L.bqkv; g.out = qkv;
                 g.M = M; g.N = Wqkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
                 g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
-                g.rope = c->rope;
-                g.qscale = ATTN_Q_SCALE;   // the softmax scale and base change, folded into q
+                g.rope = c->rope; g.head_dim = D / c->H;
+                g.qscale = attn_q_scale(D / c->H);   // the softmax scale and base change, folded into q
                 g.conc = parts;
                 TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
             }
@@ -847,7 +852,7 @@ jepa_status jepa_pool(jepa_ctx *c, int mode, float *out, void *hip_stream) {
             if (!c->d.has_cls) return fail(JEPA_E_STATE, "pool: the model has no CLS token");
             return launch(c, K_POOL, s, [&] { return launch_pool_cls(c->last_tokens, B, c->N, c->D, out, s); });
         case JEPA_POOL_MEAN:
-            return launch(c, K_POOL, s, [&] { return launch_pool_mean(c->last_tokens, B, c->N, c->D, c->d.has_cls, out, s); });
+            return launch(c, K_POOL, s, [&] { return launch_pool_mean(c->last_tokens, B, c->N, c->D, c->d.has_cls, c->w_pool, out, s); });
         case JEPA_POOL_NONE:   // a kernel, so that the copy is ordered on the compute queue like the rest
             return launch(c, K_POOL, s, [&] { return launch_copy_f32(c->last_tokens, (int64_t)B * c->N * c->D, out, s); });
     }
@@ -991,25 +996,26 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
 }
 
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,
-                             int w_dtype, const uint16_t *w_scale, int heads, const float *bias,
-                             int n_tokens, void *qk_out, int64_t ld_qk, void *vt, int64_t npad,
-                             const float *rope, float q_scale, void *hip_stream) {
+                             int w_dtype, const uint16_t *w_scale, int heads, int head_dim,
+                             const float *bias, int n_tokens, void *qk_out, int64_t ld_qk, void *vt,
+                             int64_t npad, const float *rope, float q_scale, void *hip_stream) {
     if (!a || !w || !bias || !qk_out || !vt) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_gemm_qkv: bad act dtype");
     if (heads <= 0 || n_tokens <= 0) return fail(JEPA_E_INVALID_ARG, "op_gemm_qkv: heads and n_tokens must be > 0");
+    if (head_dim != 32 && head_dim != 64) return fail(JEPA_E_UNSUPPORTED, "op_gemm_qkv: head_dim must be 32 or 64");
     GemmArgs g{};
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = qk_out;
-    g.M = M; g.N = 3 * (int64_t)heads * 64; g.K = K; g.lda = K; g.ldo = ld_qk;
-    g.ntok = n_tokens; g.vt = vt; g.npad = npad; g.vcol0 = 2 * (int64_t)heads * 64;
-    g.rope = rope;
+    g.M = M; g.N = 3 * (int64_t)heads * head_dim; g.K = K; g.lda = K; g.ldo = ld_qk;
+    g.ntok = n_tokens; g.vt = vt; g.npad = npad; g.vcol0 = 2 * (int64_t)heads * head_dim;
+    g.rope = rope; g.head_dim = head_dim;
     g.qscale = q_scale == 1.f ? 0.f : q_scale;
     return hip_status(launch_gemm(act_dtype, w_dtype, EPI_QKV, g, (hipStream_t)hip_stream), "op_gemm_qkv");
 }
 
 jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, const void *vt,
-                              int64_t npad, int batch, int n_tokens, int heads, int has_cls,
-                              int mask, int tokens_per_slot, int q_prescaled, void *out,
-                              void *hip_stream) {
+                              int64_t npad, int batch, int n_tokens, int heads, int head_dim,
+                              int has_cls, int mask, int tokens_per_slot, int q_prescaled,
+                              void *out, void *hip_stream) {
     if (!qk || !vt || !out) return fail(JEPA_E_INVALID_ARG, "op_attention: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_attention: bad act dtype");
     if (mask != JEPA_MASK_BIDIR && mask != JEPA_MASK_BLOCK_CAUSAL)
@@ -1020,14 +1026,18 @@ jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, cons
     a.has_cls = has_cls ? 1 : 0; a.block_causal = mask == JEPA_MASK_BLOCK_CAUSAL;
     a.per_slot = tokens_per_slot;
     a.q_prescaled = q_prescaled ? 1 : 0;
+    a.dh = head_dim;
+    if (head_dim != 32 && head_dim != 64) return fail(JEPA_E_UNSUPPORTED, "op_attention: head_dim must be 32 or 64");
     return hip_status(launch_attention(act_dtype, a, (hipStream_t)hip_stream), "op_attention");
 }
 
 jepa_status jepa_op_transpose_v(int act_dtype, const void *qkv, int batch, int n_tokens,
-                                int heads, void *vt, int64_t npad, void *hip_stream) {
+                                int heads, int head_dim, void *vt, int64_t npad, void *hip_stream) {
     if (!qkv || !vt) return fail(JEPA_E_INVALID_ARG, "op_transpose_v: null argument");
     if (!act_ok(act_dtype)) return fail(JEPA_E_DTYPE, "op_transpose_v: bad act dtype");
-    return hip_status(launch_transpose_v(act_dtype, qkv, batch, n_tokens, heads, vt, npad,
+    if (heads <= 0 || (head_dim != 32 && head_dim != 64))
+        return fail(JEPA_E_UNSUPPORTED, "op_transpose_v: head_dim must be 32 or 64");
+    return hip_status(launch_transpose_v(act_dtype, qkv, batch, n_tokens, heads * head_dim, vt, npad,
                                          (hipStream_t)hip_stream), "op_transpose_v");
 }
 

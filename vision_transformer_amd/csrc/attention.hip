@@ -31,21 +31,22 @@
 namespace jepa {
 namespace {
 
-constexpr int DH = 64;      // head dim
 constexpr int QT = 128;     // queries per workgroup (4 waves x 32)
 constexpr int KT = 64;      // keys per step
 
-template <typename T>
+template <typename T, int DH>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     constexpr int ES = sizeof(T);
     constexpr int VEC = MM::VEC, KC = MM::KC;
     constexpr int CE = 16 / ES;                 // elements per 16-byte chunk
-    constexpr int ROWB = 64 * ES + 16;          // LDS row bytes (64 elements + pad)
-    constexpr int TILEB = 64 * ROWB;
-    constexpr int CHUNKS = 64 * 64 / CE / 256;  // 16-byte chunks per thread per operand
-    __shared__ __attribute__((aligned(16))) unsigned char sK[2][TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char sV[2][TILEB];
+    constexpr int ROWK = DH * ES + 16;          // LDS bytes of a K row (DH elements + pad)
+    constexpr int ROWV = 64 * ES + 16;          // LDS bytes of a V^T row (64 keys + pad)
+    constexpr int KCH = DH / CE, VCH = 64 / CE; // 16-byte chunks per K row, per V^T row
+    constexpr int KCHUNKS = 64 * KCH / 256, VCHUNKS = DH * VCH / 256;   // per thread
+    static_assert(KCHUNKS >= 1 && VCHUNKS >= 1, "tile shape");
+    __shared__ __attribute__((aligned(16))) unsigned char sK[2][64 * ROWK];
+    __shared__ __attribute__((aligned(16))) unsigned char sV[2][DH * ROWV];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     // grid (head, item, query tile): with the head fastest, all query tiles of
@@ -86,34 +87,45 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
     }
 
     // ---- K / V^T tile staging: registers -> LDS ----
-    uint4 kreg[CHUNKS], vreg[CHUNKS];
+    uint4 kreg[KCHUNKS], vreg[VCHUNKS];
     auto load_tile = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
+        for (int i = 0; i < KCHUNKS; ++i) {
             const int ci = tid + 256 * i;
-            const int r = ci / (64 / CE), c = ci % (64 / CE);
+            const int r = ci / KCH, c = ci % KCH;
             const int key = k0 + r;
             kreg[i] = make_uint4(0, 0, 0, 0);
             if (key < N) kreg[i] = *(const uint4 *)(qk + (int64_t)key * a.ld_qk + D + h * DH + c * CE);
+        }
+#pragma unroll
+        for (int i = 0; i < VCHUNKS; ++i) {
             // V^T row r (= dim d), keys k0 + c*CE .. ; npad covers the tile
+            const int ci = tid + 256 * i;
+            const int r = ci / VCH, c = ci % VCH;
             vreg[i] = *(const uint4 *)(vt + (int64_t)r * a.npad + k0 + c * CE);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < CHUNKS; ++i) {
+        for (int i = 0; i < KCHUNKS; ++i) {
             const int ci = tid + 256 * i;
-            const int r = ci / (64 / CE), c = ci % (64 / CE);
-            *(uint4 *)(sK[buf] + r * ROWB + c * 16) = kreg[i];
-            *(uint4 *)(sV[buf] + r * ROWB + c * 16) = vreg[i];
+            *(uint4 *)(sK[buf] + (ci / KCH) * ROWK + (ci % KCH) * 16) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VCHUNKS; ++i) {
+            const int ci = tid + 256 * i;
+            *(uint4 *)(sV[buf] + (ci / VCH) * ROWV + (ci % VCH) * 16) = vreg[i];
         }
     };
 
-    const float sl2 = a.q_prescaled ? 1.f : ATTN_Q_SCALE;   // score -> base-2 exponent
+    const float sl2 = a.q_prescaled ? 1.f : attn_q_scale(DH);   // score -> base-2 exponent
     float m = -INFINITY, l = 0.f;
-    f32x16 o[2];
+    constexpr int NDB = DH / 32;                 // 32-dim blocks of the output
+    f32x16 o[NDB];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
     const int kbeg = lo & ~(KT - 1);
     load_tile(kbeg);
@@ -134,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
             for (int c = 0; c < DH / KC; ++c) {
-                typename MM::vec kv = MM::load(kb + (sb * 32 + (lane & 31)) * ROWB + (c * KC + g * VEC) * ES);
+                typename MM::vec kv = MM::load(kb + (sb * 32 + (lane & 31)) * ROWK + (c * KC + g * VEC) * ES);
                 s[sb] = MM::mma(kv, qv[c], s[sb]);
             }
         }
@@ -159,7 +171,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
             const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
             l *= alpha;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
             m = mn;
         }
         const float mb = m * sl2;
@@ -182,8 +196,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
                 for (int j = 0; j < VEC; ++j) pv[j] = s[sb][cc * VEC + j];
                 typename MM::vec pb = pack_operand<T>(pv);
 #pragma unroll
-                for (int db = 0; db < 2; ++db) {
-                    const unsigned char *row = vb + (db * 32 + (lane & 31)) * ROWB;
+                for (int db = 0; db < NDB; ++db) {
+                    const unsigned char *row = vb + (db * 32 + (lane & 31)) * ROWV;
                     typename MM::vec va;
                     if constexpr (VEC == 8) {
                         // keys 16*cc + 4*g + {0-3, 8-11}: 16 contiguous bytes at their V^T position
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
     const float inv = 1.f / l;
     T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
@@ -244,18 +258,23 @@ template <> __device__ __forceinline__ float round_up_t<f16_t>(float x) {
 // k chunk where K contributes 1 at dimension 64 and Q contributes -m (m kept
 // exactly representable in T).  S then comes out as the exponent s - m and
 // p = exp2(S) needs no VALU arithmetic before the exponential.
-template <typename T, bool QS>
+template <typename T, bool QS, int DH>
 __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
     static_assert(sizeof(T) == 2, "16-bit operands");
-    constexpr int TB = 64 * 128;                 // bytes of one 64 x 64 tile
+    static_assert(DH == 32 || DH == 64, "head dims built");
+    constexpr int RK = DH * 2;                   // bytes of a K row in LDS (unpadded)
+    constexpr int CK = RK / 16;                  // its 16-byte chunks: 4 or 8
+    constexpr int TBK = 64 * RK, TBV = DH * 128; // bytes of a K tile (64 keys) and a V^T tile
+    constexpr int NI = DH / 32;                  // load instructions per operand per thread
+    constexpr int NDB = DH / 32;                 // 32-dim blocks of the output
     // one array per stage: the compiler gives each its own alias scope, so
     // reads of one stage need not wait for loads landing in the other
-    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TBK];
+    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TBK];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TBV];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TBV];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-load bases in SGPRs
@@ -289,18 +308,20 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     for (int c = 0; c < DH / 16; ++c)
         qv[c] = qvalid ? MM::load(qk + (int64_t)qrow * a.ld_qk + h * DH + c * 16 + g * 8) : vec{};
 
-    // This thread's two chunks of each tile: chunk id ci = i*256 + tid, row
-    // ci >> 3, slot ci & 7 holding global chunk slot ^ swz(row).  Loads go
+    // This thread's chunks of each tile: chunk id ci = i*256 + tid; a K row
+    // has CK chunks (row ci / CK, slot ci % CK), a V^T row 8 (row ci >> 3,
+    // slot ci & 7); a slot holds global chunk slot ^ swz(row).  Loads go
     // through buffer resources over the item's K rows and the (item, head)'s
     // V^T rows: the thread's byte offsets are fixed and a tile adds a uniform
-    // one; key rows past the item's N read as 0 (masked keys).
-    // chunk i = 1 is chunk 0's, 32 rows on (same swizzle): a uniform offset
+    // one; key rows past the item's N read as 0 (masked keys).  Chunk i = 1
+    // (head dim 64) is chunk 0's, 32 rows on (same swizzle): a uniform offset.
     uint32_t koffg, voffg;
     {
-        const int r = tid >> 3;
-        const int col = ((tid & 7) ^ aswz(r)) * 8;    // element offset of the chunk
-        koffg = (uint32_t)((r * a.ld_qk + col) * (int64_t)sizeof(T));
-        voffg = (uint32_t)((r * a.npad + col) * (int64_t)sizeof(T));
+        const int rk = tid / CK, rv = tid >> 3;
+        const int colk = ((tid % CK) ^ (aswz(rk) & (CK - 1))) * 8;   // element offsets of the chunks
+        const int colv = ((tid & 7) ^ aswz(rv)) * 8;
+        koffg = (uint32_t)((rk * a.ld_qk + colk) * (int64_t)sizeof(T));
+        voffg = (uint32_t)((rv * a.npad + colv) * (int64_t)sizeof(T));
     }
     const uint32_t k32 = (uint32_t)(32 * a.ld_qk * (int64_t)sizeof(T)), v32 = (uint32_t)(32 * a.npad * (int64_t)sizeof(T));
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -313,7 +334,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         const int k0 = kbeg + t * KT;
         const uint32_t ks = (uint32_t)(k0 * a.ld_qk * (int64_t)sizeof(T)), vs = (uint32_t)(k0 * sizeof(T));
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NI; ++i) {
             const int base = (i * 256 + wave * 64) * 16;  // LDS byte offset of lane 0
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void *)(sk + base),
                                                      16, koffg, ks + i * k32, 0, 0);
@@ -322,7 +343,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         }
     };
 
-    const float sl2 = QS ? 1.f : ATTN_Q_SCALE;       // score -> base-2 exponent
+    const float sl2 = QS ? 1.f : attn_q_scale(DH);   // score -> base-2 exponent
     // The running max m is a reference, not the exact max: it is raised only
     // when a score exceeds it by TH (2^8 in p), so p <= 2^8 and the rescale of
     // O and l runs a few times per query instead of at most tiles.  Any
@@ -345,16 +366,18 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
             return __builtin_amdgcn_mfma_f32_32x32x8f16(kx, qx, c, 0, 0, 0);
         }
     };
-    f32x16 o[2];
+    f32x16 o[NDB];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { o[0][v] = 0.f; o[1][v] = 0.f; }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
     const int r0 = lane & 31, sw = aswz(r0);
     // this lane's LDS byte offsets of the tile's operands in rows 0..31; the
     // second 32-row block (same swizzle) and the stage add constants
     int koff[DH / 16], voff[4];
 #pragma unroll
-    for (int c = 0; c < DH / 16; ++c) koff[c] = r0 * 128 + (((2 * c + g) ^ sw) << 4);
+    for (int c = 0; c < DH / 16; ++c) koff[c] = r0 * RK + (((2 * c + g) ^ (sw & (CK - 1))) << 4);
     // V^T operand of 16-key group kg: keys 16*kg + 8*(j/4) + 4*g + j%4,
     // stored contiguously as chunk 2*kg + g of the row
 #pragma unroll
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         for (int sb = 0; sb < 2; ++sb) {
             vec kf[DH / 16];
 #pragma unroll
-            for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + sb * 4096 + koff[c]);
+            for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + sb * 32 * RK + koff[c]);
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
 #pragma unroll
@@ -433,7 +456,9 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                     l0 *= alpha;
                     l1 *= alpha;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
                 }
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
@@ -454,7 +479,9 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                 l0 *= alpha;
                 l1 *= alpha;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) { o[0][v] *= alpha; o[1][v] *= alpha; }
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
                 m = mn;
             }
             const float mb = m * sl2;
@@ -474,7 +501,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                 const vec pb = pack_operand<T>(pv);
                 rowsum(pb);
 #pragma unroll
-                for (int db = 0; db < 2; ++db) o[db] = MM::mma(MM::load(sv + db * 4096 + voff[2 * sb + cc]), pb, o[db]);
+                for (int db = 0; db < NDB; ++db) o[db] = MM::mma(MM::load(sv + db * 4096 + voff[2 * sb + cc]), pb, o[db]);
             }
     };
 
@@ -492,52 +519,55 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     const float inv = 1.f / l;
     T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
 }
 
-// v columns of qkv [B*N, 3D] -> vt [B, H, 64, npad], token n at vt_pos(n)
-// (positions of no token untouched)
+// v columns of qkv [B*N, 3D] -> vt [B, D, npad] (row = v column, i.e. head
+// h's dims at rows h*dh..), token n at vt_pos(n) (positions of no token
+// untouched); blockIdx.y picks a group of 64 v columns
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const T *qkv, int N, int heads, T *vt,
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T *qkv, int N, int D, T *vt,
                                                           int64_t npad) {
     __shared__ T tile[64][65];
-    const int b = blockIdx.z, h = blockIdx.y, n0 = blockIdx.x * 64;
-    const int D = heads * DH;
+    const int b = blockIdx.z, c0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int r = ty; r < 64; r += 4) {
         const int n = n0 + r;
-        if (n < N) tile[r][tx] = qkv[((int64_t)b * N + n) * 3 * D + 2 * D + h * DH + tx];
+        if (n < N) tile[r][tx] = qkv[((int64_t)b * N + n) * 3 * D + 2 * D + c0 + tx];
     }
     __syncthreads();
     for (int d = ty; d < 64; d += 4) {
         const int n = n0 + tx;
-        if (n < N) vt[(((int64_t)b * heads + h) * DH + d) * npad + vt_pos(n)] = tile[tx][d];
+        if (n < N) vt[((int64_t)b * D + c0 + d) * npad + vt_pos(n)] = tile[tx][d];
     }
 }
 
-template <typename T>
+template <typename T, int DH>
 hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     // block-causal with CLS: query tiles cover tokens 1..N-1 plus the CLS
     // slot N, i.e. N slots from 1; otherwise tokens 0..N-1
     const int q_start = (a.block_causal && a.has_cls) ? 1 : 0;
     const int n_qtiles = (int)cdiv(a.N, QT);
     if (n_qtiles > 0) {
+        const dim3 grid(a.heads, a.B, n_qtiles);
         if constexpr (sizeof(T) == 2) {
             if (a.q_prescaled)
-                hipLaunchKernelGGL((attn16_kernel<T, true>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
-                                   q_start, n_qtiles);
+                hipLaunchKernelGGL((attn16_kernel<T, true, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
             else
-                hipLaunchKernelGGL((attn16_kernel<T, false>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
-                                   q_start, n_qtiles);
+                hipLaunchKernelGGL((attn16_kernel<T, false, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
         } else
-            hipLaunchKernelGGL((attn_kernel<T>), dim3(a.heads, a.B, n_qtiles), dim3(256), 0, s, a,
-                               q_start, n_qtiles);
+            hipLaunchKernelGGL((attn_kernel<T, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_dh(const AttnArgs &a, hipStream_t s) {
+    return a.dh == 32 ? launch_t<T, 32>(a, s) : launch_t<T, 64>(a, s);
 }
 
 }  // namespace
@@ -545,6 +575,8 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.N <= 0 || a.heads <= 0 || a.heads > 65535 || a.B > 65535 || a.N / QT >= 65535)
         return hipErrorInvalidValue;
+    if (a.dh != 32 && a.dh != 64) return hipErrorInvalidValue;
+    const int DH = a.dh;
     if (a.npad < cdiv(a.N, 64) * 64 || a.npad % 64) return hipErrorInvalidValue;
     // the 16-bit kernel addresses one item's rows with 32-bit byte offsets
     if ((int64_t)(a.N + 64) * a.ld_qk * 2 >= (1ll << 31) || (int64_t)DH * a.npad * 2 >= (1ll << 31))
@@ -553,26 +585,26 @@ hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
     if (((uintptr_t)a.qk | (uintptr_t)a.vt) % 16) return hipErrorInvalidValue;
     if (a.block_causal && (a.per_slot <= 0 || (a.N - a.has_cls) % a.per_slot)) return hipErrorInvalidValue;
     switch (act_dt) {
-        case DT_F32: return launch_t<float>(a, s);
-        case DT_BF16: return launch_t<bf16_t>(a, s);
-        case DT_F16: return launch_t<f16_t>(a, s);
+        case DT_F32: return launch_dh<float>(a, s);
+        case DT_BF16: return launch_dh<bf16_t>(a, s);
+        case DT_F16: return launch_dh<f16_t>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
+hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int D, void *vt,
                               int64_t npad, hipStream_t s) {
-    if (B <= 0 || N <= 0 || heads <= 0 || npad < cdiv(N, 16) * 16) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)cdiv(N, 64), heads, B);
+    if (B <= 0 || N <= 0 || D <= 0 || D % 64 || npad < cdiv(N, 16) * 16) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cdiv(N, 64), D / 64, B);
     switch (act_dt) {
         case DT_F32:
-            hipLaunchKernelGGL(transpose_v_kernel<float>, grid, dim3(256), 0, s, (const float *)qkv, N, heads, (float *)vt, npad);
+            hipLaunchKernelGGL(transpose_v_kernel<float>, grid, dim3(256), 0, s, (const float *)qkv, N, D, (float *)vt, npad);
             break;
         case DT_BF16:
-            hipLaunchKernelGGL(transpose_v_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)qkv, N, heads, (bf16_t *)vt, npad);
+            hipLaunchKernelGGL(transpose_v_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)qkv, N, D, (bf16_t *)vt, npad);
             break;
         case DT_F16:
-            hipLaunchKernelGGL(transpose_v_kernel<f16_t>, grid, dim3(256), 0, s, (const f16_t *)qkv, N, heads, (f16_t *)vt, npad);
+            hipLaunchKernelGGL(transpose_v_kernel<f16_t>, grid, dim3(256), 0, s, (const f16_t *)qkv, N, D, (f16_t *)vt, npad);
             break;
         default: return hipErrorInvalidValue;
     }

@@ -244,8 +244,9 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                               acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
                 if constexpr (EPI == EPI_QKV) {
                     if (g.rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
-                        const uint32_t p = (uint32_t)((col0 + col) & 63) >> 1;
-                        const float4 r = *(const float4 *)(g.rope + 2 * (rn * 32 + p));
+                        const uint32_t hd = (uint32_t)g.head_dim;
+                        const uint32_t p = (uint32_t)((col0 + col) & (hd - 1)) >> 1;
+                        const float4 r = *(const float4 *)(g.rope + 2 * (rn * (hd >> 1) + p));
                         const float z0 = z[0], z2 = z[2];
                         z[0] = z0 * r.x - z[1] * r.y;
                         z[1] = z0 * r.y + z[1] * r.x;
@@ -804,7 +805,8 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (epi == EPI_QKV) {
         // v starts at a multiple of 128 columns, so no wave straddles q/k and v
         if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
-            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15))
+            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15) ||
+            (g.rope && g.head_dim != 32 && g.head_dim != 64))
             return hipErrorInvalidValue;
         if ((g.M / g.ntok) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
     }

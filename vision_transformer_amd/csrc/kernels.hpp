@@ -41,11 +41,13 @@ struct GemmArgs {
     // row r = b*ntok + n being token n of item b
     void *vt;
     int64_t npad, vcol0;
-    // EPI_QKV: with rope (else null), f32 [ntok, 32] (cos, sin) pairs, the
-    // q and k columns' dims (2p, 2p+1) of each head of token n = row % ntok
-    // are rotated by entry (n, p) first; then the q columns [0, vcol0 / 2) are
-    // multiplied by qscale before rounding (0: left as they are)
+    // EPI_QKV: with rope (else null), f32 [ntok, head_dim / 2] (cos, sin)
+    // pairs, the q and k columns' dims (2p, 2p+1) of each head of token
+    // n = row % ntok are rotated by entry (n, p) first; then the q columns
+    // [0, vcol0 / 2) are multiplied by qscale before rounding (0: left as
+    // they are)
     const float *rope;
+    int head_dim;            // 32 or 64 (the rotary pairs' period)
     float qscale;
     // launches of this shape expected to run concurrently (batch parts on
     // other streams; 0 or 1: none), a hint for the tile-shape choice
@@ -61,9 +63,9 @@ __host__ __device__ __forceinline__ int64_t vt_pos(int64_t n) {
 }
 
 // ---- attention --------------------------------------------------------------
-// Q and K: act dtype rows of pitch ld_qk, q of head h at column h*64, k at
-// column D + h*64.  V transposed: vt [B, H, 64, npad], npad = N rounded up to
-// 64, columns N..npad-1 finite (zero).
+// Q and K: act dtype rows of pitch ld_qk, q of head h at column h*dh, k at
+// column D + h*dh.  V transposed: vt [B, D, npad] (head h's dims at rows
+// h*dh..), npad = N rounded up to 64, columns N..npad-1 finite (zero).
 struct AttnArgs {
     const void *qk;
     int64_t ld_qk;
@@ -72,13 +74,16 @@ struct AttnArgs {
     void *out;               // act dtype [B*N, D]
     int B, N, heads, has_cls, block_causal, per_slot;
     int q_prescaled;         // q already multiplied by ATTN_Q_SCALE
+    int dh;                  // head dim: 32 or 64
 };
 // log2(e) / sqrt(64): with q multiplied by it, q.k is the exponent of the
-// softmax in base 2
+// softmax in base 2 (head dim 64; for head dim 32, log2(e) / sqrt(32))
 constexpr float ATTN_Q_SCALE = 0.18033688011112042f;
+constexpr float ATTN_Q_SCALE_32 = 0.25503486164919736f;
+__host__ __device__ constexpr float attn_q_scale(int dh) { return dh == 32 ? ATTN_Q_SCALE_32 : ATTN_Q_SCALE; }
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
-// vt <- the v columns of a [B*N, 3D] qkv matrix, transposed per head
-hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int heads, void *vt,
+// vt [B, D, npad] <- the v columns of a [B*N, 3D] qkv matrix, transposed
+hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int D, void *vt,
                               int64_t npad, hipStream_t s);
 
 // ---- small helpers ----------------------------------------------------------
@@ -88,7 +93,9 @@ hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, 
 // pooling of a token map y [B, N, D]
 hipError_t launch_copy_f32(const float *y, int64_t n, float *out, hipStream_t s);
 hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipStream_t s);
-hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
+// mean pool via per-chunk partial sums: part holds B * POOL_CHUNKS * D floats
+constexpr int POOL_CHUNKS = 32;
+hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *part, float *out,
                             hipStream_t s);
 // q8_0 / q4_0 matrices expanded to the activation dtype, act(f32(d) * q), the
 // values the GEMM's own dequantising tile load makes.  Job j covers the

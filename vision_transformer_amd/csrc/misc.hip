@@ -109,18 +109,34 @@ __global__ void pool_cls_kernel(const float *y, int N, int D, float *out) {
     for (int d = threadIdx.x; d < D; d += blockDim.x) out[(int64_t)b * D + d] = y[(int64_t)b * N * D + d];
 }
 
-// Mean over rows first..N-1 of item b; 64 columns x 4 row-phases per block.
-__global__ __launch_bounds__(256) void pool_mean_kernel(const float *y, int N, int D, int first, float *out) {
+// Mean over rows first..N-1 of item b in two deterministic passes, so that
+// a long token map spreads over the whole chip: pass 1 sums chunk ch of the
+// rows (POOL_CHUNKS chunks per item) for 64 columns per block, 4 row phases
+// per column; pass 2 adds an item's chunk sums in chunk order and divides.
+__global__ __launch_bounds__(256) void pool_mean_part_kernel(const float *y, int N, int D, int first,
+                                                             float *part) {
     __shared__ float red[256];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int d = blockIdx.y * 64 + (tid & 63), part = tid >> 6;
+    const int b = blockIdx.x, ch = blockIdx.z, tid = threadIdx.x;
+    const int d = blockIdx.y * 64 + (tid & 63), phase = tid >> 6;
+    const int len = (N - first + POOL_CHUNKS - 1) / POOL_CHUNKS;
+    const int r0 = first + ch * len, r1 = min(N, r0 + len);
     const float *yb = y + (int64_t)b * N * D;
     float s = 0.f;
-    for (int r = first + part; r < N; r += 4) s += yb[(int64_t)r * D + d];
+    for (int r = r0 + phase; r < r1; r += 4) s += yb[(int64_t)r * D + d];
     red[tid] = s;
     __syncthreads();
     if (tid < 64)
-        out[(int64_t)b * D + d] = (red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]) / (float)(N - first);
+        part[((int64_t)b * POOL_CHUNKS + ch) * D + d] = (red[tid] + red[tid + 64]) + (red[tid + 128] + red[tid + 192]);
+}
+
+__global__ __launch_bounds__(256) void pool_mean_fin_kernel(const float *part, int B, int N, int D, int first,
+                                                            float *out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)B * D) return;
+    const int64_t b = i / D, d = i - b * D;
+    float s = 0.f;
+    for (int ch = 0; ch < POOL_CHUNKS; ++ch) s += part[(b * POOL_CHUNKS + ch) * D + d];
+    out[i] = s / (float)(N - first);
 }
 
 // ---------------------------------------------------------------------------
@@ -267,10 +283,12 @@ hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *out,
+hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *part, float *out,
                             hipStream_t s) {
-    if (B <= 0 || D % 64 || first >= N) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pool_mean_kernel, dim3(B, D / 64), dim3(256), 0, s, y, N, D, first, out);
+    if (B <= 0 || D % 64 || first >= N || !part) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pool_mean_part_kernel, dim3(B, D / 64, POOL_CHUNKS), dim3(256), 0, s, y, N, D, first, part);
+    hipLaunchKernelGGL(pool_mean_fin_kernel, dim3((unsigned)cdiv((int64_t)B * D, 256)), dim3(256), 0, s, part, B, N,
+                       D, first, out);
     return hipGetLastError();
 }
 

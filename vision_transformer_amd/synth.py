@@ -71,6 +71,15 @@ WORKLOADS = {
         dims=_dims(**_VITL, frames=16, tubelet=2, img_h=256, img_w=256, has_cls=0,
                    act_dtype="f16", mat_dtype="f16", rest_dtype="f16", rope=1),
         batch=4, frame_seed=1005, weight_seed=2005, outputs=("mean",)),
+    # blocks of the V-JEPA 2 predictor's width (12 layers, 384-d, heads of
+    # 32) at its worst case on the benchmarks page ("Masked predictor"
+    # table: context = target = every token of a 16-frame 256x256 clip, 4096
+    # tokens), with 3-D rotary position; the tokens come from 32 frames
+    "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4": dict(
+        dims=_dims(dim=384, depth=12, heads=12, mlp_dim=1536, patch=16, frames=32, tubelet=2,
+                   img_h=256, img_w=256, has_cls=0, act_dtype="bf16", mat_dtype="bf16",
+                   rest_dtype="bf16", rope=1),
+        batch=4, frame_seed=1006, weight_seed=2006, outputs=("mean",)),
 }
 
 # Small workloads the oracle finishes in seconds.  They keep the structure of
@@ -124,6 +133,22 @@ SMALL_WORKLOADS = {
                    img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
                    rest_dtype="f32", rope=1),
         batch=2, frame_seed=18, weight_seed=28),
+    # heads of 32 (the V-JEPA 2 predictor's head width)
+    "small_dh32_cls_bf16": dict(
+        dims=_dims(dim=192, depth=2, heads=6, mlp_dim=768, patch=16, img_h=80,
+                   img_w=112, frames=3, act_dtype="bf16", mat_dtype="bf16",
+                   rest_dtype="bf16"),
+        batch=2, frame_seed=20, weight_seed=30),
+    "small_dh32_rope_blockcausal_f16": dict(
+        dims=_dims(dim=128, depth=2, heads=4, mlp_dim=512, patch=16, tubelet=2,
+                   img_h=64, img_w=96, frames=8, has_cls=0, mask="block_causal",
+                   act_dtype="f16", mat_dtype="f16", rest_dtype="f16", rope=1),
+        batch=2, frame_seed=21, weight_seed=31),
+    "small_dh32_f32": dict(
+        dims=_dims(dim=128, depth=2, heads=4, mlp_dim=256, patch=14, img_h=84,
+                   img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
+                   rest_dtype="f32", rope=1),
+        batch=2, frame_seed=22, weight_seed=32),
     "small_rope_q4_0": dict(
         dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
                    img_h=96, img_w=112, frames=6, has_cls=0, act_dtype="f16",
