@@ -299,7 +299,11 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     const int my_hi = hi_of(qi);
     const int tile_last = (q0 + QT - 1 < N - 1) ? q0 + QT - 1 : N - 1;
     const int kend = hi_of(tile_last);
-    const int hi_min = hi_of(q0);
+    const int hi_min = hi_of(q0 + wave * 32);        // this wave's queries: the smallest end
+    // and the largest (its last slot, or the CLS slot N); key tiles at or past
+    // it are masked for every lane of the wave, whose step then skips its
+    // MFMAs and softmax (p would be exactly 0) but still loads and syncs
+    const int w_end = hi_of(min(q0 + wave * 32 + 31, N));
     const int kbeg = lo & ~(KT - 1);
     const int ntiles = (kend - kbeg + KT - 1) / KT;
 
@@ -418,6 +422,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
 
         // S^T = K Q^T, one 32-key block at a time
         const int k0 = kbeg + t * KT;
+        if (k0 >= w_end) return;
         f32x16 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
