@@ -137,13 +137,31 @@ def cpu_baseline(dims: dict, stored: list, frames: np.ndarray, sample_blocks: in
                        f"(float64 numpy oracle), {dt:.1f} s"
                        + (f", scaled x{dims['depth'] / sample_blocks:g} to a whole clip"
                           if sample_blocks != dims["depth"] else "")),
-            "clips_per_s": 1.0 / per_clip, "load_avg_1min_before": load0,
+            "clips_per_s": 1.0 / per_clip, "cpu_model": cpu_model(),
+            "cpus_available": len(os.sched_getaffinity(0)), "load_avg_1min_before": load0,
             "load_avg_1min_after": os.getloadavg()[0]}
 
 
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
+
+def device_info() -> dict:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 
 def copy_probe(mib: int) -> int:
     """A plain device-to-device copy of known size: it reads and writes
@@ -218,15 +236,19 @@ def main() -> int:
         enc.pool(pool_mode, B, pooled)
 
     def timed(nsteps):
+        """Wall seconds and device ms of nsteps back-to-back steps, and each
+        step's device ms (events on the caller's stream, which every step
+        forks from and joins back onto)."""
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
         t0 = time.perf_counter()
-        ev0.record()
-        for _ in range(nsteps):
+        evs[0].record()
+        for i in range(nsteps):
             step()
-        ev1.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(nsteps)]
+        return time.perf_counter() - t0, evs[0].elapsed_time(evs[-1]), per
 
     # a short profiled pass (not timed), batch as one part, finds the dominant class
     classes = list(_lib.jepa_kernel_stats(enc.ctx).keys())
@@ -253,7 +275,7 @@ def main() -> int:
     _lib.jepa_set_batch_parts(enc.ctx, args.parts)
     for _ in range(args.warmup):
         step()
-    wall, dev_ms = timed(args.steps)
+    wall, dev_ms, per_step = timed(args.steps)
     print(f"[bench] throughput region: {1e3 * wall / args.steps:.3f} ms per step", file=sys.stderr, flush=True)
 
     # timed region 2: roofline of the dominant class, batch as one part
@@ -263,7 +285,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     _lib.jepa_reset_kernel_stats(enc.ctx)
-    wall1, _ = timed(args.steps)
+    wall1, _, _ = timed(args.steps)
     st = _lib.jepa_kernel_stats(enc.ctx)[dominant]
     _lib.jepa_set_profiling(enc.ctx, 0)
     _lib.jepa_set_batch_parts(enc.ctx, 0)
@@ -344,9 +366,12 @@ def main() -> int:
         "mfma_util_pct": round(100 * util, 2),
         "forward_tflop": round(flops / 1e12, 4),
         "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "device_ms_per_step_min": round(min(per_step), 4),
+        "device_ms_per_step_sd": round(float(np.std(per_step)), 4),
         "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "api_wall_ms_per_step_host_io": round(api_ms, 4),
         "roofline": roof,
+        "device": device_info(),
     }
     enc.close()
     if not args.no_cpu_baseline:

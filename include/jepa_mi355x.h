@@ -132,8 +132,9 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
                         jepa_ctx **out);
 
 /* Encode a batch.  frames: uint8 [batch, frames, img_h, img_w, 3], HWC,
- * contiguous; device memory if frames_on_device, else host memory (copied
- * synchronously before the launches).  tokens_out: device f32
+ * contiguous; device memory if frames_on_device, else host memory, which is
+ * copied into a context-owned pinned buffer before the call returns (the
+ * caller may reuse it at once) and sent to the device on hip_stream.  tokens_out: device f32
  * [batch, N, dim] that receives the final-LayerNorm token map, or NULL to
  * keep it in a context-owned buffer.  The token map stays readable by
  * jepa_pool until the next encode on this context. */

@@ -160,6 +160,12 @@ struct jepa_ctx {
     size_t ws_bytes = 0;
     int ws_batch = 0;
     uint8_t *w_frames = nullptr;
+    // host frames are staged through this pinned buffer; h_ev marks the end
+    // of the last copy out of it
+    uint8_t *h_frames = nullptr;
+    size_t h_frames_bytes = 0;
+    hipEvent_t h_ev = nullptr;
+    bool h_pending = false;
     void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_vt = nullptr, *w_o = nullptr, *w_u = nullptr;
     float *w_x = nullptr, *w_y = nullptr, *w_pool = nullptr;
     // last encode
@@ -725,8 +731,28 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     const uint8_t *fr = frames;
     const size_t frame_bytes = (size_t)d.frames * d.img_h * d.img_w * 3;   // per item
     if (!frames_on_device) {
-        HIP_TRY(hipMemcpyAsync(c->w_frames, frames, (size_t)batch * frame_bytes, hipMemcpyHostToDevice, s0));
-        HIP_TRY(hipStreamSynchronize(s0));
+        // copy into the pinned staging buffer (once the previous copy out of
+        // it has finished), then DMA to the device on the caller's stream:
+        // the call returns after enqueue and the caller's buffer is free
+        const size_t bytes = (size_t)batch * frame_bytes;
+        if (c->h_pending) HIP_TRY(hipEventSynchronize(c->h_ev));
+        c->h_pending = false;
+        if (bytes > c->h_frames_bytes) {
+            if (c->h_frames) HIP_TRY(hipHostFree(c->h_frames));
+            c->h_frames = nullptr;
+            c->h_frames_bytes = 0;
+            if (hipHostMalloc((void **)&c->h_frames, bytes, hipHostMallocDefault) != hipSuccess) {
+                c->h_frames = nullptr;
+                (void)hipGetLastError();
+                return fail(JEPA_E_OOM, "encode: pinned staging of %zu frame bytes failed", bytes);
+            }
+            c->h_frames_bytes = bytes;
+        }
+        if (!c->h_ev) HIP_TRY(hipEventCreateWithFlags(&c->h_ev, hipEventDisableTiming));
+        memcpy(c->h_frames, frames, bytes);
+        HIP_TRY(hipMemcpyAsync(c->w_frames, c->h_frames, bytes, hipMemcpyHostToDevice, s0));
+        HIP_TRY(hipEventRecord(c->h_ev, s0));
+        c->h_pending = true;
         fr = c->w_frames;
     }
     float *Y = tokens_out ? tokens_out : c->w_y;
@@ -865,6 +891,8 @@ void jepa_free(jepa_ctx *c) {
     if (c->arena) (void)hipFree(c->arena);
     if (c->ws) (void)hipFree(c->ws);
     if (c->xbuf) (void)hipFree(c->xbuf);
+    if (c->h_frames) (void)hipHostFree(c->h_frames);
+    if (c->h_ev) (void)hipEventDestroy(c->h_ev);
     if (c->have_events) {
         (void)hipEventDestroy(c->ev0);
         (void)hipEventDestroy(c->ev1);
