@@ -24,5 +24,6 @@ Modules:
   quant    q8_0 / q4_0 quantizer and dequantizer, widening of f16 / bfloat16.
   encoder  normalisation, patchify, LayerNorm, GELU, masked attention, the
            encoder forward and pooling.
+  head     the attentive-pool classifier head (V-JEPA 2 SSv2 card).
   metrics  the comparison metrics.
 """

@@ -205,13 +205,19 @@ def embed(dims: dict, w: dict, frames: np.ndarray) -> np.ndarray:
     return e + w["enc.pos_embed"] if "enc.pos_embed" in w else e     # none with rotary position (R12)
 
 
-def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed) -> np.ndarray:
-    """One pre-LN block on X [B, N, D]:  x += Attn(LN1 x);  x += MLP(LN2 x)."""
-    p = f"enc.blk.{i}."
+def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed, prefix: str = "enc.blk.",
+          rotary: bool | None = None) -> np.ndarray:
+    """One pre-LN block on X [B, N, D]:  x += Attn(LN1 x);  x += MLP(LN2 x).
+
+    prefix names the block's tensors ("enc.blk." or, for the classifier
+    head, "head.blk."); rotary defaults to the model's setting (R12)."""
+    p = f"{prefix}{i}."
     eps = dims["ln_eps"]
     h = layer_norm(x, w[p + "ln1.weight"], w[p + "ln1.bias"], eps)
     qkv = linear(h, w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"])
-    ang = rope_angles(dims) if dims.get("rope") else None
+    if rotary is None:
+        rotary = bool(dims.get("rope"))
+    ang = rope_angles(dims) if rotary else None
     o = np.stack([attention(qkv[b], dims["heads"], allowed, ang=ang) for b in range(x.shape[0])])
     x = x + linear(o, w[p + "attn_out.weight"], w[p + "attn_out.bias"])
     h = layer_norm(x, w[p + "ln2.weight"], w[p + "ln2.bias"], eps)

@@ -91,41 +91,81 @@ def _rotary(dims, vec):
     return out
 
 
-def encode(dims, w, frames):
-    """frames uint8 [B, T, H, W, 3] -> list [B][N][D] of floats."""
+def _block(dims, w, p, x, rotary, may_attend):
+    """One pre-LN block (tensors under prefix p) on one item's rows x [N][D]."""
     D, H = dims["dim"], dims["heads"]
     dh = D // H
     eps = dims["ln_eps"]
+    N = len(x)
+    qkv = [_lin(_ln(x[n], w[p + "ln1.weight"], w[p + "ln1.bias"], eps),
+                w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"]) for n in range(N)]
+    o = [[0.0] * D for _ in range(N)]
+    for a in range(H):
+        qa = [qkv[n][a * dh:(a + 1) * dh] for n in range(N)]
+        ka = [qkv[n][D + a * dh:D + (a + 1) * dh] for n in range(N)]
+        if rotary:
+            qa, ka = _rotary(dims, qa), _rotary(dims, ka)
+        for i in range(N):
+            js = [j for j in range(N) if may_attend(i, j)]
+            s = [sum(qa[i][t] * ka[j][t] for t in range(dh)) / math.sqrt(dh) for j in js]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            for t in range(dh):
+                o[i][a * dh + t] = sum(e[q] / z * qkv[js[q]][2 * D + a * dh + t] for q in range(len(js)))
+    att = [_lin(o[n], w[p + "attn_out.weight"], w[p + "attn_out.bias"]) for n in range(N)]
+    x = [[x[n][d] + att[n][d] for d in range(D)] for n in range(N)]
+    mlp = []
+    for n in range(N):
+        h = _lin(_ln(x[n], w[p + "ln2.weight"], w[p + "ln2.bias"], eps), w[p + "ffn_up.weight"], w[p + "ffn_up.bias"])
+        h = [0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))) for z in h]
+        mlp.append(_lin(h, w[p + "ffn_down.weight"], w[p + "ffn_down.bias"]))
+    return [[x[n][d] + mlp[n][d] for d in range(D)] for n in range(N)]
+
+
+def encode(dims, w, frames):
+    """frames uint8 [B, T, H, W, 3] -> list [B][N][D] of floats."""
     X = _embed(dims, w, frames)
     for li in range(dims["depth"]):
-        p = f"enc.blk.{li}."
         for b in range(len(X)):
-            x = X[b]
-            N = len(x)
-            qkv = [_lin(_ln(x[n], w[p + "ln1.weight"], w[p + "ln1.bias"], eps),
-                        w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"]) for n in range(N)]
-            o = [[0.0] * D for _ in range(N)]
-            for a in range(H):
-                qa = [qkv[n][a * dh:(a + 1) * dh] for n in range(N)]
-                ka = [qkv[n][D + a * dh:D + (a + 1) * dh] for n in range(N)]
-                if dims.get("rope"):
-                    qa, ka = _rotary(dims, qa), _rotary(dims, ka)
-                for i in range(N):
-                    js = [j for j in range(N) if _may_attend(dims, i, j)]
-                    s = [sum(qa[i][t] * ka[j][t] for t in range(dh)) / math.sqrt(dh) for j in js]
-                    m = max(s)
-                    e = [math.exp(v - m) for v in s]
-                    z = sum(e)
-                    for t in range(dh):
-                        o[i][a * dh + t] = sum(e[q] / z * qkv[js[q]][2 * D + a * dh + t]
-                                               for q in range(len(js)))
-            att = [_lin(o[n], w[p + "attn_out.weight"], w[p + "attn_out.bias"]) for n in range(N)]
-            x = [[x[n][d] + att[n][d] for d in range(D)] for n in range(N)]
-            mlp = []
-            for n in range(N):
-                h = _lin(_ln(x[n], w[p + "ln2.weight"], w[p + "ln2.bias"], eps),
-                         w[p + "ffn_up.weight"], w[p + "ffn_up.bias"])
-                h = [0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))) for z in h]
-                mlp.append(_lin(h, w[p + "ffn_down.weight"], w[p + "ffn_down.bias"]))
-            X[b] = [[x[n][d] + mlp[n][d] for d in range(D)] for n in range(N)]
+            X[b] = _block(dims, w, f"enc.blk.{li}.", X[b], dims.get("rope"),
+                          lambda i, j: _may_attend(dims, i, j))
+    eps = dims["ln_eps"]
     return [[_ln(r, w["enc.norm.weight"], w["enc.norm.bias"], eps) for r in xb] for xb in X]
+
+
+def classify(dims, w, y):
+    """Attentive-pool head on a token map y [B][N][D] -> class scores [B][C]:
+    the head's blocks, then one learned query attending (per head) over the
+    layer-normalised tokens, its out-projection added to the query, an MLP
+    with residual, and the classifier."""
+    D, H = dims["dim"], dims["heads"]
+    dh = D // H
+    eps = dims["ln_eps"]
+    p = "head.xattn."
+    q0 = [float(t) for t in w["head.query_token"]]
+    q = _lin(q0, w[p + "attn_q.weight"], w[p + "attn_q.bias"])
+    out = []
+    for xb in y:
+        x = [list(r) for r in xb]
+        for i in range(dims["head_blocks"]):
+            x = _block(dims, w, f"head.blk.{i}.", x, False, lambda i_, j_: True)
+        hs = [_ln(r, w[p + "ln1.weight"], w[p + "ln1.bias"], eps) for r in x]
+        ks = [_lin(h, w[p + "attn_k.weight"], w[p + "attn_k.bias"]) for h in hs]
+        vs = [_lin(h, w[p + "attn_v.weight"], w[p + "attn_v.bias"]) for h in hs]
+        o = [0.0] * D
+        for a in range(H):
+            s = [sum(q[a * dh + t] * k[a * dh + t] for t in range(dh)) / math.sqrt(dh) for k in ks]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            for t in range(dh):
+                o[a * dh + t] = sum(e[n] / z * vs[n][a * dh + t] for n in range(len(vs)))
+        att = _lin(o, w[p + "attn_out.weight"], w[p + "attn_out.bias"])
+        xq = [q0[d] + att[d] for d in range(D)]
+        u = _lin(_ln(xq, w[p + "ln2.weight"], w[p + "ln2.bias"], eps), w[p + "ffn_up.weight"], w[p + "ffn_up.bias"])
+        u = [0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))) for z in u]
+        mlp = _lin(u, w[p + "ffn_down.weight"], w[p + "ffn_down.bias"])
+        xq = [xq[d] + mlp[d] for d in range(D)]
+        out.append(_lin(xq, w["head.classifier.weight"], w["head.classifier.bias"]))
+    return out

@@ -414,6 +414,48 @@ def test_rope_encoder_matches_brute_force(kw):
 
 
 # ---------------------------------------------------------------------------
+# the attentive-pool classifier head (V-JEPA 2 SSv2 card; reading R13)
+# ---------------------------------------------------------------------------
+
+def _head_case(seed, N=5, **kw):
+    from oracle import head as HD
+    dims = _tiny_dims(dim=8, heads=2, mlp_dim=16, head_blocks=2, head_classes=3, **kw)
+    w = _tiny_weights(dims, seed)
+    y = np.random.default_rng(seed + 1).standard_normal((2, N, dims["dim"]))
+    return HD, dims, w, y
+
+
+def test_head_matches_brute_force():
+    HD, dims, w, y = _head_case(40)
+    got = HD.classify(dims, w, y)
+    ref = np.array(brute.classify(dims, w, y.tolist()))
+    assert got.shape == (2, 3)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_head_is_invariant_to_token_order():
+    """No position enters the head: shuffling the tokens leaves the scores."""
+    HD, dims, w, y = _head_case(41, N=7)
+    perm = np.random.default_rng(3).permutation(7)
+    np.testing.assert_allclose(HD.classify(dims, w, y[:, perm]), HD.classify(dims, w, y),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_head_repeated_token_equals_single_token():
+    """Attention over copies of one token averages equal values: N copies
+    score exactly like the token alone (catches a sum where a softmax-weighted
+    mean belongs)."""
+    HD, dims, w, y = _head_case(42, N=1)
+    many = np.repeat(y, 6, axis=1)
+    np.testing.assert_allclose(HD.classify(dims, w, many), HD.classify(dims, w, y), rtol=1e-12, atol=1e-13)
+    # and the head is not blind to its input (a shift of every feature alike
+    # is removed by the LayerNorms; a change of one feature is not)
+    z = y.copy()
+    z[..., 0] += 1.0
+    assert np.abs(HD.classify(dims, w, z) - HD.classify(dims, w, y)).max() > 1e-4
+
+
+# ---------------------------------------------------------------------------
 # block formats
 # ---------------------------------------------------------------------------
 

@@ -26,14 +26,15 @@ import numpy as np
 # Storage dtypes a tensor may have (jepa.cpp Quantization page, "The rule":
 # only the four 2-D block matrices may be re-typed to a block format).
 DTYPES = ("f32", "f16", "bf16", "q8_0", "q4_0")
-BLOCK_MATRICES = ("attn_qkv", "attn_out", "ffn_up", "ffn_down")
+BLOCK_MATRICES = ("attn_qkv", "attn_q", "attn_k", "attn_v", "attn_out", "ffn_up", "ffn_down")
 
 
 def _dims(**kw):
     d = dict(dim=192, depth=12, heads=3, mlp_dim=768, patch=14, tubelet=1,
              img_h=224, img_w=224, frames=1, has_cls=1, mask="bidir",
              ln_eps=1e-6, mean=(0.5, 0.5, 0.5), std=(0.5, 0.5, 0.5),
-             act_dtype="f32", mat_dtype="f32", rest_dtype="f32", rope=0)
+             act_dtype="f32", mat_dtype="f32", rest_dtype="f32", rope=0,
+             head_blocks=0, head_classes=0)
     d.update(kw)
     return d
 
@@ -208,6 +209,29 @@ def tensor_specs(dims: dict) -> list[tuple[str, int, int]]:
               (p + "ffn_up.weight", D, F), (p + "ffn_up.bias", F, 1),
               (p + "ffn_down.weight", F, D), (p + "ffn_down.bias", D, 1)]
     s += [("enc.norm.weight", D, 1), ("enc.norm.bias", D, 1)]
+    if dims.get("head_classes"):
+        # the attentive-pool classifier head (V-JEPA 2 SSv2 card): its
+        # self-attention blocks, the cross-attention query block, the classifier
+        for i in range(dims["head_blocks"]):
+            p = f"head.blk.{i}."
+            s += [(p + "ln1.weight", D, 1), (p + "ln1.bias", D, 1),
+                  (p + "attn_qkv.weight", D, 3 * D), (p + "attn_qkv.bias", 3 * D, 1),
+                  (p + "attn_out.weight", D, D), (p + "attn_out.bias", D, 1),
+                  (p + "ln2.weight", D, 1), (p + "ln2.bias", D, 1),
+                  (p + "ffn_up.weight", D, F), (p + "ffn_up.bias", F, 1),
+                  (p + "ffn_down.weight", F, D), (p + "ffn_down.bias", D, 1)]
+        p = "head.xattn."
+        s += [("head.query_token", D, 1),
+              (p + "ln1.weight", D, 1), (p + "ln1.bias", D, 1),
+              (p + "attn_q.weight", D, D), (p + "attn_q.bias", D, 1),
+              (p + "attn_k.weight", D, D), (p + "attn_k.bias", D, 1),
+              (p + "attn_v.weight", D, D), (p + "attn_v.bias", D, 1),
+              (p + "attn_out.weight", D, D), (p + "attn_out.bias", D, 1),
+              (p + "ln2.weight", D, 1), (p + "ln2.bias", D, 1),
+              (p + "ffn_up.weight", D, F), (p + "ffn_up.bias", F, 1),
+              (p + "ffn_down.weight", F, D), (p + "ffn_down.bias", D, 1),
+              ("head.classifier.weight", D, dims["head_classes"]),
+              ("head.classifier.bias", dims["head_classes"], 1)]
     return s
 
 
