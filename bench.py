@@ -1,7 +1,8 @@
 """Throughput of the JEPA ViT encoder forward on one MI355X.
 
 One step = one whole forward of a batch (patchify + patch-embed + every block +
-final LayerNorm) plus the pool the workload reports, with frames already
+final LayerNorm) plus the pool the workload reports (and, for a workload with
+the attentive-pool classifier head, its class scores), with frames already
 resident in HBM.  Default workload: the LeVJEPA-style ViT-L/16 video encoder,
 16 frames of 224x224, tubelet 1, block-causal, bf16, batch 4 (3137 tokens per
 clip), synthetic seeded frames and N(0, 0.02) weights.
@@ -72,8 +73,16 @@ def class_flops(dims: dict, B: int) -> dict:
 
 def forward_flops(dims: dict, B: int) -> int:
     f = class_flops(dims, B)
-    per_layer = f["gemm_qkv"] + f["gemm_out"] + f["gemm_fc1"] + f["gemm_fc2"] + f["attention"]
-    return f["gemm_patch"] + dims["depth"] * per_layer
+    gemms = f["gemm_qkv"] + f["gemm_out"] + f["gemm_fc1"] + f["gemm_fc2"]
+    total = f["gemm_patch"] + dims["depth"] * (gemms + f["attention"])
+    if dims.get("head_classes"):
+        # the classifier head: its blocks (bidirectional over every token), the
+        # keys and values of the tokens, the query row's products and attention
+        D, F, C, N = dims["dim"], dims["mlp_dim"], dims["head_classes"], synth.n_tokens(dims)
+        M = B * N
+        total += dims["head_blocks"] * (gemms + 4 * B * N * N * D)
+        total += 2 * (2 * M * D * D) + 2 * B * (2 * D * D + 2 * D * F + D * C) + 4 * B * N * D
+    return total
 
 
 def class_bytes(dims: dict, B: int) -> dict:
@@ -231,9 +240,14 @@ def main() -> int:
     pool_mode = "cls" if dims["has_cls"] else "mean"
     pooled = torch.empty((B, dims["dim"]), dtype=torch.float32, device="cuda")
 
+    head = bool(dims.get("head_classes"))
+    logits = torch.empty((B, dims["head_classes"]), dtype=torch.float32, device="cuda") if head else None
+
     def step():
         enc.encode(fr, tokens)
         enc.pool(pool_mode, B, pooled)
+        if head:
+            enc.classify(B, logits)
 
     def timed(nsteps):
         """Wall seconds and device ms of nsteps back-to-back steps, and each

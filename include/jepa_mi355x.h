@@ -77,7 +77,14 @@ typedef enum { JEPA_POOL_NONE = 0, JEPA_POOL_CLS = 1, JEPA_POOL_MEAN = 2 } jepa_
  * dims (2i, 2i+1) of segment a (a = 0, 1, 2: temporal slot, patch row, patch
  * column, ds = 2*floor(head_dim/6) dims each: 20 of 64, 10 of 32; the dims
  * after the three segments untouched) by pos_a * 10000^(-2i/ds) radians.  A
- * CLS token has no position and is not rotated. */
+ * CLS token has no position and is not rotated.
+ * head_classes > 0 adds the attentive-pool classifier head (V-JEPA 2 SSv2
+ * card, opening paragraph; benchmarks page, "Attentive-pool head"), run by
+ * jepa_classify on the final token map: head_blocks pre-LN blocks as the
+ * encoder's (bidirectional, no position terms) over every token; then one
+ * learned query q0 attends, per head, over LN1(tokens) projected to keys and
+ * values (the query is W_q q0 + b_q, with no LayerNorm); x = q0 +
+ * out_proj(attention); x += MLP(LN2(x)) (erf GELU); scores = W_c x + b_c. */
 typedef struct {
     int32_t dim, depth, heads, mlp_dim;
     int32_t patch, tubelet, img_h, img_w, frames;
@@ -88,6 +95,8 @@ typedef struct {
     float mean[3];
     float std[3];
     int32_t rope;       /* 0: additive enc.pos_embed; 1: 3-D rotary position */
+    int32_t head_blocks;  /* classifier head: self-attention blocks (the V-JEPA 2 SSv2 head: 3) */
+    int32_t head_classes; /* classifier head: classes (0 = no head; SSv2: 174) */
 } jepa_dims;
 
 /* One stored tensor, host memory.  ne0 = row length (in-features), ne1 =
@@ -103,10 +112,17 @@ typedef struct {
  *   enc.blk.{i}.ffn_up.weight [D, F] .bias [F]
  *   enc.blk.{i}.ffn_down.weight [F, D] .bias [D]
  *   enc.norm.weight/.bias [D]
+ * With head_classes = C > 0, also (see jepa_dims):
+ *   head.blk.{i}.* as enc.blk.{i}.*, for i < head_blocks
+ *   head.query_token [D]   head.xattn.ln1/ln2.weight/.bias [D]
+ *   head.xattn.attn_q/attn_k/attn_v/attn_out.weight [D, D] .bias [D]
+ *   head.xattn.ffn_up.weight [D, F] .bias [F]   head.xattn.ffn_down.weight [F, D] .bias [D]
+ *   head.classifier.weight [D, C] .bias [C]
  * A patch vector lists (dt, dy, dx, c) with c fastest; tokens are ordered
  * slot-major then raster; CLS is token 0 and owns pos row 0.
- * Only the four attn_qkv/attn_out/ffn_up/ffn_down weights may be Q8_0/Q4_0
- * (ne0 % 32 == 0); the rest are F32, F16 or BF16. */
+ * Only the attn_qkv / attn_q / attn_k / attn_v / attn_out / ffn_up /
+ * ffn_down weights may be Q8_0/Q4_0 (ne0 % 32 == 0); the rest are F32, F16
+ * or BF16. */
 typedef struct {
     const char *name;
     int32_t dtype;      /* jepa_dtype */
@@ -169,6 +185,14 @@ const char *jepa_last_error(void);
  * (HIP events on the encode's stream); waits for that encode to finish.
  * Negative if there was none. */
 float jepa_last_compute_ms(jepa_ctx *ctx);
+
+/* Class scores of the attentive-pool head for the token map of the last
+ * jepa_encode on this context: logits_out device f32 [batch, head_classes].
+ * JEPA_E_STATE before any encode, JEPA_E_UNSUPPORTED for a model without
+ * a head.  Work is enqueued on hip_stream; the head's blocks reuse the
+ * encode workspace, so the next encode must not start before it ends
+ * (true on one stream). */
+jepa_status jepa_classify(jepa_ctx *ctx, float *logits_out, void *hip_stream);
 
 /* Bytes of tensor data as stored (the size the weight file's tensors would
  * take: blocks for Q8_0/Q4_0, 2 or 4 bytes per element otherwise). */

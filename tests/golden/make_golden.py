@@ -33,7 +33,7 @@ from vision_transformer_amd import synth  # noqa: E402
 FULL = ["vit_l16_image_bf16_b32", "levjepa_vit_l16_16f_bf16_b4",
         "vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_f16",
         "vjepa2_vit_l16_64f256_q4_0", "vjepa2_rope_vit_l16_16f256_f16_b4",
-        "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4"]
+        "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4", "vjepa2_ssv2_classifier_vit_l16_16f256_f16_b4"]
 N_SAMPLE = 32
 
 
@@ -81,6 +81,9 @@ def make(name):
     if dims["has_cls"]:
         out["cls"] = E.pool(y, "cls", True).astype(np.float32)
     out["mean"] = E.pool(y, "mean", bool(dims["has_cls"])).astype(np.float32)
+    if dims.get("head_classes"):
+        from oracle import head as HD
+        out["logits"] = HD.classify(dims, w, y).astype(np.float32)
     sd = np.std(x, axis=-1)
     out["pre_norm_std_min_median_max"] = np.array([sd.min(), np.median(sd), sd.max()])
     path = os.path.join(HERE, f"{name}.npz")

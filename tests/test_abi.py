@@ -168,3 +168,20 @@ def test_create_with_rope_has_no_pos_table(lib):
     assert "enc.pos_embed" in msg
     _expect_error(lib, "JEPA_E_INVALID_ARG", dict(dims, rope=2), stored)
     _expect_error(lib, "JEPA_E_MISSING_TENSOR", dict(dims, rope=0), stored)
+
+
+def test_create_checks_the_classifier_head_schema(lib):
+    wl = synth.workload("small_head_bf16")
+    dims = wl["dims"]
+    stored = synth.stored_weights(dims, synth.make_f32_weights(dims, 1))
+    msg = _expect_error(lib, "JEPA_E_MISSING_TENSOR", dims,
+                        [t for t in stored if t["name"] != "head.xattn.attn_v.bias"])
+    assert "head.xattn.attn_v.bias" in msg
+    _expect_error(lib, "JEPA_E_INVALID_ARG", dict(dims, head_classes=0), stored)   # unknown head tensors
+    bad = [dict(t) for t in stored]
+    for t in bad:
+        if t["name"] == "head.classifier.weight":      # not a block matrix: stays dense
+            t["dtype"] = "q8_0"
+            t["data"] = Q.quantize("q8_0", np.zeros((t["ne1"], t["ne0"]), np.float32))
+    _expect_error(lib, "JEPA_E_DTYPE", dims, bad)
+    _expect_error(lib, "JEPA_E_INVALID_ARG", dict(dims, head_blocks=-1), stored)

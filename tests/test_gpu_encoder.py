@@ -105,6 +105,8 @@ def test_full_workload_against_stored_oracle(Encoder, name):
     if dims["has_cls"]:
         H.check_rows(act, enc.pool("cls", B).cpu().numpy(), g["cls"], "cls")
     H.check_rows(act, enc.pool("mean", B).cpu().numpy(), g["mean"], "mean")
+    if "logits" in g.files:
+        H.check_rows(act, enc.classify(B).cpu().numpy(), g["logits"], "class scores")
     enc.close()
 
 
@@ -247,6 +249,40 @@ def test_expansion_chosen_by_rows_per_part(Encoder, monkeypatch):
     y_dev = _run(enc, frames)
     ref = H.oracle_tokens(dims, stored, frames)
     H.check_rows(dims["act_dtype"], y_dev.cpu().numpy(), ref, "tokens")
+    enc.close()
+
+
+@pytest.mark.parametrize("name", ["small_head_bf16", "small_head_cls_q8_0", "small_head_dh32_f32"])
+def test_classifier_head_scores(Encoder, name):
+    """The attentive-pool head on the encoder's token map: class scores of
+    every item against the oracle (its blocks, cross-attention query, MLP and
+    classifier; rotary or additive position, CLS, q8_0 matrices, heads of 32)."""
+    from oracle import head as HD
+    H.say(f"classifier head {name}")
+    wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
+    enc = Encoder(dims, stored)
+    y_dev = _run(enc, frames)
+    logits = enc.classify(wl["batch"])
+    torch.cuda.synchronize()
+    ref_y = H.oracle_tokens(dims, stored, frames)
+    H.check_rows(dims["act_dtype"], y_dev.cpu().numpy(), ref_y, "tokens")
+    ref = HD.classify(dims, E.weights_f64(stored), ref_y)
+    H.check_rows(dims["act_dtype"], logits.cpu().numpy(), ref, "class scores")
+    enc.close()
+
+
+def test_classify_state_errors(Encoder):
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs("small_head_bf16")
+    enc = Encoder(dims, stored)
+    with pytest.raises(_lib.JepaError, match="JEPA_E_STATE"):
+        enc.classify(1)
+    enc.close()
+    wl, dims, frames, stored = H.workload_inputs("small_bidir_f32")
+    enc = Encoder(dims, stored)
+    _run(enc, frames)
+    with pytest.raises(_lib.JepaError, match="JEPA_E_UNSUPPORTED"):
+        _lib.jepa_classify(enc.ctx, torch.empty((2, 1), device="cuda"))
     enc.close()
 
 

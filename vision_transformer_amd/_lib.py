@@ -36,7 +36,7 @@ class jepa_dims(C.Structure):
                 ("img_h", C.c_int32), ("img_w", C.c_int32), ("frames", C.c_int32),
                 ("has_cls", C.c_int32), ("mask", C.c_int32), ("act_dtype", C.c_int32),
                 ("ln_eps", C.c_float), ("mean", C.c_float * 3), ("std", C.c_float * 3),
-                ("rope", C.c_int32)]
+                ("rope", C.c_int32), ("head_blocks", C.c_int32), ("head_classes", C.c_int32)]
 
 
 class jepa_tensor(C.Structure):
@@ -58,6 +58,7 @@ def _load():
         "jepa_create": (I, [C.POINTER(jepa_dims), C.POINTER(jepa_tensor), I, C.POINTER(P)]),
         "jepa_encode": (I, [P, P, I, I, P, P]),
         "jepa_pool": (I, [P, I, P, P]),
+        "jepa_classify": (I, [P, P, P]),
         "jepa_free": (None, [P]),
         "jepa_last_error": (C.c_char_p, []),
         "jepa_last_compute_ms": (C.c_float, [P]),
@@ -117,7 +118,8 @@ def make_dims(d: dict) -> jepa_dims:
     return jepa_dims(d["dim"], d["depth"], d["heads"], d["mlp_dim"], d["patch"], d["tubelet"],
                      d["img_h"], d["img_w"], d["frames"], int(d["has_cls"]), MASK[d["mask"]],
                      DTYPE[d["act_dtype"]], float(d["ln_eps"]), (C.c_float * 3)(*d["mean"]),
-                     (C.c_float * 3)(*d["std"]), int(d.get("rope", 0)))
+                     (C.c_float * 3)(*d["std"]), int(d.get("rope", 0)), int(d.get("head_blocks", 0)),
+                     int(d.get("head_classes", 0)))
 
 
 def jepa_create(dims: dict, tensors: list[dict]) -> int:
@@ -148,6 +150,11 @@ def jepa_encode(ctx: int, frames, batch: int, tokens_out=None, stream=None) -> N
 def jepa_pool(ctx: int, mode: str | int, out, stream=None) -> None:
     m = POOL[mode] if isinstance(mode, str) else mode
     _check(_lib.jepa_pool(ctx, m, _ptr(out), _stream(stream)))
+
+
+def jepa_classify(ctx: int, logits_out, stream=None) -> None:
+    """Class scores [batch, classes] of the last encode's token map."""
+    _check(_lib.jepa_classify(ctx, _ptr(logits_out), _stream(stream)))
 
 
 def jepa_free(ctx: int) -> None:

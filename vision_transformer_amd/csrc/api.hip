@@ -113,9 +113,9 @@ float stored_to_f32(int dt, const void *data, int64_t i) {
 
 const char *kClassNames[] = {"patchify", "gemm_patch", "cls_rows", "layernorm", "gemm_qkv",
                              "transpose_v", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                             "final_ln", "pool", "expand_weights"};
+                             "final_ln", "pool", "expand_weights", "head"};
 enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_TRANSPOSE_V, K_ATTN,
-              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_EXPAND, K_COUNT };
+              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_EXPAND, K_HEAD, K_COUNT };
 
 struct DevTensor {
     void *ptr = nullptr;        // device data
@@ -128,6 +128,17 @@ struct Layer {
     DevTensor qkv, out, up, down;
     DevTensor xqkv, xout, xup, xdown;   // q8_0 / q4_0 ones expanded to the act dtype (when in use)
     float *ln1g, *ln1b, *ln2g, *ln2b, *bqkv, *bout, *bup, *bdown;
+};
+
+// The attentive-pool classifier head's cross-attention block and classifier
+// (its self-attention blocks are Layers).  The classifier's rows are padded
+// with zero rows to Cpad, a multiple of 64.
+struct Head {
+    int C = 0, Cpad = 0;
+    float *q0 = nullptr, *ln1g = nullptr, *ln1b = nullptr, *ln2g = nullptr, *ln2b = nullptr;
+    DevTensor wq, wk, wv, wo, wup, wdown, wc;
+    float *bq = nullptr, *bk = nullptr, *bv = nullptr, *bo = nullptr, *bup = nullptr, *bdown = nullptr,
+          *bc = nullptr;
 };
 
 struct ProfRec {
@@ -153,7 +164,8 @@ struct jepa_ctx {
     const ExpandJob *xjobs = nullptr;
     int n_xjobs = 0;
     int64_t x_nblk = 0;
-    std::vector<Layer> layers;
+    std::vector<Layer> layers, head_layers;
+    Head head;
     std::map<std::string, DevTensor> by_name;
     // workspace
     void *ws = nullptr;
@@ -168,6 +180,11 @@ struct jepa_ctx {
     bool h_pending = false;
     void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_vt = nullptr, *w_o = nullptr, *w_u = nullptr;
     float *w_x = nullptr, *w_y = nullptr, *w_pool = nullptr;
+    // classifier head: x rows f32, LN / cast output, query, attention out,
+    // MLP hidden (act dtype), padded scores f32
+    float *w_hx = nullptr, *w_hl = nullptr;
+    void *w_hh = nullptr, *w_hq = nullptr, *w_ho = nullptr, *w_hu = nullptr;
+    bool last_expand = false;   // the last encode used the expanded matrices
     // last encode
     const float *last_tokens = nullptr;
     int last_batch = 0;
@@ -193,7 +210,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, total;
+    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, total;
 };
 
 WsLayout ws_layout(const jepa_ctx *c, int B) {
@@ -211,6 +228,14 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
     w.u = take(M * c->F * c->es);
     w.y = take(M * c->D * 4);
     w.pool = take((size_t)B * POOL_CHUNKS * c->D * 4);
+    // the classifier head's rows (one per item)
+    const size_t hb = c->head.C > 0 ? (size_t)B : 0;
+    w.hx = take(hb * c->D * 4);
+    w.hh = take(hb * c->D * c->es);
+    w.hq = take(hb * c->D * c->es);
+    w.ho = take(hb * c->D * c->es);
+    w.hu = take(hb * c->F * c->es);
+    w.hl = take(hb * c->head.Cpad * 4);
     w.total = off;
     return w;
 }
@@ -223,18 +248,26 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
 // conversion on the VALU inside the K loop, and an int8 MFMA path with
 // per-block rescaling is VALU-bound on this chip.  Small batches keep the
 // dequantising 128 x 128 tile.  JEPA_Q_EXPAND = 0 / 1 forces either.
+// the encoder's blocks and the classifier head's (which run over every token)
+std::vector<Layer *> all_blocks(jepa_ctx *c) {
+    std::vector<Layer *> v;
+    for (auto &L : c->layers) v.push_back(&L);
+    for (auto &L : c->head_layers) v.push_back(&L);
+    return v;
+}
+
 std::vector<DevTensor *> q_matrices(jepa_ctx *c) {
     std::vector<DevTensor *> v;
-    for (auto &L : c->layers)
-        for (DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
+    for (Layer *L : all_blocks(c))
+        for (DevTensor *t : {&L->qkv, &L->out, &L->up, &L->down})
             if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) v.push_back(t);
     return v;
 }
 
 size_t expand_bytes(const jepa_ctx *c) {
     size_t n = 0, jobs = 0;
-    for (const auto &L : c->layers)
-        for (const DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
+    for (Layer *L : all_blocks(const_cast<jepa_ctx *>(c)))
+        for (const DevTensor *t : {&L->qkv, &L->out, &L->up, &L->down})
             if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) {
                 n += align256((size_t)t->ne0 * t->ne1 * c->es);
                 ++jobs;
@@ -264,7 +297,8 @@ jepa_status ensure_expanded(jepa_ctx *c) {
     size_t off = align256(mats.size() * sizeof(ExpandJob));
     std::vector<ExpandJob> jobs;
     int64_t blk = 0;
-    for (auto &L : c->layers) {
+    for (Layer *Lp : all_blocks(c)) {
+        Layer &L = *Lp;
         for (auto pr : {std::make_pair(&L.qkv, &L.xqkv), std::make_pair(&L.out, &L.xout),
                         std::make_pair(&L.up, &L.xup), std::make_pair(&L.down, &L.xdown)}) {
             const DevTensor &t = *pr.first;
@@ -323,6 +357,12 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
     c->w_u = base + w.u;
     c->w_y = (float *)(base + w.y);
     c->w_pool = (float *)(base + w.pool);
+    c->w_hx = (float *)(base + w.hx);
+    c->w_hh = base + w.hh;
+    c->w_hq = base + w.hq;
+    c->w_ho = base + w.ho;
+    c->w_hu = base + w.hu;
+    c->w_hl = (float *)(base + w.hl);
     c->ws_bytes = w.total;
     c->ws_batch = B;
     return JEPA_OK;
@@ -380,6 +420,9 @@ jepa_status check_dims(const jepa_dims *d) {
     if (d->frames % d->tubelet) return fail(JEPA_E_SHAPE, "dims: frames %% tubelet != 0");
     if (d->has_cls != 0 && d->has_cls != 1) return fail(JEPA_E_INVALID_ARG, "dims: has_cls must be 0 or 1");
     if (d->rope != 0 && d->rope != 1) return fail(JEPA_E_INVALID_ARG, "dims: rope must be 0 or 1");
+    if (d->head_blocks < 0 || d->head_classes < 0 || d->head_blocks > 64 || d->head_classes > (1 << 20))
+        return fail(JEPA_E_INVALID_ARG, "dims: head_blocks %d / head_classes %d out of range", d->head_blocks,
+                    d->head_classes);
     if (d->mask != JEPA_MASK_BIDIR && d->mask != JEPA_MASK_BLOCK_CAUSAL)
         return fail(JEPA_E_INVALID_ARG, "dims: unknown mask %d", d->mask);
     if (d->act_dtype != JEPA_F32 && d->act_dtype != JEPA_F16 && d->act_dtype != JEPA_BF16)
@@ -491,8 +534,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     if (!d.rope) want["enc.pos_embed"] = {D, N, false};
     want["enc.norm.weight"] = {D, 1, false};
     want["enc.norm.bias"] = {D, 1, false};
-    for (int i = 0; i < d.depth; ++i) {
-        const std::string p = "enc.blk." + std::to_string(i) + ".";
+    auto want_block = [&](const std::string &p) {
         want[p + "ln1.weight"] = {D, 1, false};
         want[p + "ln1.bias"] = {D, 1, false};
         want[p + "ln2.weight"] = {D, 1, false};
@@ -505,6 +547,30 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         want[p + "ffn_up.bias"] = {F, 1, false};
         want[p + "ffn_down.weight"] = {F, D, true};
         want[p + "ffn_down.bias"] = {D, 1, false};
+    };
+    for (int i = 0; i < d.depth; ++i) want_block("enc.blk." + std::to_string(i) + ".");
+    // the attentive-pool classifier head: its blocks, the cross-attention
+    // query block (query token, ln1 on the tokens, q / k / v / out, ln2, MLP)
+    // and the classifier
+    const int C = d.head_classes, Cpad = (C + 63) / 64 * 64;
+    if (C > 0) {
+        for (int i = 0; i < d.head_blocks; ++i) want_block("head.blk." + std::to_string(i) + ".");
+        const std::string p = "head.xattn.";
+        want["head.query_token"] = {D, 1, false};
+        for (const char *n : {"ln1", "ln2"}) {
+            want[p + n + ".weight"] = {D, 1, false};
+            want[p + n + ".bias"] = {D, 1, false};
+        }
+        for (const char *n : {"attn_q", "attn_k", "attn_v", "attn_out"}) {
+            want[p + n + ".weight"] = {D, D, true};
+            want[p + n + ".bias"] = {D, 1, false};
+        }
+        want[p + "ffn_up.weight"] = {D, F, true};
+        want[p + "ffn_up.bias"] = {F, 1, false};
+        want[p + "ffn_down.weight"] = {F, D, true};
+        want[p + "ffn_down.bias"] = {D, 1, false};
+        want["head.classifier.weight"] = {D, C, false};
+        want["head.classifier.bias"] = {C, 1, false};
     }
     size_t model_bytes = 0;
     for (int i = 0; i < n_tensors; ++i) {
@@ -566,15 +632,17 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
             off += align256((size_t)t->ne0 * t->ne1 / 32 * 2);
             p.bytes = codes;
         } else if (vec) {
+            // (the classifier's bias padded with zeros to a multiple of 64)
             p.dev_dt = JEPA_F32;
             p.off = off;
-            p.bytes = (size_t)t->ne0 * t->ne1 * 4;
+            p.bytes = (size_t)(kv.first == "head.classifier.bias" ? Cpad : t->ne0) * t->ne1 * 4;
             off += align256(p.bytes);
         } else {
+            // (the classifier's rows padded with zero rows to a multiple of 64)
             p.dev_dt = c->act;
             p.off = off;
             const int64_t rowlen = kv.first == "enc.patch_embed.weight" ? c->Kp : t->ne0;
-            p.bytes = (size_t)rowlen * t->ne1 * c->es;
+            p.bytes = (size_t)rowlen * (kv.first == "head.classifier.weight" ? Cpad : t->ne1) * c->es;
             off += align256(p.bytes);
         }
         plan.push_back(p);
@@ -656,10 +724,10 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     c->normg = vecp("enc.norm.weight");
     c->normb = vecp("enc.norm.bias");
     c->layers.resize(d.depth);
+    c->head_layers.resize(C > 0 ? d.head_blocks : 0);
     c->has_q = false;
-    for (int i = 0; i < d.depth; ++i) {
-        const std::string p = "enc.blk." + std::to_string(i) + ".";
-        Layer &L = c->layers[i];
+    auto is_q = [](const DevTensor &t) { return t.dev_dt == JEPA_Q8_0 || t.dev_dt == JEPA_Q4_0; };
+    auto setup_layer = [&](Layer &L, const std::string &p) {
         L.qkv = c->by_name[p + "attn_qkv.weight"];
         L.out = c->by_name[p + "attn_out.weight"];
         L.up = c->by_name[p + "ffn_up.weight"];
@@ -669,7 +737,25 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         L.bqkv = vecp(p + "attn_qkv.bias"); L.bout = vecp(p + "attn_out.bias");
         L.bup = vecp(p + "ffn_up.bias"); L.bdown = vecp(p + "ffn_down.bias");
         for (const DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
-            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) c->has_q = true;
+            if (is_q(*t)) c->has_q = true;
+    };
+    for (int i = 0; i < d.depth; ++i) setup_layer(c->layers[i], "enc.blk." + std::to_string(i) + ".");
+    for (size_t i = 0; i < c->head_layers.size(); ++i) setup_layer(c->head_layers[i], "head.blk." + std::to_string(i) + ".");
+    if (C > 0) {
+        Head &h = c->head;
+        const std::string p = "head.xattn.";
+        h.C = C; h.Cpad = Cpad;
+        h.q0 = vecp("head.query_token");
+        h.ln1g = vecp(p + "ln1.weight"); h.ln1b = vecp(p + "ln1.bias");
+        h.ln2g = vecp(p + "ln2.weight"); h.ln2b = vecp(p + "ln2.bias");
+        h.wq = c->by_name[p + "attn_q.weight"]; h.bq = vecp(p + "attn_q.bias");
+        h.wk = c->by_name[p + "attn_k.weight"]; h.bk = vecp(p + "attn_k.bias");
+        h.wv = c->by_name[p + "attn_v.weight"]; h.bv = vecp(p + "attn_v.bias");
+        h.wo = c->by_name[p + "attn_out.weight"]; h.bo = vecp(p + "attn_out.bias");
+        h.wup = c->by_name[p + "ffn_up.weight"]; h.bup = vecp(p + "ffn_up.bias");
+        h.wdown = c->by_name[p + "ffn_down.weight"]; h.bdown = vecp(p + "ffn_down.bias");
+        h.wc = c->by_name["head.classifier.weight"]; h.bc = vecp("head.classifier.bias");
+        h.wc.ne1 = Cpad;   // the GEMM runs over the padded rows
     }
     if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
         jepa_free(c);
@@ -717,6 +803,49 @@ static jepa_status ensure_streams(jepa_ctx *c, int parts) {
     return JEPA_OK;
 }
 
+// One pre-LN block on the rows of items b0 .. b0+nb-1 of the residual stream
+// (row r0 = b0*N on), on stream s: LN1, the qkv GEMM (q scaled, optionally
+// rotated; v to V^T), attention, out-projection + residual, LN2, fc1 + GELU,
+// fc2 + residual.  expand: the q8_0 / q4_0 matrices' act-dtype copies.
+static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream_t s, int conc, int64_t r0,
+                             int b0, int nb, bool causal, const float *rope) {
+    const jepa_dims &d = c->d;
+    const int D = c->D, F = c->F, es = c->es, dh = D / c->H;
+    auto rows = [&](void *base, int64_t first, int64_t width, int esz) {
+        return (void *)((unsigned char *)base + first * width * esz);
+    };
+    const DevTensor &Wqkv = expand ? L.xqkv : L.qkv, &Wout = expand ? L.xout : L.out;
+    const DevTensor &Wup = expand ? L.xup : L.up, &Wdown = expand ? L.xdown : L.down;
+    const int64_t M = (int64_t)nb * c->N;
+    float *x = (float *)rows(c->w_x, r0, D, 4);
+    void *hn = rows(c->w_hn, r0, D, es), *qkv = rows(c->w_qkv, r0, 3 * D, es);
+    void *o = rows(c->w_o, r0, D, es), *u = rows(c->w_u, r0, F, es);
+    void *vt = rows(c->w_vt, b0, D * c->npad, es);
+    AttnArgs aa{};
+    aa.qk = qkv; aa.ld_qk = 3 * D; aa.vt = vt; aa.npad = c->npad;
+    aa.out = o; aa.B = nb; aa.N = c->N; aa.heads = c->H;
+    aa.has_cls = d.has_cls; aa.block_causal = causal; aa.per_slot = c->per_slot;
+    aa.q_prescaled = 1;
+    aa.dh = dh;
+    TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
+    {   // q, k to qkv; v transposed straight into V^T
+        GemmArgs g{};
+        g.a = hn; g.w = Wqkv.ptr; g.wscale = Wqkv.scale; g.bias = L.bqkv; g.out = qkv;
+        g.M = M; g.N = Wqkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
+        g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
+        g.rope = rope; g.head_dim = dh;
+        g.qscale = attn_q_scale(dh);   // the softmax scale and base change, folded into q
+        g.conc = conc;
+        TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
+    }
+    TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
+    TRY(gemm(c, K_GEMM_OUT, s, conc, o, M, D, Wout, L.bout, EPI_RESID, x, D));
+    TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
+    TRY(gemm(c, K_GEMM_FC1, s, conc, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
+    TRY(gemm(c, K_GEMM_FC2, s, conc, u, M, F, Wdown, L.bdown, EPI_RESID, x, D));
+    return JEPA_OK;
+}
+
 jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frames_on_device,
                         float *tokens_out, void *hip_stream) {
     if (!c || !frames) return fail(JEPA_E_INVALID_ARG, "encode: null argument");
@@ -758,6 +887,7 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     float *Y = tokens_out ? tokens_out : c->w_y;
     HIP_TRY(hipEventRecord(c->ev0, s0));
     const bool expand = use_expand(c, batch, parts);
+    c->last_expand = expand;
     if (expand) {
         TRY(ensure_expanded(c));
         TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
@@ -804,42 +934,10 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             }));
     }
 
-    for (int i = 0; i < c->L; ++i) {
-        const Layer &L = c->layers[i];
-        const DevTensor &Wqkv = expand ? L.xqkv : L.qkv, &Wout = expand ? L.xout : L.out;
-        const DevTensor &Wup = expand ? L.xup : L.up, &Wdown = expand ? L.xdown : L.down;
-        for (int p = 0; p < parts; ++p) {
-            const Part &q = P[p];
-            const hipStream_t s = q.s;
-            const int64_t M = q.M;
-            float *x = (float *)rows(c->w_x, q.r0, D, 4);
-            void *hn = rows(c->w_hn, q.r0, D, es), *qkv = rows(c->w_qkv, q.r0, 3 * D, es);
-            void *o = rows(c->w_o, q.r0, D, es), *u = rows(c->w_u, q.r0, F, es);
-            void *vt = rows(c->w_vt, q.b0, D * c->npad, es);
-            AttnArgs aa{};
-            aa.qk = qkv; aa.ld_qk = 3 * D; aa.vt = vt; aa.npad = c->npad;
-            aa.out = o; aa.B = q.nb; aa.N = c->N; aa.heads = c->H;
-            aa.has_cls = d.has_cls; aa.block_causal = d.mask == JEPA_MASK_BLOCK_CAUSAL; aa.per_slot = c->per_slot;
-            aa.q_prescaled = 1;
-            aa.dh = D / c->H;
-            TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
-            {   // q, k to qkv; v transposed straight into V^T
-                GemmArgs g{};
-                g.a = hn; g.w = Wqkv.ptr; g.wscale = Wqkv.scale; g.bias = L.bqkv; g.out = qkv;
-                g.M = M; g.N = Wqkv.ne1; g.K = D; g.lda = D; g.ldo = 3 * D;
-                g.ntok = c->N; g.vt = vt; g.npad = c->npad; g.vcol0 = 2 * D;
-                g.rope = c->rope; g.head_dim = D / c->H;
-                g.qscale = attn_q_scale(D / c->H);   // the softmax scale and base change, folded into q
-                g.conc = parts;
-                TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
-            }
-            TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
-            TRY(gemm(c, K_GEMM_OUT, s, parts, o, M, D, Wout, L.bout, EPI_RESID, x, D));
-            TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
-            TRY(gemm(c, K_GEMM_FC1, s, parts, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
-            TRY(gemm(c, K_GEMM_FC2, s, parts, u, M, F, Wdown, L.bdown, EPI_RESID, x, D));
-        }
-    }
+    for (int i = 0; i < c->L; ++i)
+        for (int p = 0; p < parts; ++p)
+            TRY(run_block(c, c->layers[i], expand, P[p].s, parts, P[p].r0, P[p].b0, P[p].nb,
+                          d.mask == JEPA_MASK_BLOCK_CAUSAL, c->rope));
     for (int p = 0; p < parts; ++p) {
         const Part &q = P[p];
         float *x = (float *)rows(c->w_x, q.r0, D, 4);
@@ -856,6 +954,44 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     c->last_tokens = Y;
     c->last_batch = batch;
     c->encoded = true;
+    return JEPA_OK;
+}
+
+jepa_status jepa_classify(jepa_ctx *c, float *logits_out, void *hip_stream) {
+    if (!c || !logits_out) return fail(JEPA_E_INVALID_ARG, "classify: null argument");
+    if (c->head.C <= 0) return fail(JEPA_E_UNSUPPORTED, "classify: the model has no classifier head");
+    if (!c->encoded) return fail(JEPA_E_STATE, "classify: no encode yet");
+    if (c->N > XATTN_MAX_N) return fail(JEPA_E_UNSUPPORTED, "classify: %d tokens exceed %d", c->N, XATTN_MAX_N);
+    const jepa_dims &d = c->d;
+    const Head &h = c->head;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int B = c->last_batch, D = c->D, F = c->F, dh = D / c->H;
+    const int64_t M = (int64_t)B * c->N;
+    // the head's blocks run on the residual stream, seeded with the token map
+    HIP_TRY(hipMemcpyAsync(c->w_x, c->last_tokens, (size_t)M * D * 4, hipMemcpyDeviceToDevice, s));
+    for (const Layer &L : c->head_layers) TRY(run_block(c, L, c->last_expand, s, 1, 0, 0, B, false, nullptr));
+    // keys and values of the normalised tokens (in the qkv buffer, pitch 3D)
+    TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, h.ln1g, h.ln1b, d.ln_eps, c->w_hn, c->act, s); }));
+    unsigned char *kv = (unsigned char *)c->w_qkv;
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hn, M, D, h.wk, h.bk, EPI_STORE, kv, 3 * D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hn, M, D, h.wv, h.bv, EPI_STORE, kv + (size_t)D * c->es, 3 * D));
+    // the query row of every item: W_q q0 + b_q
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cls_rows(c->w_hx, h.q0, nullptr, B, 1, D, s); }));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w_hx, (int64_t)B * D, c->w_hh, c->act, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wq, h.bq, EPI_STORE, c->w_hq, D));
+    TRY(launch(c, K_HEAD, s, [&] {
+        return launch_xattn(c->act, c->w_hq, kv, kv + (size_t)D * c->es, 3 * D, B, c->N, c->H, dh, c->w_ho, s);
+    }));
+    // x = q0 + out_proj(o); x += MLP(LN2 x); scores = W_c x + b_c
+    TRY(gemm(c, K_HEAD, s, 1, c->w_ho, B, D, h.wo, h.bo, EPI_RESID, c->w_hx, D));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_layernorm(c->w_hx, B, D, h.ln2g, h.ln2b, d.ln_eps, c->w_hh, c->act, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wup, h.bup, EPI_GELU, c->w_hu, F));
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hu, B, F, h.wdown, h.bdown, EPI_RESID, c->w_hx, D));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w_hx, (int64_t)B * D, c->w_hh, c->act, s); }));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_fill(c->w_hl, (int64_t)B * h.Cpad, 0.f, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wc, h.bc, EPI_RESID, c->w_hl, h.Cpad));
+    HIP_TRY(hipMemcpy2DAsync(logits_out, (size_t)h.C * 4, c->w_hl, (size_t)h.Cpad * 4, (size_t)h.C * 4, B,
+                             hipMemcpyDeviceToDevice, s));
     return JEPA_OK;
 }
 

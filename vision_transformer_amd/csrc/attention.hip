@@ -530,6 +530,75 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
 }
 
+// One query row per item against that item's N keys and values (the
+// classifier head's cross-attention), one workgroup per (head, item).  The
+// scores go to LDS (one key per thread per pass, 16-byte key loads), then
+// their max, the exponentials and their sum; the output is the weighted sum
+// of the value rows, DH columns by 256/DH key phases, reduced in LDS.  f32
+// arithmetic; the kernel reads K and V once and is bound by that.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void xattn_kernel(const T *q, const T *k, const T *v, int64_t ldkv, int N,
+                                                    int heads, T *out) {
+    constexpr int CE = 16 / (int)sizeof(T);     // elements per 16-byte load
+    constexpr int PH = 256 / DH;                // key phases of the value pass
+    constexpr float SC = DH == 32 ? 0.17677669529663687f : 0.125f;   // 1 / sqrt(DH)
+    __shared__ float sp[XATTN_MAX_N];
+    __shared__ float sq[DH];
+    __shared__ float red[256];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int64_t D = (int64_t)heads * DH;
+    if (tid < DH) sq[tid] = to_f32(q[b * D + h * DH + tid]) * SC;
+    __syncthreads();
+    const T *kb = k + (int64_t)b * N * ldkv + h * DH;
+    float mx = -INFINITY;
+    for (int n = tid; n < N; n += 256) {
+        const uint4 *kr = (const uint4 *)(kb + (int64_t)n * ldkv);
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < DH / CE; ++c) {
+            const uint4 w = kr[c];
+            const T *e = (const T *)&w;
+#pragma unroll
+            for (int j = 0; j < CE; ++j) s = fmaf(sq[c * CE + j], to_f32(e[j]), s);
+        }
+        sp[n] = s;
+        mx = fmaxf(mx, s);
+    }
+    red[tid] = mx;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+        __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+    float sum = 0.f;
+    for (int n = tid; n < N; n += 256) {
+        const float p = __expf(sp[n] - mx);
+        sp[n] = p;
+        sum += p;
+    }
+    red[tid] = sum;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    sum = red[0];
+    __syncthreads();
+    const int c = tid % DH, ph = tid / DH;
+    const T *vb = v + (int64_t)b * N * ldkv + h * DH + c;
+    float acc = 0.f;
+    for (int n = ph; n < N; n += PH) acc = fmaf(sp[n], to_f32(vb[(int64_t)n * ldkv]), acc);
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < DH) {
+        float o = 0.f;
+        for (int p = 0; p < PH; ++p) o += red[p * DH + tid];
+        out[b * D + h * DH + tid] = from_f32<T>(o / sum);
+    }
+}
+
 // v columns of qkv [B*N, 3D] -> vt [B, D, npad] (row = v column, i.e. head
 // h's dims at rows h*dh..), token n at vt_pos(n) (positions of no token
 // untouched); blockIdx.y picks a group of 64 v columns
@@ -595,6 +664,25 @@ hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s) {
         case DT_F16: return launch_dh<f16_t>(a, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_xattn(int act_dt, const void *q, const void *k, const void *v, int64_t ldkv, int B, int N,
+                        int heads, int dh, void *out, hipStream_t s) {
+    if (B <= 0 || B > 65535 || N <= 0 || N > XATTN_MAX_N || heads <= 0 || heads > 65535 || (dh != 32 && dh != 64))
+        return hipErrorInvalidValue;
+    const int es = act_dt == DT_F32 ? 4 : 2;
+    if (ldkv < (int64_t)heads * dh || (ldkv * es) % 16 || ((uintptr_t)k | (uintptr_t)v) % 16) return hipErrorInvalidValue;
+    const dim3 grid(heads, B);
+#define XA(T, DH_) hipLaunchKernelGGL((xattn_kernel<T, DH_>), grid, dim3(256), 0, s, (const T *)q, (const T *)k, \
+                                      (const T *)v, ldkv, N, heads, (T *)out)
+    switch (act_dt) {
+        case DT_F32: if (dh == 32) XA(float, 32); else XA(float, 64); break;
+        case DT_BF16: if (dh == 32) XA(bf16_t, 32); else XA(bf16_t, 64); break;
+        case DT_F16: if (dh == 32) XA(f16_t, 32); else XA(f16_t, 64); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef XA
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int D, void *vt,

@@ -86,7 +86,18 @@ hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
 hipError_t launch_transpose_v(int act_dt, const void *qkv, int B, int N, int D, void *vt,
                               int64_t npad, hipStream_t s);
 
+// One query row per item attending over that item's N key / value rows
+// (the classifier head's cross-attention): q act [B, D], k and v act rows
+// of pitch ldkv (token b*N + n), heads of dh (32 or 64), softmax scale
+// 1/sqrt(dh) -> out act [B, D].  N <= XATTN_MAX_N.
+constexpr int XATTN_MAX_N = 16384;
+hipError_t launch_xattn(int act_dt, const void *q, const void *k, const void *v, int64_t ldkv, int B, int N,
+                        int heads, int dh, void *out, hipStream_t s);
+
 // ---- small helpers ----------------------------------------------------------
+// y (act dtype) <- x (f32), n elements; x <- v, n elements
+hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t s);
+hipError_t launch_fill(float *x, int64_t n, float v, hipStream_t s);
 // X[b*N + 0] = cls + pos[0] for every item (pos null: cls)
 hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
                            hipStream_t s);

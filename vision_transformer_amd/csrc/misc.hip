@@ -172,6 +172,19 @@ __global__ void dequant_kernel(int w_dt, const void *w, const uint16_t *scale, i
     out[idx] = v;
 }
 
+// f32 values rounded to the act dtype, and a fill (graph-capturable, unlike
+// a memset node)
+template <typename T>
+__global__ __launch_bounds__(256) void cast_kernel(const float *x, int64_t n, T *y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = from_f32<T>(x[i]);
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float *x, int64_t n, float v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) x[i] = v;
+}
+
 // One thread per block of 32 weights: 32 (q8_0) or 16 (q4_0) code bytes and
 // the f16 scale in, 64 bytes of act values out.  Neighbouring threads take
 // neighbouring blocks, so every wave reads and writes contiguous runs.
@@ -215,6 +228,24 @@ __global__ __launch_bounds__(256) void expand_kernel(const ExpandJob *jobs, int 
 }
 
 }  // namespace
+
+hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t s) {
+    if (n <= 0 || cdiv(n, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cdiv(n, 256));
+    switch (y_dt) {
+        case DT_F32: hipLaunchKernelGGL(cast_kernel<float>, grid, dim3(256), 0, s, x, n, (float *)y); break;
+        case DT_BF16: hipLaunchKernelGGL(cast_kernel<bf16_t>, grid, dim3(256), 0, s, x, n, (bf16_t *)y); break;
+        case DT_F16: hipLaunchKernelGGL(cast_kernel<f16_t>, grid, dim3(256), 0, s, x, n, (f16_t *)y); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(float *x, int64_t n, float v, hipStream_t s) {
+    if (n <= 0 || cdiv(n, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, x, n, v);
+    return hipGetLastError();
+}
 
 hipError_t launch_expand(int act_dt, const ExpandJob *jobs, int njobs, int64_t nblk, hipStream_t s) {
     if (!jobs || njobs <= 0 || nblk <= 0 || cdiv(nblk, 256) >= (1ll << 31)) return hipErrorInvalidValue;

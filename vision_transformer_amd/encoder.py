@@ -44,6 +44,13 @@ class Encoder:
         _lib.jepa_pool(self.ctx, mode, out, stream)
         return out
 
+    def classify(self, batch: int, out=None, stream=None):
+        """Class scores f32 [batch, head_classes] of the last encode's tokens."""
+        if out is None:
+            out = torch.empty((batch, self.dims["head_classes"]), dtype=torch.float32, device="cuda")
+        _lib.jepa_classify(self.ctx, out, stream)
+        return out
+
     def dequant(self, name: str, shape, stream=None):
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
         _lib.jepa_dequant_tensor(self.ctx, name, out, stream)

@@ -81,6 +81,14 @@ WORKLOADS = {
                    img_h=256, img_w=256, has_cls=0, act_dtype="bf16", mat_dtype="bf16",
                    rest_dtype="bf16", rope=1),
         batch=4, frame_seed=1006, weight_seed=2006, outputs=("mean",)),
+    # the V-JEPA 2 ViT-L/16 SSv2 classifier (V-JEPA 2 SSv2 card, opening
+    # paragraph): the encoder with 3-D rotary position and the attentive-pool
+    # head, 3 self-attention blocks and 174 classes
+    "vjepa2_ssv2_classifier_vit_l16_16f256_f16_b4": dict(
+        dims=_dims(**_VITL, frames=16, tubelet=2, img_h=256, img_w=256, has_cls=0,
+                   act_dtype="f16", mat_dtype="f16", rest_dtype="f16", rope=1,
+                   head_blocks=3, head_classes=174),
+        batch=4, frame_seed=1007, weight_seed=2007, outputs=("logits", "mean")),
 }
 
 # Small workloads the oracle finishes in seconds.  They keep the structure of
@@ -150,6 +158,23 @@ SMALL_WORKLOADS = {
                    img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
                    rest_dtype="f32", rope=1),
         batch=2, frame_seed=22, weight_seed=32),
+    # with the attentive-pool classifier head
+    "small_head_bf16": dict(
+        dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
+                   img_h=64, img_w=96, frames=4, has_cls=0, act_dtype="bf16",
+                   mat_dtype="bf16", rest_dtype="bf16", rope=1, head_blocks=3,
+                   head_classes=10),
+        batch=3, frame_seed=23, weight_seed=33),
+    "small_head_cls_q8_0": dict(
+        dims=_dims(dim=192, depth=2, heads=3, mlp_dim=768, patch=16, img_h=80,
+                   img_w=112, frames=3, act_dtype="f16", mat_dtype="q8_0",
+                   rest_dtype="f16", head_blocks=1, head_classes=70),
+        batch=2, frame_seed=24, weight_seed=34),
+    "small_head_dh32_f32": dict(
+        dims=_dims(dim=128, depth=2, heads=4, mlp_dim=256, patch=14, img_h=84,
+                   img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
+                   rest_dtype="f32", head_blocks=2, head_classes=5),
+        batch=2, frame_seed=25, weight_seed=35),
     "small_rope_q4_0": dict(
         dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
                    img_h=96, img_w=112, frames=6, has_cls=0, act_dtype="f16",
