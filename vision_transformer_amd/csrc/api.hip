@@ -183,6 +183,7 @@ struct jepa_ctx {
     // classifier head: x rows f32, LN / cast output, query, attention out,
     // MLP hidden (act dtype), padded scores f32
     float *w_hx = nullptr, *w_hl = nullptr;
+    float *w_kpart = nullptr, *w_kvpart = nullptr;   // f32 models: split partials
     void *w_hh = nullptr, *w_hq = nullptr, *w_ho = nullptr, *w_hu = nullptr;
     bool last_expand = false;   // the last encode used the expanded matrices
     // last encode
@@ -210,7 +211,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, total;
+    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, kpart, kvpart, total;
 };
 
 WsLayout ws_layout(const jepa_ctx *c, int B) {
@@ -236,6 +237,11 @@ WsLayout ws_layout(const jepa_ctx *c, int B) {
     w.ho = take(hb * c->D * c->es);
     w.hu = take(hb * c->F * c->es);
     w.hl = take(hb * c->head.Cpad * 4);
+    // f32 models (small ones) split long residual GEMMs and attention over
+    // few workgroups; their partial results
+    const bool f32 = c->act == JEPA_F32;
+    w.kpart = take(f32 ? (size_t)KSPLIT_MAX * M * c->D * 4 : 0);
+    w.kvpart = take(f32 ? (size_t)KVSPLIT_MAX * M * c->H * (c->D / c->H + 2) * 4 : 0);
     w.total = off;
     return w;
 }
@@ -363,6 +369,8 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
     c->w_ho = base + w.ho;
     c->w_hu = base + w.hu;
     c->w_hl = (float *)(base + w.hl);
+    c->w_kpart = c->act == JEPA_F32 ? (float *)(base + w.kpart) : nullptr;
+    c->w_kvpart = c->act == JEPA_F32 ? (float *)(base + w.kvpart) : nullptr;
     c->ws_bytes = w.total;
     c->ws_batch = B;
     return JEPA_OK;
@@ -767,11 +775,13 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
 }
 
 static jepa_status gemm(jepa_ctx *c, int cls, hipStream_t s, int conc, const void *a, int64_t M, int64_t K,
-                        const DevTensor &w, const float *bias, int epi, void *out, int64_t ldo) {
+                        const DevTensor &w, const float *bias, int epi, void *out, int64_t ldo,
+                        float *kpart = nullptr) {
     GemmArgs g{};
     g.a = a; g.w = w.ptr; g.wscale = w.scale; g.bias = bias; g.out = out;
     g.M = M; g.N = w.ne1; g.K = K; g.lda = K; g.ldo = ldo;
     g.conc = conc;
+    g.kpart = kpart;
     return launch(c, cls, s, [&] { return launch_gemm(c->act, w.dev_dt, epi, g, s); });
 }
 
@@ -827,6 +837,7 @@ static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream
     aa.has_cls = d.has_cls; aa.block_causal = causal; aa.per_slot = c->per_slot;
     aa.q_prescaled = 1;
     aa.dh = dh;
+    aa.kvpart = c->w_kvpart ? c->w_kvpart + (size_t)KVSPLIT_MAX * r0 * c->H * (dh + 2) : nullptr;
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
     {   // q, k to qkv; v transposed straight into V^T
         GemmArgs g{};
@@ -839,10 +850,13 @@ static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream
         TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
     }
     TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
-    TRY(gemm(c, K_GEMM_OUT, s, conc, o, M, D, Wout, L.bout, EPI_RESID, x, D));
+    // f32 models: scratch for splitting the residual GEMMs' K (each batch
+    // part its own rows of it)
+    float *kpart = c->w_kpart ? c->w_kpart + (size_t)KSPLIT_MAX * r0 * D : nullptr;
+    TRY(gemm(c, K_GEMM_OUT, s, conc, o, M, D, Wout, L.bout, EPI_RESID, x, D, kpart));
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
     TRY(gemm(c, K_GEMM_FC1, s, conc, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
-    TRY(gemm(c, K_GEMM_FC2, s, conc, u, M, F, Wdown, L.bdown, EPI_RESID, x, D));
+    TRY(gemm(c, K_GEMM_FC2, s, conc, u, M, F, Wdown, L.bdown, EPI_RESID, x, D, kpart));
     return JEPA_OK;
 }
 

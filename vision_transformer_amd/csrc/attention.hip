@@ -54,7 +54,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
     // heads is a multiple of 8) and share its L2; block-causal tiles go
     // heaviest (latest slot) first
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tile = a.block_causal ? (n_qtiles - 1 - (int)blockIdx.z) : (int)blockIdx.z;
+    // blockIdx.z = query tile * S + key split (S = a.kvsplit, 1: no split)
+    const int S = a.kvsplit > 1 ? a.kvsplit : 1;
+    const int zq = (int)blockIdx.z / S, split = (int)blockIdx.z % S;
+    const int tile = a.block_causal ? (n_qtiles - 1 - zq) : zq;
     const int N = a.N, D = a.heads * DH;
     const T *qk = (const T *)a.qk + (int64_t)b * N * a.ld_qk;
     const T *vt = (const T *)a.vt + ((int64_t)b * a.heads + h) * DH * a.npad;
@@ -127,13 +130,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
+    // this split's key tiles: [kb0, ke) of the query tile's [kbeg, kend)
     const int kbeg = lo & ~(KT - 1);
-    load_tile(kbeg);
+    const int nt = (kend - kbeg + KT - 1) / KT, per = (nt + S - 1) / S;
+    const int kb0 = kbeg + split * per * KT, ke = min(kend, kb0 + per * KT);
+    if (kb0 < ke) {
+    load_tile(kb0);
     store_tile(0);
     __syncthreads();
     int buf = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += KT, buf ^= 1) {
-        const bool more = k0 + KT < kend;
+    for (int k0 = kb0; k0 < ke; k0 += KT, buf ^= 1) {
+        const bool more = k0 + KT < ke;
         if (more) load_tile(k0 + KT);
         const unsigned char *kb = sK[buf];
         const unsigned char *vb = sV[buf];
@@ -168,7 +175,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float mn = fmaxf(m, mt);
         if (__any(mn > m)) {          // rescale only when some running max grew
-            const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
+            // (a lane whose max is still -inf has o = l = 0: alpha 0, not the
+            // NaN of -inf - -inf)
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * sl2);
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -176,7 +185,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
                 for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
             m = mn;
         }
-        const float mb = m * sl2;
+        // (a query with no allowed key yet, possible in a key split, keeps
+        // m = -inf and p = 0)
+        const float mb = m == -INFINITY ? 0.f : m * sl2;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -213,9 +224,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_st
         if (more) store_tile(buf ^ 1);
         __syncthreads();
     }
+    }
 
     l += __shfl_xor(l, 32, 64);
     if (!qvalid) return;
+    if (S > 1) {
+        // unnormalised output, running max (score units) and sum of this
+        // split, row ((split*B + b)*heads + h)*N + qrow of the scratch
+        float *pr = a.kvpart + ((((int64_t)split * a.B + b) * a.heads + h) * N + qrow) * (DH + 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pr[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = o[db][v];
+        if (g == 0) {
+            pr[DH] = m;
+            pr[DH + 1] = l;
+        }
+        return;
+    }
     const float inv = 1.f / l;
     T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
 #pragma unroll
@@ -530,6 +556,29 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
             out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
 }
 
+// Merge of the key splits of the f32 kernel: per output row and column, the
+// splits' outputs and sums weighted by exp2((m_s - max m) * sl2), in split
+// order.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *part, int S, int B, int heads, int N, float sl2,
+                                                         T *out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)B * heads * N;
+    if (i >= rows * DH) return;
+    const int64_t r = i / DH, d = i - r * DH;            // r = (b*heads + h)*N + q
+    const int64_t q = r % N, bh = r / N, h = bh % heads, b = bh / heads;
+    float mx = -INFINITY;
+    for (int z = 0; z < S; ++z) mx = fmaxf(mx, part[(z * rows + r) * (DH + 2) + DH]);
+    float num = 0.f, den = 0.f;
+    for (int z = 0; z < S; ++z) {
+        const float *pz = part + (z * rows + r) * (DH + 2);
+        const float w = __builtin_amdgcn_exp2f((pz[DH] - mx) * sl2);
+        num += w * pz[d];
+        den += w * pz[DH + 1];
+    }
+    out[(b * N + q) * (int64_t)heads * DH + h * DH + d] = from_f32<T>(num / den);
+}
+
 // One query row per item against that item's N keys and values (the
 // classifier head's cross-attention), one workgroup per (head, item).  The
 // scores go to LDS (one key per thread per pass, 16-byte key loads), then
@@ -632,8 +681,27 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
                 hipLaunchKernelGGL((attn16_kernel<T, true, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
             else
                 hipLaunchKernelGGL((attn16_kernel<T, false, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
-        } else
-            hipLaunchKernelGGL((attn_kernel<T, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
+        } else {
+            // few workgroups (small f32 models): split each query tile's keys
+            // over S workgroups and merge the splits in a second pass
+            const int64_t wgs = (int64_t)a.heads * a.B * n_qtiles;
+            const int kt = (int)cdiv(a.N + 1, KT);
+            const int S = (a.kvpart && 2 * wgs < 256 && kt >= 2) ? (kt >= KVSPLIT_MAX ? KVSPLIT_MAX : 2) : 1;
+            if (S > 1 && (int64_t)n_qtiles * S < 65535) {
+                AttnArgs as = a;
+                as.kvsplit = S;
+                hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(a.heads, a.B, n_qtiles * S), dim3(256), 0, s, as,
+                                   q_start, n_qtiles);
+                const int64_t n = (int64_t)a.B * a.heads * a.N * DH;
+                const float sl2 = a.q_prescaled ? 1.f : attn_q_scale(DH);
+                hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                                   a.kvpart, S, a.B, a.heads, a.N, sl2, (T *)a.out);
+            } else {
+                AttnArgs a1 = a;
+                a1.kvsplit = 1;
+                hipLaunchKernelGGL((attn_kernel<T, DH>), grid, dim3(256), 0, s, a1, q_start, n_qtiles);
+            }
+        }
         return hipGetLastError();
     }
     return hipSuccess;

@@ -21,6 +21,7 @@
 //   QKV    q, k columns as STORE (q optionally scaled first); v columns
 //          transposed per head into V^T
 #include <stdlib.h>
+#include <string.h>
 
 #include <string>
 #include <type_traits>
@@ -287,25 +288,42 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
     }
 }
 
-template <typename T, int WF, int EPI>
+// TS = 2: 128 x 128 tiles (waves of 64 x 64); TS = 1: 64 x 64 tiles (waves
+// of 32 x 32, dense weights only), for GEMMs whose 128-wide tiles would
+// leave most CUs idle.
+template <typename T, int WF, int EPI, int TS>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     typedef Mfma<T> MM;
     constexpr int ES = sizeof(T);
     constexpr int BK = 128 / ES;            // elements per K step
     constexpr int VEC = MM::VEC, KC = MM::KC;
     constexpr bool DENSE = (WF == DT_F32);  // DT_F32 here tags "dense, act dtype"
+    constexpr int TB = 64 * TS;             // tile rows and columns
+    constexpr int WT = 32 * TS;             // wave tile
+    static_assert(TS == 2 || (TS == 1 && DENSE), "64-wide tiles: dense weights only");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TILEB];
-    __shared__ __attribute__((aligned(16))) float sbias[BN];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TB * ROWB];
+    __shared__ __attribute__((aligned(16))) float sbias[TB];
+    static_assert(4 * 8192 <= 2 * 2 * TB * ROWB, "epilogue scratch");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-    const int nk = (int)(g.K / BK);
+    const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
+    // K steps [kt0, kt0 + nk): all of K, or split blockIdx.z of a K split
+    // (f32 residual GEMMs; the launcher makes every split non-empty)
+    const int nk_all = (int)(g.K / BK);
+    const bool split = sizeof(T) == 4 && EPI == EPI_RESID && g.ksplit > 1;
+    int kt0 = 0, nk = nk_all;
+    if (split) {
+        const int per = (nk_all + g.ksplit - 1) / g.ksplit;
+        kt0 = (int)blockIdx.z * per;
+        nk = min(nk_all - kt0, per);
+    }
 
-    // the tile's biases (N is a multiple of 64; columns past N read as 0)
+    // the tile's biases (N is a multiple of 64; columns past N read as 0);
+    // a split's partial product leaves them to the second pass
     float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < BN / 4 && n0 + 4 * tid < g.N) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
+    if (!split && tid < TB / 4 && n0 + 4 * tid < g.N) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
 
     const unsigned char *A = (const unsigned char *)g.a;
     const unsigned char *W = (const unsigned char *)g.w;
@@ -315,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 
     auto load_global = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2 * TS; ++i) {
             const int r = (tid >> 3) + 32 * i;
             const int64_t m = m0 + r;
             areg[i] = make_uint4(0, 0, 0, 0);
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
         }
         if constexpr (DENSE) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2 * TS; ++i) {
                 const int r = (tid >> 3) + 32 * i;
                 const int64_t n = n0 + r;
                 breg.v[i] = make_uint4(0, 0, 0, 0);
@@ -359,13 +377,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
         unsigned char *sa = smem[buf][0];
         unsigned char *sb = smem[buf][1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2 * TS; ++i) {
             const int r = (tid >> 3) + 32 * i;
             *(uint4 *)(sa + r * ROWB + (tid & 7) * 16) = areg[i];
         }
         if constexpr (DENSE) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2 * TS; ++i) {
                 const int r = (tid >> 3) + 32 * i;
                 *(uint4 *)(sb + r * ROWB + (tid & 7) * 16) = breg.v[i];
             }
@@ -394,54 +412,56 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[TS][TS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TS; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TS; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const int arow = wm * 64 + (lane & 31);
-    const int brow = wn * 64 + (lane & 31);
+    const int arow = wm * WT + (lane & 31);
+    const int brow = wn * WT + (lane & 31);
     const int kofs = (lane >> 5) * VEC * ES;
 
-    load_global(0);
+    load_global(kt0);
     store_lds(0);
-    if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
+    if (tid < TB / 4) *(float4 *)(sbias + 4 * tid) = bias4;
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) load_global(kt + 1);
+        if (kt + 1 < nk) load_global(kt0 + kt + 1);
         const unsigned char *sa = smem[buf][0];
         const unsigned char *sb = smem[buf][1];
 #pragma unroll
         for (int c = 0; c < BK / KC; ++c) {
-            typename MM::vec a0 = MM::load(sa + arow * ROWB + c * KC * ES + kofs);
-            typename MM::vec a1 = MM::load(sa + (arow + 32) * ROWB + c * KC * ES + kofs);
-            typename MM::vec b0 = MM::load(sb + brow * ROWB + c * KC * ES + kofs);
-            typename MM::vec b1 = MM::load(sb + (brow + 32) * ROWB + c * KC * ES + kofs);
+            typename MM::vec av[TS], bv[TS];
+#pragma unroll
+            for (int i = 0; i < TS; ++i) {
+                av[i] = MM::load(sa + (arow + 32 * i) * ROWB + c * KC * ES + kofs);
+                bv[i] = MM::load(sb + (brow + 32 * i) * ROWB + c * KC * ES + kofs);
+            }
             // weights as the A operand: the accumulators come out transposed
-            acc[0][0] = MM::mma(b0, a0, acc[0][0]);
-            acc[0][1] = MM::mma(b1, a0, acc[0][1]);
-            acc[1][0] = MM::mma(b0, a1, acc[1][0]);
-            acc[1][1] = MM::mma(b1, a1, acc[1][1]);
+#pragma unroll
+            for (int i = 0; i < TS; ++i)
+#pragma unroll
+                for (int j = 0; j < TS; ++j) acc[i][j] = MM::mma(bv[j], av[i], acc[i][j]);
         }
         if (kt + 1 < nk) store_lds(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: block (i, j) holds rows m0 + wm*64 + i*32 + lane%32 and
-    // columns n0 + wn*64 + j*32 + 8*(v/4) + 4*g + v%4 ----
+    // ---- epilogue: block (i, j) holds rows m0 + wm*WT + i*32 + lane%32 and
+    // columns n0 + wn*WT + j*32 + 8*(v/4) + 4*g + v%4 ----
     const int g32 = lane >> 5;
     if constexpr (EPI == EPI_PATCH) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t row = m0 + wm * 64 + i * 32 + (lane & 31);
+        for (int i = 0; i < TS; ++i) {
+            const int64_t row = m0 + wm * WT + i * 32 + (lane & 31);
             if (row >= g.M) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t col0 = n0 + wn * 64 + j * 32 + 4 * g32;
+            for (int j = 0; j < TS; ++j) {
+                const int64_t col0 = n0 + wn * WT + j * 32 + 4 * g32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t col = col0 + 8 * (v >> 2) + (v & 3);
@@ -449,10 +469,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
                 }
             }
         }
-    } else if (n0 + wn * 64 < g.N) {   // a wave's 64 columns are all in or all out
+    } else if (n0 + wn * WT < g.N) {   // a wave's columns are all in or all out (N % 64 == 0)
         // the loop's last barrier has freed the operand tiles: 8 KB of scratch per wave
-        epilogue_wave<T, EPI, 2, 2>(g, acc, sbias + wn * 64, &smem[0][0][0] + wave * 8192,
-                                    m0 + wm * 64, n0 + wn * 64, lane);
+        if constexpr (sizeof(T) == 4 && EPI == EPI_RESID) {
+            if (split) {   // the partial product, plain f32, into split z's [M, N] slice
+                GemmArgs gz = g;
+                gz.out = g.kpart + (int64_t)blockIdx.z * g.M * g.N;
+                gz.ldo = g.N;
+                epilogue_wave<T, EPI_STORE, TS, TS>(gz, acc, sbias + wn * WT, &smem[0][0][0] + wave * 8192,
+                                                    m0 + wm * WT, n0 + wn * WT, lane);
+                return;
+            }
+        }
+        epilogue_wave<T, EPI, TS, TS>(g, acc, sbias + wn * WT, &smem[0][0][0] + wave * 8192,
+                                      m0 + wm * WT, n0 + wn * WT, lane);
     }
 }
 
@@ -725,7 +755,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
                                   n0 + wn * (BN / 2), lane);
 }
 
-// Variant choice (below); JEPA_GEMM_VARIANT (small | big256 | big128) pins it.
+// Variant choice (below); JEPA_GEMM_VARIANT (small | small64 | big256 | big128) pins it.
 
 int cu_count() {
     static int cached[64] = {};
@@ -737,6 +767,17 @@ int cu_count() {
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+// out[m, n] += bias[n] + the splits' partial products, added in split order
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(float *out, int64_t ldo, const float *part, int S,
+                                                            int64_t M, int N, const float *bias) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * N) return;
+    const int64_t m = i / N, n = i - m * N;
+    float v = bias[n];
+    for (int z = 0; z < S; ++z) v += part[z * M * N + i];
+    out[m * ldo + n] += v;
 }
 
 template <typename T, int EPI, int BN>
@@ -774,8 +815,43 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
             return launch_big<T, EPI, 128>(g, s);
         }
     }
+    // Dense GEMMs whose 128-wide tiles would fill fewer than half the CUs
+    // (small images, one row per item) take 64-wide tiles: four times the
+    // workgroups, each a quarter of the serial MFMA chain.
+    if constexpr (WF == DT_F32) {
+        const char *v = getenv("JEPA_GEMM_VARIANT");
+        const bool pin = v && *v;
+        const bool fits = cdiv(g.M, 64) < 65535;
+        if (fits && ((!pin && 2 * cdiv(g.M, BM) * cdiv(g.N, BN) < cu_count()) || (pin && !strcmp(v, "small64")))) {
+            dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64));
+            if constexpr (sizeof(T) == 4 && EPI == EPI_RESID) {
+                // f32 residual GEMMs with a long K and few tiles: split K into
+                // S parts of at least 3 steps (BK = 32), S the largest of 8 / 4 / 2
+                // that divides the steps, then add the parts in order
+                const int64_t nk = g.K / 32;
+                int S = 1;
+                for (int c : {8, 4, 2})
+                    if (S == 1 && nk % c == 0 && nk / c >= 3 && 4 * grid.x * grid.y * c <= (int64_t)cu_count() * 2) S = c;
+                if (g.kpart && S > 1 && g.M * g.N < (1ll << 31)) {
+                    GemmArgs gs = g;
+                    gs.ksplit = S;
+                    grid.z = S;
+                    hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 1>), grid, dim3(256), 0, s, gs);
+                    hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)cdiv(g.M * g.N, 256)), dim3(256), 0, s,
+                                       (float *)g.out, g.ldo, g.kpart, S, g.M, (int)g.N, g.bias);
+                    return hipGetLastError();
+                }
+            }
+            GemmArgs g1 = g;
+            g1.ksplit = 1;
+            hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 1>), grid, dim3(256), 0, s, g1);
+            return hipGetLastError();
+        }
+    }
+    GemmArgs g2 = g;
+    g2.ksplit = 1;
     dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(g.M, BM));
-    hipLaunchKernelGGL((gemm_kernel<T, WF, EPI>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 2>), grid, dim3(256), 0, s, g2);
     return hipGetLastError();
 }
 

@@ -52,7 +52,13 @@ struct GemmArgs {
     // launches of this shape expected to run concurrently (batch parts on
     // other streams; 0 or 1: none), a hint for the tile-shape choice
     int conc;
+    // f32 EPI_RESID with few tiles: scratch for a K split (KSPLIT_MAX * M * N
+    // floats, or null: no split); each split's partial product goes there and
+    // a second pass adds the bias and the splits in order to the output
+    float *kpart;
+    int ksplit;              // set by the launcher
 };
+constexpr int KSPLIT_MAX = 8;
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
 
 // Position of token n in a V^T row: each aligned run of 16 tokens is stored
@@ -75,10 +81,16 @@ struct AttnArgs {
     int B, N, heads, has_cls, block_causal, per_slot;
     int q_prescaled;         // q already multiplied by ATTN_Q_SCALE
     int dh;                  // head dim: 32 or 64
+    // f32 path with few workgroups: scratch for a key split (KVSPLIT_MAX *
+    // B * heads * N * (dh + 2) floats, or null: no split); each split's
+    // unnormalised output, max and sum go there and a second pass merges them
+    float *kvpart;
+    int kvsplit;             // set by the launcher
 };
 // log2(e) / sqrt(64): with q multiplied by it, q.k is the exponent of the
 // softmax in base 2 (head dim 64; for head dim 32, log2(e) / sqrt(32))
 constexpr float ATTN_Q_SCALE = 0.18033688011112042f;
+constexpr int KVSPLIT_MAX = 4;
 constexpr float ATTN_Q_SCALE_32 = 0.25503486164919736f;
 __host__ __device__ constexpr float attn_q_scale(int dh) { return dh == 32 ? ATTN_Q_SCALE_32 : ATTN_Q_SCALE; }
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);

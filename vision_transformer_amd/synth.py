@@ -158,6 +158,13 @@ SMALL_WORKLOADS = {
                    img_w=98, frames=2, act_dtype="f32", mat_dtype="f32",
                    rest_dtype="f32", rope=1),
         batch=2, frame_seed=22, weight_seed=32),
+    # f32, block-causal with CLS (small f32 models split keys and K over
+    # workgroups; queries early in a frame see no key in the later splits)
+    "small_blockcausal_f32": dict(
+        dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, img_h=64,
+                   img_w=96, frames=6, mask="block_causal", act_dtype="f32",
+                   mat_dtype="f32", rest_dtype="f32"),
+        batch=2, frame_seed=26, weight_seed=36),
     # with the attentive-pool classifier head
     "small_head_bf16": dict(
         dims=_dims(dim=128, depth=2, heads=2, mlp_dim=512, patch=16, tubelet=2,
