@@ -286,6 +286,67 @@ def test_classify_state_errors(Encoder):
     enc.close()
 
 
+@pytest.mark.parametrize("name", ["small_blockcausal_f32", "small_head_bf16"])
+def test_graph_replay_of_split_passes_and_head(Encoder, name):
+    """Captured encode (+ classify): the f32 model's K and key splits with
+    their ordered second passes, and the classifier head's fills and copies,
+    replay bit for bit, with eager work between the replays."""
+    wl, dims, frames, stored = H.workload_inputs(name)
+    enc = Encoder(dims, stored)
+    fr = torch.from_numpy(frames).cuda()
+    B = frames.shape[0]
+    head = bool(dims.get("head_classes"))
+    tokens = torch.empty((B, enc.n_tokens, dims["dim"]), dtype=torch.float32, device="cuda")
+    scores = torch.empty((B, dims["head_classes"]), dtype=torch.float32, device="cuda") if head else None
+
+    def step():
+        enc.encode(fr, tokens)
+        if head:
+            enc.classify(B, scores)
+
+    step()
+    torch.cuda.synchronize()
+    want_t = tokens.clone()
+    want_s = scores.clone() if head else None
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        H.say(f"graph replay {r}, {name}")
+        tokens.zero_()
+        if head:
+            scores.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, want_t)
+        if head:
+            assert torch.equal(scores, want_s)
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+    del graph
+    enc.close()
+
+
+def test_workspace_grows_and_contexts_coexist(Encoder):
+    """A larger batch after a smaller one reallocates the workspace; a second
+    context alive at the same time keeps its own weights and results."""
+    wl, dims, frames, stored = H.workload_inputs("small_bidir_f32")
+    a = Encoder(dims, stored)
+    wl2, dims2, frames2, stored2 = H.workload_inputs("small_blockcausal_bf16")
+    b = Encoder(dims2, stored2)
+    ya1 = _run(a, frames[:1]).cpu()
+    yb = _run(b, frames2).cpu()
+    big = synth.make_frames(dims, 5, 91)
+    big[:1] = frames[:1]
+    ya5 = _run(a, big).cpu()
+    assert torch.equal(ya5[:1], ya1)
+    assert torch.equal(_run(b, frames2).cpu(), yb)
+    ya1b = _run(a, frames[:1]).cpu()                # smaller again
+    assert torch.equal(ya1b, ya1)
+    a.close()
+    b.close()
+
+
 def test_host_frames_match_device_frames(Encoder):
     wl, dims, frames, stored = H.workload_inputs("small_bidir_cls_bf16")
     enc = Encoder(dims, stored)
