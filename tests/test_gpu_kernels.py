@@ -350,6 +350,37 @@ def test_kernels_reject_out_of_contract_shapes(lib):
         lib.jepa_op_attention("bf16", q, vt, 1, 10, 4, True, "bidir", 1, o, head_dim=16)
 
 
+def test_size_limits_are_rejected_before_launch(lib):
+    """The largest shapes each kernel's 32-bit offsets and grid limits allow
+    end in a status, not a launch: calls that claim sizes past them (on small
+    buffers the kernels would overrun) are refused during validation."""
+    raw = lib._lib
+    q = torch.zeros((64, 3 * 1024), dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros((1, 1024, 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((64, 1024), dtype=torch.bfloat16, device="cuda")
+    BF16, SHAPE = lib.DTYPE["bf16"], -2
+    # attention: (N + 64) * ld_qk * 2 bytes must stay below 2^31
+    N = 700000
+    assert raw.jepa_op_attention(BF16, q.data_ptr(), 3 * 1024, vt.data_ptr(), -(-N // 64) * 64, 1, N, 16, 64,
+                                 0, 0, 1, 1, o.data_ptr(), None) == SHAPE
+    # GEMM: at most 65534 row tiles of 128
+    w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, device="cuda")
+    assert raw.jepa_op_gemm(BF16, q.data_ptr(), 65535 * 128, 64, w.data_ptr(), BF16, None, 64, b.data_ptr(),
+                            0, o.data_ptr(), 64, None) == SHAPE
+    # attention with no items
+    assert raw.jepa_op_attention(BF16, q.data_ptr(), 3 * 1024, vt.data_ptr(), 64, 0, 10, 16, 64,
+                                 0, 0, 1, 1, o.data_ptr(), None) == SHAPE
+    # the encoder: batch * tokens beyond its grid limit, refused before any copy
+    from tests.helpers import workload_inputs
+    wl, dims, frames, stored = workload_inputs("small_bidir_f32")
+    ctx = lib.jepa_create(dims, stored)
+    fr = torch.from_numpy(frames).cuda()
+    assert raw.jepa_encode(ctx, fr.data_ptr(), 1_000_000, 1, None, None) == -7     # JEPA_E_UNSUPPORTED
+    assert raw.jepa_encode(ctx, fr.data_ptr(), 0, 1, None, None) == -1             # JEPA_E_INVALID_ARG
+    lib.jepa_free(ctx)
+
+
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 @pytest.mark.parametrize("B,N,heads,dh", [(2, 3137, 16, 64), (3, 289, 2, 64), (1, 1, 1, 64), (2, 197, 6, 32)])
 def test_transpose_v(lib, act, B, N, heads, dh):
