@@ -47,7 +47,7 @@ typedef enum {
     JEPA_E_MISSING_TENSOR = -4,  /* a required tensor is absent */
     JEPA_E_OOM = -5,             /* device allocation failed or over the cap */
     JEPA_E_HIP = -6,             /* a HIP runtime call or launch failed */
-    JEPA_E_UNSUPPORTED = -7,     /* valid but outside what this build runs */
+    JEPA_E_UNSUPPORTED = -7,     /* valid but outside what the library implements */
     JEPA_E_STATE = -8            /* e.g. pool before any encode */
 } jepa_status;
 

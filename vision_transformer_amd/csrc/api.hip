@@ -869,6 +869,7 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     TRY(ensure_workspace(c, batch));
     const int parts = n_parts(c, batch);
     TRY(ensure_streams(c, parts));
+    c->encoded = false;          // pool / classify read nothing of a failed encode
     hipStream_t s0 = (hipStream_t)hip_stream;
     const jepa_dims &d = c->d;
     const uint8_t *fr = frames;
@@ -928,6 +929,10 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
         return (void *)((unsigned char *)base + r0 * width * esz);
     };
 
+    // the launch sequence; whatever it returns, the parts are joined back
+    // onto the caller's stream, so that no part's work outlives the call's
+    // stream order
+    auto body = [&]() -> jepa_status {
     for (int p = 0; p < parts; ++p) {
         const Part &q = P[p];
         PatchifyArgs pa{};
@@ -960,10 +965,14 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
             return launch_layernorm(x, q.M, D, c->normg, c->normb, d.ln_eps, y, JEPA_F32, q.s);
         }));
     }
+    return JEPA_OK;
+    };
+    const jepa_status st = body();
     for (int p = 1; p < parts; ++p) {
         HIP_TRY(hipEventRecord(c->join_ev[p - 1], c->aux[p - 1]));
         HIP_TRY(hipStreamWaitEvent(s0, c->join_ev[p - 1], 0));
     }
+    if (st != JEPA_OK) return st;
     HIP_TRY(hipEventRecord(c->ev1, s0));
     c->last_tokens = Y;
     c->last_batch = batch;
