@@ -120,6 +120,13 @@ jepa_status jepa_op_attention(int act_dtype, const void *qk, int64_t ld_qk, cons
  * (rope itself may be 0 or 1). */
 jepa_status jepa_rope_table(const jepa_dims *dims, float *out);
 
+/* Calibration of the dense bf16 MFMA rate (not part of the encoder): each of
+ * `workgroups` workgroups of 4 waves runs iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands and writes one float
+ * per thread to out (device f32, workgroups * 256 elements).  Work per launch:
+ * workgroups * 4 * iters * 8 * 32768 flops; the caller times the launch. */
+jepa_status jepa_op_mfma_probe(int workgroups, int iters, float *out, void *hip_stream);
+
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
  * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2
  * bytes of 16-byte nibble blocks for Q4_0) and scales (rows*cols/32 f16).

@@ -395,3 +395,15 @@ def test_transpose_v(lib, act, B, N, heads, dh):
     pos = vt_pos(np.arange(N))
     assert np.array_equal(got[..., pos], v.transpose(0, 2, 1))
     assert np.all(got[..., np.setdiff1d(np.arange(got.shape[-1]), pos)] == 0)
+
+
+def test_mfma_probe_runs_and_reports_its_flops(lib):
+    """The calibration kernel: finite output from every thread, and the work
+    it reports is workgroups x 4 waves x iters x 8 MFMAs of 32x32x16x2."""
+    out = torch.full((8 * 256,), float("nan"), device="cuda")
+    flops = lib.jepa_op_mfma_probe(8, 100, out)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 100 * 8 * 32768
+    assert torch.isfinite(out).all()
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_op_mfma_probe(0, 100, out)

@@ -79,6 +79,7 @@ def _load():
         "jepa_op_transpose_v": (I, [I, P, I, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
+        "jepa_op_mfma_probe": (I, [I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -293,6 +294,12 @@ def jepa_op_transpose_v(act_dtype: str, qkv, batch: int, n_tokens: int, heads: i
                         head_dim: int = 64, stream=None) -> None:
     _check(_lib.jepa_op_transpose_v(DTYPE[act_dtype], _ptr(qkv), batch, n_tokens, heads, head_dim,
                                     _ptr(vt), vt.shape[-1], _stream(stream)))
+
+
+def jepa_op_mfma_probe(workgroups: int, iters: int, out, stream=None) -> int:
+    """Dense bf16 MFMA calibration launch; returns its flops."""
+    _check(_lib.jepa_op_mfma_probe(workgroups, iters, _ptr(out), _stream(stream)))
+    return workgroups * 4 * iters * 8 * 32 * 32 * 16 * 2
 
 
 def jepa_pack_blocks(dtype: str, blocks: np.ndarray, rows: int, cols: int):

@@ -1238,6 +1238,11 @@ jepa_status jepa_pack_blocks(int dtype, const uint8_t *blocks, int64_t rows, int
     return JEPA_OK;
 }
 
+jepa_status jepa_op_mfma_probe(int workgroups, int iters, float *out, void *hip_stream) {
+    if (!out || workgroups <= 0 || iters <= 0) return fail(JEPA_E_INVALID_ARG, "op_mfma_probe: bad arguments");
+    return hip_status(launch_mfma_probe(workgroups, iters, out, (hipStream_t)hip_stream), "op_mfma_probe");
+}
+
 jepa_status jepa_rope_table(const jepa_dims *dims, float *out) {
     if (!dims || !out) return fail(JEPA_E_INVALID_ARG, "rope_table: null argument");
     TRY(check_dims(dims));

@@ -110,6 +110,9 @@ hipError_t launch_xattn(int act_dt, const void *q, const void *k, const void *v,
 // y (act dtype) <- x (f32), n elements; x <- v, n elements
 hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t s);
 hipError_t launch_fill(float *x, int64_t n, float v, hipStream_t s);
+// dense bf16 MFMA calibration: workgroups x 4 waves, each iters x 8
+// independent 32x32x16 MFMAs; out holds workgroups * 256 floats
+hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
 // X[b*N + 0] = cls + pos[0] for every item (pos null: cls)
 hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
                            hipStream_t s);

@@ -172,6 +172,33 @@ __global__ void dequant_kernel(int w_dt, const void *w, const uint16_t *scale, i
     out[idx] = v;
 }
 
+// Dense MFMA calibration: each wave runs `iters` rounds of 8 independent
+// v_mfma_f32_32x32x16_bf16 chains on register operands (so the matrix core
+// never waits on a result), then stores the sum of its accumulators so that
+// nothing is optimised away.  32 * 32 * 16 * 2 flops per instruction.
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *out) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)(1e-3f * (float)((threadIdx.x + j) & 7));
+        b[j] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + j) & 7));
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    for (int i = 0; i < iters; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[c][v];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // f32 values rounded to the act dtype, and a fill (graph-capturable, unlike
 // a memset node)
 template <typename T>
@@ -238,6 +265,12 @@ hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t
         case DT_F16: hipLaunchKernelGGL(cast_kernel<f16_t>, grid, dim3(256), 0, s, x, n, (f16_t *)y); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s) {
+    if (workgroups <= 0 || iters <= 0 || !out) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(256), 0, s, iters, out);
     return hipGetLastError();
 }
 
