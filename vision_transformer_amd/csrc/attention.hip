@@ -470,16 +470,22 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                     if (key < my_lo || key >= my_hi) s[sb][v] = -INFINITY;
                 }
         }
-        float mt = -INFINITY;
+        // the max of this lane's half of its query's scores (the other half
+        // is in lane ^ 32), as two independent chains
+        float mh[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[sb][v]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            for (int v = 0; v < 16; ++v) mh[sb] = fmaxf(mh[sb], s[sb][v]);
+        float mt = fmaxf(mh[0], mh[1]);
+        // A query's max passes a bound iff one of its halves does, and the
+        // tests below are over the whole wave, so the halves are combined
+        // (a cross-lane exchange) only when the reference moves.
         if constexpr (QS) {
             // s already holds the exponent relative to m; the first tile sets
             // m (its max rounded up to T), later ones raise it past TH
             if (first || __any(mt > TH)) {
+                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
                 const float mn = (first || mt > 0.f) ? round_up_t<T>(m + mt) : m;
                 const float d = mn - m;
                 if (!first) {
@@ -505,6 +511,7 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
                 for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(s[sb][v]);
         } else {
             if (__any(mt > m + TH)) {
+                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
                 const float mn = fmaxf(m, mt);
                 const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
                 l0 *= alpha;
