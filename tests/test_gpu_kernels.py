@@ -315,6 +315,23 @@ def test_attention_score_range(lib, act, mag, prescaled):
     assert err.max() <= {"bf16": 2e-2, "f16": 3e-3}[act], err.max()
 
 
+@pytest.mark.parametrize("prescaled", [False, True], ids=["q", "qscaled"])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("has_cls,mag", [(False, 1.0), (True, 1.0), (False, 3.0)], ids=["nocls", "cls", "peaked"])
+def test_attention_long_bidirectional(lib, act, has_cls, mag, prescaled):
+    """Bidirectional head-64 sequences from 4096 tokens take the layout with
+    64 queries per wave (256 per workgroup); 4100 tokens leave a ragged last
+    query tile of 4 and a ragged last key tile.  mag 3.0 makes the scores
+    peaked, so each query block raises its softmax reference on its own."""
+    case = (1, 4100, 2, has_cls, "bidir", 1)
+    say(f"attention long bidir {act} cls={has_cls} mag={mag} prescaled={prescaled}")
+    got, ref = _attn_case(lib, act, *case, seed=49, prescaled=prescaled, mag=mag)
+    g = got.reshape(-1, 128)
+    r = ref.reshape(-1, 128)
+    err = np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)
+    assert err.max() <= {"bf16": 2e-2, "f16": 3e-3}[act], err.max()
+
+
 def test_attention_block_causal_rows_ignore_future_slots(lib):
     """Changing the keys and values of the last slot leaves every earlier
     patch row bit-identical (whole future tiles and masked elements alike)."""

@@ -33,6 +33,7 @@ namespace {
 
 constexpr int QT = 128;     // queries per workgroup (4 waves x 32)
 constexpr int KT = 64;      // keys per step
+constexpr int ATTN_QB2_MIN_N = 4096;   // 16-bit, bidirectional, head dim 64: 64 queries per wave from here
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a, int q_start, int n_qtiles) {
@@ -284,12 +285,20 @@ template <> __device__ __forceinline__ float round_up_t<f16_t>(float x) {
 // k chunk where K contributes 1 at dimension 64 and Q contributes -m (m kept
 // exactly representable in T).  S then comes out as the exponent s - m and
 // p = exp2(S) needs no VALU arithmetic before the exponential.
-template <typename T, bool QS, int DH>
-__global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
+// QB query blocks of 32 per wave (QB = 2: 64 queries, 256 per workgroup).
+// Every K and V^T operand a wave reads from LDS then feeds QB MFMAs, so the
+// LDS read traffic per flop is 1/QB of one block's.  With one block per wave
+// the LDS read bursts after each tile's barrier, four waves per SIMD, cap
+// the MFMA rate well below its peak.
+template <typename T, bool QS, int DH, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 3 : 2) void attn16_kernel(const AttnArgs a, int q_start, int n_qtiles) {
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
     static_assert(sizeof(T) == 2, "16-bit operands");
     static_assert(DH == 32 || DH == 64, "head dims built");
+    static_assert(QB == 1 || QB == 2, "query blocks per wave");
+    constexpr int WQ = 32 * QB;                  // queries per wave
+    constexpr int QTW = 4 * WQ;                  // queries per workgroup
     constexpr int RK = DH * 2;                   // bytes of a K row in LDS (unpadded)
     constexpr int CK = RK / 16;                  // its 16-byte chunks: 4 or 8
     constexpr int TBK = 64 * RK, TBV = DH * 128; // bytes of a K tile (64 keys) and a V^T tile
@@ -309,34 +318,43 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     const int N = a.N, D = a.heads * DH;
     const T *qk = (const T *)a.qk + (int64_t)b * N * a.ld_qk;
     const T *vt = (const T *)a.vt + ((int64_t)b * a.heads + h) * DH * a.npad;
-    const int q0 = q_start + tile * QT;
-    const int qi = q0 + wave * 32 + (lane & 31);
+    const int q0 = q_start + tile * QTW;
+    const int qw = q0 + wave * WQ;               // the wave's first query slot
     // allowed key range of a query (see header); slot N is the CLS query
     const int lo = (a.block_causal && a.has_cls) ? 1 : 0;
-    const bool cls_lane = lo && qi == N;
-    const bool qvalid = qi < N || cls_lane;
-    const int qrow = cls_lane ? 0 : qi;
-    const int my_lo = cls_lane ? 0 : lo;
     auto hi_of = [&](int q) -> int {
         if (!a.block_causal || q >= N) return N;
         const int h_ = a.has_cls + a.per_slot * ((q - a.has_cls) / a.per_slot + 1);
         return h_ < N ? h_ : N;
     };
-    const int my_hi = hi_of(qi);
-    const int tile_last = (q0 + QT - 1 < N - 1) ? q0 + QT - 1 : N - 1;
+    // this lane's query of each block
+    bool qvalid[QB];
+    int qrow[QB], my_lo[QB], my_hi[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = qw + qb * 32 + (lane & 31);
+        const bool cls_lane = lo && qi == N;
+        qvalid[qb] = qi < N || cls_lane;
+        qrow[qb] = cls_lane ? 0 : qi;
+        my_lo[qb] = cls_lane ? 0 : lo;
+        my_hi[qb] = hi_of(qi);
+    }
+    const int tile_last = (q0 + QTW - 1 < N - 1) ? q0 + QTW - 1 : N - 1;
     const int kend = hi_of(tile_last);
-    const int hi_min = hi_of(q0 + wave * 32);        // this wave's queries: the smallest end
+    const int hi_min = hi_of(qw);                // this wave's queries: the smallest end
     // and the largest (its last slot, or the CLS slot N); key tiles at or past
     // it are masked for every lane of the wave, whose step then skips its
     // MFMAs and softmax (p would be exactly 0) but still loads and syncs
-    const int w_end = hi_of(min(q0 + wave * 32 + 31, N));
+    const int w_end = hi_of(min(qw + WQ - 1, N));
     const int kbeg = lo & ~(KT - 1);
     const int ntiles = (kend - kbeg + KT - 1) / KT;
 
-    vec qv[DH / 16];
+    vec qv[QB][DH / 16];
 #pragma unroll
-    for (int c = 0; c < DH / 16; ++c)
-        qv[c] = qvalid ? MM::load(qk + (int64_t)qrow * a.ld_qk + h * DH + c * 16 + g * 8) : vec{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int c = 0; c < DH / 16; ++c)
+            qv[qb][c] = qvalid[qb] ? MM::load(qk + (int64_t)qrow[qb] * a.ld_qk + h * DH + c * 16 + g * 8) : vec{};
 
     // This thread's chunks of each tile: chunk id ci = i*256 + tid; a K row
     // has CK chunks (row ci / CK, slot ci % CK), a V^T row 8 (row ci >> 3,
@@ -379,28 +397,34 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     // O and l runs a few times per query instead of at most tiles.  Any
     // reference gives the same softmax once O is divided by l.
     const float TH = 8.f / sl2;
-    float m = QS ? 0.f : -INFINITY, l0 = 0.f, l1 = 0.f;
+    float m[QB], l0[QB], l1[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { m[qb] = QS ? 0.f : -INFINITY; l0[qb] = 0.f; l1[qb] = 0.f; }
     bool first = true;
     // QS: the extra k chunk's operands (dimension 64 of K is 1, of Q is -m),
     // for the 8-deep MFMA (4 elements per lane: half the registers and cycles
     // of a 16-deep chunk)
     typedef typename std::conditional<std::is_same<T, bf16_t>::value, __bf16, _Float16>::type elem_t;
     typedef elem_t x4 __attribute__((ext_vector_type(4)));
-    x4 kx{}, qx{};
+    x4 kx{}, qx[QB];
     kx[0] = g == 0 ? (elem_t)1.f : (elem_t)0.f;
-    auto mma_x = [&](const f32x16 &c) __attribute__((always_inline)) -> f32x16 {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) qx[qb] = x4{};
+    auto mma_x = [&](const x4 &q_x, const f32x16 &c) __attribute__((always_inline)) -> f32x16 {
         if constexpr (std::is_same<T, bf16_t>::value) {
             typedef short s4 __attribute__((ext_vector_type(4)));
-            return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, kx), __builtin_bit_cast(s4, qx), c, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, kx), __builtin_bit_cast(s4, q_x), c, 0, 0, 0);
         } else {
-            return __builtin_amdgcn_mfma_f32_32x32x8f16(kx, qx, c, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x8f16(kx, q_x, c, 0, 0, 0);
         }
     };
-    f32x16 o[NDB];
+    f32x16 o[QB][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[qb][db][v] = 0.f;
 
     const int r0 = lane & 31, sw = aswz(r0);
     // this lane's LDS byte offsets of the tile's operands in rows 0..31; the
@@ -415,29 +439,30 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     // row sums from the packed P operand (the values PV multiplies): two
     // products of (p, 1) per instruction, two chains
     const uint32_t ones = sizeof(T) == 2 && std::is_same<T, bf16_t>::value ? 0x3f803f80u : 0x3c003c00u;
-    auto rowsum = [&](const vec &pb) __attribute__((always_inline)) {
+    auto rowsum = [&](const vec &pb, float &s0, float &s1) __attribute__((always_inline)) {
         const uint4 w = __builtin_bit_cast(uint4, pb);
         if constexpr (std::is_same<T, bf16_t>::value) {
             typedef __bf16 b2 __attribute__((ext_vector_type(2)));
             const b2 one = __builtin_bit_cast(b2, ones);
-            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.x), one, l0, false);
-            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.y), one, l1, false);
-            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.z), one, l0, false);
-            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.w), one, l1, false);
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.x), one, s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.y), one, s1, false);
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.z), one, s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w.w), one, s1, false);
         } else {
             typedef _Float16 h2 __attribute__((ext_vector_type(2)));
             const h2 one = __builtin_bit_cast(h2, ones);
-            l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.x), one, l0, false);
-            l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.y), one, l1, false);
-            l0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.z), one, l0, false);
-            l1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.w), one, l1, false);
+            s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.x), one, s0, false);
+            s1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.y), one, s1, false);
+            s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.z), one, s0, false);
+            s1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w.w), one, s1, false);
         }
     };
 
     // Tile t in stage ST: the next tile's loads issued into the other stage,
-    // S = K Q^T from K operands read block by block, the softmax, then the V
-    // operands (read only now, so K's and V's registers are never live
-    // together) and O^T += V^T P^T.
+    // S = K Q^T from K operands read block by block (each feeding every query
+    // block), the softmax per query block, then the V operands (read only
+    // now, so K's and V's registers are never live together), each feeding
+    // O^T += V^T P^T of every query block.
     auto step = [&](auto ST, int t) __attribute__((always_inline)) {
         constexpr int st = decltype(ST)::value;
         const unsigned char *sk = st ? sK1 : sK0;
@@ -449,97 +474,125 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
         // S^T = K Q^T, one 32-key block at a time
         const int k0 = kbeg + t * KT;
         if (k0 >= w_end) return;
-        f32x16 s[2];
+        f32x16 s[QB][2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             vec kf[DH / 16];
 #pragma unroll
             for (int c = 0; c < DH / 16; ++c) kf[c] = MM::load(sk + sb * 32 * RK + koff[c]);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) s[sb][v] = 0.f;
+            for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int c = 0; c < DH / 16; ++c) s[sb] = MM::mma(kf[c], qv[c], s[sb]);
-            if constexpr (QS) s[sb] = mma_x(s[sb]);             // - m
+                for (int v = 0; v < 16; ++v) s[qb][sb][v] = 0.f;
+#pragma unroll
+                for (int c = 0; c < DH / 16; ++c) s[qb][sb] = MM::mma(kf[c], qv[qb][c], s[qb][sb]);
+                if constexpr (QS) s[qb][sb] = mma_x(qx[qb], s[qb][sb]);   // - m
+            }
         }
-        if (k0 < lo || k0 + KT > hi_min) {
+        // masks, in float arithmetic (no per-element lane masks to hold):
+        // the lane's keys are k0 + 4g + off, off = sb*32 + 8*(v/4) + v%4;
+        // key < lo happens only for the CLS key 0 (lo = 1, first tile)
+        if (k0 < lo) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                if (g == 0 && my_lo[qb] > 0) s[qb][0][0] = -INFINITY;
+        }
+        if (k0 + KT > hi_min) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                // key < hi  <=>  (hi - k0 - 4g) - 0.5 - off > 0; times +inf that
+                // is +inf (keep) or -inf (mask), never 0 * inf
+                const float ch = (float)(my_hi[qb] - k0 - 4 * g) - 0.5f;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float off = (float)(sb * 32 + 8 * (v >> 2) + (v & 3));
+                        s[qb][sb][v] = fminf(s[qb][sb][v], (ch - off) * INFINITY);
+                    }
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            // the max of this lane's half of its query's scores (the other
+            // half is in lane ^ 32), as two independent chains
+            float mh[2] = {-INFINITY, -INFINITY};
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = k0 + sb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-                    if (key < my_lo || key >= my_hi) s[sb][v] = -INFINITY;
-                }
-        }
-        // the max of this lane's half of its query's scores (the other half
-        // is in lane ^ 32), as two independent chains
-        float mh[2] = {-INFINITY, -INFINITY};
+                for (int v = 0; v < 16; ++v) mh[sb] = fmaxf(mh[sb], s[qb][sb][v]);
+            float mt = fmaxf(mh[0], mh[1]);
+            // A query's max passes a bound iff one of its halves does, and
+            // the tests below are over the whole wave, so the halves are
+            // combined (a cross-lane exchange) only when the reference moves.
+            if constexpr (QS) {
+                // s already holds the exponent relative to m; the first tile
+                // sets m (its max rounded up to T), later ones raise it past TH
+                if (first || __any(mt > TH)) {
+                    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                    const float mn = (first || mt > 0.f) ? round_up_t<T>(m[qb] + mt) : m[qb];
+                    const float d = mn - m[qb];
+                    if (!first) {
+                        const float alpha = __builtin_amdgcn_exp2f(-d);
+                        l0[qb] *= alpha;
+                        l1[qb] *= alpha;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+                        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mh[sb] = fmaxf(mh[sb], s[sb][v]);
-        float mt = fmaxf(mh[0], mh[1]);
-        // A query's max passes a bound iff one of its halves does, and the
-        // tests below are over the whole wave, so the halves are combined
-        // (a cross-lane exchange) only when the reference moves.
-        if constexpr (QS) {
-            // s already holds the exponent relative to m; the first tile sets
-            // m (its max rounded up to T), later ones raise it past TH
-            if (first || __any(mt > TH)) {
-                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                const float mn = (first || mt > 0.f) ? round_up_t<T>(m + mt) : m;
-                const float d = mn - m;
-                if (!first) {
-                    const float alpha = __builtin_amdgcn_exp2f(-d);
-                    l0 *= alpha;
-                    l1 *= alpha;
+                            for (int v = 0; v < 16; ++v) o[qb][db][v] *= alpha;
+                    }
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
+                    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+                        for (int v = 0; v < 16; ++v) s[qb][sb][v] -= d;
+                    m[qb] = mn;
+                    qx[qb][0] = g == 0 ? (elem_t)(-mn) : (elem_t)0.f;
                 }
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) s[sb][v] -= d;
-                m = mn;
-                qx[0] = g == 0 ? (elem_t)(-m) : (elem_t)0.f;
-                first = false;
+                    for (int v = 0; v < 16; ++v) s[qb][sb][v] = __builtin_amdgcn_exp2f(s[qb][sb][v]);
+            } else {
+                if (__any(mt > m[qb] + TH)) {
+                    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                    const float mn = fmaxf(m[qb], mt);
+                    const float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * sl2);
+                    l0[qb] *= alpha;
+                    l1[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) o[qb][db][v] *= alpha;
+                    m[qb] = mn;
+                }
+                const float mb = m[qb] * sl2;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) s[qb][sb][v] = __builtin_amdgcn_exp2f(fmaf(s[qb][sb][v], sl2, -mb));
             }
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(s[sb][v]);
-        } else {
-            if (__any(mt > m + TH)) {
-                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                const float mn = fmaxf(m, mt);
-                const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-                l0 *= alpha;
-                l1 *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-                m = mn;
-            }
-            const float mb = m * sl2;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) s[sb][v] = __builtin_amdgcn_exp2f(fmaf(s[sb][v], sl2, -mb));
         }
+        first = false;
         // O^T += V^T P^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                float pv[8];
+                vec pb[QB];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pv[j] = s[sb][cc * 8 + j];
-                const vec pb = pack_operand<T>(pv);
-                rowsum(pb);
+                for (int qb = 0; qb < QB; ++qb) {
+                    float pv[8];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] = MM::mma(MM::load(sv + db * 4096 + voff[2 * sb + cc]), pb, o[db]);
+                    for (int j = 0; j < 8; ++j) pv[j] = s[qb][sb][cc * 8 + j];
+                    pb[qb] = pack_operand<T>(pv);
+                    rowsum(pb[qb], l0[qb], l1[qb]);
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const vec vop = MM::load(sv + db * 4096 + voff[2 * sb + cc]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) o[qb][db] = MM::mma(vop, pb[qb], o[qb][db]);
+                }
             }
     };
 
@@ -551,16 +604,19 @@ __global__ __launch_bounds__(256, 3) void attn16_kernel(const AttnArgs a, int q_
     }
     if (t < ntiles) step(std::integral_constant<int, 0>{}, t);
 
-    float l = l0 + l1;
-    l += __shfl_xor(l, 32, 64);
-    if (!qvalid) return;
-    const float inv = 1.f / l;
-    T *out = (T *)a.out + ((int64_t)b * N + qrow) * D + h * DH;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+        float l = l0[qb] + l1[qb];
+        l += __shfl_xor(l, 32, 64);
+        if (!qvalid[qb]) continue;
+        const float inv = 1.f / l;
+        T *out = (T *)a.out + ((int64_t)b * N + qrow[qb]) * D + h * DH;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[db][v] * inv);
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                out[db * 32 + 8 * (v >> 2) + 4 * g + (v & 3)] = from_f32<T>(o[qb][db][v] * inv);
+    }
 }
 
 // Merge of the key splits of the f32 kernel: per output row and column, the
@@ -684,10 +740,23 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     if (n_qtiles > 0) {
         const dim3 grid(a.heads, a.B, n_qtiles);
         if constexpr (sizeof(T) == 2) {
-            if (a.q_prescaled)
-                hipLaunchKernelGGL((attn16_kernel<T, true, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
-            else
-                hipLaunchKernelGGL((attn16_kernel<T, false, DH>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
+            // 64 queries per wave (256 per workgroup) for long bidirectional
+            // head-64 sequences, where halving the LDS operand reads per flop
+            // measured faster (8192 tokens: 310 vs 320-328 us); 32 per wave
+            // elsewhere (block-causal 3137 tokens: 106 vs 121 us; 2048
+            // tokens: even; head dim 32: 173 vs 191 us)
+            if (!a.block_causal && DH == 64 && a.N >= ATTN_QB2_MIN_N) {
+                const int nq2 = (int)cdiv(a.N, 2 * QT);
+                const dim3 grid2(a.heads, a.B, nq2);
+                if (a.q_prescaled)
+                    hipLaunchKernelGGL((attn16_kernel<T, true, DH, 2>), grid2, dim3(256), 0, s, a, q_start, nq2);
+                else
+                    hipLaunchKernelGGL((attn16_kernel<T, false, DH, 2>), grid2, dim3(256), 0, s, a, q_start, nq2);
+            } else if (a.q_prescaled) {
+                hipLaunchKernelGGL((attn16_kernel<T, true, DH, 1>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
+            } else {
+                hipLaunchKernelGGL((attn16_kernel<T, false, DH, 1>), grid, dim3(256), 0, s, a, q_start, n_qtiles);
+            }
         } else {
             // few workgroups (small f32 models): split each query tile's keys
             // over S workgroups and merge the splits in a second pass
