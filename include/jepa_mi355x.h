@@ -25,6 +25,10 @@
  *     after enqueueing, except where noted.  Outputs are valid once the
  *     caller synchronises that stream.  Device faults surface there.
  *   - One context must not be used from two threads at once.
+ *   - A context's calls share its device workspace (staged frames, the
+ *     residual stream, the token map, scratch).  Successive calls on one
+ *     context must therefore be ordered on the GPU: issue them on one stream,
+ *     or synchronise the earlier call's stream before issuing on another.
  *   - The library needs a gfx950 device; it has no CPU fallback.
  */
 #ifndef JEPA_MI355X_H

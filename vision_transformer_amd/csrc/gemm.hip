@@ -27,6 +27,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -757,16 +759,18 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
 
 // Variant choice (below); JEPA_GEMM_VARIANT (small | small64 | big256 | big128) pins it.
 
+// CU count of the current device, queried once per device (threads that
+// race to fill an entry store the same value)
 int cu_count() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (!n) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // out[m, n] += bias[n] + the splits' partial products, added in split order
