@@ -104,7 +104,7 @@ def _gemm_case(lib, act, wfmt, epi, M, N, K, seed):
 
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("epi", ["store", "gelu", "resid"])
-@pytest.mark.parametrize("mnk", [(300, 192, 256), (129, 320, 512), (1000, 3072, 1024)])
+@pytest.mark.parametrize("mnk", [(300, 192, 256), (129, 320, 512), (1000, 3072, 1024), (2100, 1152, 384)])
 def test_gemm_dense(lib, act, epi, mnk):
     M, N, K = mnk
     if act == "f32" and M * N * K > 1e9:

@@ -809,7 +809,11 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
         // shapes, epilogues aside).  The wide tile wins whenever the tiles
         // fill several rounds; the narrow one when the wide tiles leave CUs
         // idle (ViT-L/16 images, batch 32: fc2 and out-proj have 100 wide tiles).
-        if (big_ok && var.empty() && g.M >= 1024) {
+        // Short K (<= 512, i.e. <= 8 steps: the 384-wide V-JEPA 2 predictor)
+        // stays on the 128 x 128 tile: the large tile's prologue and epilogue,
+        // which nothing overlaps at one workgroup per CU, outweigh its K loop
+        // (measured 3.60 vs 3.75 ms per predictor-width forward).
+        if (big_ok && var.empty() && g.M >= 1024 && g.K > 512) {
             if (g.N % 256 == 0) {
                 const int64_t cus = cu_count(), conc = g.conc > 1 ? g.conc : 1;
                 const int64_t tm = cdiv(g.M, BIG_BM);
