@@ -160,6 +160,8 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     ("bf16", "q4_0", 2, 126, 2, 128),
     ("f32", "dense", 2, 85, 2, 64),
     ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
+    ("bf16", "dense", 9, 197, 4, 640),      # 256-row tiles, 256 wide, several items per wave tile
+    ("f16", "dense", 5, 301, 6, 576),       # 256-row tiles, 128 wide (N = 1152)
 ])
 def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, qscaled, rope, dh):
     """q and k columns as a plain linear layer (rotated pairwise by a table of

@@ -220,7 +220,7 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
     };
     // this lane's biases, once for all block rows (the qkv epilogue, whose v
     // branch needs the registers, reads them per block row)
-    constexpr bool HOIST = EPI != EPI_QKV;
+    constexpr bool HOIST = true;
     float4 bias[HOIST ? NB_ : 1][4];
     if constexpr (HOIST) {
 #pragma unroll
@@ -232,11 +232,14 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
 #pragma unroll
     for (int i = 0; i < MB_; ++i) {
         __builtin_amdgcn_sched_barrier(0);       // keep the loads where they are issued
-        // EPI_QKV with rotary position: this lane's token (rows past M wrap to
-        // a valid table row; they are dropped at the store)
+        // stage block row i; the rotary branch of EPI_QKV is taken per block
+        // row, outside the element loop, so that the loop stays one block
+        auto stage = [&](auto ROPE) __attribute__((always_inline)) {
+        constexpr bool rope = decltype(ROPE)::value;
+        // with rotary position: this lane's token (rows past M wrap to a
+        // valid table row; they are dropped at the store)
         uint32_t rn = 0;
-        if constexpr (EPI == EPI_QKV) rn = (uint32_t)(row0 + 32 * i + rl) % (uint32_t)g.ntok;
-        // stage block row i
+        if constexpr (rope) rn = (uint32_t)(row0 + 32 * i + rl) % (uint32_t)g.ntok;
 #pragma unroll
         for (int j = 0; j < NB_; ++j)
 #pragma unroll
@@ -246,7 +249,7 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
                               acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
                 if constexpr (EPI == EPI_QKV) {
-                    if (g.rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
+                    if constexpr (rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
                         const uint32_t hd = (uint32_t)g.head_dim;
                         const uint32_t p = (uint32_t)((col0 + col) & (hd - 1)) >> 1;
                         const float4 r = *(const float4 *)(g.rope + 2 * (rn * (hd >> 1) + p));
@@ -272,6 +275,11 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                     *(float4 *)dst = make_float4(z[0], z[1], z[2], z[3]);
                 }
             }
+        };
+        if (EPI == EPI_QKV && g.rope)
+            stage(std::true_type{});
+        else
+            stage(std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
         if (i + 1 < MB_) load_x(i + 1, (i + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
