@@ -762,7 +762,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
             // over S workgroups and merge the splits in a second pass
             const int64_t wgs = (int64_t)a.heads * a.B * n_qtiles;
             const int kt = (int)cdiv(a.N + 1, KT);
-            const int S = (a.kvpart && 2 * wgs < 256 && kt >= 2) ? (kt >= KVSPLIT_MAX ? KVSPLIT_MAX : 2) : 1;
+            const int S = (a.kvpart && 2 * wgs < 256 && kt >= 2) ? (kt < KVSPLIT_MAX ? kt : KVSPLIT_MAX) : 1;
             if (S > 1 && (int64_t)n_qtiles * S < 65535) {
                 AttnArgs as = a;
                 as.kvsplit = S;

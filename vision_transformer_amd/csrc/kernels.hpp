@@ -90,7 +90,7 @@ struct AttnArgs {
 // log2(e) / sqrt(64): with q multiplied by it, q.k is the exponent of the
 // softmax in base 2 (head dim 64; for head dim 32, log2(e) / sqrt(32))
 constexpr float ATTN_Q_SCALE = 0.18033688011112042f;
-constexpr int KVSPLIT_MAX = 4;
+constexpr int KVSPLIT_MAX = 8;
 constexpr float ATTN_Q_SCALE_32 = 0.25503486164919736f;
 __host__ __device__ constexpr float attn_q_scale(int dh) { return dh == 32 ? ATTN_Q_SCALE_32 : ATTN_Q_SCALE; }
 hipError_t launch_attention(int act_dt, const AttnArgs &a, hipStream_t s);
