@@ -222,6 +222,55 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
+# The other specified workloads, timed by the default run after the headline
+# one (a few steps each, default concurrency): reported beside `value`,
+# which stays the headline workload's.
+OTHER_WORKLOADS = ["vit_ti14_image_f32", "vit_l16_image_bf16_b32", "vjepa2_vit_l16_16f256_q8_0_b4",
+                   "vjepa2_vit_l16_64f256_f16", "vjepa2_vit_l16_64f256_q4_0"]
+
+
+def time_workload(name: str, steps: int, warmup: int) -> dict:
+    """ms per step, tokens/s, clips/s and MFMA utilisation of one workload's
+    forward + its reported pool (+ class scores), the batch in the library's
+    default concurrent parts, frames resident."""
+    import torch
+    from vision_transformer_amd import _lib
+    from vision_transformer_amd.encoder import Encoder
+    wl = synth.workload(name)
+    dims, B = wl["dims"], wl["batch"]
+    N = synth.n_tokens(dims)
+    frames = synth.make_frames(dims, B, wl["frame_seed"])
+    stored = synth.stored_weights(dims, synth.make_f32_weights(dims, wl["weight_seed"]),
+                                  quantize=_lib.jepa_quantize)
+    enc = Encoder(dims, stored)
+    del stored
+    fr = torch.from_numpy(frames).cuda()
+    tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, device="cuda")
+    pool_mode = "cls" if dims["has_cls"] else "mean"
+    pooled = torch.empty((B, dims["dim"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        enc.encode(fr, tokens)
+        enc.pool(pool_mode, B, pooled)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    enc.close()
+    act = dims["act_dtype"]
+    util = forward_flops(dims, B) / (ms * 1e-3) / (PEAK_TFLOPS[act] * 1e12)
+    print(f"[bench] {name}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "clips_per_s": round(B / (ms * 1e-3), 2), "mfma_util_pct": round(100 * util, 2),
+            "batch": B, "tokens_per_clip": N, "dtype": act, "weights": dims["mat_dtype"],
+            "mask": dims["mask"], "steps": steps, "warmup": warmup}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +284,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=24)
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel-class times to stderr")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the other specified workloads after the headline one")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device 5 times (the reference kernel of known "
                          "traffic that scales the HBM counters) and exit")
@@ -424,6 +475,18 @@ def main() -> int:
         "mfma_probe": probe,
     }
     enc.close()
+    del enc, tokens, pooled, fr, host_tokens
+    torch.cuda.empty_cache()
+    if not args.no_other_workloads and args.workload == "levjepa_vit_l16_16f_bf16_b4" and not args.batch:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            try:
+                others[name] = time_workload(name, max(3, min(args.steps, 10)), 2)
+            except Exception as e:   # an extra row: report, do not fail the bench
+                print(f"[bench] {name} not measured: {e}", file=sys.stderr, flush=True)
+                others[name] = None
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(dims, stored, frames, args.cpu_sample_blocks)

@@ -5,10 +5,11 @@
  * patches, embedded, run through pre-LN transformer blocks with bidirectional
  * or block-causal multi-head attention, final-LayerNorm'ed into a token map,
  * and optionally pooled (CLS or mean).
- *   - LeVJEPA ViT-L/16 (VideoMix) model card, opening paragraph: tubelet 1,
- *     block-causal mask (bidirectional inside a frame, causal across frames,
- *     CLS read-only), the CLS token as the feature; "Run it": the pooling
- *     modes and the single C header.
+ *   - LeVJEPA ViT-L/16 (VideoMix) model card, opening paragraph: tubelet 1;
+ *     the mask that lets a patch token see the tokens of its own and earlier
+ *     temporal slots but never the CLS token, while CLS sees every token;
+ *     the CLS token as the feature; "Run it": the pooling modes and the
+ *     single C header.
  *   - V-JEPA 2 ViT-L/16 SSv2 card, opening paragraph: tubelet 2.
  *   - jepa.cpp Quantization page, "The rule": the tensor names and which
  *     tensors may be stored as q8_0 / q4_0 blocks; "File sizes": 8.5 / 4.5
@@ -156,8 +157,12 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
  * copied into a context-owned pinned buffer before the call returns (the
  * caller may reuse it at once) and sent to the device on hip_stream.  tokens_out: device f32
  * [batch, N, dim] that receives the final-LayerNorm token map, or NULL to
- * keep it in a context-owned buffer.  The token map stays readable by
- * jepa_pool until the next encode on this context. */
+ * keep it in a context-owned buffer.  jepa_pool and jepa_classify read the
+ * token map where this call wrote it, so a caller-given tokens_out must stay
+ * allocated (and unmodified) until the next encode on this context; they
+ * write as many rows as this call's batch.  From the moment an encode is
+ * called, the previous token map is forgotten: if the call fails, pool and
+ * classify return JEPA_E_STATE until an encode succeeds. */
 jepa_status jepa_encode(jepa_ctx *ctx, const uint8_t *frames, int batch, int frames_on_device,
                         float *tokens_out, void *hip_stream);
 

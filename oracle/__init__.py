@@ -10,9 +10,9 @@ stored weights (f32, f16 or bfloat16 widened exactly; q8_0 / q4_0 blocks
 dequantized exactly).  The pages never write the network out as equations;
 the readings taken where they are silent are listed in each function's
 docstring.  The sources followed:
-  * LeVJEPA ViT-L/16 model card, opening paragraph: tubelet 1, block-causal
-    mask (bidirectional inside a frame, causal across frames, the CLS token a
-    read-only sink), the CLS token as the feature.
+  * LeVJEPA ViT-L/16 model card, opening paragraph: tubelet 1; a mask under
+    which a patch token sees its own and earlier temporal slots and never
+    the CLS token, while CLS sees every token; the CLS token as the feature.
   * V-JEPA 2 ViT-L/16 SSv2 card, opening paragraph: tubelet 2, 256x256.
   * jepa.cpp Quantization page, "The rule" and "File sizes": the tensor
     schema, which tensors are re-typed, 8.5 / 4.5 bits per weight for

@@ -46,13 +46,29 @@ def digest_weights(stored) -> str:
 
 
 def sample_rows(dims, batch, seed=777):
-    """Deterministic (item, token) pairs: the first and last token of the
-    first and last item, the CLS rows, and uniform draws."""
+    """Deterministic (item, token) pairs covering every part of the token map
+    that a kernel tile or a mask boundary could get wrong on its own:
+      * the first and last token of the first and last item;
+      * every item's CLS row (when the model has one);
+      * one row drawn uniformly inside every 256-row block of the batch's
+        flattened rows (b * N + n), the GEMMs' largest row tile;
+      * one patch token drawn uniformly inside every (item, temporal slot);
+      * uniform draws up to at least 32 rows."""
     N = synth.n_tokens(dims)
+    has_cls = int(dims["has_cls"])
+    per_slot = synth.grid(dims)[1] * synth.grid(dims)[2]
+    n_slots = synth.grid(dims)[0]
     rng = np.random.default_rng(seed)
     pairs = {(0, 0), (0, N - 1), (batch - 1, 0), (batch - 1, N - 1)}
-    if dims["has_cls"]:
-        pairs |= {(b, 0) for b in range(min(batch, 4))}
+    if has_cls:
+        pairs |= {(b, 0) for b in range(batch)}
+    M = batch * N
+    for r0 in range(0, M, 256):
+        r = int(rng.integers(r0, min(M, r0 + 256)))
+        pairs.add((r // N, r % N))
+    for b in range(batch):
+        for t in range(n_slots):
+            pairs.add((b, has_cls + t * per_slot + int(rng.integers(per_slot))))
     while len(pairs) < N_SAMPLE:
         pairs.add((int(rng.integers(batch)), int(rng.integers(N))))
     return np.array(sorted(pairs), dtype=np.int64)

@@ -45,7 +45,7 @@ def check_rows(act_dtype: str, got: np.ndarray, ref: np.ndarray, what: str) -> d
     """Per-row (token) cosine and rel_max against the oracle, with the bar
     that applies to the path's precision."""
     r = M.report(got, ref)
-    say(f"  {what}: cos mean {r['cos_mean']:.7f} worst {r['cos_worst']:.7f} "
+    say(f"  {what}: cos mean {r['cos_mean']:.7f} median {r['cos_median']:.7f} worst {r['cos_worst']:.7f} "
         f"rel_max {r['rel_max']:.3e} rel_fro {r['rel_fro']:.3e}")
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     if act_dtype == "f32":

@@ -77,10 +77,70 @@ def test_vit_ti14_image_f32_full(Encoder):
     enc.close()
 
 
+@pytest.mark.parametrize("name", list(synth.MID_WORKLOADS))
+def test_mid_vitl_every_token(Encoder, name, monkeypatch):
+    """ViT-L/16 widths at two blocks: with the batch in one part every GEMM
+    (qkv, out-proj, fc1 with GELU, fc2 at K 4096) runs on the 256-row tiles,
+    the block matrices expanded to the act dtype; every token and the pools
+    against the live oracle.  Then the default batch parts (smaller tiles,
+    weights dequantised in the tile load) against the same oracle."""
+    from vision_transformer_amd import _lib
+    H.say(f"encoder {name}, one part")
+    wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
+    ref = H.oracle_tokens(dims, stored, frames)
+    enc = Encoder(dims, stored)
+    _lib.jepa_set_batch_parts(enc.ctx, 1)
+    if dims["mat_dtype"] in ("q8_0", "q4_0"):
+        monkeypatch.setenv("JEPA_Q_EXPAND", "1")
+    y = _run(enc, frames)
+    H.check_rows(dims["act_dtype"], y.cpu().numpy(), ref, "tokens")
+    _check_pools(enc, dims, ref, wl["batch"])
+    monkeypatch.delenv("JEPA_Q_EXPAND", raising=False)
+    _lib.jepa_set_batch_parts(enc.ctx, 0)
+    H.say(f"encoder {name}, default parts")
+    y = _run(enc, frames)
+    H.check_rows(dims["act_dtype"], y.cpu().numpy(), ref, "tokens")
+    enc.close()
+
+
+# the two workloads compared over their whole token maps against the oracle
+# computed in the test (the block-causal headline and the attention-heavy
+# 8192-token clip); about a minute of CPU each
+LIVE_FULL = ["levjepa_vit_l16_16f_bf16_b4", "vjepa2_vit_l16_64f256_f16"]
+
+
+@pytest.mark.parametrize("name", LIVE_FULL)
+def test_full_workload_whole_token_map_live(Encoder, name):
+    """Every token of a full-size token map, in the launch configuration the
+    benchmark times, against the oracle run here on the same inputs: the
+    worst-token cosine bar over all B x N tokens, with the mean and median
+    reported as the LeVJEPA card's "Files" table does."""
+    import time
+    H.say(f"encoder {name} (full size, whole token map)")
+    wl, dims, frames, stored = H.workload_inputs(name)
+    enc = Encoder(dims, stored)
+    y = _run(enc, frames).cpu().numpy()
+    B = wl["batch"]
+    pools = {}
+    if dims["has_cls"]:
+        pools["cls"] = enc.pool("cls", B).cpu().numpy()
+    pools["mean"] = enc.pool("mean", B).cpu().numpy()
+    enc.close()
+    t0 = time.time()
+    ref = H.oracle_tokens(dims, stored, frames)
+    H.say(f"  oracle: {time.time() - t0:.1f} s for {B} x {ref.shape[1]} tokens")
+    r = H.check_rows(dims["act_dtype"], y, ref, f"all {B * ref.shape[1]} tokens")
+    H.say(f"  per-token cosine: mean {r['cos_mean']:.7f} median {r['cos_median']:.7f} "
+          f"worst {r['cos_worst']:.7f}")
+    for mode, got in pools.items():
+        H.check_rows(dims["act_dtype"], got, E.pool(ref, mode, bool(dims["has_cls"])), mode)
+
+
 FULL = ["vit_l16_image_bf16_b32", "levjepa_vit_l16_16f_bf16_b4",
         "vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_f16",
         "vjepa2_vit_l16_64f256_q4_0", "vjepa2_rope_vit_l16_16f256_f16_b4",
-        "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4"]
+        "vjepa2_predictor_width_384d_dh32_4096tok_bf16_b4",
+        "vjepa2_ssv2_classifier_vit_l16_16f256_f16_b4"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -396,6 +456,42 @@ def test_model_bytes_of_a_levjepa_shaped_q8_0_set(Encoder):
     mib = (_lib.jepa_model_n_bytes(enc.ctx) - pos) / 2 ** 20
     H.say(f"  LeVJEPA-shaped q8_0 model bytes without pos: {mib:.2f} MiB")
     assert abs(mib - pages["levjepa_vitl16_mib"]["q8_0"]) <= pages["tolerance_mib"]
+    enc.close()
+
+
+def test_failed_encode_forgets_the_previous_token_map(Encoder, monkeypatch):
+    """An encode that fails (here: the workspace a larger batch needs is over
+    JEPA_MAX_WORKSPACE) leaves no token map behind: pool and classify return
+    JEPA_E_STATE instead of reading the previous encode's buffers, and the
+    next successful encode works as before."""
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs("small_head_bf16")
+    enc = Encoder(dims, stored)
+    y1 = _run(enc, frames[:1]).cpu()
+    enc.pool("mean")
+    enc.classify()
+    torch.cuda.synchronize()
+    big = synth.make_frames(dims, 5, 92)
+    monkeypatch.setenv("JEPA_MAX_WORKSPACE", str(_lib.jepa_workspace_bytes(enc.ctx, 1) + 1))
+    with pytest.raises(_lib.JepaError, match="JEPA_E_OOM"):
+        enc.encode(torch.from_numpy(big).cuda())
+    out = torch.empty((1, dims["dim"]), device="cuda")
+    with pytest.raises(_lib.JepaError, match="JEPA_E_STATE"):
+        _lib.jepa_pool(enc.ctx, "mean", out)
+    with pytest.raises(_lib.JepaError, match="JEPA_E_STATE"):
+        _lib.jepa_classify(enc.ctx, torch.empty((1, dims["head_classes"]), device="cuda"))
+    assert _lib.jepa_last_compute_ms(enc.ctx) < 0
+    monkeypatch.delenv("JEPA_MAX_WORKSPACE")
+    big[:1] = frames[:1]
+    y5 = _run(enc, big).cpu()
+    assert torch.equal(y5[:1], y1)
+    # outputs sized from a different batch are refused before the call
+    with pytest.raises(ValueError):
+        enc.pool("mean", 3)
+    with pytest.raises(ValueError):
+        enc.pool("mean", out=torch.empty((4, dims["dim"]), device="cuda"))
+    with pytest.raises(ValueError):
+        enc.encode(torch.from_numpy(big[:, :1]).cuda())               # wrong frame count
     enc.close()
 
 

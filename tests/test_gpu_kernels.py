@@ -134,6 +134,40 @@ def test_gemm_large_tile(lib, monkeypatch, variant, N, K, epi):
     assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
 
 
+FFN_CASES = [
+    # name, M, N, K, epilogue, variant ("" = the launcher's own choice)
+    ("fc1", 12548, 4096, 1024, "gelu", ""),        # LeVJEPA ViT-L/16, batch 4, in one part
+    ("fc2", 12548, 1024, 4096, "resid", ""),       # 64 K steps, 256 x 256 tiles
+    ("fc1", 1300, 4096, 1024, "gelu", "big256"),
+    ("fc2", 1300, 1024, 4096, "resid", "big256"),
+    ("fc1", 1300, 4096, 1024, "gelu", "big128"),
+    ("fc2", 1300, 1024, 4096, "resid", "big128"),
+    ("fc1", 3137, 4096, 1024, "gelu", ""),         # one clip, the batch-part shape
+    ("fc2", 3137, 1024, 4096, "resid", ""),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("case", FFN_CASES, ids=[f"{c[0]}-M{c[1]}-{c[5] or 'auto'}" for c in FFN_CASES])
+def test_gemm_ffn_shapes_every_element(lib, monkeypatch, act, case):
+    """The MLP GEMMs at the ViT-L/16 shapes (N 4096 / K 1024 with the GELU
+    epilogue, N 1024 / K 4096 with the residual one) through the 256-row
+    tiles, every output element against the oracle: full-batch M, one
+    clip's M, and a ragged M = 1300 with each tile width pinned."""
+    name, M, N, K, epi, variant = case
+    if variant:
+        monkeypatch.setenv("JEPA_GEMM_VARIANT", variant)
+    else:
+        monkeypatch.delenv("JEPA_GEMM_VARIANT", raising=False)
+    say(f"gemm {name} {act} M={M} N={N} K={K} {epi} {variant or 'auto'}")
+    got, ref, a, w = _gemm_case(lib, act, "dense", epi, M, N, K, 50)
+    # the bound's product in f32 (its own rounding covered by the 1 % margin)
+    acc = 1.01 * 4 * K * 2.0 ** -24 * (np.abs(a).astype(np.float32) @ np.abs(w).astype(np.float32).T)
+    out_r = 0.0 if epi == "resid" else OUT_REL[act]
+    err = np.abs(got - ref)
+    assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
+
+
 @pytest.mark.parametrize("wfmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 @pytest.mark.parametrize("epi", ["store", "resid"])
@@ -348,6 +382,67 @@ def test_attention_block_causal_rows_ignore_future_slots(lib):
     outs = [_attend(lib, "bf16", x, B, N, heads, True, "block_causal", per).cpu() for x in (a_dev, b_dev)]
     assert torch.equal(outs[0][1:1 + 5 * per], outs[1][1:1 + 5 * per])
     assert not torch.equal(outs[0][0], outs[1][0])          # CLS reads the last slot
+
+
+MASK_CASES = [
+    # B, N, heads, per_slot: the LeVJEPA shape (16 slots of 196 + CLS) and
+    # 8 slots of 36 + CLS (slot boundaries inside key tiles)
+    (1, 3137, 2, 196),
+    (2, 289, 2, 36),
+]
+
+
+@pytest.mark.parametrize("prescaled", [False, True], ids=["q", "qscaled"])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"{c[1]}tok" for c in MASK_CASES])
+def test_attention_block_causal_mask_is_exact(lib, act, case, prescaled):
+    """Each key on a mask boundary carries a marker value of 1000 in a
+    dimension of its own: the first patch key of slot s in dimension s, the
+    last patch key of slot s in dimension 32 + s, the CLS key in dimension 31
+    (every other value is noise of 1e-3).  With q = 0 every allowed key gets
+    probability 1 / (allowed keys), so a patch query of slot t must show
+    1000 / (196 (t + 1)) (or / (36 (t + 1))) in dimensions s and 32 + s for
+    s <= t and noise for s > t and for the CLS dimension; the CLS query sees
+    every key.  One key admitted or dropped at a boundary moves a marker
+    dimension by at least 1000 / 3136, against a bound of a few bf16 ulps."""
+    B, N, heads, per = case
+    T = (N - 1) // per
+    D = heads * 64
+    rng = np.random.default_rng(52)
+    x = np.zeros((B * N, 3 * D))
+    x[:, D:2 * D] = rng.standard_normal((B * N, D))            # keys: any values
+    v = rng.standard_normal((B, N, D)) * 1e-3
+    for h in range(heads):
+        c0 = h * 64
+        v[:, 0, c0 + 31] = 1000.0                               # CLS key
+        for s_ in range(T):
+            v[:, 1 + s_ * per, c0 + s_] = 1000.0                # first key of slot s
+            v[:, (s_ + 1) * per, c0 + 32 + s_] = 1000.0         # last key of slot s
+    x[:, 2 * D:] = v.reshape(B * N, D)
+    qkv_dev, qkv = rounded(act, x)
+    say(f"attention mask markers {act} N={N} slots={T} prescaled={prescaled}")
+    out = _attend(lib, act, qkv_dev, B, N, heads, True, "block_causal", per, prescaled)
+    got = out.double().cpu().numpy().reshape(B, N, heads, 64)
+    vr = qkv[:, 2 * D:].reshape(B, N, heads, 64)
+    slot = np.concatenate([[-1], np.repeat(np.arange(T), per)])
+    # q = 0: a query's output is the mean of its allowed values; patch keys
+    # of slots <= t are the first (t + 1) * per patch rows
+    csum = np.cumsum(vr[:, 1:], axis=1)
+    want = np.empty_like(got)
+    want[:, 0] = vr.mean(axis=1)
+    n_allowed = (slot[1:] + 1) * per
+    want[:, 1:] = csum[:, n_allowed - 1] / n_allowed[None, :, None, None]
+    # f32 accumulation and the probabilities' and output's roundings
+    tol = OUT_REL[act] * 4 * np.abs(want) + 4e-3
+    bad = np.argwhere(np.abs(got - want) > tol)
+    assert bad.size == 0, (bad[:5], np.abs(got - want).max())
+    # the markers separate the boundary cases by far more than the tolerance
+    t = 3
+    row = got[0, 1 + t * per + per // 2, 0]
+    assert abs(row[31]) < 0.1                                    # CLS key excluded
+    assert abs(row[t] - 1000 / (per * (t + 1))) < 0.1 and abs(row[t + 1]) < 0.1
+    assert abs(row[32 + t] - 1000 / (per * (t + 1))) < 0.1 and abs(row[32 + t + 1]) < 0.1
+    assert abs(got[0, 0, 0, 31] - 1000 / N) < 0.1                # the CLS query sees its own key
 
 
 def test_kernels_reject_out_of_contract_shapes(lib):

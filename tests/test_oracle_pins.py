@@ -485,6 +485,56 @@ def test_q4_0_hand_worked_block():
     np.testing.assert_array_equal(w, [2.0 * (v - 8) for v in q])
 
 
+def _ieee_value(code: int, exp_bits: int, man_bits: int) -> float:
+    """The value an IEEE-754 style code denotes, from the format's definition:
+    sign, biased exponent, fraction; exponent 0 is subnormal (no implicit 1),
+    the all-ones exponent is inf (fraction 0) or NaN.  Exact: every value of
+    binary16 and bfloat16 is a Python float."""
+    bias = (1 << (exp_bits - 1)) - 1
+    sign = -1.0 if code >> (exp_bits + man_bits) else 1.0
+    e = (code >> man_bits) & ((1 << exp_bits) - 1)
+    m = code & ((1 << man_bits) - 1)
+    if e == (1 << exp_bits) - 1:
+        return sign * math.inf if m == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(m, 1 - bias - man_bits)
+    return sign * math.ldexp((1 << man_bits) + m, e - bias - man_bits)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_widening_matches_the_format_definition(fmt):
+    """widen_half / widen_bfloat16 (and stored_to_f64's f16 / bf16 branches)
+    against the value each of the 65536 codes denotes: binary16 has 5
+    exponent and 10 fraction bits, bfloat16 8 and 7."""
+    eb, mb = (5, 10) if fmt == "f16" else (8, 7)
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = Q.widen_half(codes) if fmt == "f16" else Q.widen_bfloat16(codes)
+    want = np.array([_ieee_value(int(c), eb, mb) for c in range(1 << 16)])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # the stored-tensor path takes the same branch, as a vector and as a matrix
+    t = dict(name="x", dtype=fmt, ne0=256, ne1=256, data=codes)
+    m = Q.stored_to_f64(t)
+    assert m.shape == (256, 256)
+    assert np.array_equal(np.isnan(m.ravel()), nan)
+    assert np.array_equal(m.ravel()[~nan], want[~nan])
+
+
+def test_widening_named_codes():
+    """Codes whose values the formats fix by hand."""
+    bf = {0x3F80: 1.0, 0xC040: -3.0, 0x0001: 2.0 ** -133, 0x7F80: math.inf,
+          0x0080: 2.0 ** -126, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x8000: -0.0}
+    h = {0x3C00: 1.0, 0x0001: 2.0 ** -24, 0xFBFF: -65504.0, 0x0400: 2.0 ** -14,
+         0x3555: 0.333251953125, 0x7C00: math.inf, 0xC000: -2.0}
+    got = Q.widen_bfloat16(np.array(list(bf), np.uint16))
+    assert list(got) == list(bf.values())
+    got = Q.widen_half(np.array(list(h), np.uint16))
+    assert list(got) == list(h.values())
+
+
 def _f32_scale_q8(x):
     return np.max(np.abs(x.reshape(-1, 32)), axis=1) / np.float32(127)
 

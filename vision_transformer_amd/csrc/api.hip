@@ -146,6 +146,18 @@ struct ProfRec {
     hipEvent_t a, b;
 };
 
+// Device buffers of one encode (rows of a batch); see ws_layout.
+struct Ws {
+    uint8_t *frames = nullptr;   // host frames staged to the device
+    void *patch = nullptr, *hn = nullptr, *qkv = nullptr, *vt = nullptr, *o = nullptr, *u = nullptr;
+    float *x = nullptr, *y = nullptr, *pool = nullptr;
+    // classifier head: x rows f32, LN / cast output, query, attention out,
+    // MLP hidden (act dtype), padded scores f32
+    float *hx = nullptr, *hl = nullptr;
+    void *hh = nullptr, *hq = nullptr, *ho = nullptr, *hu = nullptr;
+    float *kpart = nullptr, *kvpart = nullptr;   // f32 models: split partials
+};
+
 }  // namespace
 
 struct jepa_ctx {
@@ -171,20 +183,13 @@ struct jepa_ctx {
     void *ws = nullptr;
     size_t ws_bytes = 0;
     int ws_batch = 0;
-    uint8_t *w_frames = nullptr;
     // host frames are staged through this pinned buffer; h_ev marks the end
     // of the last copy out of it
     uint8_t *h_frames = nullptr;
     size_t h_frames_bytes = 0;
     hipEvent_t h_ev = nullptr;
     bool h_pending = false;
-    void *w_patch = nullptr, *w_hn = nullptr, *w_qkv = nullptr, *w_vt = nullptr, *w_o = nullptr, *w_u = nullptr;
-    float *w_x = nullptr, *w_y = nullptr, *w_pool = nullptr;
-    // classifier head: x rows f32, LN / cast output, query, attention out,
-    // MLP hidden (act dtype), padded scores f32
-    float *w_hx = nullptr, *w_hl = nullptr;
-    float *w_kpart = nullptr, *w_kvpart = nullptr;   // f32 models: split partials
-    void *w_hh = nullptr, *w_hq = nullptr, *w_ho = nullptr, *w_hu = nullptr;
+    Ws w;                       // the workspace's buffers
     bool last_expand = false;   // the last encode used the expanded matrices
     // last encode
     const float *last_tokens = nullptr;
@@ -214,12 +219,13 @@ struct WsLayout {
     size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, kpart, kvpart, total;
 };
 
-WsLayout ws_layout(const jepa_ctx *c, int B) {
+// with_frames: a region for host frames staged to the device
+WsLayout ws_layout(const jepa_ctx *c, int B, bool with_frames = true) {
     WsLayout w;
     const size_t M = (size_t)B * c->N;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    w.frames = take((size_t)B * c->d.frames * c->d.img_h * c->d.img_w * 3);
+    w.frames = take(with_frames ? (size_t)B * c->d.frames * c->d.img_h * c->d.img_w * 3 : 0);
     w.patch = take((size_t)B * c->Np * c->Kp * c->es);
     w.x = take(M * c->D * 4);
     w.hn = take(M * c->D * c->es);
@@ -331,6 +337,37 @@ jepa_status ensure_expanded(jepa_ctx *c) {
     return JEPA_OK;
 }
 
+// The buffers of layout w at device address base.
+Ws ws_pointers(const jepa_ctx *c, const WsLayout &w, unsigned char *base) {
+    Ws p;
+    p.frames = base + w.frames;
+    p.patch = base + w.patch;
+    p.x = (float *)(base + w.x);
+    p.hn = base + w.hn;
+    p.qkv = base + w.qkv;
+    p.vt = base + w.vt;
+    p.o = base + w.o;
+    p.u = base + w.u;
+    p.y = (float *)(base + w.y);
+    p.pool = (float *)(base + w.pool);
+    p.hx = (float *)(base + w.hx);
+    p.hh = base + w.hh;
+    p.hq = base + w.hq;
+    p.ho = base + w.ho;
+    p.hu = base + w.hu;
+    p.hl = (float *)(base + w.hl);
+    p.kpart = c->act == JEPA_F32 ? (float *)(base + w.kpart) : nullptr;
+    p.kvpart = c->act == JEPA_F32 ? (float *)(base + w.kvpart) : nullptr;
+    return p;
+}
+
+// Forget every pointer into the workspace (before it is freed).
+void clear_workspace(jepa_ctx *c) {
+    c->w = Ws{};
+    c->ws_bytes = 0;
+    c->ws_batch = 0;
+}
+
 jepa_status ensure_workspace(jepa_ctx *c, int B) {
     if (B <= c->ws_batch) return JEPA_OK;
     WsLayout w = ws_layout(c, B);
@@ -339,38 +376,24 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
         return fail(JEPA_E_OOM, "workspace of %zu bytes for batch %d exceeds JEPA_MAX_WORKSPACE=%s",
                     w.total, B, cap);
     if (c->ws) {
+        // nothing may keep pointing into the old workspace once it is freed
+        c->encoded = false;
+        c->last_tokens = nullptr;
+        c->last_batch = 0;
         HIP_TRY(hipDeviceSynchronize());
+        clear_workspace(c);
         HIP_TRY(hipFree(c->ws));
         c->ws = nullptr;
-        c->ws_batch = 0;
     }
     if (hipMalloc(&c->ws, w.total) != hipSuccess) {
         c->ws = nullptr;
         (void)hipGetLastError();
         return fail(JEPA_E_OOM, "hipMalloc of %zu workspace bytes failed", w.total);
     }
-    unsigned char *base = (unsigned char *)c->ws;
-    c->w_frames = base + w.frames;
-    c->w_patch = base + w.patch;
-    c->w_x = (float *)(base + w.x);
-    c->w_hn = base + w.hn;
-    c->w_qkv = base + w.qkv;
-    c->w_vt = base + w.vt;
+    c->w = ws_pointers(c, w, (unsigned char *)c->ws);
     // columns N..npad-1 of V^T are read (and multiplied by zero weights) by
     // the last key tile of each head: keep them finite
-    HIP_TRY(hipMemset(c->w_vt, 0, (size_t)B * c->D * c->npad * c->es));
-    c->w_o = base + w.o;
-    c->w_u = base + w.u;
-    c->w_y = (float *)(base + w.y);
-    c->w_pool = (float *)(base + w.pool);
-    c->w_hx = (float *)(base + w.hx);
-    c->w_hh = base + w.hh;
-    c->w_hq = base + w.hq;
-    c->w_ho = base + w.ho;
-    c->w_hu = base + w.hu;
-    c->w_hl = (float *)(base + w.hl);
-    c->w_kpart = c->act == JEPA_F32 ? (float *)(base + w.kpart) : nullptr;
-    c->w_kvpart = c->act == JEPA_F32 ? (float *)(base + w.kvpart) : nullptr;
+    HIP_TRY(hipMemset(c->w.vt, 0, (size_t)B * c->D * c->npad * c->es));
     c->ws_bytes = w.total;
     c->ws_batch = B;
     return JEPA_OK;
@@ -817,8 +840,8 @@ static jepa_status ensure_streams(jepa_ctx *c, int parts) {
 // (row r0 = b0*N on), on stream s: LN1, the qkv GEMM (q scaled, optionally
 // rotated; v to V^T), attention, out-projection + residual, LN2, fc1 + GELU,
 // fc2 + residual.  expand: the q8_0 / q4_0 matrices' act-dtype copies.
-static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream_t s, int conc, int64_t r0,
-                             int b0, int nb, bool causal, const float *rope) {
+static jepa_status run_block(jepa_ctx *c, const Ws &w, const Layer &L, bool expand, hipStream_t s, int conc,
+                             int64_t r0, int b0, int nb, bool causal, const float *rope) {
     const jepa_dims &d = c->d;
     const int D = c->D, F = c->F, es = c->es, dh = D / c->H;
     auto rows = [&](void *base, int64_t first, int64_t width, int esz) {
@@ -827,17 +850,17 @@ static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream
     const DevTensor &Wqkv = expand ? L.xqkv : L.qkv, &Wout = expand ? L.xout : L.out;
     const DevTensor &Wup = expand ? L.xup : L.up, &Wdown = expand ? L.xdown : L.down;
     const int64_t M = (int64_t)nb * c->N;
-    float *x = (float *)rows(c->w_x, r0, D, 4);
-    void *hn = rows(c->w_hn, r0, D, es), *qkv = rows(c->w_qkv, r0, 3 * D, es);
-    void *o = rows(c->w_o, r0, D, es), *u = rows(c->w_u, r0, F, es);
-    void *vt = rows(c->w_vt, b0, D * c->npad, es);
+    float *x = (float *)rows(w.x, r0, D, 4);
+    void *hn = rows(w.hn, r0, D, es), *qkv = rows(w.qkv, r0, 3 * D, es);
+    void *o = rows(w.o, r0, D, es), *u = rows(w.u, r0, F, es);
+    void *vt = rows(w.vt, b0, D * c->npad, es);
     AttnArgs aa{};
     aa.qk = qkv; aa.ld_qk = 3 * D; aa.vt = vt; aa.npad = c->npad;
     aa.out = o; aa.B = nb; aa.N = c->N; aa.heads = c->H;
     aa.has_cls = d.has_cls; aa.block_causal = causal; aa.per_slot = c->per_slot;
     aa.q_prescaled = 1;
     aa.dh = dh;
-    aa.kvpart = c->w_kvpart ? c->w_kvpart + (size_t)KVSPLIT_MAX * r0 * c->H * (dh + 2) : nullptr;
+    aa.kvpart = w.kvpart ? w.kvpart + (size_t)KVSPLIT_MAX * r0 * c->H * (dh + 2) : nullptr;
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
     {   // q, k to qkv; v transposed straight into V^T
         GemmArgs g{};
@@ -852,7 +875,7 @@ static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream
     TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
     // f32 models: scratch for splitting the residual GEMMs' K (each batch
     // part its own rows of it)
-    float *kpart = c->w_kpart ? c->w_kpart + (size_t)KSPLIT_MAX * r0 * D : nullptr;
+    float *kpart = w.kpart ? w.kpart + (size_t)KSPLIT_MAX * r0 * D : nullptr;
     TRY(gemm(c, K_GEMM_OUT, s, conc, o, M, D, Wout, L.bout, EPI_RESID, x, D, kpart));
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
     TRY(gemm(c, K_GEMM_FC1, s, conc, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
@@ -860,53 +883,16 @@ static jepa_status run_block(jepa_ctx *c, const Layer &L, bool expand, hipStream
     return JEPA_OK;
 }
 
-jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frames_on_device,
-                        float *tokens_out, void *hip_stream) {
-    if (!c || !frames) return fail(JEPA_E_INVALID_ARG, "encode: null argument");
-    if (batch <= 0) return fail(JEPA_E_INVALID_ARG, "encode: batch must be > 0 (got %d)", batch);
-    if ((int64_t)batch * c->N > (int64_t)65535 * 128)
-        return fail(JEPA_E_UNSUPPORTED, "encode: batch*tokens %lld too large", (long long)batch * c->N);
-    TRY(ensure_workspace(c, batch));
-    const int parts = n_parts(c, batch);
-    TRY(ensure_streams(c, parts));
-    c->encoded = false;          // pool / classify read nothing of a failed encode
-    hipStream_t s0 = (hipStream_t)hip_stream;
+// The launch sequence of one encode of `batch` items with device frames fr
+// into the token map Y, over the buffers w, in `parts` concurrent parts
+// (part 0 on s0, the others on the context's internal streams, forked from
+// and joined back onto s0).  expand: the block matrices' act-dtype copies
+// (already written on s0).  Whatever it returns, the parts are joined back
+// onto s0, so that no part's work outlives the caller's stream order.
+static jepa_status encode_parts(jepa_ctx *c, const Ws &w, const uint8_t *fr, int batch, float *Y, hipStream_t s0,
+                                int parts, bool expand) {
     const jepa_dims &d = c->d;
-    const uint8_t *fr = frames;
     const size_t frame_bytes = (size_t)d.frames * d.img_h * d.img_w * 3;   // per item
-    if (!frames_on_device) {
-        // copy into the pinned staging buffer (once the previous copy out of
-        // it has finished), then DMA to the device on the caller's stream:
-        // the call returns after enqueue and the caller's buffer is free
-        const size_t bytes = (size_t)batch * frame_bytes;
-        if (c->h_pending) HIP_TRY(hipEventSynchronize(c->h_ev));
-        c->h_pending = false;
-        if (bytes > c->h_frames_bytes) {
-            if (c->h_frames) HIP_TRY(hipHostFree(c->h_frames));
-            c->h_frames = nullptr;
-            c->h_frames_bytes = 0;
-            if (hipHostMalloc((void **)&c->h_frames, bytes, hipHostMallocDefault) != hipSuccess) {
-                c->h_frames = nullptr;
-                (void)hipGetLastError();
-                return fail(JEPA_E_OOM, "encode: pinned staging of %zu frame bytes failed", bytes);
-            }
-            c->h_frames_bytes = bytes;
-        }
-        if (!c->h_ev) HIP_TRY(hipEventCreateWithFlags(&c->h_ev, hipEventDisableTiming));
-        memcpy(c->h_frames, frames, bytes);
-        HIP_TRY(hipMemcpyAsync(c->w_frames, c->h_frames, bytes, hipMemcpyHostToDevice, s0));
-        HIP_TRY(hipEventRecord(c->h_ev, s0));
-        c->h_pending = true;
-        fr = c->w_frames;
-    }
-    float *Y = tokens_out ? tokens_out : c->w_y;
-    HIP_TRY(hipEventRecord(c->ev0, s0));
-    const bool expand = use_expand(c, batch, parts);
-    c->last_expand = expand;
-    if (expand) {
-        TRY(ensure_expanded(c));
-        TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
-    }
     if (parts > 1) {
         HIP_TRY(hipEventRecord(c->fork_ev, s0));
         for (int p = 1; p < parts; ++p) HIP_TRY(hipStreamWaitEvent(c->aux[p - 1], c->fork_ev, 0));
@@ -924,14 +910,11 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
         P[p] = Part{p == 0 ? s0 : c->aux[p - 1], b, nb, (int64_t)b * c->N, (int64_t)nb * c->N};
         b += nb;
     }
-    const int D = c->D, F = c->F, es = c->es;
+    const int D = c->D, es = c->es;
     auto rows = [&](void *base, int64_t r0, int64_t width, int esz) {
         return (void *)((unsigned char *)base + r0 * width * esz);
     };
 
-    // the launch sequence; whatever it returns, the parts are joined back
-    // onto the caller's stream, so that no part's work outlives the call's
-    // stream order
     auto body = [&]() -> jepa_status {
     for (int p = 0; p < parts; ++p) {
         const Part &q = P[p];
@@ -939,11 +922,11 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
         pa.frames = fr + (size_t)q.b0 * frame_bytes; pa.B = q.nb; pa.T = d.frames; pa.H = d.img_h; pa.W = d.img_w;
         pa.tubelet = d.tubelet; pa.patch = d.patch;
         for (int i = 0; i < 3; ++i) { pa.mean[i] = d.mean[i]; pa.std[i] = d.std[i]; }
-        pa.out = rows(c->w_patch, (int64_t)q.b0 * c->Np, c->Kp, es); pa.ld = c->Kp;
+        pa.out = rows(w.patch, (int64_t)q.b0 * c->Np, c->Kp, es); pa.ld = c->Kp;
         TRY(launch(c, K_PATCHIFY, q.s, [&] { return launch_patchify(c->act, pa, q.s); }));
 
         GemmArgs g{};
-        g.a = pa.out; g.w = c->wpe.ptr; g.bias = c->bpe; g.out = rows(c->w_x, q.r0, D, 4);
+        g.a = pa.out; g.w = c->wpe.ptr; g.bias = c->bpe; g.out = rows(w.x, q.r0, D, 4);
         g.M = (int64_t)q.nb * c->Np; g.N = D; g.K = c->Kp; g.lda = c->Kp; g.ldo = D;
         g.pos = c->pos; g.np = c->Np; g.ntok = c->N; g.has_cls = d.has_cls;
         TRY(launch(c, K_GEMM_PATCH, q.s, [&] { return launch_gemm(c->act, c->act, EPI_PATCH, g, q.s); }));
@@ -955,11 +938,11 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
 
     for (int i = 0; i < c->L; ++i)
         for (int p = 0; p < parts; ++p)
-            TRY(run_block(c, c->layers[i], expand, P[p].s, parts, P[p].r0, P[p].b0, P[p].nb,
+            TRY(run_block(c, w, c->layers[i], expand, P[p].s, parts, P[p].r0, P[p].b0, P[p].nb,
                           d.mask == JEPA_MASK_BLOCK_CAUSAL, c->rope));
     for (int p = 0; p < parts; ++p) {
         const Part &q = P[p];
-        float *x = (float *)rows(c->w_x, q.r0, D, 4);
+        float *x = (float *)rows(w.x, q.r0, D, 4);
         float *y = Y + q.r0 * D;
         TRY(launch(c, K_FINAL_LN, q.s, [&] {
             return launch_layernorm(x, q.M, D, c->normg, c->normb, d.ln_eps, y, JEPA_F32, q.s);
@@ -972,7 +955,65 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
         HIP_TRY(hipEventRecord(c->join_ev[p - 1], c->aux[p - 1]));
         HIP_TRY(hipStreamWaitEvent(s0, c->join_ev[p - 1], 0));
     }
-    if (st != JEPA_OK) return st;
+    return st;
+}
+
+static jepa_status check_encode_args(const jepa_ctx *c, const uint8_t *frames, int batch) {
+    if (!c || !frames) return fail(JEPA_E_INVALID_ARG, "encode: null argument");
+    if (batch <= 0) return fail(JEPA_E_INVALID_ARG, "encode: batch must be > 0 (got %d)", batch);
+    if ((int64_t)batch * c->N > (int64_t)65535 * 128)
+        return fail(JEPA_E_UNSUPPORTED, "encode: batch*tokens %lld too large", (long long)batch * c->N);
+    return JEPA_OK;
+}
+
+jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frames_on_device,
+                        float *tokens_out, void *hip_stream) {
+    TRY(check_encode_args(c, frames, batch));
+    // pool / classify read nothing of a failed encode, nor of the previous
+    // one once this call has started (its workspace may be reallocated)
+    c->encoded = false;
+    c->last_tokens = nullptr;
+    c->last_batch = 0;
+    TRY(ensure_workspace(c, batch));
+    const int parts = n_parts(c, batch);
+    TRY(ensure_streams(c, parts));
+    hipStream_t s0 = (hipStream_t)hip_stream;
+    const jepa_dims &d = c->d;
+    const uint8_t *fr = frames;
+    if (!frames_on_device) {
+        // copy into the pinned staging buffer (once the previous copy out of
+        // it has finished), then DMA to the device on the caller's stream:
+        // the call returns after enqueue and the caller's buffer is free
+        const size_t bytes = (size_t)batch * d.frames * d.img_h * d.img_w * 3;
+        if (c->h_pending) HIP_TRY(hipEventSynchronize(c->h_ev));
+        c->h_pending = false;
+        if (bytes > c->h_frames_bytes) {
+            if (c->h_frames) HIP_TRY(hipHostFree(c->h_frames));
+            c->h_frames = nullptr;
+            c->h_frames_bytes = 0;
+            if (hipHostMalloc((void **)&c->h_frames, bytes, hipHostMallocDefault) != hipSuccess) {
+                c->h_frames = nullptr;
+                (void)hipGetLastError();
+                return fail(JEPA_E_OOM, "encode: pinned staging of %zu frame bytes failed", bytes);
+            }
+            c->h_frames_bytes = bytes;
+        }
+        if (!c->h_ev) HIP_TRY(hipEventCreateWithFlags(&c->h_ev, hipEventDisableTiming));
+        memcpy(c->h_frames, frames, bytes);
+        HIP_TRY(hipMemcpyAsync(c->w.frames, c->h_frames, bytes, hipMemcpyHostToDevice, s0));
+        HIP_TRY(hipEventRecord(c->h_ev, s0));
+        c->h_pending = true;
+        fr = c->w.frames;
+    }
+    float *Y = tokens_out ? tokens_out : c->w.y;
+    HIP_TRY(hipEventRecord(c->ev0, s0));
+    const bool expand = use_expand(c, batch, parts);
+    c->last_expand = expand;
+    if (expand) {
+        TRY(ensure_expanded(c));
+        TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
+    }
+    TRY(encode_parts(c, c->w, fr, batch, Y, s0, parts, expand));
     HIP_TRY(hipEventRecord(c->ev1, s0));
     c->last_tokens = Y;
     c->last_batch = batch;
@@ -991,29 +1032,29 @@ jepa_status jepa_classify(jepa_ctx *c, float *logits_out, void *hip_stream) {
     const int B = c->last_batch, D = c->D, F = c->F, dh = D / c->H;
     const int64_t M = (int64_t)B * c->N;
     // the head's blocks run on the residual stream, seeded with the token map
-    HIP_TRY(hipMemcpyAsync(c->w_x, c->last_tokens, (size_t)M * D * 4, hipMemcpyDeviceToDevice, s));
-    for (const Layer &L : c->head_layers) TRY(run_block(c, L, c->last_expand, s, 1, 0, 0, B, false, nullptr));
+    HIP_TRY(hipMemcpyAsync(c->w.x, c->last_tokens, (size_t)M * D * 4, hipMemcpyDeviceToDevice, s));
+    for (const Layer &L : c->head_layers) TRY(run_block(c, c->w, L, c->last_expand, s, 1, 0, 0, B, false, nullptr));
     // keys and values of the normalised tokens (in the qkv buffer, pitch 3D)
-    TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w_x, M, D, h.ln1g, h.ln1b, d.ln_eps, c->w_hn, c->act, s); }));
-    unsigned char *kv = (unsigned char *)c->w_qkv;
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hn, M, D, h.wk, h.bk, EPI_STORE, kv, 3 * D));
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hn, M, D, h.wv, h.bv, EPI_STORE, kv + (size_t)D * c->es, 3 * D));
+    TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w.x, M, D, h.ln1g, h.ln1b, d.ln_eps, c->w.hn, c->act, s); }));
+    unsigned char *kv = (unsigned char *)c->w.qkv;
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, h.wk, h.bk, EPI_STORE, kv, 3 * D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, h.wv, h.bv, EPI_STORE, kv + (size_t)D * c->es, 3 * D));
     // the query row of every item: W_q q0 + b_q
-    TRY(launch(c, K_HEAD, s, [&] { return launch_cls_rows(c->w_hx, h.q0, nullptr, B, 1, D, s); }));
-    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w_hx, (int64_t)B * D, c->w_hh, c->act, s); }));
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wq, h.bq, EPI_STORE, c->w_hq, D));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cls_rows(c->w.hx, h.q0, nullptr, B, 1, D, s); }));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w.hx, (int64_t)B * D, c->w.hh, c->act, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wq, h.bq, EPI_STORE, c->w.hq, D));
     TRY(launch(c, K_HEAD, s, [&] {
-        return launch_xattn(c->act, c->w_hq, kv, kv + (size_t)D * c->es, 3 * D, B, c->N, c->H, dh, c->w_ho, s);
+        return launch_xattn(c->act, c->w.hq, kv, kv + (size_t)D * c->es, 3 * D, B, c->N, c->H, dh, c->w.ho, s);
     }));
     // x = q0 + out_proj(o); x += MLP(LN2 x); scores = W_c x + b_c
-    TRY(gemm(c, K_HEAD, s, 1, c->w_ho, B, D, h.wo, h.bo, EPI_RESID, c->w_hx, D));
-    TRY(launch(c, K_HEAD, s, [&] { return launch_layernorm(c->w_hx, B, D, h.ln2g, h.ln2b, d.ln_eps, c->w_hh, c->act, s); }));
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wup, h.bup, EPI_GELU, c->w_hu, F));
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hu, B, F, h.wdown, h.bdown, EPI_RESID, c->w_hx, D));
-    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w_hx, (int64_t)B * D, c->w_hh, c->act, s); }));
-    TRY(launch(c, K_HEAD, s, [&] { return launch_fill(c->w_hl, (int64_t)B * h.Cpad, 0.f, s); }));
-    TRY(gemm(c, K_HEAD, s, 1, c->w_hh, B, D, h.wc, h.bc, EPI_RESID, c->w_hl, h.Cpad));
-    HIP_TRY(hipMemcpy2DAsync(logits_out, (size_t)h.C * 4, c->w_hl, (size_t)h.Cpad * 4, (size_t)h.C * 4, B,
+    TRY(gemm(c, K_HEAD, s, 1, c->w.ho, B, D, h.wo, h.bo, EPI_RESID, c->w.hx, D));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_layernorm(c->w.hx, B, D, h.ln2g, h.ln2b, d.ln_eps, c->w.hh, c->act, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wup, h.bup, EPI_GELU, c->w.hu, F));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hu, B, F, h.wdown, h.bdown, EPI_RESID, c->w.hx, D));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w.hx, (int64_t)B * D, c->w.hh, c->act, s); }));
+    TRY(launch(c, K_HEAD, s, [&] { return launch_fill(c->w.hl, (int64_t)B * h.Cpad, 0.f, s); }));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wc, h.bc, EPI_RESID, c->w.hl, h.Cpad));
+    HIP_TRY(hipMemcpy2DAsync(logits_out, (size_t)h.C * 4, c->w.hl, (size_t)h.Cpad * 4, (size_t)h.C * 4, B,
                              hipMemcpyDeviceToDevice, s));
     return JEPA_OK;
 }
@@ -1037,7 +1078,7 @@ jepa_status jepa_pool(jepa_ctx *c, int mode, float *out, void *hip_stream) {
             if (!c->d.has_cls) return fail(JEPA_E_STATE, "pool: the model has no CLS token");
             return launch(c, K_POOL, s, [&] { return launch_pool_cls(c->last_tokens, B, c->N, c->D, out, s); });
         case JEPA_POOL_MEAN:
-            return launch(c, K_POOL, s, [&] { return launch_pool_mean(c->last_tokens, B, c->N, c->D, c->d.has_cls, c->w_pool, out, s); });
+            return launch(c, K_POOL, s, [&] { return launch_pool_mean(c->last_tokens, B, c->N, c->D, c->d.has_cls, c->w.pool, out, s); });
         case JEPA_POOL_NONE:   // a kernel, so that the copy is ordered on the compute queue like the rest
             return launch(c, K_POOL, s, [&] { return launch_copy_f32(c->last_tokens, (int64_t)B * c->N * c->D, out, s); });
     }

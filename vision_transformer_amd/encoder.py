@@ -1,6 +1,7 @@
 """An owning wrapper around one jepa_ctx."""
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -9,17 +10,25 @@ from . import synth
 
 class Encoder:
     """Weights resident on the current GPU; encode() and pool() enqueue on a
-    torch stream (the current one by default)."""
+    torch stream (the current one by default).
+
+    The library's pool() and classify() read the token map where the last
+    encode() wrote it, so the wrapper keeps that tensor alive until the next
+    encode, and sizes their outputs from that encode's batch."""
 
     def __init__(self, dims: dict, tensors: list[dict]):
         self.dims = dict(dims)
         self.n_tokens = synth.n_tokens(dims)
         self.ctx = _lib.jepa_create(dims, tensors)
+        self._last_tokens = None
+        self.last_batch = 0
 
     def close(self):
         if getattr(self, "ctx", None):
             _lib.jepa_free(self.ctx)
             self.ctx = None
+        self._last_tokens = None
+        self.last_batch = 0
 
     def __del__(self):
         try:
@@ -27,27 +36,66 @@ class Encoder:
         except Exception:
             pass
 
+    def _frame_shape(self, batch: int) -> tuple:
+        d = self.dims
+        return (batch, d["frames"], d["img_h"], d["img_w"], 3)
+
     def encode(self, frames, tokens_out=None, stream=None):
-        """frames: uint8 [B, T, H, W, 3] (CUDA tensor, or host numpy).  Returns
-        tokens_out (allocated if None): f32 [B, N, D] on the GPU."""
-        B = frames.shape[0]
+        """frames: uint8 [B, T, H, W, 3] (CUDA tensor, or host numpy / CPU
+        tensor).  Returns tokens_out (allocated if None): f32 [B, N, D] on the
+        GPU.  The tensor stays referenced here until the next encode."""
+        B = int(frames.shape[0])
+        if tuple(frames.shape) != self._frame_shape(B):
+            raise ValueError(f"frames shape {tuple(frames.shape)}, expected {self._frame_shape(B)}")
+        is_uint8 = frames.dtype == torch.uint8 if isinstance(frames, torch.Tensor) else frames.dtype == np.uint8
+        if not is_uint8:
+            raise ValueError(f"frames dtype {frames.dtype}, expected uint8")
+        want = (B, self.n_tokens, self.dims["dim"])
         if tokens_out is None:
-            tokens_out = torch.empty((B, self.n_tokens, self.dims["dim"]), dtype=torch.float32,
-                                     device="cuda")
+            tokens_out = torch.empty(want, dtype=torch.float32, device="cuda")
+        elif (tuple(tokens_out.shape) != want or tokens_out.dtype != torch.float32
+              or not tokens_out.is_cuda):
+            raise ValueError(f"tokens_out must be a CUDA f32 tensor of shape {want}")
+        # the previous token map is forgotten as soon as the call starts
+        self._last_tokens = None
+        self.last_batch = 0
         _lib.jepa_encode(self.ctx, frames, B, tokens_out, stream)
+        self._last_tokens = tokens_out
+        self.last_batch = B
         return tokens_out
 
-    def pool(self, mode: str, batch: int, out=None, stream=None):
+    def _check_batch(self, batch):
+        if self.last_batch == 0:
+            return 0          # the library reports JEPA_E_STATE
+        if batch is not None and batch != self.last_batch:
+            raise ValueError(f"batch {batch} differs from the last encode's {self.last_batch}")
+        return self.last_batch
+
+    @staticmethod
+    def _check_out(out, shape):
+        if tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_cuda:
+            raise ValueError(f"out must be a CUDA f32 tensor of shape {shape}")
+
+    def pool(self, mode: str, batch: int | None = None, out=None, stream=None):
+        """Pool the last encode's token map: [B, D] (cls, mean) or [B, N, D]
+        (none).  batch, if given, must equal the last encode's."""
+        B = self._check_batch(batch)
+        shape = (B, self.n_tokens, self.dims["dim"]) if mode == "none" else (B, self.dims["dim"])
         if out is None:
-            shape = (batch, self.n_tokens, self.dims["dim"]) if mode == "none" else (batch, self.dims["dim"])
-            out = torch.empty(shape, dtype=torch.float32, device="cuda")
+            out = torch.empty((max(B, 1),) + shape[1:], dtype=torch.float32, device="cuda")
+        elif B:
+            self._check_out(out, shape)
         _lib.jepa_pool(self.ctx, mode, out, stream)
         return out
 
-    def classify(self, batch: int, out=None, stream=None):
-        """Class scores f32 [batch, head_classes] of the last encode's tokens."""
+    def classify(self, batch: int | None = None, out=None, stream=None):
+        """Class scores f32 [B, head_classes] of the last encode's tokens."""
+        B = self._check_batch(batch)
+        shape = (B, self.dims["head_classes"])
         if out is None:
-            out = torch.empty((batch, self.dims["head_classes"]), dtype=torch.float32, device="cuda")
+            out = torch.empty((max(B, 1), shape[1]), dtype=torch.float32, device="cuda")
+        elif B:
+            self._check_out(out, shape)
         _lib.jepa_classify(self.ctx, out, stream)
         return out
 

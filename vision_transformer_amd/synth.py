@@ -4,10 +4,10 @@ This module only draws random numbers and names tensors.  It holds none of
 the encoder's arithmetic.  The HIP path and the CPU oracle both take their
 inputs from here, as plain numpy arrays.
 
-The jepa.cpp "measured benchmarks" page ("Box and build" section) times its
-encoders on synthetic but deterministic input: a seeded uint8 stream put
-through the model's own normalisation.  The workloads below follow that idea
-with the model shapes the pages describe:
+The jepa.cpp "measured benchmarks" page ("Box and build" section) feeds its
+encoder timings with seeded random bytes as pixels, normalised by the
+model's own recipe, rather than real clips.  The workloads below do the same
+at the model shapes the pages describe:
   * ViT-Ti/14 image encoder, 224x224 (LeWorldModel Push-T card, "Files");
   * ViT-L/16 224x224 image encoder;
   * LeVJEPA ViT-L/16, 16 frames, tubelet 1, block-causal (LeVJEPA card,
@@ -190,10 +190,32 @@ SMALL_WORKLOADS = {
 }
 
 
+# ViT-L/16 widths (D 1024, 16 heads, MLP 4096) at two blocks and about a
+# thousand rows per batch: every GEMM shape of the full-size encoders (qkv,
+# out-proj, fc1, fc2) on the 256-row tiles, small enough for the oracle to
+# check every token.
+MID_WORKLOADS = {
+    "mid_vitl_blockcausal_bf16": dict(
+        dims=_dims(**dict(_VITL, depth=2), frames=4, mask="block_causal", act_dtype="bf16",
+                   mat_dtype="bf16", rest_dtype="bf16"),
+        batch=2, frame_seed=41, weight_seed=51),
+    "mid_vitl_tubelet2_q8_0": dict(
+        dims=_dims(**dict(_VITL, depth=2), frames=4, tubelet=2, img_h=256, img_w=256, has_cls=0,
+                   act_dtype="f16", mat_dtype="q8_0", rest_dtype="f16"),
+        batch=2, frame_seed=42, weight_seed=52),
+    "mid_vitl_rope_q4_0": dict(
+        dims=_dims(**dict(_VITL, depth=2), frames=4, tubelet=2, img_h=256, img_w=256, has_cls=0,
+                   act_dtype="f16", mat_dtype="q4_0", rest_dtype="f16", rope=1),
+        batch=2, frame_seed=43, weight_seed=53),
+}
+
+
 def workload(name: str) -> dict:
-    """A deep copy of a named workload (full-size or small)."""
-    table = WORKLOADS if name in WORKLOADS else SMALL_WORKLOADS
-    return copy.deepcopy(table[name])
+    """A deep copy of a named workload (full-size, mid-size or small)."""
+    for table in (WORKLOADS, MID_WORKLOADS, SMALL_WORKLOADS):
+        if name in table:
+            return copy.deepcopy(table[name])
+    raise KeyError(name)
 
 
 # ----------------------------------------------------------------------------
