@@ -166,6 +166,32 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
 jepa_status jepa_encode(jepa_ctx *ctx, const uint8_t *frames, int batch, int frames_on_device,
                         float *tokens_out, void *hip_stream);
 
+/* Size in bytes of the static device array jepa_encode_noalloc works in. */
+#define JEPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* jepa_encode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It runs jepa_encode's launch sequence with the batch as one part, and its
+ * buffers (residual stream, activations, V^T, split partial sums) live in
+ * one static device array of JEPA_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds, at its own address, until the process ends.  No
+ * hipMalloc, hipFree or other allocating call is made, and no timing events
+ * are recorded.  frames: device uint8 [batch, frames, img_h, img_w, 3];
+ * tokens_out: device f32 [batch, N, dim], required.  Q8_0 / Q4_0 matrices
+ * are dequantised in the GEMM's tile load (no expanded copy).  A batch whose
+ * buffers do not fit the array is refused with JEPA_E_OOM before anything
+ * is enqueued: it serves small models (ViT-Ti/14 f32 needs about 6 MB per
+ * image), not the ViT-L video batches, which need jepa_encode.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the call clears what must start at zero itself): calls that
+ * overlap on one GPU, from any stream, thread or context, race and corrupt
+ * each other's results; order them on one stream.  Like jepa_encode it
+ * forgets the context's previous token map: jepa_pool and jepa_classify
+ * return JEPA_E_STATE and jepa_last_compute_ms -1 until the next
+ * jepa_encode. */
+jepa_status jepa_encode_noalloc(jepa_ctx *ctx, const uint8_t *frames, int batch, float *tokens_out,
+                                void *hip_stream);
+
 /* Concurrency of jepa_encode: the batch is split into `parts` contiguous
  * groups of items, encoded concurrently on the caller's stream and parts-1
  * internal non-blocking HIP streams (default priority) forked from and

@@ -57,6 +57,7 @@ def _load():
     sig = {
         "jepa_create": (I, [C.POINTER(jepa_dims), C.POINTER(jepa_tensor), I, C.POINTER(P)]),
         "jepa_encode": (I, [P, P, I, I, P, P]),
+        "jepa_encode_noalloc": (I, [P, P, I, P, P]),
         "jepa_pool": (I, [P, I, P, P]),
         "jepa_classify": (I, [P, P, P]),
         "jepa_free": (None, [P]),
@@ -146,6 +147,18 @@ def jepa_encode(ctx: int, frames, batch: int, tokens_out=None, stream=None) -> N
     array / CPU tensor (host).  tokens_out: f32 CUDA tensor [batch, N, D] or None."""
     on_dev = int(hasattr(frames, "is_cuda") and frames.is_cuda)
     _check(_lib.jepa_encode(ctx, _ptr(frames), batch, on_dev, _ptr(tokens_out), _stream(stream)))
+
+
+# bytes of the static device array jepa_encode_noalloc works in
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def jepa_encode_noalloc(ctx: int, frames, batch: int, tokens_out, stream=None) -> None:
+    """frames: uint8 CUDA tensor [batch, T, H, W, 3]; tokens_out: f32 CUDA
+    tensor [batch, N, D] (required).  Allocates nothing on the device."""
+    if not (hasattr(frames, "is_cuda") and frames.is_cuda):
+        raise ValueError("jepa_encode_noalloc takes frames in device memory")
+    _check(_lib.jepa_encode_noalloc(ctx, _ptr(frames), batch, _ptr(tokens_out), _stream(stream)))
 
 
 def jepa_pool(ctx: int, mode: str | int, out, stream=None) -> None:

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -506,6 +507,37 @@ struct Expect {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// The no-allocation encode's buffers: one static device array, one copy per
+// device.  Host code never uses the array's name as an address: each
+// device's copy is looked up once, with that device current, and kept here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[JEPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch` (looked up on first use).
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 const char *jepa_last_error(void) { return g_err.c_str(); }
@@ -793,6 +825,11 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         return fail(JEPA_E_HIP, "create: hipEventCreate failed");
     }
     c->have_events = true;
+    {   // this device's copy of the no-allocation encode's scratch; a failure
+        // here only matters to jepa_encode_noalloc, which looks it up again
+        void *p = nullptr;
+        if (scratch_address(&p) != hipSuccess) (void)hipGetLastError();
+    }
     *out = c;
     return JEPA_OK;
 }
@@ -964,6 +1001,35 @@ static jepa_status check_encode_args(const jepa_ctx *c, const uint8_t *frames, i
     if ((int64_t)batch * c->N > (int64_t)65535 * 128)
         return fail(JEPA_E_UNSUPPORTED, "encode: batch*tokens %lld too large", (long long)batch * c->N);
     return JEPA_OK;
+}
+
+jepa_status jepa_encode_noalloc(jepa_ctx *c, const uint8_t *frames, int batch, float *tokens_out,
+                                void *hip_stream) {
+    TRY(check_encode_args(c, frames, batch));
+    if (!tokens_out) return fail(JEPA_E_INVALID_ARG, "encode_noalloc: tokens_out is required");
+    c->encoded = false;
+    c->last_tokens = nullptr;
+    c->last_batch = 0;
+    const WsLayout lay = ws_layout(c, batch, false);
+    if (lay.total > JEPA_NOALLOC_SCRATCH_BYTES)
+        return fail(JEPA_E_OOM, "encode_noalloc: batch %d needs %zu bytes of buffers; the static scratch holds %zu",
+                    batch, lay.total, (size_t)JEPA_NOALLOC_SCRATCH_BYTES);
+    void *base = nullptr;
+    const hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return fail(JEPA_E_HIP, "encode_noalloc: address of the static scratch: %s", hipGetErrorString(e));
+    const Ws w = ws_pointers(c, lay, (unsigned char *)base);
+    hipStream_t s = (hipStream_t)hip_stream;
+    // the last key tile of each head reads V^T's padding columns: finite
+    // values, cleared by a kernel (the array holds whatever the last call left)
+    const int64_t vt_words = (int64_t)batch * c->D * c->npad * c->es / 4;
+    const hipError_t fe = launch_fill((float *)w.vt, vt_words, 0.f, s);
+    if (fe != hipSuccess) return fail(JEPA_E_HIP, "encode_noalloc: clearing V^T: %s", hipGetErrorString(fe));
+    // no timing events (they are created on demand)
+    const uint32_t prof = c->prof;
+    c->prof = 0;
+    const jepa_status st = encode_parts(c, w, frames, batch, tokens_out, s, 1, false);
+    c->prof = prof;
+    return st;
 }
 
 jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frames_on_device,
