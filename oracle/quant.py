@@ -1,4 +1,4 @@
-"""Block quantisation formats q8_0 and q4_0, and exact widening.  Test infrastructure.
+"""Block quantisation formats q8_0, q4_0, q4_K and q6_K, and exact widening.  Test infrastructure.
 
 The jepa.cpp Quantization page ("File sizes") gives q8_0 as 8.5 bits per
 weight and q4_0 as 4.5: one f16 scale per block of 32 weights along a row,
@@ -76,7 +76,8 @@ def quantize_q4_0(x: np.ndarray) -> np.ndarray:
 
 
 def quantize(dtype: str, x: np.ndarray) -> np.ndarray:
-    return {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0}[dtype](x)
+    return {"q8_0": quantize_q8_0, "q4_0": quantize_q4_0, "q4_k": quantize_q4_k,
+            "q6_k": quantize_q6_k}[dtype](x)
 
 
 def _unpack(raw: np.ndarray, rows: int, cols: int, bb: int):
@@ -99,6 +100,187 @@ def dequantize_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     hi = (qs >> 4).astype(np.int32) - 8
     q = np.concatenate([lo, hi], axis=2).astype(np.float32)
     return (d[:, :, None] * q).reshape(rows, cols).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# K-quants: super-blocks of 256 weights along a row (Quantization page, "The
+# rule": "block 256"; "File sizes": q4_k has q4_0's 4.5 bits per weight).  The
+# pages name the formats by their ggml names (q4_K, q6_K); their layouts are
+# the published ggml ones, restated here:
+#   q4_K (144 bytes): f16 d, f16 dmin, 12 bytes of 6-bit sub-block scales and
+#        mins, 128 bytes of 4-bit codes.  Sub-block j (32 weights) has scale
+#        sc_j and min m_j: for j < 4, sc_j = s[j] & 63 and m_j = s[j+4] & 63;
+#        for j >= 4, sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4 and
+#        m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4.  Bytes 32p .. 32p+31 of the
+#        codes hold sub-block 2p in their low nibbles and 2p+1 in their high
+#        ones.  w = d sc_j q - dmin m_j.
+#   q6_K (210 bytes): 128 bytes of low code bits, 64 bytes of high code
+#        bits, 16 int8 sub-block scales, f16 d.  Weight k of a half
+#        h = k // 128 (r = k % 128 = 32 t + l, l < 32) has the 6-bit code
+#        whose low 4 bits are the low (t < 2) or high (t >= 2) nibble of low
+#        byte 64 h + l + 32 (t % 2) and whose high 2 bits are bits 2t, 2t+1
+#        of high byte 32 h + l; its scale is scales[k // 16].
+#        w = d scales[k // 16] (code - 32).
+# Dequantised values are the exact results rounded once to f32: every
+# product above is exact in f32 but d scales[.] (code - 32) of q6_K, and
+# q4_K's subtraction.
+# ---------------------------------------------------------------------------
+QK_K = 256
+Q4_K_BLOCK_BYTES = 144
+Q6_K_BLOCK_BYTES = 210
+
+
+def _superblocks(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] % QK_K:
+        raise ValueError("rows must be a multiple of 256 long")
+    return x.reshape(x.shape[0], x.shape[1] // QK_K, QK_K)
+
+
+def _f16(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float32).astype(np.float16)
+
+
+def q4_k_scale_min(scales: np.ndarray):
+    """The 12 packed bytes of q4_K -> (sc, m), each [..., 8] of 6-bit integers."""
+    s = scales.astype(np.int64)
+    sc = np.empty(s.shape[:-1] + (8,), np.int64)
+    m = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = s[..., j] & 63
+        m[..., j] = s[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (s[..., j + 4] & 15) | ((s[..., j - 4] >> 6) << 4)
+        m[..., j] = (s[..., j + 4] >> 4) | ((s[..., j] >> 6) << 4)
+    return sc, m
+
+
+def dequantize_q4_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """uint8 q4_K super-blocks -> f32 weights [rows, cols] (exact, rounded once)."""
+    b = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // QK_K, Q4_K_BLOCK_BYTES)
+    d = b[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    dmin = b[..., 2:4].copy().view(np.float16)[..., 0].astype(np.float64)
+    sc, m = q4_k_scale_min(b[..., 4:16])
+    qs = b[..., 16:144].astype(np.int64)
+    w = np.empty((rows, cols // QK_K, QK_K), np.float64)
+    for p in range(4):
+        byte = qs[..., 32 * p:32 * p + 32]
+        for half, code in ((0, byte & 15), (1, byte >> 4)):
+            j = 2 * p + half
+            w[..., 64 * p + 32 * half:64 * p + 32 * half + 32] = (
+                (d * sc[..., j])[..., None] * code - (dmin * m[..., j])[..., None])
+    return w.reshape(rows, cols).astype(np.float32)
+
+
+def q6_k_codes(ql: np.ndarray, qh: np.ndarray) -> np.ndarray:
+    """low [..., 128] and high [..., 64] code bytes -> the 256 6-bit codes."""
+    ql = ql.astype(np.int64)
+    qh = qh.astype(np.int64)
+    c = np.empty(ql.shape[:-1] + (QK_K,), np.int64)
+    for h in range(2):
+        for t in range(4):
+            lo = ql[..., 64 * h + 32 * (t % 2):64 * h + 32 * (t % 2) + 32]
+            lo = lo & 15 if t < 2 else lo >> 4
+            hi = (qh[..., 32 * h:32 * h + 32] >> (2 * t)) & 3
+            c[..., 128 * h + 32 * t:128 * h + 32 * t + 32] = lo | (hi << 4)
+    return c
+
+
+def dequantize_q6_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """uint8 q6_K super-blocks -> f32 weights [rows, cols] (exact, rounded once)."""
+    b = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // QK_K, Q6_K_BLOCK_BYTES)
+    code = q6_k_codes(b[..., 0:128], b[..., 128:192])
+    sc = b[..., 192:208].view(np.int8).astype(np.float64)
+    d = b[..., 208:210].copy().view(np.float16)[..., 0].astype(np.float64)
+    w = d[..., None] * np.repeat(sc, 16, axis=-1) * (code - 32)
+    return w.reshape(rows, cols).astype(np.float32)
+
+
+def quantize_q6_k(x: np.ndarray) -> np.ndarray:
+    """f32 [rows, K] -> q6_K blocks [rows, K/256*210].
+
+    A plain encoder (any encoder that writes the format is valid; this one is
+    not ggml's search): sub-block scale s = max|x| / 31 over 16 weights,
+    d = max(s) / 127 stored as f16, scales[i] = round(s_i / d16) clamped to
+    127, codes round(x / (d16 scales[i])) + 32 clamped to 0 .. 63."""
+    b = _superblocks(x).astype(np.float64)
+    R, NB, _ = b.shape
+    sub = b.reshape(R, NB, 16, 16)
+    s = np.max(np.abs(sub), axis=-1) / 31.0
+    d16 = _f16(np.max(s, axis=-1) / 127.0).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d16[..., None] > 0, np.round(s / d16[..., None]), 0)
+        sc = np.clip(sc, 0, 127)
+        step = d16[..., None] * sc
+        q = np.where(step[..., None] > 0, np.round(sub / step[..., None]), 0)
+    code = (np.clip(q, -32, 31) + 32).astype(np.int64).reshape(R, NB, QK_K)
+    ql = np.zeros((R, NB, 128), np.int64)
+    qh = np.zeros((R, NB, 64), np.int64)
+    for h in range(2):
+        for t in range(4):
+            c = code[..., 128 * h + 32 * t:128 * h + 32 * t + 32]
+            lo = slice(64 * h + 32 * (t % 2), 64 * h + 32 * (t % 2) + 32)
+            ql[..., lo] |= (c & 15) << (0 if t < 2 else 4)
+            qh[..., 32 * h:32 * h + 32] |= (c >> 4) << (2 * t)
+    out = np.concatenate([ql.astype(np.uint8), qh.astype(np.uint8), sc.astype(np.int8).view(np.uint8),
+                          d16.astype(np.float16).view(np.uint8).reshape(R, NB, 2)], axis=-1)
+    return np.ascontiguousarray(out.reshape(R, NB * Q6_K_BLOCK_BYTES))
+
+
+def quantize_q4_k(x: np.ndarray) -> np.ndarray:
+    """f32 [rows, K] -> q4_K blocks [rows, K/256*144].
+
+    A plain encoder: over each 32 weights, the min mn = min(x, 0) and the
+    scale (max x - mn) / 15; d = max(scale) / 63 and dmin = max(-mn) / 63
+    stored as f16; sc = round(scale / d16), m = round(-mn / dmin16), both
+    clamped to 0 .. 63; codes round((x + dmin16 m) / (d16 sc)) clamped to
+    0 .. 15."""
+    b = _superblocks(x).astype(np.float64)
+    R, NB, _ = b.shape
+    sub = b.reshape(R, NB, 8, 32)
+    mn = np.minimum(np.min(sub, axis=-1), 0.0)
+    scale = (np.max(sub, axis=-1) - mn) / 15.0
+    d16 = _f16(np.max(scale, axis=-1) / 63.0).astype(np.float64)
+    dm16 = _f16(np.max(-mn, axis=-1) / 63.0).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.clip(np.where(d16[..., None] > 0, np.round(scale / d16[..., None]), 0), 0, 63)
+        m = np.clip(np.where(dm16[..., None] > 0, np.round(-mn / dm16[..., None]), 0), 0, 63)
+        step = d16[..., None] * sc
+        q = np.where(step[..., None] > 0, np.round((sub + (dm16[..., None] * m)[..., None]) / step[..., None]), 0)
+    q = np.clip(q, 0, 15).astype(np.int64)
+    sc = sc.astype(np.int64)
+    m = m.astype(np.int64)
+    s = np.zeros((R, NB, 12), np.int64)
+    for j in range(4):
+        s[..., j] = sc[..., j] | ((sc[..., j + 4] >> 4) << 6)
+        s[..., j + 4] = m[..., j] | ((m[..., j + 4] >> 4) << 6)
+        s[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    qs = np.zeros((R, NB, 128), np.int64)
+    for p in range(4):
+        qs[..., 32 * p:32 * p + 32] = q[..., 2 * p, :] | (q[..., 2 * p + 1, :] << 4)
+    out = np.concatenate([d16.astype(np.float16).view(np.uint8).reshape(R, NB, 2),
+                          dm16.astype(np.float16).view(np.uint8).reshape(R, NB, 2),
+                          s.astype(np.uint8), qs.astype(np.uint8)], axis=-1)
+    return np.ascontiguousarray(out.reshape(R, NB * Q4_K_BLOCK_BYTES))
+
+
+# The re-typing tool's fallback (Quantization page, "The rule"): a matrix
+# whose row length ne0 is not a multiple of a K-quant's 256 keeps to the
+# legacy type of the same width.
+K_QUANT_FALLBACK = {"q4_k": "q4_0", "q5_k": "q5_0", "q6_k": "q8_0"}
+
+
+def type_for(target: str, ne0: int) -> str:
+    """The type a block matrix of row length ne0 gets when `target` is asked for."""
+    if target in K_QUANT_FALLBACK and ne0 % QK_K:
+        return K_QUANT_FALLBACK[target]
+    return target
+
+
+def block_bytes_of(dtype: str) -> tuple[int, int]:
+    """(weights per block, bytes per block) of a block format."""
+    return {"q8_0": (32, Q8_0_BLOCK_BYTES), "q4_0": (32, Q4_0_BLOCK_BYTES),
+            "q4_k": (QK_K, Q4_K_BLOCK_BYTES), "q6_k": (QK_K, Q6_K_BLOCK_BYTES)}[dtype]
 
 
 def widen_half(bits: np.ndarray) -> np.ndarray:
@@ -126,6 +308,10 @@ def stored_to_f64(t: dict) -> np.ndarray:
         v = dequantize_q8_0(data, ne1, ne0).astype(np.float64)
     elif dt == "q4_0":
         v = dequantize_q4_0(data, ne1, ne0).astype(np.float64)
+    elif dt == "q4_k":
+        v = dequantize_q4_k(data, ne1, ne0).astype(np.float64)
+    elif dt == "q6_k":
+        v = dequantize_q6_k(data, ne1, ne0).astype(np.float64)
     else:
         raise ValueError(dt)
     return v.reshape(ne1, ne0) if ne1 > 1 else v.reshape(ne0)

@@ -630,6 +630,128 @@ def test_levjepa_file_sizes_and_counts():
 
 
 # ---------------------------------------------------------------------------
+# K-quants (q4_K, q6_K)
+# ---------------------------------------------------------------------------
+
+def test_q6_k_hand_worked_block():
+    """Every low byte 0x21 (low nibble 1, high 2), every high byte 0b11100100
+    (bit pairs 0, 1, 2, 3 from the bottom), d = 1, all scales 1.  By the
+    format, the four 32-weight runs t of each half take their low bits from
+    the low nibble (t = 0, 1) or high nibble (t = 2, 3) and their high bits
+    from bit pair t: codes 1, 1 + 16, 2 + 32, 2 + 48, i.e. weights -31, -15,
+    2, 18.  Then scales 1..16 (weight k uses scale k // 16) and d = 0.5."""
+    blk = np.zeros(210, np.uint8)
+    blk[:128] = 0x21
+    blk[128:192] = 0b11100100
+    blk[192:208] = 1
+    blk[208:210] = np.array([1.0], np.float16).view(np.uint8)
+    run = np.repeat([-31.0, -15.0, 2.0, 18.0], 32)
+    np.testing.assert_array_equal(Q.dequantize_q6_k(blk, 1, 256)[0], np.tile(run, 2))
+    blk[192:208] = np.arange(1, 17).astype(np.int8).view(np.uint8)
+    blk[208:210] = np.array([0.5], np.float16).view(np.uint8)
+    want = 0.5 * np.repeat(np.arange(1, 17), 16) * np.tile(run, 2)
+    np.testing.assert_array_equal(Q.dequantize_q6_k(blk, 1, 256)[0], want)
+    blk[192] = np.int8(-3).view(np.uint8)                   # a negative scale
+    assert Q.dequantize_q6_k(blk, 1, 256)[0][0] == 0.5 * -3 * -31
+
+
+def test_q4_k_hand_worked_block():
+    """Sub-block scales 1, 2, 3, 4, 17, 33, 49, 63 and mins 0, 1, 2, 3, 16,
+    32, 48, 63 packed by hand into the 12 bytes (the j >= 4 values split into
+    a low nibble in bytes 8-11 and two high bits in bytes 0-7), d = 1,
+    dmin = 0.5, every code byte 0x25 (low nibble 5 for the even sub-blocks,
+    high 2 for the odd ones): sub-block j weighs sc_j q - 0.5 m_j."""
+    blk = np.zeros(144, np.uint8)
+    blk[0:2] = np.array([1.0], np.float16).view(np.uint8)
+    blk[2:4] = np.array([0.5], np.float16).view(np.uint8)
+    blk[4:16] = [65, 130, 195, 196, 64, 129, 194, 195, 1, 1, 1, 255]
+    blk[16:144] = 0x25
+    sc, m = Q.q4_k_scale_min(blk[4:16])
+    assert list(sc) == [1, 2, 3, 4, 17, 33, 49, 63]
+    assert list(m) == [0, 1, 2, 3, 16, 32, 48, 63]
+    want = np.repeat([5.0, 3.5, 14.0, 6.5, 77.0, 50.0, 221.0, 94.5], 32)
+    np.testing.assert_array_equal(Q.dequantize_q4_k(blk, 1, 256)[0], want)
+
+
+@pytest.mark.parametrize("dt", ["q4_k", "q6_k"])
+def test_k_quant_round_trip_and_zero_block(dt):
+    """The oracle's encoders: codes within the format's ranges reproduce a
+    zero super-block exactly, and every other weight within one quantisation
+    step of the sub-block (q4_K: plus half a min step)."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    x[2, 256:] = 0.0
+    raw = Q.quantize(dt, x)
+    per, bb = Q.block_bytes_of(dt)
+    assert raw.shape == (6, 512 // per * bb)
+    w = Q.stored_to_f64(dict(dtype=dt, ne0=512, ne1=6, data=raw))
+    assert np.all(w[2, 256:] == 0.0)
+    blk = raw.reshape(-1, bb)
+    if dt == "q6_k":
+        d = blk[:, 208:210].copy().view(np.float16)[:, 0].astype(np.float64)
+        sc = blk[:, 192:208].view(np.int8).astype(np.float64)
+        step = np.repeat(d[:, None] * np.abs(sc), 16, axis=1)
+        slack = 0.0
+    else:
+        d = blk[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+        dmin = blk[:, 2:4].copy().view(np.float16)[:, 0].astype(np.float64)
+        sc, _ = Q.q4_k_scale_min(blk[:, 4:16])
+        step = np.repeat(d[:, None] * sc, 32, axis=1)
+        slack = np.repeat(dmin[:, None], 256, axis=1) / 2
+    err = np.abs(w.reshape(-1, 256) - x.astype(np.float64).reshape(-1, 256))
+    assert np.all(err <= step + slack + 1e-12)
+
+
+def test_k_quant_block_bytes_match_printed_sizes():
+    """q4_K: 144 bytes per 256 weights, the 4.5 bits per weight of q4_0; the
+    CLI's ffn_down [384,1536] -> q4_K 324.0 KiB."""
+    g = json.load(open(os.path.join(GOLDEN, "page_file_sizes.json")))
+    assert Q.quantize_q4_k(np.ones((1, 256), np.float32)).nbytes * 8 / 256 == g["bits_per_weight"]["q4_k"]
+    raw = Q.quantize_q4_k(np.ones((384, 1536), np.float32))
+    assert raw.nbytes / 1024 == g["vits_ffn_down_q4_k_kib"]
+
+
+def test_k_quant_fallback_rule():
+    """Quantization page, "The rule": K-quants need row lengths that are a
+    multiple of 256, else the legacy type of the same width; ViT-S's 384-wide
+    matrices fall back, its ffn_down (1536) does not, ViT-L (1024 / 4096)
+    never does."""
+    assert Q.type_for("q4_k", 384) == "q4_0" and Q.type_for("q6_k", 384) == "q8_0"
+    assert Q.type_for("q5_k", 384) == "q5_0"
+    assert Q.type_for("q4_k", 1536) == "q4_k" and Q.type_for("q6_k", 1536) == "q6_k"
+    assert all(Q.type_for(t, n) == t for t in ("q4_k", "q6_k") for n in (1024, 4096, 768, 3072, 1280, 5120))
+    assert Q.type_for("q8_0", 384) == "q8_0"
+
+
+def test_vits16_file_sizes_per_type():
+    """The LeJEPA ViT-S/16 file (224^2, CLS, pos table) at each type, with the
+    fallback rule: the f32 remainder and the q4_k tensor data to the byte, the
+    type counts, and the 'File sizes' row within its 0.1 MiB rounding."""
+    g = json.load(open(os.path.join(GOLDEN, "page_file_sizes.json")))
+    v = g["vits16"]
+    dims = synth._dims(**v["dims"])
+    totals, counts = {}, {}
+    for target in v["mib"]:
+        tot, n = 0, {}
+        for name, ne0, ne1 in synth.tensor_specs(dims):
+            if synth.is_block_matrix(name) and target != "f32":
+                t = Q.type_for(target, ne0)
+                b = ne0 * ne1 * 2 if t == "f16" else ne0 * ne1 // Q.block_bytes_of(t)[0] * Q.block_bytes_of(t)[1]
+            else:
+                t, b = "f32", ne0 * ne1 * 4
+            n[t.upper().replace("_K", "_K")] = n.get(t.upper(), 0) + 1
+            tot += b
+        totals[target], counts[target] = tot, n
+    rest = sum(ne0 * ne1 * 4 for name, ne0, ne1 in synth.tensor_specs(dims) if not synth.is_block_matrix(name))
+    assert rest == v["f32_remainder_bytes"]
+    assert totals["q4_k"] == v["q4_k_tensor_data_bytes"]
+    for t, mib in v["mib"].items():
+        assert abs(totals[t] / 2 ** 20 - mib) <= g["tolerance_mib"], t
+    for t, want in v["counts"].items():
+        assert counts[t] == want, (t, counts[t])
+
+
+# ---------------------------------------------------------------------------
 # metrics
 # ---------------------------------------------------------------------------
 
