@@ -11,9 +11,10 @@
  *     the CLS token as the feature; "Run it": the pooling modes and the
  *     single C header.
  *   - V-JEPA 2 ViT-L/16 SSv2 card, opening paragraph: tubelet 2.
- *   - jepa.cpp Quantization page, "The rule": the tensor names and which
- *     tensors may be stored as q8_0 / q4_0 blocks; "File sizes": 8.5 / 4.5
- *     bits per weight.
+ *   - jepa.cpp Quantization page, "The rule": the tensor names, which
+ *     tensors may be stored as q8_0 / q4_0 / q4_K / q6_K blocks, and the
+ *     K-quants' fallback for rows that are not a multiple of 256; "File
+ *     sizes": 8.5 / 4.5 bits per weight; "CLI": q4_K block sizes.
  *   - jepa.cpp benchmarks page, "What the milliseconds are": the per-call
  *     compute time and the resident model bytes the API reports.
  *
@@ -53,14 +54,29 @@ typedef enum {
     JEPA_E_OOM = -5,             /* device allocation failed or over the cap */
     JEPA_E_HIP = -6,             /* a HIP runtime call or launch failed */
     JEPA_E_UNSUPPORTED = -7,     /* valid but outside what the library implements */
-    JEPA_E_STATE = -8            /* e.g. pool before any encode */
+    JEPA_E_STATE = -8,           /* e.g. pool before any encode */
+    JEPA_E_FORMAT = -9           /* a model file is malformed or lacks a required key */
 } jepa_status;
 
 /* Storage dtypes.  Q8_0: blocks of 32 weights along a row, each an f16
  * scale d then 32 int8 codes (34 bytes), weight = d * q.  Q4_0: blocks of
  * 32, an f16 scale d then 16 bytes whose byte j holds code j in the low
- * nibble and code j + 16 in the high nibble (18 bytes), weight = d*(q-8). */
-typedef enum { JEPA_F32 = 0, JEPA_F16 = 1, JEPA_BF16 = 2, JEPA_Q8_0 = 3, JEPA_Q4_0 = 4 } jepa_dtype;
+ * nibble and code j + 16 in the high nibble (18 bytes), weight = d*(q-8).
+ * The K-quants (ggml's published layouts; 256 weights per super-block,
+ * eight sub-blocks of 32):
+ * Q4_K (144 bytes): f16 d, f16 dmin, 12 bytes of 6-bit sub-block scales
+ *   sc_j and mins m_j (j < 4: sc_j = s[j] & 63, m_j = s[j+4] & 63; j >= 4:
+ *   sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4, m_j = (s[j+4] >> 4) |
+ *   (s[j] >> 6) << 4), then 128 code bytes: bytes 32p..32p+31 hold
+ *   sub-block 2p in their low nibbles and 2p+1 in their high ones;
+ *   weight = d sc_j q - dmin m_j.
+ * Q6_K (210 bytes): 128 bytes of low 4 code bits, 64 bytes of high 2 bits,
+ *   16 int8 scales (one per 16 weights), f16 d.  Weight 128h + 32t + l
+ *   (h < 2, t < 4, l < 32) takes the low (t < 2) or high nibble of low byte
+ *   64h + 32(t%2) + l and bits 2t, 2t+1 of high byte 32h + l;
+ *   weight = d scale (q - 32). */
+typedef enum { JEPA_F32 = 0, JEPA_F16 = 1, JEPA_BF16 = 2, JEPA_Q8_0 = 3, JEPA_Q4_0 = 4, JEPA_Q4_K = 5,
+               JEPA_Q6_K = 6 } jepa_dtype;
 
 typedef enum { JEPA_MASK_BIDIR = 0, JEPA_MASK_BLOCK_CAUSAL = 1 } jepa_mask;
 
@@ -126,8 +142,10 @@ typedef struct {
  * A patch vector lists (dt, dy, dx, c) with c fastest; tokens are ordered
  * slot-major then raster; CLS is token 0 and owns pos row 0.
  * Only the attn_qkv / attn_q / attn_k / attn_v / attn_out / ffn_up /
- * ffn_down weights may be Q8_0/Q4_0 (ne0 % 32 == 0); the rest are F32, F16
- * or BF16. */
+ * ffn_down weights may take a block dtype (Q8_0 / Q4_0 with ne0 % 64 == 0,
+ * Q4_K / Q6_K with ne0 % 256 == 0, else JEPA_E_SHAPE: a writer stores such
+ * rows as Q4_0 / Q8_0 instead), and only with act_dtype F16 or BF16; the
+ * rest are F32, F16 or BF16. */
 typedef struct {
     const char *name;
     int32_t dtype;      /* jepa_dtype */
@@ -136,6 +154,56 @@ typedef struct {
     const void *data;   /* host pointer */
     size_t nbytes;
 } jepa_tensor;
+
+/* ---- GGUF model files ----
+ * The models travel as GGUF files that carry every dimension, the
+ * positional scheme and the preprocessing recipe (LeVJEPA card, opening
+ * paragraph), re-typed by the rule of the jepa.cpp Quantization page ("The
+ * rule"), whose general.file_type names the requested type even where a
+ * K-quant tensor fell back.
+ * Container read: GGUF version 2 or 3, little-endian; general.alignment
+ * (default 32).  Tensor types (ggml ids): f32 0, f16 1, q4_0 2, q8_0 8,
+ * q4_K 12, q6_K 14, bf16 30; the other ggml types are reported by name as
+ * JEPA_E_UNSUPPORTED.  A tensor's first dimension is its row length ne0,
+ * the product of the others its ne1; names and shapes as in jepa_tensor.
+ * Keys (this library's schema, the file's own model description):
+ *   general.architecture  string "jepa" (required)
+ *   jepa.dim, jepa.depth, jepa.heads, jepa.mlp_dim, jepa.patch, jepa.img_h,
+ *   jepa.img_w, jepa.has_cls   integers (required)
+ *   jepa.tubelet, jepa.frames  integers (default 1)
+ *   jepa.rope, jepa.head.blocks, jepa.head.classes  integers (default 0)
+ *   jepa.mask      string "bidirectional" (default) or "block_causal"
+ *   jepa.ln_eps    number (default 1e-6)
+ *   jepa.pre.mean, jepa.pre.std   arrays of 3 floats (required)
+ *   general.file_type   integer (optional, reported)
+ * Other keys are ignored.  Every offset and length is checked against the
+ * file's size before use: a malformed file returns JEPA_E_FORMAT (or
+ * JEPA_E_UNSUPPORTED for a valid file this library cannot run), never a
+ * crash. */
+typedef struct {
+    jepa_dims dims;        /* from the keys; act_dtype = JEPA_F32 */
+    int32_t version;
+    int32_t file_type;     /* general.file_type, -1 when absent */
+    int64_t n_tensors, n_kv;
+    int64_t alignment;
+    int64_t data_offset;   /* byte offset of the tensor data section */
+    int64_t tensor_bytes;  /* sum of the tensors' storage sizes */
+} jepa_gguf_info;
+
+/* Read a GGUF file's header, keys and tensor records (host only; touches
+ * no device). */
+jepa_status jepa_gguf_read_info(const char *path, jepa_gguf_info *info);
+
+/* jepa_create from a GGUF file, its tensors read from a read-only mapping
+ * of the file (unmapped before return).  act_dtype: JEPA_F32, JEPA_F16 or
+ * JEPA_BF16, or -1 for F32 when every tensor is f32, BF16 when the others
+ * are bf16, else F16. */
+jepa_status jepa_create_from_gguf(const char *path, int act_dtype, jepa_ctx **out);
+
+/* The type a general.file_type code names ("f32", "f16", "q4_0", "q4_1",
+ * "q8_0", "q5_0", "q5_1", "q4_k", "q5_k", "q6_k": the codes 0, 1, 2, 3, 7,
+ * 8, 9, 12, 13, 14 of the Quantization page, "The rule"), or NULL. */
+const char *jepa_file_type_name(int code);
 
 /* Per-kernel-class timing record (see jepa_set_profiling). */
 typedef struct {
@@ -178,7 +246,9 @@ jepa_status jepa_encode(jepa_ctx *ctx, const uint8_t *frames, int batch, int fra
  * hipMalloc, hipFree or other allocating call is made, and no timing events
  * are recorded.  frames: device uint8 [batch, frames, img_h, img_w, 3];
  * tokens_out: device f32 [batch, N, dim], required.  Q8_0 / Q4_0 matrices
- * are dequantised in the GEMM's tile load (no expanded copy).  A batch whose
+ * are dequantised in the GEMM's tile load (no expanded copy); a model with
+ * Q4_K / Q6_K matrices, which run from an expanded copy, is refused with
+ * JEPA_E_UNSUPPORTED.  A batch whose
  * buffers do not fit the array is refused with JEPA_E_OOM before anything
  * is enqueued: it serves small models (ViT-Ti/14 f32 needs about 6 MB per
  * image), not the ViT-L video batches, which need jepa_encode.
@@ -230,24 +300,28 @@ float jepa_last_compute_ms(jepa_ctx *ctx);
 jepa_status jepa_classify(jepa_ctx *ctx, float *logits_out, void *hip_stream);
 
 /* Bytes of tensor data as stored (the size the weight file's tensors would
- * take: blocks for Q8_0/Q4_0, 2 or 4 bytes per element otherwise). */
+ * take: 34 / 18 bytes per 32 weights for Q8_0 / Q4_0, 144 / 210 per 256 for
+ * Q4_K / Q6_K, 2 or 4 bytes per element otherwise). */
 size_t jepa_model_n_bytes(const jepa_ctx *ctx);
 
 /* Bytes of device memory the context holds for weights. */
 size_t jepa_device_weight_bytes(const jepa_ctx *ctx);
 
 /* Bytes of device workspace an encode of `batch` items needs (with the
- * current batch-part setting).  It includes, for a model with Q8_0 / Q4_0
- * block matrices and batch parts of 1024 or more token rows, an
- * activation-dtype copy of those matrices that each such encode rewrites
- * from the blocks before its first layer (the GEMMs then run dense);
- * smaller batches dequantise inside the GEMM and need no copy.  The
- * environment variable JEPA_Q_EXPAND = 0 or 1 forces either way. */
+ * current batch-part setting).  It includes, for a model with block
+ * matrices and batch parts of 1024 or more token rows, an activation-dtype
+ * copy of those matrices that each such encode rewrites from the blocks
+ * before its first layer (the GEMMs then run dense); smaller batches
+ * dequantise inside the GEMM and need no copy.  The environment variable
+ * JEPA_Q_EXPAND = 0 or 1 forces either way, except that a model with a
+ * Q4_K / Q6_K matrix always takes the copy. */
 size_t jepa_workspace_bytes(const jepa_ctx *ctx, int batch);
 
 /* Write the f32 value of every element of the named tensor, as the GEMMs
  * see it before rounding to act_dtype, into device memory out_dev
- * ([ne1, ne0] row-major).  For Q8_0/Q4_0 this is f32(d) * code, exact. */
+ * ([ne1, ne0] row-major).  For Q8_0/Q4_0 this is f32(d) * code, exact; for
+ * Q6_K d * scale * (q - 32), exact; for Q4_K the exact d sc q - dmin m
+ * rounded once to f32. */
 jepa_status jepa_dequant_tensor(jepa_ctx *ctx, const char *name, float *out_dev, void *hip_stream);
 
 /* Host quantizer: f32 [rows, cols] -> Q8_0 or Q4_0 blocks [rows, cols/32]

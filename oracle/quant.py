@@ -121,9 +121,9 @@ def dequantize_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
 #        byte 64 h + l + 32 (t % 2) and whose high 2 bits are bits 2t, 2t+1
 #        of high byte 32 h + l; its scale is scales[k // 16].
 #        w = d scales[k // 16] (code - 32).
-# Dequantised values are the exact results rounded once to f32: every
-# product above is exact in f32 but d scales[.] (code - 32) of q6_K, and
-# q4_K's subtraction.
+# Dequantised values are the exact results rounded once to f32.  (Every
+# product above has at most 24 significant bits -- an f16 significand of 11
+# bits times 6- to 8-bit integers -- so only q4_K's subtraction rounds.)
 # ---------------------------------------------------------------------------
 QK_K = 256
 Q4_K_BLOCK_BYTES = 144

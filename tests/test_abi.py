@@ -109,6 +109,55 @@ def test_create_rejects_block_format_outside_the_rule(lib):
     _expect_error(lib, "JEPA_E_DTYPE", dims, bad)
 
 
+def _retyped(dims, target):
+    """The small weight set with every block matrix of row length ne0 stored
+    as `target` regardless of the fallback (zero bytes of the right size)."""
+    stored = []
+    for name, ne0, ne1 in synth.tensor_specs(dims):
+        if synth.is_block_matrix(name):
+            per, nb = Q.block_bytes_of(target)
+            data = np.zeros(ne0 * ne1 // per * nb, np.uint8)
+            stored.append(dict(name=name, dtype=target, ne0=ne0, ne1=ne1, data=data))
+        else:
+            stored.append(dict(name=name, dtype="f32", ne0=ne0, ne1=ne1, data=np.zeros(ne0 * ne1, np.float32)))
+    return stored
+
+
+@pytest.mark.parametrize("dt", ["q4_k", "q6_k"])
+def test_create_rejects_k_quant_rows_not_a_multiple_of_256(lib, dt):
+    """Quantization page, "The rule": a K-quant needs rows of a multiple of
+    256 (D = 192 here); such rows must be stored as q4_0 / q8_0."""
+    dims, _ = _small()
+    msg = _expect_error(lib, "JEPA_E_SHAPE", dict(dims, act_dtype="f16"), _retyped(dims, dt))
+    assert "256" in msg
+
+
+def test_create_rejects_k_quant_outside_the_rule_and_on_f32(lib):
+    dims = synth.workload("small_q4_k_dh32_cls_bf16")["dims"]
+    w32 = synth.make_f32_weights(dims, 3)
+    stored = synth.stored_weights(dims, w32, quantize=Q.quantize)
+    bad = [dict(t) for t in stored]
+    for t in bad:
+        if t["name"] == "enc.norm.weight":          # a vector
+            t["dtype"] = "q4_k"
+            t["data"] = Q.quantize("q4_k", np.ones((1, t["ne0"]), np.float32))
+    _expect_error(lib, "JEPA_E_DTYPE", dims, bad)
+    _expect_error(lib, "JEPA_E_UNSUPPORTED", dict(dims, act_dtype="f32"),
+                  synth.stored_weights(dict(dims, rest_dtype="f32"), w32, quantize=Q.quantize))
+
+
+@pytest.mark.parametrize("name", [n for n, w in synth.SMALL_WORKLOADS.items()
+                                  if w["dims"]["mat_dtype"] in ("q4_k", "q6_k")]
+                         + ["mid_vitl_q4_k"])
+def test_synthetic_k_quant_sets_follow_the_fallback(name):
+    """The stored types the workloads hand to both sides are the oracle's
+    choice under the fallback rule, and the sizes its block formats give."""
+    dims = synth.workload(name)["dims"]
+    for tname, ne0, ne1 in synth.tensor_specs(dims):
+        if synth.is_block_matrix(tname):
+            assert synth.storage_dtype(dims, tname, ne0) == Q.type_for(dims["mat_dtype"], ne0), tname
+
+
 def test_create_rejects_unknown_and_duplicate_names(lib):
     dims, stored = _small()
     _expect_error(lib, "JEPA_E_INVALID_ARG", dims, stored + [dict(stored[0], name="enc.bogus")])

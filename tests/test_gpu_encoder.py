@@ -18,6 +18,7 @@ import pytest
 
 from oracle import encoder as E
 from oracle import quant as Q
+from tests import gguf_file as G
 from tests import helpers as H
 from vision_transformer_amd import synth
 
@@ -91,7 +92,7 @@ def test_mid_vitl_every_token(Encoder, name, monkeypatch):
     enc = Encoder(dims, stored)
     _lib.jepa_set_batch_parts(enc.ctx, 1)
     if dims["mat_dtype"] in ("q8_0", "q4_0"):
-        monkeypatch.setenv("JEPA_Q_EXPAND", "1")
+        monkeypatch.setenv("JEPA_Q_EXPAND", "1")     # (K-quants always expand)
     y = _run(enc, frames)
     H.check_rows(dims["act_dtype"], y.cpu().numpy(), ref, "tokens")
     _check_pools(enc, dims, ref, wl["batch"])
@@ -312,7 +313,8 @@ def test_expansion_chosen_by_rows_per_part(Encoder, monkeypatch):
     enc.close()
 
 
-@pytest.mark.parametrize("name", ["small_head_bf16", "small_head_cls_q8_0", "small_head_dh32_f32"])
+@pytest.mark.parametrize("name", ["small_head_bf16", "small_head_cls_q8_0", "small_head_dh32_f32",
+                                  "small_q4_k_fallback_head_bf16"])
 def test_classifier_head_scores(Encoder, name):
     """The attentive-pool head on the encoder's token map: class scores of
     every item against the oracle (its blocks, cross-attention query, MLP and
@@ -422,7 +424,8 @@ def test_host_frames_match_device_frames(Encoder):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["small_tubelet2_q8_0", "small_tubelet2_q4_0", "small_bidir_f32",
-                                  "small_blockcausal_bf16"])
+                                  "small_blockcausal_bf16", "small_q4_k_fallback_head_bf16",
+                                  "small_q6_k_rope_blockcausal_f16", "small_q4_k_dh32_cls_bf16"])
 def test_dequantised_weights_bit_exact(Encoder, name):
     wl, dims, frames, stored = H.workload_inputs(name)
     enc = Encoder(dims, stored)
@@ -456,6 +459,66 @@ def test_model_bytes_of_a_levjepa_shaped_q8_0_set(Encoder):
     mib = (_lib.jepa_model_n_bytes(enc.ctx) - pos) / 2 ** 20
     H.say(f"  LeVJEPA-shaped q8_0 model bytes without pos: {mib:.2f} MiB")
     assert abs(mib - pages["levjepa_vitl16_mib"]["q8_0"]) <= pages["tolerance_mib"]
+    enc.close()
+
+
+def test_model_bytes_of_a_vits16_q4_k_set(Encoder):
+    """jepa_model_n_bytes of a ViT-S/16 weight set re-typed to q4_K (the
+    rows of 384 fall back to q4_0, the 1536-long ffn_down rows stay q4_K)
+    with an f32 remainder: the Quantization page's tensor counts per type
+    and the tensor-data total they give with the block sizes."""
+    import json
+    pages = json.load(open(os.path.join(H.GOLDEN, "page_file_sizes.json")))
+    v = pages["vits16"]
+    from vision_transformer_amd import _lib
+    dims = synth._dims(dim=384, depth=12, heads=6, mlp_dim=1536, patch=16, img_h=224,
+                       img_w=224, act_dtype="f16", mat_dtype="q4_k", rest_dtype="f32")
+    stored, kinds = [], {}
+    for name, ne0, ne1 in synth.tensor_specs(dims):
+        dt = synth.storage_dtype(dims, name, ne0)
+        kinds[dt] = kinds.get(dt, 0) + 1
+        data = np.zeros(Q.block_bytes_of(dt)[1] * (ne0 * ne1 // Q.block_bytes_of(dt)[0]), np.uint8) \
+            if dt in ("q4_0", "q4_k") else np.zeros(ne0 * ne1, np.float32)
+        stored.append(dict(name=name, dtype=dt, ne0=ne0, ne1=ne1, data=data))
+    assert kinds["q4_k"] == 12 and kinds["q4_0"] == 36
+    enc = Encoder(dims, stored)
+    got = _lib.jepa_model_n_bytes(enc.ctx)    # (the page's f32 remainder includes the pos table)
+    H.say(f"  ViT-S/16 q4_K set: {got} bytes")
+    assert got == v["q4_k_tensor_data_bytes"]
+    enc.close()
+
+
+@pytest.mark.parametrize("name", ["small_q4_k_fallback_head_bf16", "small_q6_k_rope_blockcausal_f16",
+                                  "small_tubelet2_q8_0", "small_bidir_f32"])
+def test_gguf_file_runs_as_the_in_memory_set(Encoder, name, tmp_path):
+    """A weight set written as a GGUF file and read back by
+    jepa_create_from_gguf encodes (and classifies) bit for bit as the same
+    set given to jepa_create; the model bytes agree with the file's."""
+    from vision_transformer_amd import _lib
+    H.say(f"gguf {name}")
+    wl, dims, frames, stored = H.workload_inputs(name)
+    path = str(tmp_path / f"{name}.gguf")
+    G.write(path, dims, stored, file_type=G.file_type_codes().get(dims["mat_dtype"]), alignment=64)
+    info = _lib.jepa_gguf_read_info(path)
+    a = Encoder(dims, stored)
+    b = Encoder.from_gguf(path, dims["act_dtype"])
+    assert _lib.jepa_model_n_bytes(b.ctx) == _lib.jepa_model_n_bytes(a.ctx) == info["tensor_bytes"]
+    ya = _run(a, frames)
+    yb = _run(b, frames)
+    assert torch.equal(ya, yb)
+    if dims["head_classes"]:
+        assert torch.equal(a.classify(), b.classify())
+    a.close()
+    b.close()
+
+
+def test_k_quant_model_refused_by_noalloc(Encoder):
+    from vision_transformer_amd import _lib
+    wl, dims, frames, stored = H.workload_inputs("small_q4_k_dh32_cls_bf16")
+    enc = Encoder(dims, stored)
+    out = torch.empty((1, synth.n_tokens(dims), dims["dim"]), device="cuda")
+    with pytest.raises(_lib.JepaError, match="JEPA_E_UNSUPPORTED"):
+        _lib.jepa_encode_noalloc(enc.ctx, torch.from_numpy(frames[:1]).cuda(), 1, out)
     enc.close()
 
 

@@ -15,13 +15,13 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libjepa_mi355x.so")
 
-F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
-DTYPE = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0}
+F32, F16, BF16, Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3, 4, 5, 6
+DTYPE = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}
 MASK = {"bidir": 0, "block_causal": 1}
 POOL = {"none": 0, "cls": 1, "mean": 2}
 STATUS = {0: "JEPA_OK", -1: "JEPA_E_INVALID_ARG", -2: "JEPA_E_SHAPE", -3: "JEPA_E_DTYPE",
           -4: "JEPA_E_MISSING_TENSOR", -5: "JEPA_E_OOM", -6: "JEPA_E_HIP",
-          -7: "JEPA_E_UNSUPPORTED", -8: "JEPA_E_STATE"}
+          -7: "JEPA_E_UNSUPPORTED", -8: "JEPA_E_STATE", -9: "JEPA_E_FORMAT"}
 
 
 class JepaError(RuntimeError):
@@ -42,6 +42,12 @@ class jepa_dims(C.Structure):
 class jepa_tensor(C.Structure):
     _fields_ = [("name", C.c_char_p), ("dtype", C.c_int32), ("ne0", C.c_int64),
                 ("ne1", C.c_int64), ("data", C.c_void_p), ("nbytes", C.c_size_t)]
+
+
+class jepa_gguf_info(C.Structure):
+    _fields_ = [("dims", jepa_dims), ("version", C.c_int32), ("file_type", C.c_int32),
+                ("n_tensors", C.c_int64), ("n_kv", C.c_int64), ("alignment", C.c_int64),
+                ("data_offset", C.c_int64), ("tensor_bytes", C.c_int64)]
 
 
 class jepa_kernel_stat(C.Structure):
@@ -81,6 +87,9 @@ def _load():
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
         "jepa_op_mfma_probe": (I, [I, I, P, P]),
+        "jepa_gguf_read_info": (I, [C.c_char_p, C.POINTER(jepa_gguf_info)]),
+        "jepa_create_from_gguf": (I, [C.c_char_p, I, C.POINTER(P)]),
+        "jepa_file_type_name": (C.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -94,7 +103,7 @@ _lib = _load()
 
 def _check(status: int):
     if status != 0:
-        raise JepaError(status, _lib.jepa_last_error().decode())
+        raise JepaError(status, _lib.jepa_last_error().decode(errors="replace"))
 
 
 def _ptr(x) -> int | None:
@@ -140,6 +149,37 @@ def jepa_create(dims: dict, tensors: list[dict]) -> int:
     d = make_dims(dims)
     _check(_lib.jepa_create(C.byref(d), arr, len(tensors), C.byref(ctx)))
     return ctx.value
+
+
+def dims_to_dict(d: jepa_dims) -> dict:
+    inv_mask = {v: k for k, v in MASK.items()}
+    inv_dt = {v: k for k, v in DTYPE.items()}
+    return dict(dim=d.dim, depth=d.depth, heads=d.heads, mlp_dim=d.mlp_dim, patch=d.patch,
+                tubelet=d.tubelet, img_h=d.img_h, img_w=d.img_w, frames=d.frames,
+                has_cls=d.has_cls, mask=inv_mask.get(d.mask, d.mask),
+                act_dtype=inv_dt.get(d.act_dtype, d.act_dtype), ln_eps=d.ln_eps,
+                mean=tuple(d.mean), std=tuple(d.std), rope=d.rope, head_blocks=d.head_blocks,
+                head_classes=d.head_classes)
+
+
+def jepa_gguf_read_info(path: str) -> dict:
+    info = jepa_gguf_info()
+    _check(_lib.jepa_gguf_read_info(os.fsencode(path), C.byref(info)))
+    return dict(dims=dims_to_dict(info.dims), version=info.version, file_type=info.file_type,
+                n_tensors=info.n_tensors, n_kv=info.n_kv, alignment=info.alignment,
+                data_offset=info.data_offset, tensor_bytes=info.tensor_bytes)
+
+
+def jepa_create_from_gguf(path: str, act_dtype: str | None = None) -> int:
+    ctx = C.c_void_p()
+    _check(_lib.jepa_create_from_gguf(os.fsencode(path), -1 if act_dtype is None else DTYPE[act_dtype],
+                                      C.byref(ctx)))
+    return ctx.value
+
+
+def jepa_file_type_name(code: int) -> str | None:
+    r = _lib.jepa_file_type_name(code)
+    return r.decode() if r is not None else None
 
 
 def jepa_encode(ctx: int, frames, batch: int, tokens_out=None, stream=None) -> None:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjepa_mi355x.so")
-SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "api.hip"]
+SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "api.hip", "gguf.cpp"]
 ARCH = "gfx950"
 
 

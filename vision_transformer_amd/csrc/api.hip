@@ -16,15 +16,17 @@
 
 #include "../../include/jepa_mi355x.h"
 #include "../../include/jepa_mi355x_ops.h"
+#include "host.hpp"
 #include "kernels.hpp"
 
 using namespace jepa;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-jepa_status fail(jepa_status st, const char *fmt, ...) {
+// the message jepa_last_error returns (host.hpp)
+jepa_status jepa::fail(jepa_status st, const char *fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -33,6 +35,8 @@ jepa_status fail(jepa_status st, const char *fmt, ...) {
     g_err = buf;
     return st;
 }
+
+namespace {
 
 #define HIP_TRY(expr)                                                                      \
     do {                                                                                   \
@@ -99,9 +103,14 @@ size_t storage_bytes(int dt, int64_t n) {
         case JEPA_BF16: return (size_t)n * 2;
         case JEPA_Q8_0: return (size_t)(n / 32) * 34;
         case JEPA_Q4_0: return (size_t)(n / 32) * 18;
+        case JEPA_Q4_K: return (size_t)(n / 256) * 144;
+        case JEPA_Q6_K: return (size_t)(n / 256) * 210;
     }
     return 0;
 }
+
+bool is_block_dt(int dt) { return dt == JEPA_Q8_0 || dt == JEPA_Q4_0 || dt == JEPA_Q4_K || dt == JEPA_Q6_K; }
+bool is_kquant_dt(int dt) { return dt == JEPA_Q4_K || dt == JEPA_Q6_K; }
 
 float stored_to_f32(int dt, const void *data, int64_t i) {
     switch (dt) {
@@ -120,14 +129,15 @@ enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_TRANSPOS
 
 struct DevTensor {
     void *ptr = nullptr;        // device data
-    uint16_t *scale = nullptr;  // q formats: f16 scales
+    uint16_t *scale = nullptr;  // block formats: f16 scales (K-quants: per super-block)
+    const uint8_t *sub = nullptr;   // K-quants: the sub-block scale bytes
     int dev_dt = 0;             // device dtype
     int64_t ne0 = 0, ne1 = 0;
 };
 
 struct Layer {
     DevTensor qkv, out, up, down;
-    DevTensor xqkv, xout, xup, xdown;   // q8_0 / q4_0 ones expanded to the act dtype (when in use)
+    DevTensor xqkv, xout, xup, xdown;   // block-format ones expanded to the act dtype (when in use)
     float *ln1g, *ln1b, *ln2g, *ln2b, *bqkv, *bout, *bup, *bdown;
 };
 
@@ -138,6 +148,7 @@ struct Head {
     int C = 0, Cpad = 0;
     float *q0 = nullptr, *ln1g = nullptr, *ln1b = nullptr, *ln2g = nullptr, *ln2b = nullptr;
     DevTensor wq, wk, wv, wo, wup, wdown, wc;
+    DevTensor xwq, xwk, xwv, xwo, xwup, xwdown;   // block-format ones expanded (when in use)
     float *bq = nullptr, *bk = nullptr, *bv = nullptr, *bo = nullptr, *bup = nullptr, *bdown = nullptr,
           *bc = nullptr;
 };
@@ -170,8 +181,9 @@ struct jepa_ctx {
     DevTensor wpe;
     float *bpe = nullptr, *cls = nullptr, *pos = nullptr, *normg = nullptr, *normb = nullptr;
     float *rope = nullptr;      // 3-D rotary table [N, 32] (cos, sin), or null
-    // q8_0 / q4_0 block matrices expanded to the act dtype for large batches
-    bool has_q = false;
+    // block-format matrices expanded to the act dtype for large batches (and
+    // always when a K-quant matrix is present)
+    bool has_q = false, has_k = false;
     void *xbuf = nullptr;       // expansion jobs, then the expanded matrices
     size_t xbuf_bytes = 0;
     const ExpandJob *xjobs = nullptr;
@@ -253,43 +265,46 @@ WsLayout ws_layout(const jepa_ctx *c, int B, bool with_frames = true) {
     return w;
 }
 
-// Large batches run the q8_0 / q4_0 layers as dense GEMMs on an act-dtype copy
-// of the block matrices, expanded once per encode (a bandwidth-bound pass:
-// 1 + 1/16 bytes read and 2 written per weight for q8_0).  Above ~1024 rows
-// per batch part the GEMMs take the 256-row MFMA tiles, whose operands flow
-// straight from memory into LDS; a dequantising load would put the
+// Large batches run the block-format layers as dense GEMMs on an act-dtype
+// copy of the block matrices, expanded once per encode (a bandwidth-bound
+// pass: 1 + 1/16 bytes read and 2 written per weight for q8_0).  Above ~1024
+// rows per batch part the GEMMs take the 256-row MFMA tiles, whose operands
+// flow straight from memory into LDS; a dequantising load would put the
 // conversion on the VALU inside the K loop, and an int8 MFMA path with
 // per-block rescaling is VALU-bound on this chip.  Small batches keep the
-// dequantising 128 x 128 tile.  JEPA_Q_EXPAND = 0 / 1 forces either.
-// the encoder's blocks and the classifier head's (which run over every token)
-std::vector<Layer *> all_blocks(jepa_ctx *c) {
-    std::vector<Layer *> v;
-    for (auto &L : c->layers) v.push_back(&L);
-    for (auto &L : c->head_layers) v.push_back(&L);
-    return v;
-}
-
-std::vector<DevTensor *> q_matrices(jepa_ctx *c) {
-    std::vector<DevTensor *> v;
-    for (Layer *L : all_blocks(c))
-        for (DevTensor *t : {&L->qkv, &L->out, &L->up, &L->down})
-            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) v.push_back(t);
+// dequantising 128 x 128 tile for q8_0 / q4_0; the K-quants (whose 256-weight
+// super-blocks straddle that tile's 64-wide K steps) are always expanded.
+// JEPA_Q_EXPAND = 0 / 1 forces either for models without K-quants.
+// Every (block matrix, its expanded copy) pair: the encoder's blocks, the
+// classifier head's blocks and its cross-attention matrices.
+std::vector<std::pair<DevTensor *, DevTensor *>> expand_pairs(jepa_ctx *c) {
+    std::vector<std::pair<DevTensor *, DevTensor *>> v;
+    auto add = [&](DevTensor &t, DevTensor &x) { v.emplace_back(&t, &x); };
+    for (auto *Ls : {&c->layers, &c->head_layers})
+        for (Layer &L : *Ls) {
+            add(L.qkv, L.xqkv); add(L.out, L.xout); add(L.up, L.xup); add(L.down, L.xdown);
+        }
+    if (c->head.C > 0) {
+        Head &h = c->head;
+        add(h.wq, h.xwq); add(h.wk, h.xwk); add(h.wv, h.xwv); add(h.wo, h.xwo);
+        add(h.wup, h.xwup); add(h.wdown, h.xwdown);
+    }
     return v;
 }
 
 size_t expand_bytes(const jepa_ctx *c) {
     size_t n = 0, jobs = 0;
-    for (Layer *L : all_blocks(const_cast<jepa_ctx *>(c)))
-        for (const DevTensor *t : {&L->qkv, &L->out, &L->up, &L->down})
-            if (t->dev_dt == JEPA_Q8_0 || t->dev_dt == JEPA_Q4_0) {
-                n += align256((size_t)t->ne0 * t->ne1 * c->es);
-                ++jobs;
-            }
+    for (auto &pr : expand_pairs(const_cast<jepa_ctx *>(c)))
+        if (is_block_dt(pr.first->dev_dt)) {
+            n += align256((size_t)pr.first->ne0 * pr.first->ne1 * c->es);
+            ++jobs;
+        }
     return jobs ? align256(jobs * sizeof(ExpandJob)) + n : 0;
 }
 
 bool use_expand(const jepa_ctx *c, int batch, int parts) {
     if (!c->has_q) return false;
+    if (c->has_k) return true;
     if (const char *e = getenv("JEPA_Q_EXPAND")) {
         if (!strcmp(e, "0")) return false;
         if (!strcmp(e, "1")) return true;
@@ -305,26 +320,25 @@ jepa_status ensure_expanded(jepa_ctx *c) {
         (void)hipGetLastError();
         return fail(JEPA_E_OOM, "hipMalloc of %zu bytes for the expanded block matrices failed", bytes);
     }
-    auto mats = q_matrices(c);
+    const auto pairs = expand_pairs(c);
+    size_t n_jobs = 0;
+    for (auto &pr : pairs) n_jobs += is_block_dt(pr.first->dev_dt);
     unsigned char *base = (unsigned char *)c->xbuf;
-    size_t off = align256(mats.size() * sizeof(ExpandJob));
+    size_t off = align256(n_jobs * sizeof(ExpandJob));
     std::vector<ExpandJob> jobs;
     int64_t blk = 0;
-    for (Layer *Lp : all_blocks(c)) {
-        Layer &L = *Lp;
-        for (auto pr : {std::make_pair(&L.qkv, &L.xqkv), std::make_pair(&L.out, &L.xout),
-                        std::make_pair(&L.up, &L.xup), std::make_pair(&L.down, &L.xdown)}) {
-            const DevTensor &t = *pr.first;
-            DevTensor &x = *pr.second;
-            x = t;
-            if (t.dev_dt != JEPA_Q8_0 && t.dev_dt != JEPA_Q4_0) continue;
-            x.dev_dt = c->act;
-            x.scale = nullptr;
-            x.ptr = base + off;
-            jobs.push_back(ExpandJob{t.ptr, t.scale, x.ptr, blk, t.dev_dt});
-            blk += t.ne0 * t.ne1 / 32;
-            off += align256((size_t)t.ne0 * t.ne1 * c->es);
-        }
+    for (auto &pr : pairs) {
+        const DevTensor &t = *pr.first;
+        DevTensor &x = *pr.second;
+        x = t;
+        if (!is_block_dt(t.dev_dt)) continue;
+        x.dev_dt = c->act;
+        x.scale = nullptr;
+        x.sub = nullptr;
+        x.ptr = base + off;
+        jobs.push_back(ExpandJob{t.ptr, t.scale, t.sub, x.ptr, blk, t.dev_dt});
+        blk += t.ne0 * t.ne1 / 32;
+        off += align256((size_t)t.ne0 * t.ne1 * c->es);
     }
     if (hipMemcpy(c->xbuf, jobs.data(), jobs.size() * sizeof(ExpandJob), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(c->xbuf);
@@ -498,6 +512,27 @@ void pack_blocks(int dt, const unsigned char *src, int64_t nb, unsigned char *co
     }
 }
 
+// K-quant super-blocks as stored -> codes, f16 scales, sub-block scale bytes
+// (the device layout; no value changes).  q4_K (144 bytes): d, dmin, 12
+// scale bytes, 128 code bytes.  q6_K (210 bytes): 128 low-bit and 64
+// high-bit code bytes, 16 int8 scales, d.
+void pack_superblocks(int dt, const unsigned char *src, int64_t nsb, unsigned char *codes, uint16_t *scales,
+                      unsigned char *sub) {
+    for (int64_t i = 0; i < nsb; ++i) {
+        if (dt == JEPA_Q4_K) {
+            const unsigned char *b = src + i * 144;
+            memcpy(scales + 2 * i, b, 4);
+            memcpy(sub + i * 12, b + 4, 12);
+            memcpy(codes + i * 128, b + 16, 128);
+        } else {
+            const unsigned char *b = src + i * 210;
+            memcpy(codes + i * 192, b, 192);
+            memcpy(sub + i * 16, b + 192, 16);
+            memcpy(scales + i, b + 208, 2);
+        }
+    }
+}
+
 struct Expect {
     int64_t ne0, ne1;
     bool matrix;      // may be re-typed to a block format
@@ -646,13 +681,16 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         if (t.ne0 != e.ne0 || t.ne1 != e.ne1)
             return fail(JEPA_E_SHAPE, "create: '%s' is [%lld, %lld], expected [%lld, %lld]", t.name,
                         (long long)t.ne0, (long long)t.ne1, (long long)e.ne0, (long long)e.ne1);
-        if (t.dtype < JEPA_F32 || t.dtype > JEPA_Q4_0)
+        if (t.dtype < JEPA_F32 || t.dtype > JEPA_Q6_K)
             return fail(JEPA_E_DTYPE, "create: '%s' has unknown dtype %d", t.name, t.dtype);
-        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && !e.matrix)
+        if (is_block_dt(t.dtype) && !e.matrix)
             return fail(JEPA_E_DTYPE, "create: '%s' must keep a dense dtype (only the block matrices may be re-typed)", t.name);
-        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && (t.ne0 % 64))
+        if (is_block_dt(t.dtype) && (t.ne0 % 64))
             return fail(JEPA_E_SHAPE, "create: '%s' row length %lld not a multiple of 64 for block formats", t.name, (long long)t.ne0);
-        if ((t.dtype == JEPA_Q8_0 || t.dtype == JEPA_Q4_0) && d.act_dtype == JEPA_F32)
+        if (is_kquant_dt(t.dtype) && (t.ne0 % 256))
+            return fail(JEPA_E_SHAPE, "create: '%s' row length %lld not a multiple of 256 for a K-quant (such rows "
+                        "take q4_0 / q8_0 instead)", t.name, (long long)t.ne0);
+        if (is_block_dt(t.dtype) && d.act_dtype == JEPA_F32)
             return fail(JEPA_E_UNSUPPORTED, "create: block-format '%s' needs act_dtype F16 or BF16", t.name);
         const size_t nb = storage_bytes(t.dtype, t.ne0 * t.ne1);
         if (t.nbytes != nb)
@@ -678,15 +716,27 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
 
     // device layout of every tensor: block matrices keep their format (codes
     // then scales); other matrices take the act dtype; vectors become f32.
-    struct Plan { std::string name; const jepa_tensor *t; int dev_dt; size_t off, scale_off, bytes; };
+    struct Plan { std::string name; const jepa_tensor *t; int dev_dt; size_t off, scale_off, sub_off, bytes; };
     std::vector<Plan> plan;
     size_t off = 0;
     for (auto &kv : want) {
         const jepa_tensor *t = kv.second.t;
-        Plan p{kv.first, t, 0, 0, 0, 0};
+        Plan p{kv.first, t, 0, 0, 0, 0, 0};
         // vectors and the pos table are consumed in f32 by the epilogues
         const bool vec = t->ne1 == 1 || kv.first == "enc.pos_embed";
-        if (t->dtype == JEPA_Q8_0 || t->dtype == JEPA_Q4_0) {
+        if (is_kquant_dt(t->dtype)) {
+            // codes, then f16 scales, then the sub-block scale bytes
+            const bool q4 = t->dtype == JEPA_Q4_K;
+            const size_t nsb = (size_t)t->ne0 * t->ne1 / 256;
+            p.dev_dt = t->dtype;
+            p.off = off;
+            p.bytes = nsb * (q4 ? 128 : 192);
+            off += align256(p.bytes);
+            p.scale_off = off;
+            off += align256(nsb * (q4 ? 4 : 2));
+            p.sub_off = off;
+            off += align256(nsb * (q4 ? 12 : 16));
+        } else if (t->dtype == JEPA_Q8_0 || t->dtype == JEPA_Q4_0) {
             p.dev_dt = t->dtype;
             p.off = off;
             const size_t codes = t->dtype == JEPA_Q8_0 ? (size_t)t->ne0 * t->ne1 : (size_t)t->ne0 * t->ne1 / 2;
@@ -739,7 +789,22 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         dt.ne1 = t->ne1;
         dt.ptr = arena + p.off;
         const int64_t n = t->ne0 * t->ne1;
-        if (p.dev_dt == JEPA_Q8_0 || p.dev_dt == JEPA_Q4_0) {
+        if (is_kquant_dt(p.dev_dt)) {
+            const bool q4 = p.dev_dt == JEPA_Q4_K;
+            const int64_t nsb = n / 256;
+            const size_t sbytes = nsb * (q4 ? 4 : 2), ubytes = nsb * (q4 ? 12 : 16);
+            host.assign(p.bytes + sbytes + ubytes, 0);
+            pack_superblocks(p.dev_dt, (const unsigned char *)t->data, nsb, host.data(),
+                             (uint16_t *)(host.data() + p.bytes), host.data() + p.bytes + sbytes);
+            dt.scale = (uint16_t *)(arena + p.scale_off);
+            dt.sub = arena + p.sub_off;
+            if (hipMemcpy(dt.ptr, host.data(), p.bytes, hipMemcpyHostToDevice) != hipSuccess ||
+                hipMemcpy(dt.scale, host.data() + p.bytes, sbytes, hipMemcpyHostToDevice) != hipSuccess ||
+                hipMemcpy((void *)dt.sub, host.data() + p.bytes + sbytes, ubytes, hipMemcpyHostToDevice) != hipSuccess) {
+                jepa_free(c);
+                return fail(JEPA_E_HIP, "create: upload of '%s' failed", p.name.c_str());
+            }
+        } else if (p.dev_dt == JEPA_Q8_0 || p.dev_dt == JEPA_Q4_0) {
             // repack [rows][blocks](scale, payload) into codes then scales
             const int64_t nb = n / 32;
             host.assign(p.bytes + nb * 2, 0);
@@ -788,8 +853,7 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     c->normb = vecp("enc.norm.bias");
     c->layers.resize(d.depth);
     c->head_layers.resize(C > 0 ? d.head_blocks : 0);
-    c->has_q = false;
-    auto is_q = [](const DevTensor &t) { return t.dev_dt == JEPA_Q8_0 || t.dev_dt == JEPA_Q4_0; };
+    c->has_q = c->has_k = false;
     auto setup_layer = [&](Layer &L, const std::string &p) {
         L.qkv = c->by_name[p + "attn_qkv.weight"];
         L.out = c->by_name[p + "attn_out.weight"];
@@ -799,8 +863,6 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         L.ln2g = vecp(p + "ln2.weight"); L.ln2b = vecp(p + "ln2.bias");
         L.bqkv = vecp(p + "attn_qkv.bias"); L.bout = vecp(p + "attn_out.bias");
         L.bup = vecp(p + "ffn_up.bias"); L.bdown = vecp(p + "ffn_down.bias");
-        for (const DevTensor *t : {&L.qkv, &L.out, &L.up, &L.down})
-            if (is_q(*t)) c->has_q = true;
     };
     for (int i = 0; i < d.depth; ++i) setup_layer(c->layers[i], "enc.blk." + std::to_string(i) + ".");
     for (size_t i = 0; i < c->head_layers.size(); ++i) setup_layer(c->head_layers[i], "head.blk." + std::to_string(i) + ".");
@@ -819,6 +881,10 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
         h.wdown = c->by_name[p + "ffn_down.weight"]; h.bdown = vecp(p + "ffn_down.bias");
         h.wc = c->by_name["head.classifier.weight"]; h.bc = vecp("head.classifier.bias");
         h.wc.ne1 = Cpad;   // the GEMM runs over the padded rows
+    }
+    for (auto &pr : expand_pairs(c)) {
+        c->has_q |= is_block_dt(pr.first->dev_dt);
+        c->has_k |= is_kquant_dt(pr.first->dev_dt);
     }
     if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
         jepa_free(c);
@@ -1007,6 +1073,9 @@ jepa_status jepa_encode_noalloc(jepa_ctx *c, const uint8_t *frames, int batch, f
                                 void *hip_stream) {
     TRY(check_encode_args(c, frames, batch));
     if (!tokens_out) return fail(JEPA_E_INVALID_ARG, "encode_noalloc: tokens_out is required");
+    if (c->has_k)
+        return fail(JEPA_E_UNSUPPORTED, "encode_noalloc: K-quant matrices run from an expanded copy that "
+                    "jepa_encode allocates");
     c->encoded = false;
     c->last_tokens = nullptr;
     c->last_batch = 0;
@@ -1094,6 +1163,9 @@ jepa_status jepa_classify(jepa_ctx *c, float *logits_out, void *hip_stream) {
     if (c->N > XATTN_MAX_N) return fail(JEPA_E_UNSUPPORTED, "classify: %d tokens exceed %d", c->N, XATTN_MAX_N);
     const jepa_dims &d = c->d;
     const Head &h = c->head;
+    const bool xp = c->last_expand;   // the block matrices' copies are current
+    const DevTensor &wq = xp ? h.xwq : h.wq, &wk = xp ? h.xwk : h.wk, &wv = xp ? h.xwv : h.wv;
+    const DevTensor &wo = xp ? h.xwo : h.wo, &wup = xp ? h.xwup : h.wup, &wdown = xp ? h.xwdown : h.wdown;
     hipStream_t s = (hipStream_t)hip_stream;
     const int B = c->last_batch, D = c->D, F = c->F, dh = D / c->H;
     const int64_t M = (int64_t)B * c->N;
@@ -1103,20 +1175,20 @@ jepa_status jepa_classify(jepa_ctx *c, float *logits_out, void *hip_stream) {
     // keys and values of the normalised tokens (in the qkv buffer, pitch 3D)
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(c->w.x, M, D, h.ln1g, h.ln1b, d.ln_eps, c->w.hn, c->act, s); }));
     unsigned char *kv = (unsigned char *)c->w.qkv;
-    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, h.wk, h.bk, EPI_STORE, kv, 3 * D));
-    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, h.wv, h.bv, EPI_STORE, kv + (size_t)D * c->es, 3 * D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, wk, h.bk, EPI_STORE, kv, 3 * D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hn, M, D, wv, h.bv, EPI_STORE, kv + (size_t)D * c->es, 3 * D));
     // the query row of every item: W_q q0 + b_q
     TRY(launch(c, K_HEAD, s, [&] { return launch_cls_rows(c->w.hx, h.q0, nullptr, B, 1, D, s); }));
     TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w.hx, (int64_t)B * D, c->w.hh, c->act, s); }));
-    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wq, h.bq, EPI_STORE, c->w.hq, D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, wq, h.bq, EPI_STORE, c->w.hq, D));
     TRY(launch(c, K_HEAD, s, [&] {
         return launch_xattn(c->act, c->w.hq, kv, kv + (size_t)D * c->es, 3 * D, B, c->N, c->H, dh, c->w.ho, s);
     }));
     // x = q0 + out_proj(o); x += MLP(LN2 x); scores = W_c x + b_c
-    TRY(gemm(c, K_HEAD, s, 1, c->w.ho, B, D, h.wo, h.bo, EPI_RESID, c->w.hx, D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.ho, B, D, wo, h.bo, EPI_RESID, c->w.hx, D));
     TRY(launch(c, K_HEAD, s, [&] { return launch_layernorm(c->w.hx, B, D, h.ln2g, h.ln2b, d.ln_eps, c->w.hh, c->act, s); }));
-    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wup, h.bup, EPI_GELU, c->w.hu, F));
-    TRY(gemm(c, K_HEAD, s, 1, c->w.hu, B, F, h.wdown, h.bdown, EPI_RESID, c->w.hx, D));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, wup, h.bup, EPI_GELU, c->w.hu, F));
+    TRY(gemm(c, K_HEAD, s, 1, c->w.hu, B, F, wdown, h.bdown, EPI_RESID, c->w.hx, D));
     TRY(launch(c, K_HEAD, s, [&] { return launch_cast(c->w.hx, (int64_t)B * D, c->w.hh, c->act, s); }));
     TRY(launch(c, K_HEAD, s, [&] { return launch_fill(c->w.hl, (int64_t)B * h.Cpad, 0.f, s); }));
     TRY(gemm(c, K_HEAD, s, 1, c->w.hh, B, D, h.wc, h.bc, EPI_RESID, c->w.hl, h.Cpad));
@@ -1201,12 +1273,12 @@ jepa_status jepa_dequant_tensor(jepa_ctx *c, const char *name, float *out_dev, v
     if (std::string(name) == "enc.patch_embed.weight" && c->Kp != t.ne0) {
         for (int64_t r = 0; r < t.ne1; ++r) {
             hipError_t e = launch_dequant(t.dev_dt, (const unsigned char *)t.ptr + r * c->Kp * c->es,
-                                          nullptr, 1, t.ne0, out_dev + r * t.ne0, s);
+                                          nullptr, nullptr, 1, t.ne0, out_dev + r * t.ne0, s);
             if (e != hipSuccess) return fail(JEPA_E_HIP, "dequant: %s", hipGetErrorString(e));
         }
         return JEPA_OK;
     }
-    hipError_t e = launch_dequant(t.dev_dt, t.ptr, t.scale, t.ne1, t.ne0, out_dev, s);
+    hipError_t e = launch_dequant(t.dev_dt, t.ptr, t.scale, t.sub, t.ne1, t.ne0, out_dev, s);
     if (e != hipSuccess) return fail(JEPA_E_HIP, "dequant: %s", hipGetErrorString(e));
     return JEPA_OK;
 }

@@ -16,7 +16,7 @@ typedef _Float16 f16x8  __attribute__((ext_vector_type(8)));
 typedef float    f32x16 __attribute__((ext_vector_type(16)));
 typedef float    f32x4  __attribute__((ext_vector_type(4)));
 
-enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8_0 = 3, DT_Q4_0 = 4 };
+enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_Q8_0 = 3, DT_Q4_0 = 4, DT_Q4_K = 5, DT_Q6_K = 6 };
 
 // ---------------------------------------------------------------------------
 // scalar conversions (round to nearest even)

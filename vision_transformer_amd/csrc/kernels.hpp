@@ -123,21 +123,33 @@ hipError_t launch_pool_cls(const float *y, int B, int N, int D, float *out, hipS
 constexpr int POOL_CHUNKS = 32;
 hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, float *part, float *out,
                             hipStream_t s);
-// q8_0 / q4_0 matrices expanded to the activation dtype, act(f32(d) * q), the
-// values the GEMM's own dequantising tile load makes.  Job j covers the
-// matrix's blocks of 32 weights [blk0_j, blk0_{j+1}) of the concatenated
-// range (blk0 ascending, blk0_0 = 0); codes and scales as the GEMM reads
-// them, dst the act-dtype matrix [rows, cols] (16-byte aligned).
+// Block-format matrices expanded to the activation dtype, act(w) with w the
+// f32 value of each weight (for q8_0 / q4_0 f32(d) * q, the values the
+// GEMM's own dequantising tile load makes).  Job j covers the matrix's units
+// of 32 weights [blk0_j, blk0_{j+1}) of the concatenated range (blk0
+// ascending, blk0_0 = 0); dst is the act-dtype matrix [rows, cols] (16-byte
+// aligned).  Device layouts (each field as stored, split into arrays):
+//   q8_0: codes int8 [units][32]; scale f16 [units]
+//   q4_0: codes [units][16] (byte j: code j low nibble, code j+16 high);
+//         scale f16 [units]
+//   q4_K: codes [super-blocks][128] (the stored 4-bit codes); scale f16
+//         [super-blocks][2] (d, dmin); sub [super-blocks][12] (the stored
+//         6-bit sub-block scales and mins)
+//   q6_K: codes [super-blocks][192] (the 128 low-bit then 64 high-bit
+//         bytes); scale f16 [super-blocks] (d); sub int8 [super-blocks][16]
+// (a super-block is 256 weights, 8 units, along a row)
 struct ExpandJob {
     const void *codes;
     const uint16_t *scale;
+    const uint8_t *sub;
     void *dst;
     int64_t blk0;
     int w_dt;
 };
 hipError_t launch_expand(int act_dt, const ExpandJob *jobs, int njobs, int64_t nblk, hipStream_t s);
-// dequantise packed blocks, or widen f16 / bf16 / f32 storage, into f32 [rows, cols]
-hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
+// dequantise block formats (layouts as above), or widen f16 / bf16 / f32
+// storage, into f32 [rows, cols]
+hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, const uint8_t *sub, int64_t rows,
                           int64_t cols, float *out, hipStream_t s);
 
 }  // namespace jepa

@@ -140,36 +140,114 @@ __global__ __launch_bounds__(256) void pool_mean_fin_kernel(const float *part, i
 }
 
 // ---------------------------------------------------------------------------
-// dequantisation to f32 (exact: f32(d) * integer code)
-//   q8_0 packed: codes int8 [rows, cols], scales f16 [rows, cols/32]
-//   q4_0 packed: blocks of 16 bytes [rows, cols/32], byte j = code j (low
-//                nibble) | code j+16 (high nibble); scales as q8_0
+// Block formats (device layouts in kernels.hpp).  unit_values writes the f32
+// values of unit k, 32 consecutive weights of a row; each is the exact value
+// rounded once to f32: q8_0 f32(d) q and q4_0 f32(d) (q - 8) (exact);
+// q6_K d sc (q - 32) (at most 24 significant bits, exact); q4_K
+// d sc_j q - dmin m_j (both products exact, the difference rounded once).
+// Formats: jepa.cpp Quantization page, "The rule" and "File sizes" (block
+// 32 for q8_0 / q4_0, super-block 256 for the K-quants), with ggml's
+// published super-block layouts.
 // ---------------------------------------------------------------------------
-__global__ void dequant_kernel(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
-                               int64_t cols, float *out) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= rows * cols) return;
-    const int64_t r = idx / cols, c = idx - r * cols;
-    float v;
-    if (w_dt == DT_Q8_0 || w_dt == DT_Q4_0) {
-        const float d = (float)__builtin_bit_cast(_Float16, scale[r * (cols / 32) + c / 32]);
-        int q;
-        if (w_dt == DT_Q8_0) {
-            q = ((const int8_t *)w)[idx];
-        } else {
-            const int e = (int)(c & 31);
-            const uint8_t byte = ((const uint8_t *)w)[r * (cols / 2) + (c / 32) * 16 + (e & 15)];
-            q = (e < 16 ? (byte & 15) : (byte >> 4)) - 8;
+__device__ __forceinline__ float half_at(const uint16_t *p, int64_t i) {
+    return (float)__builtin_bit_cast(_Float16, p[i]);
+}
+
+__device__ __forceinline__ void unit_values(int w_dt, const void *codes, const uint16_t *scale,
+                                            const uint8_t *sub, int64_t k, float *x) {
+    if (w_dt == DT_Q8_0) {
+        const float d = half_at(scale, k);
+        const uint4 *src = (const uint4 *)((const int8_t *)codes + k * 32);
+        const uint4 q0 = src[0], q1 = src[1];
+        const int8_t *c0 = (const int8_t *)&q0, *c1 = (const int8_t *)&q1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = d * (float)c0[i];
+            x[16 + i] = d * (float)c1[i];
         }
-        v = d * (float)q;
-    } else if (w_dt == DT_F16) {
-        v = to_f32(((const f16_t *)w)[idx]);
-    } else if (w_dt == DT_BF16) {
-        v = to_f32(((const bf16_t *)w)[idx]);
-    } else {
-        v = ((const float *)w)[idx];
+    } else if (w_dt == DT_Q4_0) {
+        const float d = half_at(scale, k);
+        const uint4 q = *(const uint4 *)((const uint8_t *)codes + k * 16);
+        const uint8_t *c = (const uint8_t *)&q;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = d * (float)((int)(c[i] & 15) - 8);
+            x[16 + i] = d * (float)((int)(c[i] >> 4) - 8);
+        }
+    } else if (w_dt == DT_Q4_K) {
+        // sub-block j of super-block sb: 6-bit scale and min from the 12
+        // packed bytes; its codes are the low (j even) or high (j odd)
+        // nibbles of code bytes 32 (j / 2) .. 32 (j / 2) + 31
+        const int64_t sb = k >> 3;
+        const int j = (int)(k & 7);
+        const float d = half_at(scale, 2 * sb), dmin = half_at(scale, 2 * sb + 1);
+        const uint8_t *s = sub + sb * 12;
+        int sc, m;
+        if (j < 4) {
+            sc = s[j] & 63;
+            m = s[j + 4] & 63;
+        } else {
+            sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+            m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        }
+        const float d1 = d * (float)sc, m1 = dmin * (float)m;
+        const uint4 *src = (const uint4 *)((const uint8_t *)codes + sb * 128 + (j >> 1) * 32);
+        const uint4 q0 = src[0], q1 = src[1];
+        const uint8_t *c0 = (const uint8_t *)&q0, *c1 = (const uint8_t *)&q1;
+        const int sh = (j & 1) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = d1 * (float)((c0[i] >> sh) & 15) - m1;
+            x[16 + i] = d1 * (float)((c1[i] >> sh) & 15) - m1;
+        }
+    } else {  // DT_Q6_K
+        // unit j = 4 h + t of super-block sb covers weights 128 h + 32 t ..
+        // +31: low 4 bits from the low (t < 2) or high nibble of low bytes
+        // 64 h + 32 (t % 2) + l, high 2 bits from bits 2t, 2t+1 of high byte
+        // 32 h + l; scales 8 h + 2 t (l < 16) and 8 h + 2 t + 1
+        const int64_t sb = k >> 3;
+        const int j = (int)(k & 7), h = j >> 2, t = j & 3;
+        const float d = half_at(scale, sb);
+        const int8_t *sc = (const int8_t *)sub + sb * 16 + 8 * h + 2 * t;
+        const float d0 = d * (float)sc[0], d1 = d * (float)sc[1];
+        const uint8_t *base = (const uint8_t *)codes + sb * 192;
+        const uint4 *lo = (const uint4 *)(base + 64 * h + 32 * (t & 1));
+        const uint4 *hi = (const uint4 *)(base + 128 + 32 * h);
+        const uint4 l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];
+        const uint8_t *L0 = (const uint8_t *)&l0, *L1 = (const uint8_t *)&l1;
+        const uint8_t *H0 = (const uint8_t *)&h0, *H1 = (const uint8_t *)&h1;
+        const int lsh = (t >> 1) * 4, hsh = 2 * t;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int q0 = ((L0[i] >> lsh) & 15) | (((H0[i] >> hsh) & 3) << 4);
+            const int q1 = ((L1[i] >> lsh) & 15) | (((H1[i] >> hsh) & 3) << 4);
+            x[i] = d0 * (float)(q0 - 32);
+            x[16 + i] = d1 * (float)(q1 - 32);
+        }
     }
+}
+
+// dense storage widened to f32, one thread per element
+__global__ void widen_kernel(int w_dt, const void *w, int64_t n, float *out) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    float v;
+    if (w_dt == DT_F16) v = to_f32(((const f16_t *)w)[idx]);
+    else if (w_dt == DT_BF16) v = to_f32(((const bf16_t *)w)[idx]);
+    else v = ((const float *)w)[idx];
     out[idx] = v;
+}
+
+// block formats to f32, one thread per unit of 32 weights
+__global__ __launch_bounds__(256) void dequant_units_kernel(int w_dt, const void *codes, const uint16_t *scale,
+                                                            const uint8_t *sub, int64_t units, float *out) {
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= units) return;
+    float x[32];
+    unit_values(w_dt, codes, scale, sub, k, x);
+    float4 *dst = (float4 *)(out + k * 32);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dst[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
 }
 
 // Dense MFMA calibration: each wave runs `iters` rounds of 8 independent
@@ -212,9 +290,9 @@ __global__ __launch_bounds__(256) void fill_kernel(float *x, int64_t n, float v)
     if (i < n) x[i] = v;
 }
 
-// One thread per block of 32 weights: 32 (q8_0) or 16 (q4_0) code bytes and
-// the f16 scale in, 64 bytes of act values out.  Neighbouring threads take
-// neighbouring blocks, so every wave reads and writes contiguous runs.
+// One thread per unit of 32 weights: the unit's codes and scales in, 64
+// bytes of act values out.  Neighbouring threads take neighbouring units, so
+// every wave reads and writes contiguous runs.
 template <typename T>
 __global__ __launch_bounds__(256) void expand_kernel(const ExpandJob *jobs, int njobs, int64_t nblk) {
     const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -227,26 +305,8 @@ __global__ __launch_bounds__(256) void expand_kernel(const ExpandJob *jobs, int 
     }
     const ExpandJob j = jobs[lo];
     const int64_t k = b - j.blk0;
-    const float d = (float)__builtin_bit_cast(_Float16, j.scale[k]);
     float x[32];
-    if (j.w_dt == DT_Q8_0) {
-        const uint4 *src = (const uint4 *)((const int8_t *)j.codes + k * 32);
-        const uint4 q0 = src[0], q1 = src[1];
-        const int8_t *c0 = (const int8_t *)&q0, *c1 = (const int8_t *)&q1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            x[i] = d * (float)c0[i];
-            x[16 + i] = d * (float)c1[i];
-        }
-    } else {
-        const uint4 q = *(const uint4 *)((const uint8_t *)j.codes + k * 16);
-        const uint8_t *c = (const uint8_t *)&q;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            x[i] = d * (float)((int)(c[i] & 15) - 8);
-            x[16 + i] = d * (float)((int)(c[i] >> 4) - 8);
-        }
-    }
+    unit_values(j.w_dt, j.codes, j.scale, j.sub, k, x);
     uint4 *dst = (uint4 *)((T *)j.dst + k * 32);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -356,12 +416,23 @@ hipError_t launch_pool_mean(const float *y, int B, int N, int D, int first, floa
     return hipGetLastError();
 }
 
-hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, int64_t rows,
+hipError_t launch_dequant(int w_dt, const void *w, const uint16_t *scale, const uint8_t *sub, int64_t rows,
                           int64_t cols, float *out, hipStream_t s) {
-    if (rows <= 0 || cols <= 0) return hipErrorInvalidValue;
-    if ((w_dt == DT_Q8_0 || w_dt == DT_Q4_0) && (cols % 32 || !scale)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)cdiv(rows * cols, 256)), dim3(256), 0, s,
-                       w_dt, w, scale, rows, cols, out);
+    if (rows <= 0 || cols <= 0 || !w || !out) return hipErrorInvalidValue;
+    const int64_t n = rows * cols;
+    if (w_dt == DT_Q8_0 || w_dt == DT_Q4_0 || w_dt == DT_Q4_K || w_dt == DT_Q6_K) {
+        const int64_t unit = (w_dt == DT_Q4_K || w_dt == DT_Q6_K) ? 256 : 32;
+        if (cols % unit || !scale || ((w_dt == DT_Q4_K || w_dt == DT_Q6_K) && !sub)) return hipErrorInvalidValue;
+        const int64_t units = n / 32;
+        if (cdiv(units, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(dequant_units_kernel, dim3((unsigned)cdiv(units, 256)), dim3(256), 0, s, w_dt, w, scale,
+                           sub, units, out);
+    } else if (w_dt == DT_F32 || w_dt == DT_F16 || w_dt == DT_BF16) {
+        if (cdiv(n, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(widen_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, w_dt, w, n, out);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -23,6 +23,19 @@ class Encoder:
         self._last_tokens = None
         self.last_batch = 0
 
+    @classmethod
+    def from_gguf(cls, path: str, act_dtype: str | None = None) -> "Encoder":
+        """A model read from a GGUF file (dims from its keys; act_dtype None
+        lets the library choose from the stored types)."""
+        info = _lib.jepa_gguf_read_info(path)
+        self = cls.__new__(cls)
+        self.dims = dict(info["dims"], act_dtype=act_dtype)
+        self.n_tokens = synth.n_tokens(self.dims)
+        self._last_tokens = None
+        self.last_batch = 0
+        self.ctx = _lib.jepa_create_from_gguf(path, act_dtype)
+        return self
+
     def close(self):
         if getattr(self, "ctx", None):
             _lib.jepa_free(self.ctx)

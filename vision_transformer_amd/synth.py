@@ -25,7 +25,11 @@ import numpy as np
 
 # Storage dtypes a tensor may have (jepa.cpp Quantization page, "The rule":
 # only the four 2-D block matrices may be re-typed to a block format).
-DTYPES = ("f32", "f16", "bf16", "q8_0", "q4_0")
+DTYPES = ("f32", "f16", "bf16", "q8_0", "q4_0", "q4_k", "q6_k")
+# The same rule: a K-quant target applies only to rows that are a multiple
+# of 256 long; other rows take these formats instead.
+K_QUANT_ROW = 256
+K_QUANT_FALLBACK = {"q4_k": "q4_0", "q6_k": "q8_0"}
 BLOCK_MATRICES = ("attn_qkv", "attn_q", "attn_k", "attn_v", "attn_out", "ffn_up", "ffn_down")
 
 
@@ -187,6 +191,23 @@ SMALL_WORKLOADS = {
                    img_h=96, img_w=112, frames=6, has_cls=0, act_dtype="f16",
                    mat_dtype="q4_0", rest_dtype="f16", rope=1),
         batch=2, frame_seed=19, weight_seed=29),
+    # K-quant targets (super-blocks of 256 weights): D = 192 rows fall back
+    # to q4_0, the 768-long ffn_down rows (and the head's) stay q4_K
+    "small_q4_k_fallback_head_bf16": dict(
+        dims=_dims(dim=192, depth=2, heads=3, mlp_dim=768, patch=16, img_h=80,
+                   img_w=112, frames=3, act_dtype="bf16", mat_dtype="q4_k",
+                   rest_dtype="bf16", head_blocks=1, head_classes=12),
+        batch=2, frame_seed=61, weight_seed=71),
+    "small_q6_k_rope_blockcausal_f16": dict(
+        dims=_dims(dim=256, depth=2, heads=4, mlp_dim=1024, patch=16, tubelet=2,
+                   img_h=64, img_w=96, frames=4, has_cls=0, mask="block_causal",
+                   act_dtype="f16", mat_dtype="q6_k", rest_dtype="f16", rope=1),
+        batch=2, frame_seed=62, weight_seed=72),
+    "small_q4_k_dh32_cls_bf16": dict(
+        dims=_dims(dim=256, depth=2, heads=8, mlp_dim=512, patch=16, img_h=96,
+                   img_w=80, frames=2, act_dtype="bf16", mat_dtype="q4_k",
+                   rest_dtype="bf16"),
+        batch=3, frame_seed=63, weight_seed=73),
 }
 
 
@@ -207,6 +228,10 @@ MID_WORKLOADS = {
         dims=_dims(**dict(_VITL, depth=2), frames=4, tubelet=2, img_h=256, img_w=256, has_cls=0,
                    act_dtype="f16", mat_dtype="q4_0", rest_dtype="f16", rope=1),
         batch=2, frame_seed=43, weight_seed=53),
+    "mid_vitl_q4_k": dict(
+        dims=_dims(**dict(_VITL, depth=2), frames=4, tubelet=2, img_h=256, img_w=256, has_cls=0,
+                   act_dtype="f16", mat_dtype="q4_k", rest_dtype="f16"),
+        batch=2, frame_seed=44, weight_seed=54),
 }
 
 
@@ -297,9 +322,15 @@ def is_layernorm(name: str) -> bool:
     return name.startswith("enc.norm.") or ".ln1." in name or ".ln2." in name
 
 
-def storage_dtype(dims: dict, name: str) -> str:
-    """The stored dtype of a tensor under the re-typing rule."""
-    return dims["mat_dtype"] if is_block_matrix(name) else dims["rest_dtype"]
+def storage_dtype(dims: dict, name: str, ne0: int | None = None) -> str:
+    """The stored dtype of a tensor under the re-typing rule (ne0, its row
+    length, decides the K-quant fallback)."""
+    if not is_block_matrix(name):
+        return dims["rest_dtype"]
+    dt = dims["mat_dtype"]
+    if dt in K_QUANT_FALLBACK and ne0 is not None and ne0 % K_QUANT_ROW:
+        return K_QUANT_FALLBACK[dt]
+    return dt
 
 
 # ----------------------------------------------------------------------------
@@ -359,7 +390,7 @@ def stored_weights(dims: dict, w32: dict, quantize=None) -> list[dict]:
     """
     out = []
     for name, ne0, ne1 in tensor_specs(dims):
-        dt = storage_dtype(dims, name)
+        dt = storage_dtype(dims, name, ne0)
         w = w32[name]
         if dt == "f32":
             data = np.ascontiguousarray(w, dtype=np.float32)
