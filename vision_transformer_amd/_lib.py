@@ -13,7 +13,8 @@ import numpy as np
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libjepa_mi355x.so")
+# JEPA_LIB_PATH selects another build of the library (e.g. the sanitized one)
+LIB_PATH = os.environ.get("JEPA_LIB_PATH") or os.path.join(_PKG, "libjepa_mi355x.so")
 
 F32, F16, BF16, Q8_0, Q4_0, Q4_K, Q6_K = 0, 1, 2, 3, 4, 5, 6
 DTYPE = {"f32": F32, "f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}

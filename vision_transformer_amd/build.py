@@ -1,6 +1,13 @@
 """Build libjepa_mi355x.so for gfx950 with hipcc, in-tree.
 
-usage: python -m vision_transformer_amd.build [-j N] [--debug]
+usage: python -m vision_transformer_amd.build [-j N] [--debug] [--sanitize]
+
+--sanitize builds a second copy, _build/sanitize/libjepa_mi355x.so, whose
+host code (argument checks, the quantizer, block packing, the rotary table,
+the GGUF reader) carries AddressSanitizer and UndefinedBehaviorSanitizer
+checks; device code is built as usual.  It runs on the CPU only, loaded into
+a Python whose first preloaded library is the sanitizer runtime
+(SANITIZER_RUNTIME), with JEPA_LIB_PATH pointing at it.
 """
 from __future__ import annotations
 
@@ -15,6 +22,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjepa_mi355x.so")
+SAN_DIR = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libjepa_mi355x.so")
+# host-only sanitizer flags (-Xarch_host keeps them off the device code)
+SAN_FLAGS = "-Xarch_host -fsanitize=address,undefined -Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer -g".split()
 SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "api.hip", "gguf.cpp"]
 ARCH = "gfx950"
 
@@ -40,12 +51,21 @@ def _run(cmd):
     return r.returncode, out
 
 
-def build(jobs: int = 4, debug: bool = False, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    fl = flags(debug)
+def sanitizer_runtime() -> str:
+    """The clang ASan runtime hipcc's host compiler links against."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if os.path.isabs(path) and os.path.exists(path) else ""
+
+
+def build(jobs: int = 4, debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir = SAN_DIR if sanitize else BUILD
+    out_lib = SAN_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
+    fl = flags(debug or sanitize) + (SAN_FLAGS if sanitize else [])
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(out_dir, src + ".o")
         cmd = [hipcc()] + fl + ["-c", os.path.join(CSRC, src), "-o", obj]
         rc, out = _run(cmd)
         if verbose or rc:
@@ -58,14 +78,15 @@ def build(jobs: int = 4, debug: bool = False, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out_lib + ".tmp"
+    # (the sanitized copy leaves the runtime's symbols to the preloaded runtime)
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     rc, out = _run(cmd)
     if rc:
         print(" ".join(cmd) + "\n" + out, file=sys.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
@@ -73,5 +94,6 @@ if __name__ == "__main__":
     ap.add_argument("-j", type=int, default=4)
     ap.add_argument("--debug", action="store_true")
     ap.add_argument("-v", action="store_true")
+    ap.add_argument("--sanitize", action="store_true")
     a = ap.parse_args()
-    print(build(a.j, a.debug, a.v))
+    print(build(a.j, a.debug, a.v, a.sanitize))
