@@ -127,6 +127,21 @@ jepa_status jepa_rope_table(const jepa_dims *dims, float *out);
  * workgroups * 4 * iters * 8 * 32768 flops; the caller times the launch. */
 jepa_status jepa_op_mfma_probe(int workgroups, int iters, float *out, void *hip_stream);
 
+/* The int8 MFMA rate, and what consuming it costs when every 32-wide K block
+ * carries its own scales (the q8_0 weight format of the jepa.cpp
+ * Quantization page, "The rule"; the int8 matrix path the Benchmarks page's
+ * "Effect of the weight dtype" GPU table measures).  Each of `workgroups`
+ * workgroups of 4 waves runs iters x 4 independent v_mfma_i32_32x32x32_i8
+ * (65536 ops each) on register operands.  mode 0: products accumulate in
+ * int32.  mode 1: each block's int32 result starts from zero and is added
+ * into f32 accumulators scaled by a per-block scale of each of the lane's
+ * rows times one of its column (convert, multiply, fused multiply-add per
+ * element; scales read from LDS).  mode 2: as 1 with a single scale per
+ * row for all of K (convert, fused multiply-add).  out: device f32,
+ * workgroups * 256 elements (one sum per thread).  Ops per launch:
+ * workgroups * 4 * iters * 4 * 65536; the caller times the launch. */
+jepa_status jepa_op_mfma_i8_probe(int workgroups, int iters, int mode, float *out, void *hip_stream);
+
 /* Host: split Q8_0 / Q4_0 blocks [rows, cols/32] into the device layout
  * the GEMM reads: codes (rows*cols bytes of int8 for Q8_0; rows*cols/2
  * bytes of 16-byte nibble blocks for Q4_0) and scales (rows*cols/32 f16).

@@ -511,6 +511,35 @@ def test_transpose_v(lib, act, B, N, heads, dh):
     assert np.all(got[..., np.setdiff1d(np.arange(got.shape[-1]), pos)] == 0)
 
 
+def test_int8_mfma_and_its_per_block_rescale(lib):
+    """The int8 matrix path's ceiling on this chip: the plain int8 MFMA rate
+    and the rate left when each 32-wide K block's int32 result is rescaled
+    into f32 (per-row and per-column block scales; one scale per row),
+    beside the dense bf16 rate.  Prints the rates; checks the launches and
+    their op counts."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.full((2 * cus * 256,), float("nan"), device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, *args):
+        fn(*args)                                 # warm-up
+        torch.cuda.synchronize()
+        e0.record()
+        ops = fn(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out[:args[0] * 256]).all()
+        return ops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+    bf16 = rate(lib.jepa_op_mfma_probe, cus, 20000, out)
+    i8 = [rate(lib.jepa_op_mfma_i8_probe, 2 * cus, 10000, m, out) for m in (0, 1, 2)]
+    say(f"  dense bf16 MFMA {bf16:.0f} TFLOP/s; int8 MFMA {i8[0]:.0f} TOP/s; with per-block row and "
+          f"column scales {i8[1]:.0f} TOP/s; with per-block column scales {i8[2]:.0f} TOP/s")
+    assert lib.jepa_op_mfma_i8_probe(1, 3, 1, out) == 1 * 4 * 3 * 4 * 65536
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_op_mfma_i8_probe(1, 3, 3, out)
+
+
 def test_mfma_probe_runs_and_reports_its_flops(lib):
     """The calibration kernel: finite output from every thread, and the work
     it reports is workgroups x 4 waves x iters x 8 MFMAs of 32x32x16x2."""

@@ -88,6 +88,7 @@ def _load():
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
         "jepa_op_mfma_probe": (I, [I, I, P, P]),
+        "jepa_op_mfma_i8_probe": (I, [I, I, I, P, P]),
         "jepa_gguf_read_info": (I, [C.c_char_p, C.POINTER(jepa_gguf_info)]),
         "jepa_create_from_gguf": (I, [C.c_char_p, I, C.POINTER(P)]),
         "jepa_file_type_name": (C.c_char_p, [I]),
@@ -354,6 +355,12 @@ def jepa_op_mfma_probe(workgroups: int, iters: int, out, stream=None) -> int:
     """Dense bf16 MFMA calibration launch; returns its flops."""
     _check(_lib.jepa_op_mfma_probe(workgroups, iters, _ptr(out), _stream(stream)))
     return workgroups * 4 * iters * 8 * 32 * 32 * 16 * 2
+
+
+def jepa_op_mfma_i8_probe(workgroups: int, iters: int, mode: int, out, stream=None) -> int:
+    """int8 MFMA calibration launch (mode 0 plain, 1 / 2 rescaled); returns its ops."""
+    _check(_lib.jepa_op_mfma_i8_probe(workgroups, iters, mode, _ptr(out), _stream(stream)))
+    return workgroups * 4 * iters * 4 * 32 * 32 * 32 * 2
 
 
 def jepa_pack_blocks(dtype: str, blocks: np.ndarray, rows: int, cols: int):

@@ -113,6 +113,9 @@ hipError_t launch_fill(float *x, int64_t n, float v, hipStream_t s);
 // dense bf16 MFMA calibration: workgroups x 4 waves, each iters x 8
 // independent 32x32x16 MFMAs; out holds workgroups * 256 floats
 hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
+// int8 MFMA calibration: mode 0 plain, 1 / 2 with per-block rescaling into
+// f32 (see misc.hip); workgroups x 4 waves, each iters x 4 32x32x32 MFMAs
+hipError_t launch_mfma_i8_probe(int workgroups, int iters, int mode, float *out, hipStream_t s);
 // X[b*N + 0] = cls + pos[0] for every item (pos null: cls)
 hipError_t launch_cls_rows(float *x, const float *cls, const float *pos, int B, int N, int D,
                            hipStream_t s);

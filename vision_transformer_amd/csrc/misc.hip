@@ -277,6 +277,99 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *out) 
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// int8 MFMA calibration, and the cost of consuming it for block-scaled
+// weights.  Each wave runs `iters` rounds of 4 independent
+// v_mfma_i32_32x32x32_i8 (one 32-wide K block each, 65536 ops):
+//   mode 0: the products accumulate in int32 (the plain int8 rate);
+//   mode 1: every block's int32 result starts from zero and is folded into
+//           f32 accumulators with a per-block scale for each of the lane's
+//           16 rows (activations quantised per 32-block) times a per-block
+//           scale for its column (the weight block's d): cvt, mul, fma per
+//           element; the scales come from LDS, as they would in a GEMM;
+//   mode 2: as mode 1 with one scale per activation row for all of K, so
+//           only the column scale remains per block: cvt, fma per element.
+typedef signed char i8x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Rescale chain c's block result t into facc (modes 1, 2); the scales of K
+// block kb come from LDS.
+template <int MODE>
+__device__ __forceinline__ void i8_rescale(f32x16 &facc, const i32x16 &t, const float (*scales)[1024], int kb,
+                                           int col, int g32) {
+    const float sw = scales[1][kb * 32 + col];
+    if constexpr (MODE == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 sa = *(const float4 *)&scales[0][kb * 32 + 8 * q + 4 * g32];
+            const float s4[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[4 * q + r] = fmaf(s4[r] * sw, (float)t[4 * q + r], facc[4 * q + r]);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) facc[v] = fmaf(sw, (float)t[v], facc[v]);
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void mfma_i8_probe_kernel(int iters, float *out) {
+    __shared__ float scales[2][1024];
+    for (int i = threadIdx.x; i < 2048; i += 256) scales[i >> 10][i & 1023] = 1e-3f * (float)((i * 37) & 63) + 1e-4f;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, g32 = lane >> 5, col = lane & 31;
+    i8x16 a, b[4];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        a[j] = (signed char)(((threadIdx.x + j) & 15) - 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c][j] = (signed char)(((threadIdx.x * 3 + j + 5 * c) & 15) - 8);
+    }
+    i32x16 t[4];
+    f32x16 facc[4];
+    const i32x16 zero = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        t[c] = zero;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) facc[c][v] = 0.f;
+    }
+    // The A operand passes through an empty asm statement once per round, so
+    // that the compiler can neither hoist the rounds' identical products out
+    // of the loop nor merge them; it emits no instruction.
+    i32x4 ao = __builtin_bit_cast(i32x4, a);
+    if constexpr (MODE == 0) {
+        for (int i = 0; i < iters; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[c], t[c], 0, 0, 0);
+    } else {
+        // software-pipelined: block i of chain c is rescaled while the other
+        // chains' MFMAs run, then chain c's next block is issued
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            t[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i8x16, ao), b[c], zero, 0, 0, 0);
+        for (int i = 0; i < iters - 1; ++i) {
+            asm volatile("" : "+v"(ao));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                i8_rescale<MODE>(facc[c], t[c], scales, (i * 4 + c) & 31, col, g32);
+                t[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i8x16, ao), b[c], zero, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            i8_rescale<MODE>(facc[c], t[c], scales, ((iters - 1) * 4 + c) & 31, col, g32);
+            t[c] = zero;
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += facc[c][v] + (float)t[c][v];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // f32 values rounded to the act dtype, and a fill (graph-capturable, unlike
 // a memset node)
 template <typename T>
@@ -331,6 +424,14 @@ hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t
 hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s) {
     if (workgroups <= 0 || iters <= 0 || !out) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(256), 0, s, iters, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_i8_probe(int workgroups, int iters, int mode, float *out, hipStream_t s) {
+    if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 2 || !out) return hipErrorInvalidValue;
+    if (mode == 0) hipLaunchKernelGGL(mfma_i8_probe_kernel<0>, dim3(workgroups), dim3(256), 0, s, iters, out);
+    else if (mode == 1) hipLaunchKernelGGL(mfma_i8_probe_kernel<1>, dim3(workgroups), dim3(256), 0, s, iters, out);
+    else hipLaunchKernelGGL(mfma_i8_probe_kernel<2>, dim3(workgroups), dim3(256), 0, s, iters, out);
     return hipGetLastError();
 }
 
