@@ -50,6 +50,25 @@ jepa_status jepa_op_patchify(int act_dtype, const uint8_t *frames, int batch, in
 jepa_status jepa_op_layernorm(const float *x, int64_t rows, int dim, const float *gamma,
                               const float *beta, float eps, void *y, int y_dtype, void *hip_stream);
 
+/* Patch embedding straight from the frames (the encoder's front end: LeVJEPA
+ * card and V-JEPA 2 card, opening paragraphs: tubelet 1 or 2, patch 16):
+ * out[b, has_cls + n, :] = W * x + bias (+ pos[has_cls + n, :]) for patch n
+ * of item b, where x is its patch vector (dt, dy, dx, c; c fastest) of the
+ * normalised pixels u * (1 / (255 std_c)) + (-mean_c / std_c) (constants
+ * rounded once from double to f32), rounded to act_dtype; the f32 product
+ * sums in f32.  The GEMM gathers x from the frames as it loads its tiles;
+ * no patch matrix is written.  frames: device uint8 [B, T, H, W, 3],
+ * 8-byte aligned; (patch * 3) % 8 == 0 and (W * 3) % 8 == 0.  w: act_dtype
+ * [n, k_pitch], k_pitch >= tubelet * patch^2 * 3 a multiple of 64 up to
+ * 2048 (columns past the patch length are never read as data: the gathered
+ * values there are 0).  bias f32 [n], pos f32 [N_tok, n] or NULL, out f32
+ * [B, N_tok, n] with N_tok = patches + has_cls; CLS rows are not written.
+ * n % 64 == 0.  JEPA_E_HIP (invalid value) for shapes outside these. */
+jepa_status jepa_op_patch_embed(int act_dtype, const uint8_t *frames, int B, int T, int H, int W, int tubelet,
+                                int patch, const float *mean, const float *std, const void *w, int64_t k_pitch,
+                                int64_t n, const float *bias, const float *pos, int has_cls, float *out,
+                                void *hip_stream);
+
 /* Linear layer (attn_qkv / attn_out / ffn_up / ffn_down, Quantization page
  * "The rule"): acc = a[M, K] * w[N, K]^T in f32, then the epilogue.  a is
  * act_dtype; w is act_dtype (dense) or packed Q8_0 / Q4_0 (see

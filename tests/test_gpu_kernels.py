@@ -52,6 +52,58 @@ def test_patchify(lib, act, shape):
     assert np.all(err <= OUT_REL[act] * np.abs(ref) + 1e-6), err.max()
 
 
+# (act, B, T, H, W, tubelet, patch, n, has_cls, pos): ragged row tiles, the
+# LeVJEPA front end (3136 patch rows, K 768) and the V-JEPA 2 one (K 1536)
+PATCH_EMBED_CASES = [
+    ("bf16", 3, 2, 96, 112, 1, 16, 192, True, True),
+    ("f16", 2, 4, 64, 96, 2, 16, 128, False, True),
+    ("bf16", 1, 16, 224, 224, 1, 16, 1024, True, True),
+    ("f16", 1, 4, 256, 256, 2, 16, 256, False, False),
+]
+
+
+@pytest.mark.parametrize("case", PATCH_EMBED_CASES)
+def test_patch_embed_from_frames_every_element(lib, case):
+    """The patch-embed GEMM that gathers its A tile from the uint8 frames:
+    every output element against the oracle's normalise + patchify + linear
+    (+ pos), in float64 on the act-dtype-rounded patch values; CLS rows are
+    left as they were.  Bound: 2e-3 of sum |x||w| (one rounding flip of a
+    patch value where the f32 normalisation and the exact one straddle an
+    act-dtype boundary, plus f32 accumulation); a wrong index in the gather
+    moves an output by about sum |x||w| / sqrt(K)."""
+    act, B, T, H, W, kt, p, n, has_cls, use_pos = case
+    say(f"patch_embed {case}")
+    rng = np.random.default_rng(44)
+    frames = rng.integers(0, 256, (B, T, H, W, 3), dtype=np.uint8)
+    mean, std = (0.485, 0.456, 0.406), (0.229, 0.224, 0.225)
+    P = kt * p * p * 3
+    kp = -(-P // 64) * 64
+    np_ = (T // kt) * (H // p) * (W // p)
+    ntok = np_ + int(has_cls)
+    w = np.zeros((n, kp), np.float32)
+    w[:, :P] = rng.standard_normal((n, P)) * 0.02
+    w_dev, w64 = rounded(act, w)
+    bias = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    pos = (rng.standard_normal((ntok, n)) * 0.1).astype(np.float32) if use_pos else None
+    out = torch.full((B, ntok, n), 7.0, device="cuda")
+    lib.jepa_op_patch_embed(act, torch.from_numpy(frames).cuda(), kt, p, mean, std, w_dev,
+                            torch.from_numpy(bias).cuda(), None if pos is None else torch.from_numpy(pos).cuda(),
+                            has_cls, out)
+    got = out.double().cpu().numpy()
+    x = E.patchify(E.normalize(frames, mean, std), kt, p).reshape(B * np_, P)
+    _, x64 = rounded(act, x)
+    ref = x64 @ w64[:, :P].T + bias.astype(np.float64)
+    scale = np.abs(x64) @ np.abs(w64[:, :P]).T
+    ref = ref.reshape(B, np_, n)
+    if use_pos:
+        ref = ref + pos[int(has_cls):].astype(np.float64)
+    err = np.abs(got[:, int(has_cls):] - ref)
+    bound = 2e-3 * scale.reshape(B, np_, n) + 1e-6
+    assert np.all(err <= bound), (err / bound).max()
+    if has_cls:
+        assert np.all(got[:, 0] == 7.0)
+
+
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dim", [128, 192, 1024])
 def test_layernorm(lib, act, dim):

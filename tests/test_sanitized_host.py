@@ -18,6 +18,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_host_code_is_clean_under_asan_and_ubsan():
     if not os.path.exists(B.SAN_LIB):
         pytest.skip("sanitized library not built (python -m vision_transformer_amd.build --sanitize)")
+    if os.path.exists(B.LIB) and os.path.getmtime(B.SAN_LIB) < os.path.getmtime(B.LIB):
+        pytest.fail("the sanitized library is older than the main one: rebuild both "
+                    "(python -m vision_transformer_amd.build && python -m vision_transformer_amd.build --sanitize)")
     rt = B.sanitizer_runtime()
     if not rt:
         pytest.skip("no sanitizer runtime beside hipcc")

@@ -89,6 +89,8 @@ def _load():
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
         "jepa_op_mfma_probe": (I, [I, I, P, P]),
         "jepa_op_mfma_i8_probe": (I, [I, I, I, P, P]),
+        "jepa_op_patch_embed": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64,
+                                    I64, P, P, I, P, P]),
         "jepa_gguf_read_info": (I, [C.c_char_p, C.POINTER(jepa_gguf_info)]),
         "jepa_create_from_gguf": (I, [C.c_char_p, I, C.POINTER(P)]),
         "jepa_file_type_name": (C.c_char_p, [I]),
@@ -355,6 +357,17 @@ def jepa_op_mfma_probe(workgroups: int, iters: int, out, stream=None) -> int:
     """Dense bf16 MFMA calibration launch; returns its flops."""
     _check(_lib.jepa_op_mfma_probe(workgroups, iters, _ptr(out), _stream(stream)))
     return workgroups * 4 * iters * 8 * 32 * 32 * 16 * 2
+
+
+def jepa_op_patch_embed(act_dtype: str, frames, tubelet: int, patch: int, mean, std, w, bias, pos,
+                        has_cls: bool, out, stream=None) -> None:
+    """Patch embedding gathered from device frames [B, T, H, W, 3]; w [n, k_pitch]; out f32 [B, N_tok, n]."""
+    B, T, H, W, _ = frames.shape
+    m = (C.c_float * 3)(*mean)
+    sd = (C.c_float * 3)(*std)
+    _check(_lib.jepa_op_patch_embed(DTYPE[act_dtype], _ptr(frames), B, T, H, W, tubelet, patch, m, sd, _ptr(w),
+                                    w.shape[1], w.shape[0], _ptr(bias), _ptr(pos), int(has_cls), _ptr(out),
+                                    _stream(stream)))
 
 
 def jepa_op_mfma_i8_probe(workgroups: int, iters: int, mode: int, out, stream=None) -> int:

@@ -181,6 +181,9 @@ struct jepa_ctx {
     DevTensor wpe;
     float *bpe = nullptr, *cls = nullptr, *pos = nullptr, *normg = nullptr, *normb = nullptr;
     float *rope = nullptr;      // 3-D rotary table [N, 32] (cos, sin), or null
+    // pixel normalisation as one f32 FMA per value, u * pix_scale[c] +
+    // pix_shift[c] (1/(255 std_c) and -mean_c/std_c, rounded once from double)
+    float pix_scale[3] = {}, pix_shift[3] = {};
     // block-format matrices expanded to the act dtype for large batches (and
     // always when a K-quant matrix is present)
     bool has_q = false, has_k = false;
@@ -713,6 +716,10 @@ jepa_status jepa_create(const jepa_dims *dims, const jepa_tensor *tensors, int n
     c->Np = Np; c->N = N; c->per_slot = Hp * Wp;
     c->npad = (N + 63) / 64 * 64;
     c->model_bytes = model_bytes;
+    for (int i = 0; i < 3; ++i) {
+        c->pix_scale[i] = (float)(1.0 / (255.0 * (double)d.std[i]));
+        c->pix_shift[i] = (float)(-(double)d.mean[i] / (double)d.std[i]);
+    }
 
     // device layout of every tensor: block matrices keep their format (codes
     // then scales); other matrices take the act dtype; vectors become f32.
@@ -986,6 +993,18 @@ static jepa_status run_block(jepa_ctx *c, const Ws &w, const Layer &L, bool expa
     return JEPA_OK;
 }
 
+// Whether the patch-embed GEMM can gather its A tile straight from these
+// frames: a 16-bit act dtype, 8-byte runs of a patch row ((patch * 3) % 8
+// == 0, rows of (img_w * 3) % 8 == 0 bytes, 8-byte aligned frames) and at
+// most 256 8-element K chunks, 32-bit frame offsets.  Otherwise the frames go through the
+// patchify kernel into the patch matrix first.
+static bool implicit_patch(const jepa_ctx *c, const uint8_t *frames, int items) {
+    const jepa_dims &d = c->d;
+    return c->act != JEPA_F32 && (3 * d.patch) % 8 == 0 && (3 * d.img_w) % 8 == 0 &&
+           ((uintptr_t)frames & 7) == 0 && c->Kp / 8 <= 256 &&
+           (int64_t)items * d.frames * d.img_h * d.img_w * 3 < (1ll << 32);
+}
+
 // The launch sequence of one encode of `batch` items with device frames fr
 // into the token map Y, over the buffers w, in `parts` concurrent parts
 // (part 0 on s0, the others on the context's internal streams, forked from
@@ -1021,17 +1040,26 @@ static jepa_status encode_parts(jepa_ctx *c, const Ws &w, const uint8_t *fr, int
     auto body = [&]() -> jepa_status {
     for (int p = 0; p < parts; ++p) {
         const Part &q = P[p];
-        PatchifyArgs pa{};
-        pa.frames = fr + (size_t)q.b0 * frame_bytes; pa.B = q.nb; pa.T = d.frames; pa.H = d.img_h; pa.W = d.img_w;
-        pa.tubelet = d.tubelet; pa.patch = d.patch;
-        for (int i = 0; i < 3; ++i) { pa.mean[i] = d.mean[i]; pa.std[i] = d.std[i]; }
-        pa.out = rows(w.patch, (int64_t)q.b0 * c->Np, c->Kp, es); pa.ld = c->Kp;
-        TRY(launch(c, K_PATCHIFY, q.s, [&] { return launch_patchify(c->act, pa, q.s); }));
-
+        const uint8_t *qf = fr + (size_t)q.b0 * frame_bytes;
         GemmArgs g{};
-        g.a = pa.out; g.w = c->wpe.ptr; g.bias = c->bpe; g.out = rows(w.x, q.r0, D, 4);
+        g.w = c->wpe.ptr; g.bias = c->bpe; g.out = rows(w.x, q.r0, D, 4);
         g.M = (int64_t)q.nb * c->Np; g.N = D; g.K = c->Kp; g.lda = c->Kp; g.ldo = D;
         g.pos = c->pos; g.np = c->Np; g.ntok = c->N; g.has_cls = d.has_cls;
+        if (implicit_patch(c, qf, q.nb)) {
+            // the GEMM gathers and normalises its A tile from the frames
+            g.a = nullptr;
+            g.frames = qf; g.fT = d.frames; g.fH = d.img_h; g.fW = d.img_w; g.tubelet = d.tubelet;
+            g.patch = d.patch; g.patch_len = c->P;
+            for (int i = 0; i < 3; ++i) { g.pix_scale[i] = c->pix_scale[i]; g.pix_shift[i] = c->pix_shift[i]; }
+        } else {
+            PatchifyArgs pa{};
+            pa.frames = qf; pa.B = q.nb; pa.T = d.frames; pa.H = d.img_h; pa.W = d.img_w;
+            pa.tubelet = d.tubelet; pa.patch = d.patch;
+            for (int i = 0; i < 3; ++i) { pa.mean[i] = d.mean[i]; pa.std[i] = d.std[i]; }
+            pa.out = rows(w.patch, (int64_t)q.b0 * c->Np, c->Kp, es); pa.ld = c->Kp;
+            TRY(launch(c, K_PATCHIFY, q.s, [&] { return launch_patchify(c->act, pa, q.s); }));
+            g.a = pa.out;
+        }
         TRY(launch(c, K_GEMM_PATCH, q.s, [&] { return launch_gemm(c->act, c->act, EPI_PATCH, g, q.s); }));
         if (d.has_cls)
             TRY(launch(c, K_CLS_ROWS, q.s, [&] {
@@ -1359,6 +1387,30 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = out;
     g.M = M; g.N = N; g.K = K; g.lda = K; g.ldo = ldo;
     return hip_status(launch_gemm(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm");
+}
+
+jepa_status jepa_op_patch_embed(int act_dtype, const uint8_t *frames, int B, int T, int H, int W, int tubelet,
+                                int patch, const float *mean, const float *std, const void *w, int64_t k_pitch,
+                                int64_t n, const float *bias, const float *pos, int has_cls, float *out,
+                                void *hip_stream) {
+    if (!frames || !mean || !std || !w || !bias || !out) return fail(JEPA_E_INVALID_ARG, "op_patch_embed: null argument");
+    if (act_dtype != JEPA_F16 && act_dtype != JEPA_BF16) return fail(JEPA_E_DTYPE, "op_patch_embed: act must be F16 or BF16");
+    if (B <= 0 || T <= 0 || H <= 0 || W <= 0 || tubelet <= 0 || patch <= 0 || (has_cls != 0 && has_cls != 1) ||
+        H % patch || W % patch || T % tubelet)
+        return fail(JEPA_E_SHAPE, "op_patch_embed: bad shape");
+    GemmArgs g{};
+    g.w = w; g.bias = bias; g.out = out; g.pos = pos;
+    g.np = (T / tubelet) * (H / patch) * (W / patch);
+    g.ntok = g.np + has_cls; g.has_cls = has_cls;
+    g.M = (int64_t)B * g.np; g.N = n; g.K = k_pitch; g.lda = k_pitch; g.ldo = n;
+    g.frames = frames; g.fT = T; g.fH = H; g.fW = W; g.tubelet = tubelet; g.patch = patch;
+    g.patch_len = tubelet * patch * patch * 3;
+    for (int i = 0; i < 3; ++i) {
+        if (!(std[i] > 0.f)) return fail(JEPA_E_INVALID_ARG, "op_patch_embed: std must be > 0");
+        g.pix_scale[i] = (float)(1.0 / (255.0 * (double)std[i]));
+        g.pix_shift[i] = (float)(-(double)mean[i] / (double)std[i]);
+    }
+    return hip_status(launch_gemm(act_dtype, act_dtype, EPI_PATCH, g, (hipStream_t)hip_stream), "op_patch_embed");
 }
 
 jepa_status jepa_op_gemm_qkv(int act_dtype, const void *a, int64_t M, int64_t K, const void *w,

@@ -188,14 +188,19 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
             return;
         }
     }
-    constexpr int OES = EPI == EPI_RESID ? 4 : (int)sizeof(T);
+    constexpr int OES = (EPI == EPI_RESID || EPI == EPI_PATCH) ? 4 : (int)sizeof(T);
     constexpr int RB = 32 * NB_ * OES;           // bytes of one scratch row
     constexpr int CH = RB / 16;                  // 16-byte chunks per row = lanes per row
     constexpr int RPI = 64 / CH;                 // rows per read instruction
     constexpr int NRD = 32 / RPI;                // read instructions per 32-row block
     constexpr int SWM = (CH < 16 ? CH : 16) - 1; // chunk swizzle mask
     static_assert(CH <= 64 && 64 % CH == 0, "scratch row shape");
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g.out, (uint32_t)(g.M * g.ldo * OES));
+    // EPI_PATCH writes row b*np + n to row b*ntok + has_cls + n of an
+    // output of (M / np) * ntok rows, adding pos row has_cls + n
+    const uint32_t out_rows = EPI == EPI_PATCH ? (uint32_t)(g.M / g.np * g.ntok) : (uint32_t)g.M;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g.out, (uint32_t)(out_rows * g.ldo * OES));
+    const __amdgpu_buffer_rsrc_t rpos = buffer_rsrc(EPI == EPI_PATCH ? g.pos : nullptr,
+                                                    EPI == EPI_PATCH && g.pos ? (uint32_t)(g.ntok * g.ldo * 4) : 0u);
     const int rl = lane & 31, g32 = lane >> 5;
     const int rr = lane / CH, rc = lane % CH;     // read side: row in instruction, chunk
     const uint32_t rowb = (uint32_t)(g.ldo * OES);
@@ -292,8 +297,23 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 const float4 x = xv[i & 1][t];
                 v.x = x.x + v.x; v.y = x.y + v.y; v.z = x.z + v.z; v.w = x.w + v.w;
             }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
-                                                   gbase + (32 * i + t * RPI) * rowb, 0, 0);
+            if constexpr (EPI == EPI_PATCH) {
+                // rows past M map past the output's end, where the store is dropped
+                const uint32_t m = (uint32_t)(row0 + 32 * i + r);
+                const uint32_t b = m / (uint32_t)g.np, n = m - b * (uint32_t)g.np;
+                const uint32_t t_ = (uint32_t)g.has_cls + n;
+                const uint32_t cb = (uint32_t)(col0 * 4) + rc * 16;
+                if (g.pos) {
+                    const float4 q = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rpos, t_ * rowb + cb, 0, 0));
+                    v.x = v.x + q.x; v.y = v.y + q.y; v.z = v.z + q.z; v.w = v.w + q.w;
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                       (b * (uint32_t)g.ntok + t_) * rowb + cb, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                       gbase + (32 * i + t * RPI) * rowb, 0, 0);
+            }
         }
     }
 }
@@ -301,7 +321,7 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
 // TS = 2: 128 x 128 tiles (waves of 64 x 64); TS = 1: 64 x 64 tiles (waves
 // of 32 x 32, dense weights only), for GEMMs whose 128-wide tiles would
 // leave most CUs idle.
-template <typename T, int WF, int EPI, int TS>
+template <typename T, int WF, int EPI, int TS, bool IMPL = false>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     typedef Mfma<T> MM;
     constexpr int ES = sizeof(T);
@@ -341,14 +361,63 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     uint4 areg[4];
     BRegs<WF> breg;
 
-    auto load_global = [&](int kt) {
+    // Implicit patch-embed (IMPL): the A tile is gathered from the uint8
+    // frames.  K chunk q (8 elements, 8 consecutive bytes of one patch row:
+    // (patch * 3) % 8 == 0) sits at byte s_koff[q] past a row's patch origin
+    // fbase; its elements' channels run (k0 % 3, k0 % 3 + 1, ...), whose
+    // affines s_aff[k0 % 3][e] normalise them.  Rows past M read a clamped
+    // valid row: they only feed outputs that are never stored.
+    static_assert(!IMPL || (sizeof(T) == 2 && TS == 2 && DENSE), "implicit A: 16-bit, 128-wide tiles");
+    constexpr int MAX_KCH = 256;                     // K <= 2048
+    __shared__ uint32_t s_koff[IMPL ? MAX_KCH : 1];
+    __shared__ float2 s_aff[IMPL ? 24 : 1];
+    uint32_t fbase[IMPL ? 2 * TS : 1];
+    uint2 preg[IMPL ? 2 * TS : 1];
+    int a_r0 = 0;
+    bool a_pad = false;
+    if constexpr (IMPL) {
+        const int p = g.patch, p3 = 3 * p, pp3 = p * p3;
+        const uint32_t row_b = (uint32_t)g.fW * 3, frame_b = (uint32_t)g.fH * row_b;
+        for (int q = tid; q < (int)(g.K / 8); q += 256) {
+            const int k0 = 8 * q, dt = k0 / pp3, rem = k0 - dt * pp3, dy = rem / p3, w = rem - dy * p3;
+            s_koff[q] = k0 < g.patch_len ? (uint32_t)dt * frame_b + (uint32_t)dy * row_b + (uint32_t)w : 0xffffffffu;
+        }
+        if (tid < 24) {
+            const int ch = (tid / 8 + tid % 8) % 3;
+            s_aff[tid] = make_float2(g.pix_scale[ch], g.pix_shift[ch]);
+        }
+        const int Hp = g.fH / p, Wp = g.fW / p;
 #pragma unroll
         for (int i = 0; i < 2 * TS; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            const int64_t m = m0 + r;
-            areg[i] = make_uint4(0, 0, 0, 0);
-            if (m < g.M)
-                areg[i] = *(const uint4 *)(A + (m * g.lda + (int64_t)kt * BK) * ES + (tid & 7) * 16);
+            int64_t m = m0 + (tid >> 3) + 32 * i;
+            if (m >= g.M) m = g.M - 1;
+            const uint32_t b = (uint32_t)(m / g.np), n = (uint32_t)(m - (int64_t)b * g.np);
+            const uint32_t tt = n / (uint32_t)(Hp * Wp), rr = n - tt * (uint32_t)(Hp * Wp);
+            const uint32_t py = rr / (uint32_t)Wp, px = rr - py * (uint32_t)Wp;
+            fbase[i] = (b * (uint32_t)g.fT + tt * (uint32_t)g.tubelet) * frame_b + py * (uint32_t)p * row_b +
+                       px * (uint32_t)p3;
+        }
+        __syncthreads();
+    }
+
+    auto load_global = [&](int kt) {
+        if constexpr (IMPL) {
+            const int q = kt * 8 + (tid & 7);
+            const uint32_t ko = s_koff[q];
+            a_r0 = (8 * q) % 3;
+            a_pad = ko == 0xffffffffu;
+#pragma unroll
+            for (int i = 0; i < 2 * TS; ++i)
+                preg[i] = a_pad ? make_uint2(0, 0) : *(const uint2 *)(g.frames + fbase[i] + ko);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * TS; ++i) {
+                const int r = (tid >> 3) + 32 * i;
+                const int64_t m = m0 + r;
+                areg[i] = make_uint4(0, 0, 0, 0);
+                if (m < g.M)
+                    areg[i] = *(const uint4 *)(A + (m * g.lda + (int64_t)kt * BK) * ES + (tid & 7) * 16);
+            }
         }
         if constexpr (DENSE) {
 #pragma unroll
@@ -386,10 +455,31 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     auto store_lds = [&](int buf) {
         unsigned char *sa = smem[buf][0];
         unsigned char *sb = smem[buf][1];
+        if constexpr (IMPL) {
+            float sc[8], sh[8];
 #pragma unroll
-        for (int i = 0; i < 2 * TS; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            *(uint4 *)(sa + r * ROWB + (tid & 7) * 16) = areg[i];
+            for (int e = 0; e < 8; ++e) {
+                const float2 v = s_aff[8 * a_r0 + e];
+                sc[e] = a_pad ? 0.f : v.x;
+                sh[e] = a_pad ? 0.f : v.y;
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * TS; ++i) {
+                const int r = (tid >> 3) + 32 * i;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = fmaf((float)((preg[i].x >> (8 * e)) & 255u), sc[e], sh[e]);
+                    x[4 + e] = fmaf((float)((preg[i].y >> (8 * e)) & 255u), sc[4 + e], sh[4 + e]);
+                }
+                store_f16x8<T>(sa + r * ROWB + (tid & 7) * 16, x);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * TS; ++i) {
+                const int r = (tid >> 3) + 32 * i;
+                *(uint4 *)(sa + r * ROWB + (tid & 7) * 16) = areg[i];
+            }
         }
         if constexpr (DENSE) {
 #pragma unroll
@@ -463,23 +553,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 
     // ---- epilogue: block (i, j) holds rows m0 + wm*WT + i*32 + lane%32 and
     // columns n0 + wn*WT + j*32 + 8*(v/4) + 4*g + v%4 ----
-    const int g32 = lane >> 5;
-    if constexpr (EPI == EPI_PATCH) {
-#pragma unroll
-        for (int i = 0; i < TS; ++i) {
-            const int64_t row = m0 + wm * WT + i * 32 + (lane & 31);
-            if (row >= g.M) continue;
-#pragma unroll
-            for (int j = 0; j < TS; ++j) {
-                const int64_t col0 = n0 + wn * WT + j * 32 + 4 * g32;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t col = col0 + 8 * (v >> 2) + (v & 3);
-                    if (col < g.N) epilogue<T, EPI>(g, row, col, acc[i][j][v] + g.bias[col]);
-                }
-            }
-        }
-    } else if (n0 + wn * WT < g.N) {   // a wave's columns are all in or all out (N % 64 == 0)
+    if (n0 + wn * WT < g.N) {   // a wave's columns are all in or all out (N % 64 == 0)
         // the loop's last barrier has freed the operand tiles: 8 KB of scratch per wave
         if constexpr (sizeof(T) == 4 && EPI == EPI_RESID) {
             if (split) {   // the partial product, plain f32, into split z's [M, N] slice
@@ -801,6 +875,15 @@ hipError_t launch_big(const GemmArgs &g, hipStream_t s) {
 
 template <typename T, int WF, int EPI>
 hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
+    if constexpr (EPI == EPI_PATCH && sizeof(T) == 2 && WF == DT_F32) {
+        if (g.frames) {   // implicit: the A tile gathered from the frames
+            GemmArgs gi = g;
+            gi.ksplit = 1;
+            dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(g.M, BM));
+            hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 2, true>), grid, dim3(256), 0, s, gi);
+            return hipGetLastError();
+        }
+    }
     if constexpr (sizeof(T) == 2 && WF == DT_F32 && EPI != EPI_PATCH) {
         const char *v = getenv("JEPA_GEMM_VARIANT");
         const std::string var = v ? v : "";
@@ -893,7 +976,23 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % bk || g.N % 64) return hipErrorInvalidValue;
     if (g.lda < g.K || (epi != EPI_PATCH && g.ldo < g.N)) return hipErrorInvalidValue;
     if (g.M / BM >= 65535) return hipErrorInvalidValue;
-    if (epi == EPI_PATCH && (g.np <= 0 || g.M % g.np)) return hipErrorInvalidValue;
+    if (epi == EPI_PATCH) {
+        if (g.np <= 0 || g.M % g.np || g.ntok < g.np + g.has_cls) return hipErrorInvalidValue;
+        // rows up to M + 255 map below 2^32 bytes of output; pos rows are 16-byte vectors
+        if (((g.M + 256) / g.np + 1) * g.ntok * g.ldo * 4 >= (1ll << 32) || (g.ldo * 4) % 16 ||
+            ((uintptr_t)g.pos & 15))
+            return hipErrorInvalidValue;
+        if (g.frames) {
+            const int64_t p = g.patch, row_b = (int64_t)g.fW * 3;
+            const int64_t items = g.M / g.np;
+            if (act_dt == DT_F32 || w_dt != act_dt || p <= 0 || g.tubelet <= 0 || g.fH % p || g.fW % p ||
+                g.fT % g.tubelet || (3 * p) % 8 || row_b % 8 || ((uintptr_t)g.frames & 7) ||
+                g.patch_len != g.tubelet * p * p * 3 || g.K < g.patch_len || g.K / 8 > 256 ||
+                g.np != (g.fT / g.tubelet) * (g.fH / p) * (g.fW / p) ||
+                items * g.fT * g.fH * row_b >= (1ll << 32))
+                return hipErrorInvalidValue;
+        }
+    }
     if (epi == EPI_QKV) {
         // v starts at a multiple of 128 columns, so no wave straddles q/k and v
         if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||

@@ -57,6 +57,15 @@ struct GemmArgs {
     // a second pass adds the bias and the splits in order to the output
     float *kpart;
     int ksplit;              // set by the launcher
+    // EPI_PATCH straight from the frames (implicit GEMM; a unused): uint8
+    // [items, fT, fH, fW, 3], row r = b*np + n being patch n of item b, its
+    // patch vector (dt, dy, dx, c) gathered and normalised on the way into
+    // LDS as act(u * pix_scale[c] + pix_shift[c]); K columns >= patch_len
+    // read as 0.  Needs a 16-bit act dtype, (patch * 3) % 8 == 0,
+    // (fW * 3) % 8 == 0 and 8-byte aligned frames.
+    const uint8_t *frames;
+    int fT, fH, fW, tubelet, patch, patch_len;
+    float pix_scale[3], pix_shift[3];
 };
 constexpr int KSPLIT_MAX = 8;
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
