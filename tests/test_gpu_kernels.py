@@ -248,6 +248,10 @@ def test_gemm_block_formats(lib, wfmt, act, epi):
     ("bf16", "dense", 2, 3137, 16, 1024),   # the LeVJEPA ViT-L/16 qkv layer, two clips
     ("bf16", "dense", 9, 197, 4, 640),      # 256-row tiles, 256 wide, several items per wave tile
     ("f16", "dense", 5, 301, 6, 576),       # 256-row tiles, 128 wide (N = 1152)
+    # items starting at multiples of 16 rows: V^T rows written straight from the accumulators
+    ("bf16", "dense", 1, 3137, 16, 1024),   # one LeVJEPA clip (one batch part): the last run crosses M
+    ("f16", "dense", 3, 512, 4, 640),       # 256 wide, items of 512 tokens
+    ("bf16", "dense", 2, 1024, 6, 640),     # 128 wide (N = 1152), items of 1024 tokens
 ])
 def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, qscaled, rope, dh):
     """q and k columns as a plain linear layer (rotated pairwise by a table of

@@ -163,6 +163,61 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
     }
 }
 
+// The v columns of the qkv product written to V^T straight from the
+// accumulators, when the MFMAs took the token operand first: element 4q + r
+// of block (i, j) of lane l is token row 32 i + 8 q + 4 (l / 32) + r of the
+// wave's tile and v column 32 j + l % 32.  Tokens are aligned in runs of 16
+// within their item (items a multiple of 16 tokens long, or one item), and
+// a V^T row holds each run as tokens 0-3, 8-11, 4-7, 12-15: so the two
+// 4-token groups q = 2h, 2h + 1 of a lane are 8 consecutive positions of
+// its column's V^T row, stored as one 16-byte vector.  A run that crosses
+// M (the one item's last, when it is not a multiple of 16 long) is stored
+// element by element for the tokens below M: V^T's free positions stay
+// untouched.  Runs past M fall past the end of V^T and are dropped.
+template <typename T, int MB_, int NB_>
+__device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
+                                                   const float *sb, int64_t row0, int64_t col0, int lane) {
+    constexpr int OES = (int)sizeof(T);
+    static_assert(OES == 2, "16-bit V^T");
+    const int64_t D = g.N - g.vcol0;
+    const int64_t nitems = g.M / g.ntok;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g.vt, (uint32_t)(nitems * D * g.npad * OES));
+    const int cl = lane & 31, g32 = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < NB_; ++j) {
+        const uint32_t dc = (uint32_t)(col0 + 32 * j + cl - g.vcol0);   // V^T row within an item
+        const float bj = sb[32 * j + cl];
+#pragma unroll
+        for (int i = 0; i < MB_; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t ms = (uint32_t)(row0 + 32 * i + 16 * h);    // the run's first token row
+                const uint32_t b = ms / (uint32_t)g.ntok, ns = ms - b * (uint32_t)g.ntok;
+                const uint32_t off = ((b * (uint32_t)D + dc) * (uint32_t)g.npad + ns + 8 * g32) * OES;
+                float x[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[r] = acc[i][j][4 * (2 * h) + r] + bj;
+                    x[4 + r] = acc[i][j][4 * (2 * h + 1) + r] + bj;
+                }
+                if (ms + 16 <= (uint32_t)g.M || ms >= (uint32_t)g.M) {
+                    const u32x4 v = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]), pack2<T>(x[4], x[5]),
+                                     pack2<T>(x[6], x[7])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        // position 8 g32 + e of the run holds token (e < 4 ? e : e + 4) + 4 g32
+                        const uint32_t tok = ms + 4 * g32 + (e < 4 ? e : e + 4);
+                        if (tok < (uint32_t)g.M)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                __builtin_bit_cast(unsigned short, from_f32<T>(x[e])), rs, off + 2 * e, 0, 0);
+                    }
+                }
+            }
+    }
+}
+
 // The output stage of one wave's MB_ x NB_ accumulator blocks (STORE / GELU
 // / RESID).  The blocks are accumulated transposed (the weights are the
 // MFMA's A operand): element 4q + r of block (i, j) of lane l is output row
@@ -177,11 +232,11 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
 // rows past M need no branch.  RESID reads X one block ahead of its writes
 // (issued after the block's staging, to keep one buffer live there), and each
 // element is read and written by one lane only.
-template <typename T, int EPI, int MB_, int NB_>
+template <typename T, int EPI, int MB_, int NB_, bool NO_VT = false>
 __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
                                               const float *sb, unsigned char *ls, int64_t row0,
                                               int64_t col0, int lane) {
-    if constexpr (EPI == EPI_QKV) {
+    if constexpr (EPI == EPI_QKV && !NO_VT) {   // (NO_VT: the caller writes v columns itself)
         // a wave's columns are all q/k or all v (v starts at a multiple of 128)
         if (col0 >= g.vcol0) {
             epilogue_wave_vt<T, MB_, NB_>(g, acc, sb, ls, row0, col0, lane);
@@ -628,7 +683,7 @@ __device__ __forceinline__ void sched_chunk() {
     sched_chunk_seq<ID, MBNB, NDS, NVM>(std::make_integer_sequence<int, MBNB>{});
 }
 
-template <typename T, int EPI, int BN>
+template <typename T, int EPI, int BN, bool VTD = false>
 __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int tiles_m, int tiles_n) {
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
@@ -708,135 +763,154 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         }
     };
 
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // operand rows of this lane (same swizzle for every row of a 32-row block)
-    const int rl = lane & 31, sw = swz8(rl);
-    int arow[MB], brow[NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) arow[i] = (wm * 128 + i * 32 + rl) * 128;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) brow[j] = A_BYTES + (wn * (BN / 2) + j * 32 + rl) * 128;
-
-    // Operands move LDS -> registers one 16-element K chunk (of 4 per step)
-    // ahead of the MFMAs that use them, in two register sets; the first chunk
-    // of step kt+1 is read, after the step's barrier, while the MFMAs of the
-    // last chunk of step kt run.
-    vec a[2][MB], b[2][NB];                       // [register set][block]
-    auto read_chunk = [&](const unsigned char *sm, int c, int buf) __attribute__((always_inline)) {
-        const int slot = ((2 * c + g32) ^ sw) << 4;
-#pragma unroll
-        for (int i = 0; i < MB; ++i) a[buf][i] = MM::load(sm + arow[i] + slot);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) b[buf][j] = MM::load(sm + brow[j] + slot);
-    };
-    auto mma_chunk = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
+    auto body = [&](auto SWAPC) __attribute__((always_inline)) {
+        constexpr bool SWAP = decltype(SWAPC)::value;
+        f32x16 acc[MB][NB];
+    #pragma unroll
         for (int i = 0; i < MB; ++i)
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < NB; ++j)
-                acc[i][j] = MM::mma(b[buf][j], a[buf][i], acc[i][j]);   // transposed
-    };
-    // s_waitcnt lgkmcnt(0) with at most n of this thread's loads in flight
-    auto wait_loads = [&](int n) __attribute__((always_inline)) {
-        switch (n) {
-            case 0: __builtin_amdgcn_s_waitcnt(0x070); break;
-            case HALF: __builtin_amdgcn_s_waitcnt(0x070 | (HALF & 15) | ((HALF >> 4) << 14)); break;
-            case LPS: __builtin_amdgcn_s_waitcnt(0x070 | (LPS & 15) | ((LPS >> 4) << 14)); break;
-            default: __builtin_amdgcn_s_waitcnt(0x070 | ((LPS + HALF) & 15) | (((LPS + HALF) >> 4) << 14)); break;
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        // operand rows of this lane (same swizzle for every row of a 32-row block)
+        const int rl = lane & 31, sw = swz8(rl);
+        int arow[MB], brow[NB];
+    #pragma unroll
+        for (int i = 0; i < MB; ++i) arow[i] = (wm * 128 + i * 32 + rl) * 128;
+    #pragma unroll
+        for (int j = 0; j < NB; ++j) brow[j] = A_BYTES + (wn * (BN / 2) + j * 32 + rl) * 128;
+
+        // Operands move LDS -> registers one 16-element K chunk (of 4 per step)
+        // ahead of the MFMAs that use them, in two register sets; the first chunk
+        // of step kt+1 is read, after the step's barrier, while the MFMAs of the
+        // last chunk of step kt run.
+        vec a[2][MB], b[2][NB];                       // [register set][block]
+        auto read_chunk = [&](const unsigned char *sm, int c, int buf) __attribute__((always_inline)) {
+            const int slot = ((2 * c + g32) ^ sw) << 4;
+    #pragma unroll
+            for (int i = 0; i < MB; ++i) a[buf][i] = MM::load(sm + arow[i] + slot);
+    #pragma unroll
+            for (int j = 0; j < NB; ++j) b[buf][j] = MM::load(sm + brow[j] + slot);
+        };
+        auto mma_chunk = [&](int buf) __attribute__((always_inline)) {
+    #pragma unroll
+            for (int i = 0; i < MB; ++i)
+    #pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    if constexpr (SWAP)
+                        acc[i][j] = MM::mma(a[buf][i], b[buf][j], acc[i][j]);   // tokens first: V^T layout
+                    else
+                        acc[i][j] = MM::mma(b[buf][j], a[buf][i], acc[i][j]);   // transposed
+                }
+        };
+        // s_waitcnt lgkmcnt(0) with at most n of this thread's loads in flight
+        auto wait_loads = [&](int n) __attribute__((always_inline)) {
+            switch (n) {
+                case 0: __builtin_amdgcn_s_waitcnt(0x070); break;
+                case HALF: __builtin_amdgcn_s_waitcnt(0x070 | (HALF & 15) | ((HALF >> 4) << 14)); break;
+                case LPS: __builtin_amdgcn_s_waitcnt(0x070 | (LPS & 15) | ((LPS >> 4) << 14)); break;
+                default: __builtin_amdgcn_s_waitcnt(0x070 | ((LPS + HALF) & 15) | (((LPS + HALF) >> 4) << 14)); break;
+            }
+        };
+
+        // Step kt (stage S = kt % NS, a compile-time constant): chunk 0 carries the
+        // second half of step kt+NS-1's loads, chunk 3 (after the barrier that
+        // frees stage S) the first half of step kt+NS's.  At the barrier the loads
+        // allowed in flight are those of the steps after kt+1.
+        auto steady_step = [&](auto S, int kt) __attribute__((always_inline)) {
+            constexpr int s = decltype(S)::value;
+            unsigned char *cur = stage(S);
+            unsigned char *nxt = stage(std::integral_constant<int, (s + 1) % NS>{});
+            unsigned char *prv = stage(std::integral_constant<int, (s + NS - 1) % NS>{});
+            read_chunk(cur, 1, 1);
+            issue_half(prv, kt + NS - 1, 1);
+            mma_chunk(0);
+            sched_chunk<0, MBNB, NRD, HALF>();
+            read_chunk(cur, 2, 0);
+            mma_chunk(1);
+            sched_chunk<1, MBNB, NRD, 0>();
+            read_chunk(cur, 3, 1);
+            mma_chunk(0);
+            sched_chunk<2, MBNB, NRD, 0>();
+            wait_loads((NS - 2) * LPS);               // step kt+1 landed
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_chunk(nxt, 0, 0);
+            issue_half(cur, kt + NS, 0);
+            mma_chunk(1);
+            sched_chunk<3, MBNB, NRD, HALF>();
+        };
+
+        // the tile's biases, to LDS behind the first stages' loads (N % BN == 0)
+        float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < BN / 4) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
+        // prologue: stages 0 .. NS-2 whole, the first half of stage NS-1
+    #pragma unroll
+        for (int s0 = 0; s0 < NS - 1; ++s0)
+            if (s0 < nk) { issue_half(stage_rt(s0), s0, 0); issue_half(stage_rt(s0), s0, 1); }
+        if (NS - 1 < nk) issue_half(stage_rt(NS - 1), NS - 1, 0);
+        if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
+        wait_loads(min(NS - 2, nk - 1) * LPS + (NS - 1 < nk ? HALF : 0));   // step 0 landed
+        __builtin_amdgcn_s_barrier();
+        read_chunk(lds0, 0, 0);
+
+        // Steady steps (a stage to start) in groups of NS, so that every stage is
+        // named at compile time; the loop bodies have no branch around their
+        // operand reads (a join with a path that skipped them makes the compiler
+        // wait for all of them).
+        int kt = 0;
+        for (; kt + 2 * NS - 1 < nk; kt += NS) {
+            steady_step(std::integral_constant<int, 0>{}, kt);
+            steady_step(std::integral_constant<int, 1>{}, kt + 1);
+            if constexpr (NS == 3) steady_step(std::integral_constant<int, 2>{}, kt + 2);
         }
-    };
+        // the remaining steps but the last, with run-time stages (a second set of
+        // compile-time bodies here would exhaust the registers)
+        for (; kt < nk - 1; ++kt) {
+            unsigned char *cur = stage_rt(kt % NS);
+            read_chunk(cur, 1, 1);
+            if (kt + NS - 1 < nk) issue_half(stage_rt((kt + NS - 1) % NS), kt + NS - 1, 1);
+            mma_chunk(0);
+            read_chunk(cur, 2, 0);
+            mma_chunk(1);
+            read_chunk(cur, 3, 1);
+            mma_chunk(0);
+            wait_loads(min(NS - 2, nk - 2 - kt) * LPS);   // step kt+1 landed
+            __builtin_amdgcn_s_barrier();
+            read_chunk(stage_rt((kt + 1) % NS), 0, 0);
+            if (kt + NS < nk) issue_half(cur, kt + NS, 0);
+            mma_chunk(1);
+        }
+        {
+            const unsigned char *cur = stage_rt((nk - 1) % NS);
+            read_chunk(cur, 1, 1);
+            mma_chunk(0);
+            read_chunk(cur, 2, 0);
+            mma_chunk(1);
+            read_chunk(cur, 3, 1);
+            mma_chunk(0);
+            mma_chunk(1);
+        }
 
-    // Step kt (stage S = kt % NS, a compile-time constant): chunk 0 carries the
-    // second half of step kt+NS-1's loads, chunk 3 (after the barrier that
-    // frees stage S) the first half of step kt+NS's.  At the barrier the loads
-    // allowed in flight are those of the steps after kt+1.
-    auto steady_step = [&](auto S, int kt) __attribute__((always_inline)) {
-        constexpr int s = decltype(S)::value;
-        unsigned char *cur = stage(S);
-        unsigned char *nxt = stage(std::integral_constant<int, (s + 1) % NS>{});
-        unsigned char *prv = stage(std::integral_constant<int, (s + NS - 1) % NS>{});
-        read_chunk(cur, 1, 1);
-        issue_half(prv, kt + NS - 1, 1);
-        mma_chunk(0);
-        sched_chunk<0, MBNB, NRD, HALF>();
-        read_chunk(cur, 2, 0);
-        mma_chunk(1);
-        sched_chunk<1, MBNB, NRD, 0>();
-        read_chunk(cur, 3, 1);
-        mma_chunk(0);
-        sched_chunk<2, MBNB, NRD, 0>();
-        wait_loads((NS - 2) * LPS);               // step kt+1 landed
+        // every wave has read its last operands: stage 0 becomes output scratch
+        static_assert(4 * 64 * BN <= ST, "epilogue scratch");
         __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_chunk(nxt, 0, 0);
-        issue_half(cur, kt + NS, 0);
-        mma_chunk(1);
-        sched_chunk<3, MBNB, NRD, HALF>();
+        if constexpr (SWAP)
+            epilogue_vt_direct<T, MB, NB>(g, acc, sbias + wn * (BN / 2), m0 + wm * 128, n0 + wn * (BN / 2), lane);
+        else
+            epilogue_wave<T, EPI, MB, NB, VTD>(g, acc, sbias + wn * (BN / 2), lds0 + wave * (64 * BN),
+                                               m0 + wm * 128, n0 + wn * (BN / 2), lane);
     };
-
-    // the tile's biases, to LDS behind the first stages' loads (N % BN == 0)
-    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < BN / 4) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
-    // prologue: stages 0 .. NS-2 whole, the first half of stage NS-1
-#pragma unroll
-    for (int s0 = 0; s0 < NS - 1; ++s0)
-        if (s0 < nk) { issue_half(stage_rt(s0), s0, 0); issue_half(stage_rt(s0), s0, 1); }
-    if (NS - 1 < nk) issue_half(stage_rt(NS - 1), NS - 1, 0);
-    if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
-    wait_loads(min(NS - 2, nk - 1) * LPS + (NS - 1 < nk ? HALF : 0));   // step 0 landed
-    __builtin_amdgcn_s_barrier();
-    read_chunk(lds0, 0, 0);
-
-    // Steady steps (a stage to start) in groups of NS, so that every stage is
-    // named at compile time; the loop bodies have no branch around their
-    // operand reads (a join with a path that skipped them makes the compiler
-    // wait for all of them).
-    int kt = 0;
-    for (; kt + 2 * NS - 1 < nk; kt += NS) {
-        steady_step(std::integral_constant<int, 0>{}, kt);
-        steady_step(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (NS == 3) steady_step(std::integral_constant<int, 2>{}, kt + 2);
+    // VTD (qkv with vt_direct, launched only when v starts at a multiple of
+    // BN, so that every tile is all q / k or all v): the v tiles take the
+    // token operand first and write V^T rows straight from the accumulators
+    if constexpr (EPI == EPI_QKV && VTD) {
+        if (n0 >= g.vcol0) body(std::true_type{});
+        else body(std::false_type{});
+    } else {
+        body(std::false_type{});
     }
-    // the remaining steps but the last, with run-time stages (a second set of
-    // compile-time bodies here would exhaust the registers)
-    for (; kt < nk - 1; ++kt) {
-        unsigned char *cur = stage_rt(kt % NS);
-        read_chunk(cur, 1, 1);
-        if (kt + NS - 1 < nk) issue_half(stage_rt((kt + NS - 1) % NS), kt + NS - 1, 1);
-        mma_chunk(0);
-        read_chunk(cur, 2, 0);
-        mma_chunk(1);
-        read_chunk(cur, 3, 1);
-        mma_chunk(0);
-        wait_loads(min(NS - 2, nk - 2 - kt) * LPS);   // step kt+1 landed
-        __builtin_amdgcn_s_barrier();
-        read_chunk(stage_rt((kt + 1) % NS), 0, 0);
-        if (kt + NS < nk) issue_half(cur, kt + NS, 0);
-        mma_chunk(1);
-    }
-    {
-        const unsigned char *cur = stage_rt((nk - 1) % NS);
-        read_chunk(cur, 1, 1);
-        mma_chunk(0);
-        read_chunk(cur, 2, 0);
-        mma_chunk(1);
-        read_chunk(cur, 3, 1);
-        mma_chunk(0);
-        mma_chunk(1);
-    }
-
-    // every wave has read its last operands: stage 0 becomes output scratch
-    static_assert(4 * 64 * BN <= ST, "epilogue scratch");
-    __builtin_amdgcn_s_barrier();
-    epilogue_wave<T, EPI, MB, NB>(g, acc, sbias + wn * (BN / 2), lds0 + wave * (64 * BN), m0 + wm * 128,
-                                  n0 + wn * (BN / 2), lane);
 }
 
 // Variant choice (below); JEPA_GEMM_VARIANT (small | small64 | big256 | big128) pins it.
@@ -869,6 +943,12 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float *out, int64_t 
 template <typename T, int EPI, int BN>
 hipError_t launch_big(const GemmArgs &g, hipStream_t s) {
     const int tm = (int)cdiv(g.M, BIG_BM), tn = (int)cdiv(g.N, BN);
+    if constexpr (EPI == EPI_QKV) {
+        if (g.vt_direct && g.vcol0 % BN == 0) {
+            hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN, true>), dim3(tm * tn), dim3(256), 0, s, g, tm, tn);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN>), dim3(tm * tn), dim3(256), 0, s, g, tm, tn);
     return hipGetLastError();
 }
@@ -999,7 +1079,7 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
             g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15) ||
             (g.rope && g.head_dim != 32 && g.head_dim != 64))
             return hipErrorInvalidValue;
-        if ((g.M / g.ntok) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
+        if ((g.M / g.ntok + 1) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
     }
     // the epilogue addresses the output through a buffer resource with 32-bit
     // byte offsets (rows up to M + 255 are formed, those past M dropped)
@@ -1011,16 +1091,18 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     const bool dense = (w_dt == act_dt);
     if (!dense && (act_dt == DT_F32 || (w_dt != DT_Q8_0 && w_dt != DT_Q4_0) || !g.wscale))
         return hipErrorInvalidValue;
+    GemmArgs ga = g;
+    ga.vt_direct = epi == EPI_QKV && (g.ntok % 16 == 0 || g.M == g.ntok);
     switch (act_dt) {
-        case DT_F32: return launch_epi<float, DT_F32>(epi, g, s);
+        case DT_F32: return launch_epi<float, DT_F32>(epi, ga, s);
         case DT_BF16:
-            if (dense) return launch_epi<bf16_t, DT_F32>(epi, g, s);
-            if (w_dt == DT_Q8_0) return launch_epi<bf16_t, DT_Q8_0>(epi, g, s);
-            return launch_epi<bf16_t, DT_Q4_0>(epi, g, s);
+            if (dense) return launch_epi<bf16_t, DT_F32>(epi, ga, s);
+            if (w_dt == DT_Q8_0) return launch_epi<bf16_t, DT_Q8_0>(epi, ga, s);
+            return launch_epi<bf16_t, DT_Q4_0>(epi, ga, s);
         case DT_F16:
-            if (dense) return launch_epi<f16_t, DT_F32>(epi, g, s);
-            if (w_dt == DT_Q8_0) return launch_epi<f16_t, DT_Q8_0>(epi, g, s);
-            return launch_epi<f16_t, DT_Q4_0>(epi, g, s);
+            if (dense) return launch_epi<f16_t, DT_F32>(epi, ga, s);
+            if (w_dt == DT_Q8_0) return launch_epi<f16_t, DT_Q8_0>(epi, ga, s);
+            return launch_epi<f16_t, DT_Q4_0>(epi, ga, s);
     }
     return hipErrorInvalidValue;
 }

@@ -49,6 +49,10 @@ struct GemmArgs {
     const float *rope;
     int head_dim;            // 32 or 64 (the rotary pairs' period)
     float qscale;
+    // EPI_QKV: set by the launcher when every item starts its tokens at a
+    // multiple of 16 rows (ntok % 16 == 0, or one item): the large tile
+    // then writes V^T straight from its accumulators
+    int vt_direct;
     // launches of this shape expected to run concurrently (batch parts on
     // other streams; 0 or 1: none), a hint for the tile-shape choice
     int conc;
