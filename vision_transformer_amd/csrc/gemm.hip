@@ -1093,6 +1093,8 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
         return hipErrorInvalidValue;
     GemmArgs ga = g;
     ga.vt_direct = epi == EPI_QKV && (g.ntok % 16 == 0 || g.M == g.ntok);
+    if (const char *e = getenv("JEPA_VT_DIRECT"))
+        if (!strcmp(e, "0")) ga.vt_direct = 0;
     switch (act_dt) {
         case DT_F32: return launch_epi<float, DT_F32>(epi, ga, s);
         case DT_BF16:

@@ -1,5 +1,8 @@
 // The bandwidth-bound kernels of the encoder: patchify (pixel ingest and
 // normalisation), LayerNorm, CLS rows, pooling and dequantisation.
+#include <stdlib.h>
+#include <string.h>
+
 #include <algorithm>
 
 #include "common.hpp"
@@ -79,10 +82,64 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
     }
 }
 
+// The same LayerNorm for D a multiple of 256, one wavefront per row with
+// 16-byte accesses: lane l holds elements 4 l + 256 i + {0..3}.
+template <int EV, typename TO>
+__global__ __launch_bounds__(256) void layernorm_vec_kernel(const float *__restrict__ x, int64_t rows,
+                                                            const float *__restrict__ gam,
+                                                            const float *__restrict__ bet, float eps,
+                                                            TO *__restrict__ y) {
+    constexpr int D = 256 * EV;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float4 *xr = (const float4 *)(x + row * D);
+    float4 v[EV];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < EV; ++i) v[i] = xr[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < EV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    const float mean = wave_sum(s) * (1.f / D);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < EV; ++i) {
+        const float c0 = v[i].x - mean, c1 = v[i].y - mean, c2 = v[i].z - mean, c3 = v[i].w - mean;
+        q = fmaf(c0, c0, q);
+        q = fmaf(c1, c1, q);
+        q = fmaf(c2, c2, q);
+        q = fmaf(c3, c3, q);
+    }
+    const float rs = rsqrtf(wave_sum(q) * (1.f / D) + eps);
+#pragma unroll
+    for (int i = 0; i < EV; ++i) {
+        const int d = 4 * (lane + 64 * i);
+        const float4 gv = *(const float4 *)(gam + d), bv = *(const float4 *)(bet + d);
+        const float o0 = (v[i].x - mean) * rs * gv.x + bv.x, o1 = (v[i].y - mean) * rs * gv.y + bv.y;
+        const float o2 = (v[i].z - mean) * rs * gv.z + bv.z, o3 = (v[i].w - mean) * rs * gv.w + bv.w;
+        if constexpr (sizeof(TO) == 4) {
+            *(float4 *)((float *)y + row * D + d) = make_float4(o0, o1, o2, o3);
+        } else {
+            *(uint2 *)((TO *)y + row * D + d) = make_uint2(pack2<TO>(o0, o1), pack2<TO>(o2, o3));
+        }
+    }
+}
+
 template <typename TO>
 hipError_t ln_dispatch(const float *x, int64_t rows, int dim, const float *g, const float *b,
                        float eps, void *y, hipStream_t s) {
     dim3 grid((unsigned)cdiv(rows, 4));
+    const char *e = getenv("JEPA_LN_VEC");
+    const bool vec = !(e && !strcmp(e, "0")) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)g % 16 == 0) &&
+                     ((uintptr_t)b % 16 == 0) && ((uintptr_t)y % 16 == 0);
+    if (vec) {
+        switch (dim) {
+            case 1024: hipLaunchKernelGGL((layernorm_vec_kernel<4, TO>), grid, dim3(256), 0, s, x, rows, g, b, eps, (TO *)y); return hipGetLastError();
+            case 768: hipLaunchKernelGGL((layernorm_vec_kernel<3, TO>), grid, dim3(256), 0, s, x, rows, g, b, eps, (TO *)y); return hipGetLastError();
+            case 512: hipLaunchKernelGGL((layernorm_vec_kernel<2, TO>), grid, dim3(256), 0, s, x, rows, g, b, eps, (TO *)y); return hipGetLastError();
+            case 1280: hipLaunchKernelGGL((layernorm_vec_kernel<5, TO>), grid, dim3(256), 0, s, x, rows, g, b, eps, (TO *)y); return hipGetLastError();
+        }
+    }
 #define LN_CASE(E)                                                                         \
     case E:                                                                                \
         hipLaunchKernelGGL((layernorm_kernel<E, TO>), grid, dim3(256), 0, s, x, rows, g, b, \
