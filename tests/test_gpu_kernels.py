@@ -188,7 +188,12 @@ def test_gemm_large_tile(lib, monkeypatch, variant, N, K, epi):
 
 FFN_CASES = [
     # name, M, N, K, epilogue, variant ("" = the launcher's own choice)
-    ("fc1", 12548, 4096, 1024, "gelu", ""),        # LeVJEPA ViT-L/16, batch 4, in one part
+    # LeVJEPA ViT-L/16, batch 4, in one part: the 256 x 256 tiles would leave
+    # a 4th round 12 % full, so 12288 rows take them and 260 the 64-wide tiles
+    ("fc1", 12548, 4096, 1024, "gelu", ""),
+    # the qkv width with a plain store: 10752 rows on 256 x 256 tiles, 1796 on
+    # 256 x 128 ones (a 3rd round 34 % full avoided)
+    ("qkv", 12548, 3072, 1024, "store", ""),
     ("fc2", 12548, 1024, 4096, "resid", ""),       # 64 K steps, 256 x 256 tiles
     ("fc1", 1300, 4096, 1024, "gelu", "big256"),
     ("fc2", 1300, 1024, 4096, "resid", "big256"),
@@ -318,6 +323,15 @@ def test_gemm_qkv_writes_v_transposed(lib, act, wfmt, B, N, heads, K, qscaled, r
     assert np.all(np.abs(got_vt[..., pos] - want) <= bnd)
     free = np.setdiff1d(np.arange(npad), pos)
     assert np.all(got_vt[..., free] == 7.0)                      # positions of no token untouched
+
+
+@pytest.mark.parametrize("rope", [False, True], ids=["norope", "rope"])
+def test_gemm_qkv_rows_split_over_two_tilings(lib, rope):
+    """The LeVJEPA ViT-L/16 qkv layer on the whole batch of 4 clips in one
+    launch (12548 rows): the rows of the full rounds of 256 x 256 tiles
+    (10752) and the rest (1796, 256 x 128 tiles) go to two launches, both
+    writing V^T from the accumulators; every q, k and V^T element checked."""
+    test_gemm_qkv_writes_v_transposed(lib, "bf16", "dense", 4, 3137, 16, 1024, True, rope, 64)
 
 
 def _vt_of(lib, act, qkv_dev, B, N, heads, dh=64):

@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
+    const int64_t m0 = g.m_begin + (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
     // K steps [kt0, kt0 + nk): all of K, or split blockIdx.z of a K split
     // (f32 residual GEMMs; the launcher makes every split non-empty)
     const int nk_all = (int)(g.K / BK);
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     const int gm = min(tiles_m - first_m, GROUP_M);
     const int tm = first_m + (pid % (GROUP_M * tiles_n)) % gm;
     const int tn = (pid % (GROUP_M * tiles_n)) / gm;
-    const int64_t m0 = (int64_t)tm * BIG_BM, n0 = (int64_t)tn * BN;
+    const int64_t m0 = g.m_begin + (int64_t)tm * BIG_BM, n0 = (int64_t)tn * BN;
     const int nk = (int)(g.K / BIG_BK);
 
     const unsigned char *A = (const unsigned char *)g.a;
@@ -941,25 +941,29 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float *out, int64_t 
 }
 
 template <typename T, int EPI, int BN>
-hipError_t launch_big(const GemmArgs &g, hipStream_t s) {
-    const int tm = (int)cdiv(g.M, BIG_BM), tn = (int)cdiv(g.N, BN);
+hipError_t launch_big(const GemmArgs &g, hipStream_t s, int64_t tm = 0) {
+    // tm: the launch's row tiles (0: enough for rows [m_begin, M))
+    if (tm <= 0) tm = cdiv(g.M - g.m_begin, BIG_BM);
+    const int64_t tn = cdiv(g.N, BN);
     if constexpr (EPI == EPI_QKV) {
         if (g.vt_direct && g.vcol0 % BN == 0) {
-            hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN, true>), dim3(tm * tn), dim3(256), 0, s, g, tm, tn);
+            hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN, true>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, g,
+                               (int)tm, (int)tn);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN>), dim3(tm * tn), dim3(256), 0, s, g, tm, tn);
+    hipLaunchKernelGGL((gemm_big_kernel<T, EPI, BN>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, g, (int)tm, (int)tn);
     return hipGetLastError();
 }
 
 template <typename T, int WF, int EPI>
 hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
+    const int64_t rows = g.M - g.m_begin;          // this launch's rows [m_begin, M)
     if constexpr (EPI == EPI_PATCH && sizeof(T) == 2 && WF == DT_F32) {
         if (g.frames) {   // implicit: the A tile gathered from the frames
             GemmArgs gi = g;
             gi.ksplit = 1;
-            dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(g.M, BM));
+            dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(rows, BM));
             hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 2, true>), grid, dim3(256), 0, s, gi);
             return hipGetLastError();
         }
@@ -984,12 +988,32 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
         // stays on the 128 x 128 tile: the large tile's prologue and epilogue,
         // which nothing overlaps at one workgroup per CU, outweigh its K loop
         // (measured 3.60 vs 3.75 ms per predictor-width forward).
-        if (big_ok && var.empty() && g.M >= 1024 && g.K > 512) {
+        if (big_ok && var.empty() && rows >= 1024 && g.K > 512) {
+            const int64_t cus = cu_count(), conc = g.conc > 1 ? g.conc : 1;
             if (g.N % 256 == 0) {
-                const int64_t cus = cu_count(), conc = g.conc > 1 ? g.conc : 1;
-                const int64_t tm = cdiv(g.M, BIG_BM);
-                const int64_t r256 = cdiv(tm * (g.N / 256) * conc, cus), r128 = cdiv(tm * (g.N / 128) * conc, cus);
-                if (10 * r256 <= 6 * r128) return launch_big<T, EPI, 256>(g, s);
+                const int64_t tm = cdiv(rows, BIG_BM), tn = g.N / 256;
+                const int64_t r256 = cdiv(tm * tn * conc, cus), r128 = cdiv(tm * (g.N / 128) * conc, cus);
+                if (10 * r256 <= 6 * r128) {
+                    // A launch of its own (no concurrent parts) whose wide
+                    // tiles leave a last round at most 40 % full: the full
+                    // rounds' rows keep the wide tiles, and the rows left
+                    // over (fewer than a round's worth) take the tiles the
+                    // rules here pick for them, in a second launch right
+                    // behind.  ViT-L/16 LeVJEPA, batch 4 (12548 rows): fc1
+                    // 147.5 us in 4 rounds -> 115.6 us for 12288 rows + 12.2 us
+                    // for 260 (MI355X).
+                    const int64_t full = tm * tn / cus, last = tm * tn - full * cus;
+                    const int64_t tm_main = full * cus / tn;
+                    if (conc == 1 && full >= 1 && last > 0 && 10 * last <= 4 * cus && tm_main >= 1 &&
+                        tm_main < tm) {
+                        hipError_t e = launch_big<T, EPI, 256>(g, s, tm_main);
+                        if (e != hipSuccess) return e;
+                        GemmArgs gt = g;
+                        gt.m_begin = g.m_begin + tm_main * BIG_BM;
+                        return launch_t<T, WF, EPI>(gt, s);
+                    }
+                    return launch_big<T, EPI, 256>(g, s);
+                }
             }
             return launch_big<T, EPI, 128>(g, s);
         }
@@ -1000,9 +1024,9 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
     if constexpr (WF == DT_F32) {
         const char *v = getenv("JEPA_GEMM_VARIANT");
         const bool pin = v && *v;
-        const bool fits = cdiv(g.M, 64) < 65535;
-        if (fits && ((!pin && 2 * cdiv(g.M, BM) * cdiv(g.N, BN) < cu_count()) || (pin && !strcmp(v, "small64")))) {
-            dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64));
+        const bool fits = cdiv(rows, 64) < 65535;
+        if (fits && ((!pin && 2 * cdiv(rows, BM) * cdiv(g.N, BN) < cu_count()) || (pin && !strcmp(v, "small64")))) {
+            dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(rows, 64));
             if constexpr (sizeof(T) == 4 && EPI == EPI_RESID) {
                 // f32 residual GEMMs with a long K and few tiles: split K into
                 // S parts of at least 3 steps (BK = 32), S the largest of 8 / 4 / 2
@@ -1011,7 +1035,7 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
                 int S = 1;
                 for (int c : {8, 4, 2})
                     if (S == 1 && nk % c == 0 && nk / c >= 3 && 4 * grid.x * grid.y * c <= (int64_t)cu_count() * 2) S = c;
-                if (g.kpart && S > 1 && g.M * g.N < (1ll << 31)) {
+                if (g.kpart && g.m_begin == 0 && S > 1 && g.M * g.N < (1ll << 31)) {
                     GemmArgs gs = g;
                     gs.ksplit = S;
                     grid.z = S;
@@ -1029,7 +1053,7 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
     }
     GemmArgs g2 = g;
     g2.ksplit = 1;
-    dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(g.M, BM));
+    dim3 grid((unsigned)cdiv(g.N, BN), (unsigned)cdiv(rows, BM));
     hipLaunchKernelGGL((gemm_kernel<T, WF, EPI, 2>), grid, dim3(256), 0, s, g2);
     return hipGetLastError();
 }
@@ -1092,6 +1116,7 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
     if (!dense && (act_dt == DT_F32 || (w_dt != DT_Q8_0 && w_dt != DT_Q4_0) || !g.wscale))
         return hipErrorInvalidValue;
     GemmArgs ga = g;
+    ga.m_begin = 0;
     ga.vt_direct = epi == EPI_QKV && (g.ntok % 16 == 0 || g.M == g.ntok);
     if (const char *e = getenv("JEPA_VT_DIRECT"))
         if (!strcmp(e, "0")) ga.vt_direct = 0;

@@ -56,6 +56,10 @@ struct GemmArgs {
     // launches of this shape expected to run concurrently (batch parts on
     // other streams; 0 or 1: none), a hint for the tile-shape choice
     int conc;
+    // first row of this launch: a launch covers rows [m_begin, M), all row
+    // indices above stay absolute (set by the launcher when it gives a
+    // GEMM's last rows their own, smaller tiles; callers pass 0)
+    int64_t m_begin;
     // f32 EPI_RESID with few tiles: scratch for a K split (KSPLIT_MAX * M * N
     // floats, or null: no split); each split's partial product goes there and
     // a second pass adds the bias and the splits in order to the output
