@@ -112,7 +112,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // back by column: a wave store writes two columns of 32 tokens, i.e. two runs
 // of 64 (2-byte types) or 128 bytes of V^T, one element per lane.  Rows past
 // M fall past the end of V^T, where the buffer resource drops them.
-template <typename T, int MB_, int NB_>
+template <typename T, int MB_, int NB_, bool PRE = false>
 __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
                                                  const float *sb, unsigned char *ls, int64_t row0,
                                                  int64_t col0, int lane) {
@@ -133,9 +133,11 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * j + 8 * q + 4 * g32;
-                const float4 b = *(const float4 *)(sb + col);
-                const float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
-                                    acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
+                float z[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if constexpr (!PRE) {
+                    const float4 b = *(const float4 *)(sb + col);
+                    z[0] += b.x; z[1] += b.y; z[2] += b.z; z[3] += b.w;
+                }
                 const int cb = col * OES;
                 unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
                 if constexpr (OES == 2) {
@@ -174,7 +176,7 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
 // M (the one item's last, when it is not a multiple of 16 long) is stored
 // element by element for the tokens below M: V^T's free positions stay
 // untouched.  Runs past M fall past the end of V^T and are dropped.
-template <typename T, int MB_, int NB_>
+template <typename T, int MB_, int NB_, bool PRE = false>
 __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
                                                    const float *sb, int64_t row0, int64_t col0, int lane) {
     constexpr int OES = (int)sizeof(T);
@@ -186,7 +188,7 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
 #pragma unroll
     for (int j = 0; j < NB_; ++j) {
         const uint32_t dc = (uint32_t)(col0 + 32 * j + cl - g.vcol0);   // V^T row within an item
-        const float bj = sb[32 * j + cl];
+        const float bj = PRE ? 0.f : sb[32 * j + cl];
 #pragma unroll
         for (int i = 0; i < MB_; ++i)
 #pragma unroll
@@ -197,8 +199,12 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
                 float x[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    x[r] = acc[i][j][4 * (2 * h) + r] + bj;
-                    x[4 + r] = acc[i][j][4 * (2 * h + 1) + r] + bj;
+                    x[r] = acc[i][j][4 * (2 * h) + r];
+                    x[4 + r] = acc[i][j][4 * (2 * h + 1) + r];
+                    if constexpr (!PRE) {
+                        x[r] += bj;
+                        x[4 + r] += bj;
+                    }
                 }
                 if (ms + 16 <= (uint32_t)g.M || ms >= (uint32_t)g.M) {
                     const u32x4 v = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]), pack2<T>(x[4], x[5]),
@@ -232,14 +238,14 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
 // rows past M need no branch.  RESID reads X one block ahead of its writes
 // (issued after the block's staging, to keep one buffer live there), and each
 // element is read and written by one lane only.
-template <typename T, int EPI, int MB_, int NB_, bool NO_VT = false>
+template <typename T, int EPI, int MB_, int NB_, bool NO_VT = false, bool PRE = false>
 __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
                                               const float *sb, unsigned char *ls, int64_t row0,
                                               int64_t col0, int lane) {
     if constexpr (EPI == EPI_QKV && !NO_VT) {   // (NO_VT: the caller writes v columns itself)
         // a wave's columns are all q/k or all v (v starts at a multiple of 128)
         if (col0 >= g.vcol0) {
-            epilogue_wave_vt<T, MB_, NB_>(g, acc, sb, ls, row0, col0, lane);
+            epilogue_wave_vt<T, MB_, NB_, PRE>(g, acc, sb, ls, row0, col0, lane);
             return;
         }
     }
@@ -278,9 +284,9 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                     rs, gbase + (32 * i + t * RPI) * rowb, 0, 0));
         }
     };
-    // this lane's biases, once for all block rows (the qkv epilogue, whose v
-    // branch needs the registers, reads them per block row)
-    constexpr bool HOIST = true;
+    // this lane's biases, once for all block rows (PRE: the accumulators
+    // started from them, nothing to add)
+    constexpr bool HOIST = !PRE;
     float4 bias[HOIST ? NB_ : 1][4];
     if constexpr (HOIST) {
 #pragma unroll
@@ -305,9 +311,11 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * j + 8 * q + 4 * g32;
-                const float4 b = HOIST ? bias[HOIST ? j : 0][q] : *(const float4 *)(sb + col);
-                float z[4] = {acc[i][j][4 * q] + b.x, acc[i][j][4 * q + 1] + b.y,
-                              acc[i][j][4 * q + 2] + b.z, acc[i][j][4 * q + 3] + b.w};
+                float z[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if constexpr (!PRE) {
+                    const float4 b = HOIST ? bias[HOIST ? j : 0][q] : *(const float4 *)(sb + col);
+                    z[0] += b.x; z[1] += b.y; z[2] += b.z; z[3] += b.w;
+                }
                 if constexpr (EPI == EPI_QKV) {
                     if constexpr (rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
                         const uint32_t hd = (uint32_t)g.head_dim;
@@ -695,7 +703,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     constexpr int LPS = A_CH + B_CH;                 // loads per thread per stage
     constexpr int HALF = LPS / 2;
     constexpr int MBNB = MB * NB, NRD = MB + NB;     // MFMAs and LDS reads per K chunk
-    static_assert(LPS % 2 == 0 && NS * ST + 1024 <= 160 * 1024 - BN * 4, "LDS");
+    static_assert(LPS % 2 == 0 && NS * ST <= 160 * 1024, "LDS");
     static_assert((NS - 1) * LPS < 64, "vmcnt range");
     static_assert(NRD % 2 == 0 && NRD / 2 <= MBNB && HALF <= MBNB, "chunk schedule");
     // One array per stage: the compiler gives each its own alias scope, so a
@@ -703,14 +711,17 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     // single indexed array makes it wait for every load in flight).
     __shared__ __attribute__((aligned(1024))) unsigned char lds0[ST];
     __shared__ __attribute__((aligned(1024))) unsigned char lds1[ST];
-    __shared__ __attribute__((aligned(1024))) unsigned char lds2[NS == 3 ? ST : 1024];
-    __shared__ __attribute__((aligned(16))) float sbias[BN];
+    // (the third stage only where NS = 3: an array no code names takes no LDS)
+    __shared__ __attribute__((aligned(1024))) unsigned char lds2[ST];
     auto stage = [&](auto S) -> unsigned char * __attribute__((always_inline)) {
         if constexpr (decltype(S)::value == 0) return lds0;
         else if constexpr (decltype(S)::value == 1) return lds1;
         else return lds2;
     };
-    auto stage_rt = [&](int s) -> unsigned char * __attribute__((always_inline)) { return s == 0 ? lds0 : s == 1 ? lds1 : lds2; };
+    auto stage_rt = [&](int s) -> unsigned char * __attribute__((always_inline)) {
+        if constexpr (NS == 3) return s == 0 ? lds0 : s == 1 ? lds1 : lds2;
+        else return s == 0 ? lds0 : lds1;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, g32 = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS-load bases in SGPRs
@@ -765,13 +776,33 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
 
     auto body = [&](auto SWAPC) __attribute__((always_inline)) {
         constexpr bool SWAP = decltype(SWAPC)::value;
+        // The accumulators start from the biases (N % BN == 0), so that the
+        // epilogue has nothing to add.  Element 4q + r of block (i, j) is
+        // column 32 j + 8 q + 4 (lane / 32) + r of the wave's tile, or, with
+        // the token operand first (SWAP), column 32 j + lane % 32.
         f32x16 acc[MB][NB];
+        {
+            const float *bw = g.bias + n0 + wn * (BN / 2);
     #pragma unroll
-        for (int i = 0; i < MB; ++i)
+            for (int j = 0; j < NB; ++j) {
+                float bv[16];
+                if constexpr (SWAP) {
+                    const float b1 = bw[32 * j + (lane & 31)];
     #pragma unroll
-            for (int j = 0; j < NB; ++j)
+                    for (int v = 0; v < 16; ++v) bv[v] = b1;
+                } else {
     #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 b4 = *(const float4 *)(bw + 32 * j + 8 * q + 4 * g32);
+                        bv[4 * q] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
+                    }
+                }
+    #pragma unroll
+                for (int i = 0; i < MB; ++i)
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = bv[v];
+            }
+        }
 
         // operand rows of this lane (same swizzle for every row of a 32-row block)
         const int rl = lane & 31, sw = swz8(rl);
@@ -842,15 +873,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
             sched_chunk<3, MBNB, NRD, HALF>();
         };
 
-        // the tile's biases, to LDS behind the first stages' loads (N % BN == 0)
-        float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tid < BN / 4) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
         // prologue: stages 0 .. NS-2 whole, the first half of stage NS-1
     #pragma unroll
         for (int s0 = 0; s0 < NS - 1; ++s0)
             if (s0 < nk) { issue_half(stage_rt(s0), s0, 0); issue_half(stage_rt(s0), s0, 1); }
         if (NS - 1 < nk) issue_half(stage_rt(NS - 1), NS - 1, 0);
-        if (tid < BN / 4) *(float4 *)(sbias + 4 * tid) = bias4;
         wait_loads(min(NS - 2, nk - 1) * LPS + (NS - 1 < nk ? HALF : 0));   // step 0 landed
         __builtin_amdgcn_s_barrier();
         read_chunk(lds0, 0, 0);
@@ -897,10 +924,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         static_assert(4 * 64 * BN <= ST, "epilogue scratch");
         __builtin_amdgcn_s_barrier();
         if constexpr (SWAP)
-            epilogue_vt_direct<T, MB, NB>(g, acc, sbias + wn * (BN / 2), m0 + wm * 128, n0 + wn * (BN / 2), lane);
+            epilogue_vt_direct<T, MB, NB, true>(g, acc, nullptr, m0 + wm * 128, n0 + wn * (BN / 2), lane);
         else
-            epilogue_wave<T, EPI, MB, NB, VTD>(g, acc, sbias + wn * (BN / 2), lds0 + wave * (64 * BN),
-                                               m0 + wm * 128, n0 + wn * (BN / 2), lane);
+            epilogue_wave<T, EPI, MB, NB, VTD, true>(g, acc, nullptr, lds0 + wave * (64 * BN), m0 + wm * 128,
+                                                     n0 + wn * (BN / 2), lane);
     };
     // VTD (qkv with vt_direct, launched only when v starts at a multiple of
     // BN, so that every tile is all q / k or all v): the v tiles take the
