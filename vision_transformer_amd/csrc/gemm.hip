@@ -78,23 +78,6 @@ __device__ __forceinline__ void store_f16x8(unsigned char *dst, const float *x) 
                                pack2<T>(x[6], x[7]));
 }
 
-// One output element: z = acc + bias, applied per the epilogue.
-template <typename T, int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs &g, int64_t row, int64_t col, float z) {
-    if constexpr (EPI == EPI_STORE) {
-        ((T *)g.out)[row * g.ldo + col] = from_f32<T>(z);
-    } else if constexpr (EPI == EPI_GELU) {
-        ((T *)g.out)[row * g.ldo + col] = from_f32<T>(gelu_erf<T>(z));
-    } else if constexpr (EPI == EPI_RESID) {
-        float *x = (float *)g.out + row * g.ldo + col;
-        *x = *x + z;
-    } else {  // EPI_PATCH
-        const int64_t b = row / g.np, n = row - b * g.np;
-        const int64_t t = g.has_cls + n;
-        ((float *)g.out)[(b * g.ntok + t) * g.ldo + col] = g.pos ? z + g.pos[t * g.ldo + col] : z;
-    }
-}
-
 // Raw buffer resource over the first nbytes at p (gfx9 descriptor word 3):
 // loads past the end return 0 and stores past the end are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t nbytes) {
@@ -108,13 +91,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // npad] holds, for every head and dim, the item's tokens in a row (token n at
 // vt_pos(n)).  Each
 // 32-row block (32 consecutive tokens, possibly of two items) is finished in
-// registers (bias, rounding) and staged in LDS as in the STORE case, then read
+// registers (rounding) and staged in LDS as in the STORE case, then read
 // back by column: a wave store writes two columns of 32 tokens, i.e. two runs
 // of 64 (2-byte types) or 128 bytes of V^T, one element per lane.  Rows past
 // M fall past the end of V^T, where the buffer resource drops them.
-template <typename T, int MB_, int NB_, bool PRE = false>
+template <typename T, int MB_, int NB_>
 __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
-                                                 const float *sb, unsigned char *ls, int64_t row0,
+                                                 unsigned char *ls, int64_t row0,
                                                  int64_t col0, int lane) {
     constexpr int OES = (int)sizeof(T);
     constexpr int RB = 32 * NB_ * OES;
@@ -127,17 +110,14 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
     const int64_t dcol0 = col0 - g.vcol0;        // first v column of the wave (multiple of 64)
 #pragma unroll
     for (int i = 0; i < MB_; ++i) {
-        // stage block row i (bias, rounding), row-major with swizzled chunks
+        // stage block row i (rounding), row-major with swizzled chunks
 #pragma unroll
         for (int j = 0; j < NB_; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * j + 8 * q + 4 * g32;
-                float z[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if constexpr (!PRE) {
-                    const float4 b = *(const float4 *)(sb + col);
-                    z[0] += b.x; z[1] += b.y; z[2] += b.z; z[3] += b.w;
-                }
+                const float z[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]};
                 const int cb = col * OES;
                 unsigned char *dst = ls + rl * RB + (((cb >> 4) ^ (rl & SWM)) << 4) + (cb & 15);
                 if constexpr (OES == 2) {
@@ -176,9 +156,9 @@ __device__ __forceinline__ void epilogue_wave_vt(const GemmArgs &g, const f32x16
 // M (the one item's last, when it is not a multiple of 16 long) is stored
 // element by element for the tokens below M: V^T's free positions stay
 // untouched.  Runs past M fall past the end of V^T and are dropped.
-template <typename T, int MB_, int NB_, bool PRE = false>
+template <typename T, int MB_, int NB_>
 __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
-                                                   const float *sb, int64_t row0, int64_t col0, int lane) {
+                                                   int64_t row0, int64_t col0, int lane) {
     constexpr int OES = (int)sizeof(T);
     static_assert(OES == 2, "16-bit V^T");
     const int64_t D = g.N - g.vcol0;
@@ -188,7 +168,6 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
 #pragma unroll
     for (int j = 0; j < NB_; ++j) {
         const uint32_t dc = (uint32_t)(col0 + 32 * j + cl - g.vcol0);   // V^T row within an item
-        const float bj = PRE ? 0.f : sb[32 * j + cl];
 #pragma unroll
         for (int i = 0; i < MB_; ++i)
 #pragma unroll
@@ -201,10 +180,6 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
                 for (int r = 0; r < 4; ++r) {
                     x[r] = acc[i][j][4 * (2 * h) + r];
                     x[4 + r] = acc[i][j][4 * (2 * h + 1) + r];
-                    if constexpr (!PRE) {
-                        x[r] += bj;
-                        x[4 + r] += bj;
-                    }
                 }
                 if (ms + 16 <= (uint32_t)g.M || ms >= (uint32_t)g.M) {
                     const u32x4 v = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]), pack2<T>(x[4], x[5]),
@@ -225,10 +200,11 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
 }
 
 // The output stage of one wave's MB_ x NB_ accumulator blocks (STORE / GELU
-// / RESID).  The blocks are accumulated transposed (the weights are the
+// / RESID / PATCH / QKV), which already include the biases (the K loops
+// start from them).  The blocks are accumulated transposed (the weights are the
 // MFMA's A operand): element 4q + r of block (i, j) of lane l is output row
 // 32 i + l % 32, column 32 j + 8 q + 4 (l / 32) + r of the wave's tile.  Each
-// 32-row block is finished in registers (bias, GELU, rounding), written to
+// 32-row block is finished in registers (GELU, rounding), written to
 // the wave's LDS scratch, and read back so that consecutive lanes hold
 // consecutive 16 bytes of a row: every global access then covers whole
 // 128-byte lines (32 partial-line writes per row, the register layout's
@@ -238,14 +214,14 @@ __device__ __forceinline__ void epilogue_vt_direct(const GemmArgs &g, const f32x
 // rows past M need no branch.  RESID reads X one block ahead of its writes
 // (issued after the block's staging, to keep one buffer live there), and each
 // element is read and written by one lane only.
-template <typename T, int EPI, int MB_, int NB_, bool NO_VT = false, bool PRE = false>
+template <typename T, int EPI, int MB_, int NB_, bool NO_VT = false>
 __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&acc)[MB_][NB_],
-                                              const float *sb, unsigned char *ls, int64_t row0,
+                                              unsigned char *ls, int64_t row0,
                                               int64_t col0, int lane) {
     if constexpr (EPI == EPI_QKV && !NO_VT) {   // (NO_VT: the caller writes v columns itself)
         // a wave's columns are all q/k or all v (v starts at a multiple of 128)
         if (col0 >= g.vcol0) {
-            epilogue_wave_vt<T, MB_, NB_, PRE>(g, acc, sb, ls, row0, col0, lane);
+            epilogue_wave_vt<T, MB_, NB_>(g, acc, ls, row0, col0, lane);
             return;
         }
     }
@@ -284,16 +260,6 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                     rs, gbase + (32 * i + t * RPI) * rowb, 0, 0));
         }
     };
-    // this lane's biases, once for all block rows (PRE: the accumulators
-    // started from them, nothing to add)
-    constexpr bool HOIST = !PRE;
-    float4 bias[HOIST ? NB_ : 1][4];
-    if constexpr (HOIST) {
-#pragma unroll
-        for (int j = 0; j < NB_; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bias[j][q] = *(const float4 *)(sb + 32 * j + 8 * q + 4 * g32);
-    }
     load_x(0, 0);
 #pragma unroll
     for (int i = 0; i < MB_; ++i) {
@@ -312,10 +278,6 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * j + 8 * q + 4 * g32;
                 float z[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if constexpr (!PRE) {
-                    const float4 b = HOIST ? bias[HOIST ? j : 0][q] : *(const float4 *)(sb + col);
-                    z[0] += b.x; z[1] += b.y; z[2] += b.z; z[3] += b.w;
-                }
                 if constexpr (EPI == EPI_QKV) {
                     if constexpr (rope) {   // dims (d, d+1) and (d+2, d+3) of a head, d % 4 == 0
                         const uint32_t hd = (uint32_t)g.head_dim;
@@ -396,7 +358,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
     static_assert(TS == 2 || (TS == 1 && DENSE), "64-wide tiles: dense weights only");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TB * ROWB];
-    __shared__ __attribute__((aligned(16))) float sbias[TB];
     static_assert(4 * 8192 <= 2 * 2 * TB * ROWB, "epilogue scratch");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -412,11 +373,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
         kt0 = (int)blockIdx.z * per;
         nk = min(nk_all - kt0, per);
     }
-
-    // the tile's biases (N is a multiple of 64; columns past N read as 0);
-    // a split's partial product leaves them to the second pass
-    float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!split && tid < TB / 4 && n0 + 4 * tid < g.N) bias4 = *(const float4 *)(g.bias + n0 + 4 * tid);
 
     const unsigned char *A = (const unsigned char *)g.a;
     const unsigned char *W = (const unsigned char *)g.w;
@@ -575,13 +531,31 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
         }
     };
 
+    // The accumulators start from the biases, as in the large tile, so
+    // that a row's value does not depend on which tile computed it (a
+    // split's partial product starts from 0 and leaves them to the second
+    // pass).  Element 4q + r of block (i, j) is column 32 j + 8 q + 4 (lane
+    // / 32) + r of the wave's tile; a wave's columns are all below N or all
+    // past it (N % 64 == 0).
     f32x16 acc[TS][TS];
+    {
+        const bool with_bias = !split && n0 + wn * WT < g.N;
+        const float *bw = g.bias + n0 + wn * WT;
 #pragma unroll
-    for (int i = 0; i < TS; ++i)
+        for (int j = 0; j < TS; ++j) {
+            float bv[16];
 #pragma unroll
-        for (int j = 0; j < TS; ++j)
+            for (int q = 0; q < 4; ++q) {
+                float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (with_bias) b4 = *(const float4 *)(bw + 32 * j + 8 * q + 4 * (lane >> 5));
+                bv[4 * q] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
+            }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            for (int i = 0; i < TS; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = bv[v];
+        }
+    }
 
     const int arow = wm * WT + (lane & 31);
     const int brow = wn * WT + (lane & 31);
@@ -589,7 +563,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 
     load_global(kt0);
     store_lds(0);
-    if (tid < TB / 4) *(float4 *)(sbias + 4 * tid) = bias4;
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
@@ -623,13 +596,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
                 GemmArgs gz = g;
                 gz.out = g.kpart + (int64_t)blockIdx.z * g.M * g.N;
                 gz.ldo = g.N;
-                epilogue_wave<T, EPI_STORE, TS, TS>(gz, acc, sbias + wn * WT, &smem[0][0][0] + wave * 8192,
-                                                    m0 + wm * WT, n0 + wn * WT, lane);
+                epilogue_wave<T, EPI_STORE, TS, TS>(gz, acc, &smem[0][0][0] + wave * 8192,
+                                                                 m0 + wm * WT, n0 + wn * WT, lane);
                 return;
             }
         }
-        epilogue_wave<T, EPI, TS, TS>(g, acc, sbias + wn * WT, &smem[0][0][0] + wave * 8192,
-                                      m0 + wm * WT, n0 + wn * WT, lane);
+        epilogue_wave<T, EPI, TS, TS>(g, acc, &smem[0][0][0] + wave * 8192,
+                                                   m0 + wm * WT, n0 + wn * WT, lane);
     }
 }
 
@@ -924,9 +897,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         static_assert(4 * 64 * BN <= ST, "epilogue scratch");
         __builtin_amdgcn_s_barrier();
         if constexpr (SWAP)
-            epilogue_vt_direct<T, MB, NB, true>(g, acc, nullptr, m0 + wm * 128, n0 + wn * (BN / 2), lane);
+            epilogue_vt_direct<T, MB, NB>(g, acc, m0 + wm * 128, n0 + wn * (BN / 2), lane);
         else
-            epilogue_wave<T, EPI, MB, NB, VTD, true>(g, acc, nullptr, lds0 + wave * (64 * BN), m0 + wm * 128,
+            epilogue_wave<T, EPI, MB, NB, VTD>(g, acc, lds0 + wave * (64 * BN), m0 + wm * 128,
                                                      n0 + wn * (BN / 2), lane);
     };
     // VTD (qkv with vt_direct, launched only when v starts at a multiple of
