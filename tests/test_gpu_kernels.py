@@ -186,6 +186,23 @@ def test_gemm_large_tile(lib, monkeypatch, variant, N, K, epi):
     assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
 
 
+@pytest.mark.parametrize("M", [1088, 1152, 1153, 1300])
+@pytest.mark.parametrize("epi", ["store", "gelu", "resid"])
+def test_gemm_large_tile_half_row_tile(lib, monkeypatch, M, epi):
+    """The 256-row tile's last row tile when at most 128 of its rows exist:
+    the four waves then share those 128 rows (64 each).  M = 1088 and 1152
+    leave 64 and 128 rows (the half tile), 1153 leaves 129 (the full tile),
+    1300 leaves 20; K = 1024, every element against the oracle."""
+    monkeypatch.setenv("JEPA_GEMM_VARIANT", "big256")
+    N, K = 512, 1024
+    say(f"gemm big256 bf16 {epi} M={M} N={N} K={K} (last row tile {M - 1024} rows)")
+    got, ref, a, w = _gemm_case(lib, "bf16", "dense", epi, M, N, K, 45)
+    acc = 4 * K * 2.0 ** -24 * (np.abs(a) @ np.abs(w).T)
+    out_r = 0.0 if epi == "resid" else OUT_REL["bf16"]
+    err = np.abs(got - ref)
+    assert np.all(err <= acc + out_r * np.abs(ref) + 1e-6), (err - acc - out_r * np.abs(ref)).max()
+
+
 FFN_CASES = [
     # name, M, N, K, epilogue, variant ("" = the launcher's own choice)
     # LeVJEPA ViT-L/16, batch 4, in one part: the 256 x 256 tiles would leave

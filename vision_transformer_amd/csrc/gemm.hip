@@ -669,16 +669,14 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
     typedef Mfma<T> MM;
     typedef typename MM::vec vec;
     static_assert(sizeof(T) == 2, "16-bit operands only");
-    constexpr int MB = 4, NB = BN / 64;              // 32x32 blocks per wave
+    constexpr int NB = BN / 64;                      // 32-column blocks per wave
     constexpr int NS = BN == 256 ? 2 : 3;            // stages: 64 KB or 48 KB each
     constexpr int A_BYTES = BIG_BM * 128, B_BYTES = BN * 128, ST = A_BYTES + B_BYTES;
     constexpr int A_CH = BIG_BM * 8 / 256, B_CH = BN * 8 / 256;   // 16-byte chunks per thread
     constexpr int LPS = A_CH + B_CH;                 // loads per thread per stage
     constexpr int HALF = LPS / 2;
-    constexpr int MBNB = MB * NB, NRD = MB + NB;     // MFMAs and LDS reads per K chunk
     static_assert(LPS % 2 == 0 && NS * ST <= 160 * 1024, "LDS");
     static_assert((NS - 1) * LPS < 64, "vmcnt range");
-    static_assert(NRD % 2 == 0 && NRD / 2 <= MBNB && HALF <= MBNB, "chunk schedule");
     // One array per stage: the compiler gives each its own alias scope, so a
     // read of one stage needs no wait for loads still landing in another (a
     // single indexed array makes it wait for every load in flight).
@@ -747,8 +745,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         }
     };
 
-    auto body = [&](auto SWAPC) __attribute__((always_inline)) {
+    // HMC: rows per wave, 128 (the full 256-row tile) or 64 (a half tile: the
+    // launch's last row tile when at most its first 128 rows exist, e.g. one
+    // 3137-token clip's 13th tile; the four waves then share 128 rows instead
+    // of idling on padding)
+    auto body = [&](auto SWAPC, auto HMC) __attribute__((always_inline)) {
         constexpr bool SWAP = decltype(SWAPC)::value;
+        constexpr int HM = decltype(HMC)::value;
+        constexpr int MB = HM / 32, MBNB = MB * NB, NRD = MB + NB;
+        static_assert(NRD % 2 == 0 && NRD / 2 <= MBNB && HALF <= MBNB, "chunk schedule");
+        // (differing first instructions: the compiler then hoists none of the
+        // two shapes' identical bias loads above their branch, where they
+        // would stay live across it and spill)
+        if constexpr (HM == 64) asm volatile("; half row tile");
+        else asm volatile("; full row tile");
         // The accumulators start from the biases (N % BN == 0), so that the
         // epilogue has nothing to add.  Element 4q + r of block (i, j) is
         // column 32 j + 8 q + 4 (lane / 32) + r of the wave's tile, or, with
@@ -781,7 +791,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         const int rl = lane & 31, sw = swz8(rl);
         int arow[MB], brow[NB];
     #pragma unroll
-        for (int i = 0; i < MB; ++i) arow[i] = (wm * 128 + i * 32 + rl) * 128;
+        for (int i = 0; i < MB; ++i) arow[i] = (wm * HM + i * 32 + rl) * 128;
     #pragma unroll
         for (int j = 0; j < NB; ++j) brow[j] = A_BYTES + (wn * (BN / 2) + j * 32 + rl) * 128;
 
@@ -897,19 +907,28 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const GemmArgs g, int 
         static_assert(4 * 64 * BN <= ST, "epilogue scratch");
         __builtin_amdgcn_s_barrier();
         if constexpr (SWAP)
-            epilogue_vt_direct<T, MB, NB>(g, acc, m0 + wm * 128, n0 + wn * (BN / 2), lane);
+            epilogue_vt_direct<T, MB, NB>(g, acc, m0 + wm * HM, n0 + wn * (BN / 2), lane);
         else
-            epilogue_wave<T, EPI, MB, NB, VTD>(g, acc, lds0 + wave * (64 * BN), m0 + wm * 128,
+            epilogue_wave<T, EPI, MB, NB, VTD>(g, acc, lds0 + wave * (64 * BN), m0 + wm * HM,
                                                      n0 + wn * (BN / 2), lane);
     };
     // VTD (qkv with vt_direct, launched only when v starts at a multiple of
     // BN, so that every tile is all q / k or all v): the v tiles take the
     // token operand first and write V^T rows straight from the accumulators
+    auto rows_body = [&](auto SWAPC) __attribute__((always_inline)) {
+        if constexpr (BN == 256) {
+            if (m0 + 128 >= g.M) {
+                body(SWAPC, std::integral_constant<int, 64>{});
+                return;
+            }
+        }
+        body(SWAPC, std::integral_constant<int, 128>{});
+    };
     if constexpr (EPI == EPI_QKV && VTD) {
-        if (n0 >= g.vcol0) body(std::true_type{});
-        else body(std::false_type{});
+        if (n0 >= g.vcol0) rows_body(std::true_type{});
+        else rows_body(std::false_type{});
     } else {
-        body(std::false_type{});
+        rows_body(std::false_type{});
     }
 }
 
