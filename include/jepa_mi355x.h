@@ -310,9 +310,11 @@ size_t jepa_device_weight_bytes(const jepa_ctx *ctx);
 /* Bytes of device workspace an encode of `batch` items needs (with the
  * current batch-part setting).  It includes, for a model with block
  * matrices and batch parts of 1024 or more token rows, an activation-dtype
- * copy of those matrices that each such encode rewrites from the blocks
- * before its first layer (the GEMMs then run dense); smaller batches
- * dequantise inside the GEMM and need no copy.  The environment variable
+ * copy of those matrices (the GEMMs then run dense): the first such encode
+ * allocates it and writes it from the blocks before its first layer, later
+ * encodes reuse it (on any stream: they wait for that write), and it is
+ * held until jepa_free; smaller batches dequantise inside the GEMM and need
+ * no copy.  The environment variable
  * JEPA_Q_EXPAND = 0 or 1 forces either way, except that a model with a
  * Q4_K / Q6_K matrix always takes the copy. */
 size_t jepa_workspace_bytes(const jepa_ctx *ctx, int batch);

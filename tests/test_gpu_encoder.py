@@ -277,8 +277,8 @@ def test_graph_replay_matches_eager(Encoder, parts):
 @pytest.mark.parametrize("name", ["small_tubelet2_q8_0", "small_tubelet2_q4_0", "small_rope_q4_0"])
 def test_expanded_block_matrices_every_token(Encoder, name, monkeypatch):
     """JEPA_Q_EXPAND=1: the q8_0 / q4_0 matrices are expanded to the act dtype
-    at the start of the encode and the GEMMs run dense; every token and the
-    mean pool against the oracle.  The workspace size counts the copy."""
+    before the first layer and the GEMMs run dense; every token and the mean
+    pool against the oracle.  The workspace size counts the copy."""
     from vision_transformer_amd import _lib
     wl, dims, frames, stored = H.workload_inputs(name, ln_affine=True)
     enc = Encoder(dims, stored)
@@ -290,6 +290,38 @@ def test_expanded_block_matrices_every_token(Encoder, name, monkeypatch):
     ref = H.oracle_tokens(dims, stored, frames)
     H.check_rows(dims["act_dtype"], y_dev.cpu().numpy(), ref, "tokens")
     _check_pools(enc, dims, ref, wl["batch"])
+    enc.close()
+
+
+def test_expanded_copy_written_once_and_reused(Encoder, monkeypatch):
+    """The act-dtype copy of the block matrices depends on the weights only:
+    the first encode that takes the expanded path writes it, later ones (a
+    different batch, an encode without it in between, another stream) reuse
+    it.  Each token map matches the oracle's, a repeat is bit-identical, and
+    the expansion kernel ran once."""
+    from vision_transformer_amd import _lib
+    monkeypatch.setenv("JEPA_Q_EXPAND", "1")
+    wl, dims, frames, stored = H.workload_inputs("small_tubelet2_q8_0", ln_affine=True)
+    enc = Encoder(dims, stored)
+    _lib.jepa_set_profiling(enc.ctx, 0xFFFFFFFF)
+    H.say("encoder small_tubelet2_q8_0: three expanded encodes, one plain between")
+    y1 = _run(enc, frames).clone()
+    H.check_rows(dims["act_dtype"], y1.cpu().numpy(), H.oracle_tokens(dims, stored, frames), "first")
+    monkeypatch.setenv("JEPA_Q_EXPAND", "0")
+    fr2 = synth.make_frames(dims, 3, 79)
+    y2 = _run(enc, fr2).clone()
+    monkeypatch.setenv("JEPA_Q_EXPAND", "1")
+    ref2 = H.oracle_tokens(dims, stored, fr2)
+    H.check_rows(dims["act_dtype"], y2.cpu().numpy(), ref2, "plain path")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y3 = enc.encode(torch.from_numpy(fr2).cuda()).clone()
+    torch.cuda.synchronize()
+    H.check_rows(dims["act_dtype"], y3.cpu().numpy(), ref2, "expanded, other stream")
+    y4 = _run(enc, frames)
+    assert torch.equal(y4, y1)
+    stats = _lib.jepa_kernel_stats(enc.ctx)
+    assert stats["expand_weights"]["launches"] == 1, stats["expand_weights"]
     enc.close()
 
 

@@ -192,6 +192,11 @@ struct jepa_ctx {
     const ExpandJob *xjobs = nullptr;
     int n_xjobs = 0;
     int64_t x_nblk = 0;
+    // the copy depends on the weights alone, which never change after
+    // create: it is written by the first encode that uses it (x_written,
+    // recorded by x_ev on that encode's stream) and read by every later one
+    bool x_written = false;
+    hipEvent_t x_ev = nullptr;
     std::vector<Layer> layers, head_layers;
     Head head;
     std::map<std::string, DevTensor> by_name;
@@ -269,8 +274,9 @@ WsLayout ws_layout(const jepa_ctx *c, int B, bool with_frames = true) {
 }
 
 // Large batches run the block-format layers as dense GEMMs on an act-dtype
-// copy of the block matrices, expanded once per encode (a bandwidth-bound
-// pass: 1 + 1/16 bytes read and 2 written per weight for q8_0).  Above ~1024
+// copy of the block matrices, expanded by the first encode that needs it (a
+// bandwidth-bound pass: 1 + 1/16 bytes read and 2 written per weight for
+// q8_0) and kept, like the weights, until the context is freed.  Above ~1024
 // rows per batch part the GEMMs take the 256-row MFMA tiles, whose operands
 // flow straight from memory into LDS; a dequantising load would put the
 // conversion on the VALU inside the K loop, and an int8 MFMA path with
@@ -1174,7 +1180,15 @@ jepa_status jepa_encode(jepa_ctx *c, const uint8_t *frames, int batch, int frame
     c->last_expand = expand;
     if (expand) {
         TRY(ensure_expanded(c));
-        TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
+        if (!c->x_written) {
+            if (!c->x_ev) HIP_TRY(hipEventCreateWithFlags(&c->x_ev, hipEventDisableTiming));
+            TRY(launch(c, K_EXPAND, s0, [&] { return launch_expand(c->act, c->xjobs, c->n_xjobs, c->x_nblk, s0); }));
+            HIP_TRY(hipEventRecord(c->x_ev, s0));
+            c->x_written = true;
+        } else {
+            // written by an earlier encode, possibly on another stream
+            HIP_TRY(hipStreamWaitEvent(s0, c->x_ev, 0));
+        }
     }
     TRY(encode_parts(c, c->w, fr, batch, Y, s0, parts, expand));
     HIP_TRY(hipEventRecord(c->ev1, s0));
@@ -1259,6 +1273,7 @@ void jepa_free(jepa_ctx *c) {
     if (c->xbuf) (void)hipFree(c->xbuf);
     if (c->h_frames) (void)hipHostFree(c->h_frames);
     if (c->h_ev) (void)hipEventDestroy(c->h_ev);
+    if (c->x_ev) (void)hipEventDestroy(c->x_ev);
     if (c->have_events) {
         (void)hipEventDestroy(c->ev0);
         (void)hipEventDestroy(c->ev1);
