@@ -46,7 +46,8 @@ constexpr int TILEB = 128 * ROWB;         // LDS bytes per 128-row tile
 // erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
 // t = 1 / (1 + p x) from Abramowitz & Stegun, Handbook of Mathematical
 // Functions, 7.1.26 (Hastings): |error| <= 1.5e-7 for x >= 0.  One
-// reciprocal, one exponential and ten other operations per value.
+// reciprocal, one exponential and nine other operations per value (the last
+// an FMA onto max(z, 0)).
 __device__ __forceinline__ float gelu_as7126(float z) {
     constexpr float P = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2: t in terms of |z|
     const float t = __builtin_amdgcn_rcpf(fmaf(P, fabsf(z), 1.0f));
@@ -55,8 +56,10 @@ __device__ __forceinline__ float gelu_as7126(float z) {
     q = fmaf(q, t, 0.5f * -0.284496736f);
     q = fmaf(q, t, 0.5f * 0.254829592f);
     const float e = __builtin_amdgcn_exp2f(z * z * (-0.5f * 1.4426950408889634f));   // exp(-z^2 / 2)
-    const float h = (z * q) * (t * e);                                             // z erfc(|z|/sqrt2) / 2
-    return fmaxf(z, 0.f) - fabsf(h);
+    const float u = q * (t * e);                                                   // erfc(|z|/sqrt2) / 2
+    // max(z, 0) - |z| u, with max(z, 0) as a median (no NaN-quieting
+    // instruction in front of it, as fmaxf would need)
+    return fmaf(-fabsf(z), u, __builtin_amdgcn_fmed3f(z, 0.f, 3.0e38f));
 }
 
 template <typename T>
