@@ -21,6 +21,7 @@ algorithmic work per launch / average launch duration.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--parts P] [--no-cpu-baseline] [--breakdown]
+       python bench.py --gemm-k-sweep    (the large GEMM tile's fixed and per-K-step costs)
 """
 from __future__ import annotations
 
@@ -155,9 +156,12 @@ def cpu_baseline(dims: dict, stored: list, frames: np.ndarray, sample_blocks: in
 # main
 # ---------------------------------------------------------------------------
 
-def mfma_probe(_lib) -> dict | None:
+def mfma_probe(_lib, operands: int = 0) -> dict | None:
     """Dense bf16 MFMA TFLOP/s of the calibration kernel: one workgroup per
-    CU, about 0.1 s of independent 32x32x16 MFMA chains, timed with events."""
+    CU, about 0.1 s of independent 32x32x16 MFMA chains, timed with events;
+    operands 0: constant small values, 1: random values whose bits toggle
+    from one MFMA to the next, as a GEMM's do (the rate the chip's power
+    allows on real data)."""
     import torch
     try:
         cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -167,7 +171,7 @@ def mfma_probe(_lib) -> dict | None:
         def run(iters):
             torch.cuda.synchronize()
             e0.record()
-            flops = _lib.jepa_op_mfma_probe(cus, iters, out)
+            flops = _lib.jepa_op_mfma_probe(cus, iters, out, operands)
             e1.record()
             torch.cuda.synchronize()
             return flops, e0.elapsed_time(e1)
@@ -219,6 +223,64 @@ def copy_probe(mib: int) -> int:
     ms = e0.elapsed_time(e1) / 5
     print(json.dumps({"copy_probe_bytes": n, "ms": round(ms, 4), "GB_per_s_read_plus_write": round(2 * n / ms / 1e6, 1)}),
           flush=True)
+    return 0
+
+
+def gemm_k_sweep() -> int:
+    """The 256 x 256 tile's time against K at whole rounds of 256 tiles
+    (one tile per CU per round): per round, time = fixed + steps * per_step,
+    fixed being a tile's prologue (first operand stages in flight, biases)
+    plus its epilogue, per_step the steady K loop's 64-deep step.  A
+    least-squares line over K >= 512 gives both; per_step is set against the
+    same step's MFMA time at the rate jepa_op_mfma_probe measures with random
+    operands."""
+    import torch
+    from vision_transformer_amd import _lib
+    os.environ["JEPA_GEMM_VARIANT"] = "big256"
+    probe = mfma_probe(_lib, 1)   # random operands: the rate real data allows
+    torch.manual_seed(0)
+    dev = torch.device("cuda")
+    cases = [("store", 12288, 4096), ("gelu", 12288, 4096), ("resid", 16384, 1024)]
+    ks = [128, 256, 512, 1024, 2048, 4096]
+    res = {"mfma_probe_random_operands_tflops": probe["tflops"] if probe else None, "cases": []}
+    for epi, M, N in cases:
+        rounds = (M // 256) * (N // 256) / 256
+        b = torch.randn(N, device=dev) * 0.02
+        out = torch.zeros(M, N, device=dev, dtype=torch.float32 if epi == "resid" else torch.bfloat16)
+        pts = []
+        for K in ks:
+            a = (torch.randn(M, K, device=dev) * 0.5).to(torch.bfloat16)
+            w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:   # clocks settle under this load
+                _lib.jepa_op_gemm("bf16", a, w, "bf16", N, b, epi, out)
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            it = 20
+            e0.record()
+            for _ in range(it):
+                _lib.jepa_op_gemm("bf16", a, w, "bf16", N, b, epi, out)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / it
+            pts.append({"K": K, "us": round(us, 2), "us_per_round": round(us / rounds, 3),
+                        "tflops": round(2.0 * M * N * K / us / 1e6, 1)})
+            print(f"[bench] gemm {epi} M={M} N={N} K={K}: {us:.2f} us", file=sys.stderr, flush=True)
+        fit = [(p["K"] / 64, p["us_per_round"]) for p in pts if p["K"] >= 512]
+        n = len(fit)
+        sx = sum(x for x, _ in fit); sy = sum(y for _, y in fit)
+        sxx = sum(x * x for x, _ in fit); sxy = sum(x * y for x, y in fit)
+        slope = (n * sxy - sx * sy) / (n * sxx - sx * sx)
+        icpt = (sy - slope * sx) / n
+        case = {"epilogue": epi, "M": M, "N": N, "rounds": rounds, "points": pts,
+                "fixed_us_per_tile": round(icpt, 2), "us_per_k_step": round(slope, 4)}
+        if probe:
+            # one step: 2 * 256 * 256 * 64 flops on one CU
+            ideal = 2.0 * 256 * 256 * 64 / (probe["tflops"] * 1e12 / 256) * 1e6
+            case["mfma_us_per_k_step_at_probe_rate"] = round(ideal, 4)
+            case["k_loop_fraction_of_probe_rate"] = round(ideal / slope, 3)
+        res["cases"].append(case)
+    print(json.dumps({"gemm_k_sweep": res}), flush=True)
     return 0
 
 
@@ -289,9 +351,14 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device 5 times (the reference kernel of known "
                          "traffic that scales the HBM counters) and exit")
+    ap.add_argument("--gemm-k-sweep", action="store_true",
+                    help="only time the 256 x 256 GEMM tile against K at whole rounds of tiles "
+                         "(fixed cost per tile and per-K-step rate) and exit")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.gemm_k_sweep:
+        return gemm_k_sweep()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the encoder path is built and measured on a single "
@@ -408,9 +475,12 @@ def main() -> int:
     except Exception as e:  # capture is an extra row: report, do not fail the bench
         print(f"[bench] graph replay not measured: {e}", file=sys.stderr, flush=True)
     # the chip's dense bf16 MFMA rate as a single calibration kernel sustains
-    # it (one workgroup per CU, independent MFMA chains, about 0.1 s): the
-    # practical ceiling the roofline fraction is also quoted against
+    # it (one workgroup per CU, independent MFMA chains, about 0.1 s): with
+    # constant operands, and with random operands, whose toggling bits draw
+    # more power and lower the clock the chip holds (the practical ceiling on
+    # real data; the roofline fraction is also quoted against both)
     probe = mfma_probe(_lib)
+    probe_rnd = mfma_probe(_lib, 1)
     host_tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, pin_memory=True)
     api_steps = max(1, min(args.steps, 5))
     enc.encode(frames, tokens)
@@ -450,6 +520,8 @@ def main() -> int:
         roof["traffic"], roof["traffic_source"] = tr
     if roof["unit"] == "TFLOP/s" and probe and act != "f32":
         roof["frac_of_measured_mfma"] = round(roof["achieved"] / probe["tflops"], 4)
+    if roof["unit"] == "TFLOP/s" and probe_rnd and act != "f32":
+        roof["frac_of_measured_mfma_random_operands"] = round(roof["achieved"] / probe_rnd["tflops"], 4)
     roof["batch_parts"] = 1
     roof["region_ms_per_step"] = round(1e3 * wall1 / args.steps, 4)
 
@@ -473,6 +545,7 @@ def main() -> int:
         "roofline": roof,
         "device": device_info(),
         "mfma_probe": probe,
+        "mfma_probe_random_operands": probe_rnd,
     }
     enc.close()
     del enc, tokens, pooled, fr, host_tokens

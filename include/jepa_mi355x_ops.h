@@ -143,8 +143,13 @@ jepa_status jepa_rope_table(const jepa_dims *dims, float *out);
  * `workgroups` workgroups of 4 waves runs iters x 8 independent
  * v_mfma_f32_32x32x16_bf16 chains on register operands and writes one float
  * per thread to out (device f32, workgroups * 256 elements).  Work per launch:
- * workgroups * 4 * iters * 8 * 32768 flops; the caller times the launch. */
-jepa_status jepa_op_mfma_probe(int workgroups, int iters, float *out, void *hip_stream);
+ * workgroups * 4 * iters * 8 * 32768 flops; the caller times the launch.
+ * operands: 0 = small constant values, the same bits in every instruction;
+ * 1 = random values in [-1, 1), consecutive instructions differing in both
+ * operands as in a GEMM (the matrix core's power, hence the clock the chip
+ * sustains, grows with the operand bits that toggle).  Other values:
+ * JEPA_E_INVALID_ARG. */
+jepa_status jepa_op_mfma_probe(int workgroups, int iters, int operands, float *out, void *hip_stream);
 
 /* The int8 MFMA rate, and what consuming it costs when every 32-wide K block
  * carries its own scales (the q8_0 weight format of the jepa.cpp

@@ -619,21 +619,27 @@ def test_int8_mfma_and_its_per_block_rescale(lib):
         return ops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
     bf16 = rate(lib.jepa_op_mfma_probe, cus, 20000, out)
+    bf16r = rate(lib.jepa_op_mfma_probe, cus, 20000, out, 1)
     i8 = [rate(lib.jepa_op_mfma_i8_probe, 2 * cus, 10000, m, out) for m in (0, 1, 2)]
-    say(f"  dense bf16 MFMA {bf16:.0f} TFLOP/s; int8 MFMA {i8[0]:.0f} TOP/s; with per-block row and "
-          f"column scales {i8[1]:.0f} TOP/s; with per-block column scales {i8[2]:.0f} TOP/s")
+    say(f"  dense bf16 MFMA {bf16:.0f} TFLOP/s ({bf16r:.0f} with random operands); int8 MFMA "
+        f"{i8[0]:.0f} TOP/s; with per-block row and column scales {i8[1]:.0f} TOP/s; with "
+        f"per-block column scales {i8[2]:.0f} TOP/s")
     assert lib.jepa_op_mfma_i8_probe(1, 3, 1, out) == 1 * 4 * 3 * 4 * 65536
     with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
         lib.jepa_op_mfma_i8_probe(1, 3, 3, out)
 
 
-def test_mfma_probe_runs_and_reports_its_flops(lib):
-    """The calibration kernel: finite output from every thread, and the work
-    it reports is workgroups x 4 waves x iters x 8 MFMAs of 32x32x16x2."""
+@pytest.mark.parametrize("operands", [0, 1])
+def test_mfma_probe_runs_and_reports_its_flops(lib, operands):
+    """The calibration kernel, constant or random operands: finite output
+    from every thread, and the work it reports is workgroups x 4 waves x
+    iters x 8 MFMAs of 32x32x16x2."""
     out = torch.full((8 * 256,), float("nan"), device="cuda")
-    flops = lib.jepa_op_mfma_probe(8, 100, out)
+    flops = lib.jepa_op_mfma_probe(8, 100, out, operands)
     torch.cuda.synchronize()
     assert flops == 8 * 4 * 100 * 8 * 32768
     assert torch.isfinite(out).all()
     with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
-        lib.jepa_op_mfma_probe(0, 100, out)
+        lib.jepa_op_mfma_probe(0, 100, out, operands)
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_op_mfma_probe(8, 100, out, 2)

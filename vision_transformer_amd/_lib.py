@@ -87,7 +87,7 @@ def _load():
         "jepa_op_transpose_v": (I, [I, P, I, I, I, I, P, I64, P]),
         "jepa_pack_blocks": (I, [I, P, I64, I64, P, P]),
         "jepa_rope_table": (I, [C.POINTER(jepa_dims), P]),
-        "jepa_op_mfma_probe": (I, [I, I, P, P]),
+        "jepa_op_mfma_probe": (I, [I, I, I, P, P]),
         "jepa_op_mfma_i8_probe": (I, [I, I, I, P, P]),
         "jepa_op_patch_embed": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64,
                                     I64, P, P, I, P, P]),
@@ -353,9 +353,10 @@ def jepa_op_transpose_v(act_dtype: str, qkv, batch: int, n_tokens: int, heads: i
                                     _ptr(vt), vt.shape[-1], _stream(stream)))
 
 
-def jepa_op_mfma_probe(workgroups: int, iters: int, out, stream=None) -> int:
-    """Dense bf16 MFMA calibration launch; returns its flops."""
-    _check(_lib.jepa_op_mfma_probe(workgroups, iters, _ptr(out), _stream(stream)))
+def jepa_op_mfma_probe(workgroups: int, iters: int, out, operands: int = 0, stream=None) -> int:
+    """Dense bf16 MFMA calibration launch (operands 0: constant, 1: random);
+    returns its flops."""
+    _check(_lib.jepa_op_mfma_probe(workgroups, iters, operands, _ptr(out), _stream(stream)))
     return workgroups * 4 * iters * 8 * 32 * 32 * 16 * 2
 
 

@@ -1538,9 +1538,10 @@ jepa_status jepa_op_mfma_i8_probe(int workgroups, int iters, int mode, float *ou
     return hip_status(launch_mfma_i8_probe(workgroups, iters, mode, out, (hipStream_t)hip_stream), "op_mfma_i8_probe");
 }
 
-jepa_status jepa_op_mfma_probe(int workgroups, int iters, float *out, void *hip_stream) {
-    if (!out || workgroups <= 0 || iters <= 0) return fail(JEPA_E_INVALID_ARG, "op_mfma_probe: bad arguments");
-    return hip_status(launch_mfma_probe(workgroups, iters, out, (hipStream_t)hip_stream), "op_mfma_probe");
+jepa_status jepa_op_mfma_probe(int workgroups, int iters, int operands, float *out, void *hip_stream) {
+    if (!out || workgroups <= 0 || iters <= 0 || operands < 0 || operands > 1)
+        return fail(JEPA_E_INVALID_ARG, "op_mfma_probe: bad arguments");
+    return hip_status(launch_mfma_probe(workgroups, iters, operands, out, (hipStream_t)hip_stream), "op_mfma_probe");
 }
 
 jepa_status jepa_rope_table(const jepa_dims *dims, float *out) {

@@ -129,7 +129,7 @@ hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t
 hipError_t launch_fill(float *x, int64_t n, float v, hipStream_t s);
 // dense bf16 MFMA calibration: workgroups x 4 waves, each iters x 8
 // independent 32x32x16 MFMAs; out holds workgroups * 256 floats
-hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
+hipError_t launch_mfma_probe(int workgroups, int iters, int operands, float *out, hipStream_t s);
 // int8 MFMA calibration: mode 0 plain, 1 / 2 with per-block rescaling into
 // f32 (see misc.hip); workgroups x 4 waves, each iters x 4 32x32x32 MFMAs
 hipError_t launch_mfma_i8_probe(int workgroups, int iters, int mode, float *out, hipStream_t s);

@@ -311,13 +311,33 @@ __global__ __launch_bounds__(256) void dequant_units_kernel(int w_dt, const void
 // v_mfma_f32_32x32x16_bf16 chains on register operands (so the matrix core
 // never waits on a result), then stores the sum of its accumulators so that
 // nothing is optimised away.  32 * 32 * 16 * 2 flops per instruction.
+// Operands (RND = false): small constant values, one A and one B register
+// set, the same bits in every instruction.  RND = true: four A and four B
+// sets of random bf16 values in [-1, 1) (a counter hash of thread, set and
+// element), paired so that consecutive MFMAs differ in both operands, as
+// they do in a GEMM.  The matrix core's power, and with it the clock the chip
+// holds, depends on how many operand bits toggle, so the two rates differ.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+    x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+    return x;
+}
+template <bool RND>
 __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *out) {
-    bf16x8 a, b;
+    constexpr int SETS = RND ? 4 : 1;
+    bf16x8 a[SETS], b[SETS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        a[j] = (__bf16)(1e-3f * (float)((threadIdx.x + j) & 7));
-        b[j] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + j) & 7));
-    }
+    for (int t = 0; t < SETS; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (RND) {
+                const uint32_t h = probe_hash((blockIdx.x * 256 + threadIdx.x) * 64 + t * 8 + j);
+                a[t][j] = (__bf16)((float)(h & 0xffff) * (1.f / 32768.f) - 1.f);
+                b[t][j] = (__bf16)((float)(h >> 16) * (1.f / 32768.f) - 1.f);
+            } else {
+                a[t][j] = (__bf16)(1e-3f * (float)((threadIdx.x + j) & 7));
+                b[t][j] = (__bf16)(1e-3f * (float)((threadIdx.x * 3 + j) & 7));
+            }
+        }
     f32x16 acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -325,7 +345,8 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *out) 
         for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
     for (int i = 0; i < iters; ++i)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        for (int c = 0; c < 8; ++c)   // (a, b) sets (0,0) (1,1) (2,2) (3,3) (0,1) (1,2) (2,3) (3,0)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c % SETS], b[(c + c / 4) % SETS], acc[c], 0, 0, 0);
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -478,9 +499,10 @@ hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_probe(int workgroups, int iters, float *out, hipStream_t s) {
-    if (workgroups <= 0 || iters <= 0 || !out) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mfma_probe_kernel, dim3(workgroups), dim3(256), 0, s, iters, out);
+hipError_t launch_mfma_probe(int workgroups, int iters, int operands, float *out, hipStream_t s) {
+    if (workgroups <= 0 || iters <= 0 || operands < 0 || operands > 1 || !out) return hipErrorInvalidValue;
+    if (operands == 0) hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3(workgroups), dim3(256), 0, s, iters, out);
+    else hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3(workgroups), dim3(256), 0, s, iters, out);
     return hipGetLastError();
 }
 
