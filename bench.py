@@ -280,6 +280,35 @@ def gemm_k_sweep() -> int:
             case["mfma_us_per_k_step_at_probe_rate"] = round(ideal, 4)
             case["k_loop_fraction_of_probe_rate"] = round(ideal / slope, 3)
         res["cases"].append(case)
+    # The same K step with a quarter, half and all of the CUs holding a tile
+    # (N 1024, plain store, K 2048 -> 4096): a step slower at full occupancy
+    # than on a part of the chip is the clock the chip's power limit allows,
+    # not the kernel's schedule.
+    occ = []
+    N = 1024
+    b = torch.randn(N, device=dev) * 0.02
+    for M in (4096, 8192, 16384):
+        out = torch.zeros(M, N, device=dev, dtype=torch.bfloat16)
+        row = {"M": M, "tiles": (M // 256) * (N // 256)}
+        for K in (2048, 4096):
+            a = (torch.randn(M, K, device=dev) * 0.5).to(torch.bfloat16)
+            w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:
+                _lib.jepa_op_gemm("bf16", a, w, "bf16", N, b, "store", out)
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                _lib.jepa_op_gemm("bf16", a, w, "bf16", N, b, "store", out)
+            e1.record()
+            torch.cuda.synchronize()
+            row[f"us_K{K}"] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
+        row["us_per_k_step"] = round((row["us_K4096"] - row["us_K2048"]) / 32, 4)
+        row["tflops_per_cu"] = round(2.0 * 256 * 256 * 64 / (row["us_per_k_step"] * 1e-6) / 1e12, 2)
+        occ.append(row)
+        print(f"[bench] gemm store M={M} N={N}: {row['us_per_k_step']:.4f} us per K step", file=sys.stderr, flush=True)
+    res["occupancy"] = occ
     print(json.dumps({"gemm_k_sweep": res}), flush=True)
     return 0
 
