@@ -30,6 +30,9 @@ Where the pages are silent the readings are:
       a segment is rotated by pos_axis * 10000^(-2i/ds).  q and k are rotated
       before the scores; v is not.  A CLS token has no position (angle 0),
       and with rotary position the model has no additive table.
+  R17 The int8 path of block matrices (see quant.quantize_act_q8): the input
+      of each of a block's four products is quantised per 32-block and
+      dequantised exactly before the product; nothing else changes.
 """
 from __future__ import annotations
 
@@ -72,6 +75,11 @@ def patchify(x: np.ndarray, tubelet: int, patch: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # per-token operations
 # ---------------------------------------------------------------------------
+
+def linear_act_q8(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """x w^T + b with x first quantised per 32-block as the int8 path does (R17)."""
+    return linear(quant.act_q8_values(*quant.quantize_act_q8(x)), w, b)
+
 
 def linear(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
     """x [..., in] times w [out, in] transposed, plus b [out]."""
@@ -206,12 +214,14 @@ def embed(dims: dict, w: dict, frames: np.ndarray) -> np.ndarray:
 
 
 def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed, prefix: str = "enc.blk.",
-          rotary: bool | None = None) -> np.ndarray:
+          rotary: bool | None = None, act_q8: bool = False) -> np.ndarray:
     """One pre-LN block on X [B, N, D]:  x += Attn(LN1 x);  x += MLP(LN2 x).
 
     prefix names the block's tensors ("enc.blk." or, for the classifier
-    head, "head.blk."); rotary defaults to the model's setting (R12)."""
+    head, "head.blk."); rotary defaults to the model's setting (R12);
+    act_q8 runs the four products on quantised inputs (R17)."""
     p = f"{prefix}{i}."
+    linear = linear_act_q8 if act_q8 else globals()["linear"]
     eps = dims["ln_eps"]
     h = layer_norm(x, w[p + "ln1.weight"], w[p + "ln1.bias"], eps)
     qkv = linear(h, w[p + "attn_qkv.weight"], w[p + "attn_qkv.bias"])
@@ -226,17 +236,17 @@ def block(dims: dict, w: dict, i: int, x: np.ndarray, allowed, prefix: str = "en
 
 
 def encode(dims: dict, w: dict, frames: np.ndarray, depth: int | None = None,
-           return_pre_norm: bool = False):
+           return_pre_norm: bool = False, act_q8: bool = False):
     """frames uint8 [B, T, H, W, 3] -> final-LN token map [B, N, D] (float64).
 
     `depth` evaluates only the first blocks (used to time a bounded sample).
     With return_pre_norm, also returns the residual stream before the final
-    LayerNorm.
+    LayerNorm.  act_q8: the int8 path of block matrices (R17).
     """
     allowed = allowed_for(dims)
     x = embed(dims, w, frames)
     for i in range(dims["depth"] if depth is None else depth):
-        x = block(dims, w, i, x, allowed)
+        x = block(dims, w, i, x, allowed, act_q8=act_q8)
     y = layer_norm(x, w["enc.norm.weight"], w["enc.norm.bias"], dims["ln_eps"])
     return (y, x) if return_pre_norm else y
 

@@ -103,6 +103,50 @@ def dequantize_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Activation blocks for integer matrix products (the int8 path of block
+# matrices).  The Benchmarks page ("Effect of the weight dtype on a GPU
+# (encoder)") times q8_0 and K-quant encoders whose products run on int8
+# arithmetic, and the Quantization page says the q8_0 CPU path quantises the
+# activations of every product; neither prints the activation format.  The
+# reading taken (R17): each row of a product's input is cut into blocks of 32
+# along K, like the weight blocks, and quantised the way q8_0 weights are
+# (symmetric, d = max|x| / 127, code round(x / d) half away from zero), with
+# the scale kept in f32, not rounded to f16.  x / d is one correctly rounded
+# f32 division: the codes are integer decisions taken in f32, the precision
+# the GPU kernel takes them in.  An all-zero block has d = 0 and codes 0.
+#
+# The product of such a row with a q8_0 / q4_0 weight row is
+#   sum_b d_a[b] d_w[b] sum_{k in b} q_a[k] q_w[k] = sum_k (d_a q_a)[k] w[k],
+# exactly, with w the exactly dequantised weights: so the plain product of
+# the dequantised activations (act_q8_values) with the stored weights is the
+# int8 path's result, with nothing about the integer arithmetic left out.
+# ---------------------------------------------------------------------------
+
+def quantize_act_q8(x: np.ndarray):
+    """[..., K] -> (int8 codes [..., K], f32 scales [..., K/32])  (R17)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    K = x32.shape[-1]
+    if K % QK:
+        raise ValueError("rows must be a multiple of 32 long")
+    b = x32.reshape(*x32.shape[:-1], K // QK, QK)
+    amax = np.max(np.abs(b), axis=-1)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(d[..., None] != 0, b / d[..., None], np.float32(0.0)).astype(np.float32)
+    v = v.astype(np.float64)
+    # round half away from zero; |v| + 0.5 is exact in float64 for an f32 v
+    q = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -127, 127).astype(np.int8)
+    return q.reshape(x32.shape), d
+
+
+def act_q8_values(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Codes and scales of quantize_act_q8 -> the float64 values d * q."""
+    K = q.shape[-1]
+    v = q.reshape(*q.shape[:-1], K // QK, QK).astype(np.float64) * np.asarray(d, np.float64)[..., None]
+    return v.reshape(q.shape)
+
+
+# ---------------------------------------------------------------------------
 # K-quants: super-blocks of 256 weights along a row (Quantization page, "The
 # rule": "block 256"; "File sizes": q4_k has q4_0's 4.5 bits per weight).  The
 # pages name the formats by their ggml names (q4_K, q6_K); their layouts are

@@ -169,3 +169,33 @@ def classify(dims, w, y):
         xq = [xq[d] + mlp[d] for d in range(D)]
         out.append(_lin(xq, w["head.classifier.weight"], w["head.classifier.bias"]))
     return out
+
+
+def _f32(v: float) -> float:
+    """v rounded to the nearest f32 (ties to even), as a Python float."""
+    import struct
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def quantize_act_q8(row):
+    """One row (a multiple of 32 long) -> (codes, scales), scalar loops.
+
+    The f32 quotient of two f32 values is the f64 quotient rounded to f32 (the
+    double rounding is harmless for division: 53 >= 2*24 + 2)."""
+    codes, scales = [], []
+    for b0 in range(0, len(row), 32):
+        blk = [_f32(float(v)) for v in row[b0:b0 + 32]]
+        amax = 0.0
+        for v in blk:
+            amax = max(amax, abs(v))
+        d = _f32(amax / 127.0)
+        scales.append(d)
+        for v in blk:
+            if d == 0.0:
+                codes.append(0)
+                continue
+            t = _f32(v / d)
+            q = math.floor(abs(t) + 0.5)
+            q = min(q, 127)
+            codes.append(int(q) if t >= 0 else -int(q))
+    return codes, scales

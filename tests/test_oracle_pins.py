@@ -762,3 +762,108 @@ def test_metrics_closed_forms():
     np.testing.assert_allclose(c, [1 / math.sqrt(2), 1.0])
     assert M.rel_max(a, b) == pytest.approx(0.5)
     assert M.rel_fro(a, b) == pytest.approx(1 / math.sqrt(5))
+
+
+# ---------------------------------------------------------------------------
+# int8 path: activations quantised per 32-block (R17)
+# ---------------------------------------------------------------------------
+
+def test_act_q8_closed_form_integer_multiples():
+    # a block of k * 2^e with k integers and max |k| = 127: d is exactly 2^e
+    # and every code is its k
+    rng = np.random.default_rng(5)
+    k = rng.integers(-127, 128, size=(3, 64))
+    k[:, 7] = 127
+    k[:, 40] = -127
+    for e in (-9, 0, 4):
+        q, d = Q.quantize_act_q8(k * 2.0 ** e)
+        assert d.dtype == np.float32 and q.dtype == np.int8
+        assert np.all(d == np.float32(2.0 ** e))
+        assert np.array_equal(q.astype(np.int64), k)
+
+
+def test_act_q8_ties_round_half_away_from_zero():
+    x = np.zeros(32)
+    x[:9] = [127.0, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, 0.49999997]
+    q, d = Q.quantize_act_q8(x[None])
+    assert d[0, 0] == 1.0
+    assert list(q[0, :9]) == [127, 1, -1, 2, -2, 3, -3, 127, 0]
+
+
+def test_act_q8_zero_and_single_value_blocks():
+    x = np.zeros((2, 64))
+    x[1, 33] = -3.0e-5
+    q, d = Q.quantize_act_q8(x)
+    assert np.all(d[0] == 0) and np.all(q[0] == 0) and d[1, 0] == 0
+    assert d[1, 1] == np.float32(np.float32(3.0e-5) / np.float32(127.0))
+    assert q[1, 33] == -127 and np.count_nonzero(q[1]) == 1
+
+
+def test_act_q8_error_bound_and_extremes():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 6, (64, 1)))).astype(np.float32)
+    q, d = Q.quantize_act_q8(x)
+    b = x.reshape(64, 8, 32).astype(np.float64)
+    amax = np.max(np.abs(b), axis=2)
+    # the scale is amax / 127 rounded once to f32
+    assert np.all(np.abs(d - amax / 127.0) <= 2.0 ** -24 * amax / 127.0)
+    # every value is within half a step of d * q, and the largest maps to 127
+    err = np.abs(Q.act_q8_values(q, d).reshape(64, 8, 32) - b)
+    assert np.all(err <= 0.5 * d[..., None].astype(np.float64) * (1 + 2.0 ** -20))
+    qa = np.abs(q.astype(np.int64)).reshape(64, 8, 32)
+    assert np.all(qa <= 127) and np.all(np.max(qa, axis=2) == 127)
+
+
+def test_act_q8_matches_scalar_brute_force():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((5, 96)) * 0.3).astype(np.float32)
+    x[2, 32:64] = 0.0
+    q, d = Q.quantize_act_q8(x)
+    for r in range(5):
+        bq, bd = brute.quantize_act_q8([float(v) for v in x[r]])
+        assert list(q[r].astype(int)) == bq
+        assert [float(v) for v in d[r]] == bd
+
+
+def test_int8_product_is_the_block_sum_of_integer_dots():
+    # the int8 path's sum over blocks of d_a d_w (q_a . q_w), in exact
+    # rationals, against the oracle's product of the dequantised operands
+    from fractions import Fraction
+    rng = np.random.default_rng(8)
+    K, N = 96, 3
+    x = rng.standard_normal((2, K)).astype(np.float32)
+    wt = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    bias = rng.standard_normal(N)
+    for dt in ("q8_0", "q4_0"):
+        raw = Q.quantize(dt, wt)
+        wdq = (Q.dequantize_q8_0 if dt == "q8_0" else Q.dequantize_q4_0)(raw, N, K)
+        bb = Q.block_bytes(dt)
+        blocks = raw.reshape(N, K // 32, bb)
+        dw = blocks[:, :, :2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+        if dt == "q8_0":
+            qw = blocks[:, :, 2:].view(np.int8).astype(np.int64)
+        else:
+            nib = blocks[:, :, 2:].astype(np.int64)
+            qw = np.concatenate([(nib & 15) - 8, (nib >> 4) - 8], axis=2)
+        qa, da = Q.quantize_act_q8(x)
+        got = E.linear_act_q8(x.astype(np.float64), wdq.astype(np.float64), bias)
+        for m in range(2):
+            for n in range(N):
+                s = Fraction(float(bias[n]))
+                for b in range(K // 32):
+                    dot = sum(int(qa[m, 32 * b + k]) * int(qw[n, b, k]) for k in range(32))
+                    s += Fraction(float(da[m, b])) * Fraction(float(dw[n, b])) * dot
+                assert abs(got[m, n] - float(s)) <= 1e-12 * (1 + abs(float(s)))
+
+
+def test_act_q8_encoder_stays_close_to_dense():
+    # the int8 path changes each product's input by at most half a step per
+    # 32-block, so on a tiny encoder its tokens stay close to the dense ones
+    dims = _tiny_dims(dim=32, mlp_dim=64)
+    w = _tiny_weights(dims, 3)
+    frames = synth.make_frames(dims, 2, 3)
+    y = E.encode(dims, w, frames)
+    y8 = E.encode(dims, w, frames, act_q8=True)
+    assert not np.array_equal(y, y8)
+    cos = np.sum(y * y8, -1) / np.linalg.norm(y, axis=-1) / np.linalg.norm(y8, axis=-1)
+    assert cos.min() > 0.999
