@@ -274,6 +274,24 @@ jepa_status jepa_encode_noalloc(jepa_ctx *ctx, const uint8_t *frames, int batch,
  * JEPA_E_INVALID_ARG unless 0 <= parts <= 4. */
 jepa_status jepa_set_batch_parts(jepa_ctx *ctx, int parts);
 
+/* The int8 path of q8_0 / q4_0 matrices (Benchmarks page, "Effect of the
+ * weight dtype on a GPU (encoder)": the quantised encoders' products run on
+ * integer arithmetic; Quantization page: the q8_0 path quantises the
+ * activations of every product).  With enable = 1, each of a block's four
+ * products whose matrix is Q8_0 or Q4_0 first quantises its input per
+ * 32-block along K (d = max|x| / 127 in f32, codes round(x / d) half away
+ * from zero), then runs every block's integer dot product on int8 MFMA and
+ * adds d_a * d_w * dot into f32 accumulators; the epilogues are unchanged.
+ * The result differs from the default path by the activations'
+ * quantisation (up to half a step per value).  enable = 0 restores the
+ * default (act-dtype MFMA on dequantised weights).  Changing it frees the
+ * workspace (after a device synchronisation); the next encode allocates
+ * one with room for the quantised inputs.  The classifier head's blocks
+ * follow it; its other products do not.  JEPA_E_UNSUPPORTED for f32
+ * models, models with K-quant matrices, or dim / mlp_dim not multiples of
+ * 128; JEPA_E_INVALID_ARG unless enable is 0 or 1. */
+jepa_status jepa_set_int8_matmul(jepa_ctx *ctx, int enable);
+
 /* Pool the token map of the last encode.  out: device f32 [batch, dim] for
  * CLS (token 0; needs has_cls) and MEAN (mean of the patch tokens, CLS
  * excluded), [batch, N, dim] for NONE (a copy of the token map).

@@ -69,6 +69,27 @@ jepa_status jepa_op_patch_embed(int act_dtype, const uint8_t *frames, int B, int
                                 int64_t n, const float *bias, const float *pos, int has_cls, float *out,
                                 void *hip_stream);
 
+/* Activations quantised per 32-block for the int8 path (see
+ * jepa_set_int8_matmul): x act_dtype (F16 / BF16) [rows, k], k % 32 == 0,
+ * 16-byte aligned -> codes_out int8 [rows, k] (16-byte aligned) and
+ * scales_out f32 [rows, k / 32]: for each block of 32 values of a row,
+ * d = max|x| / 127 and code = round(x / d) half away from zero (0 when d is
+ * 0), both in f32. */
+jepa_status jepa_op_quantize_act(int act_dtype, const void *x, int64_t rows, int64_t k, int8_t *codes_out,
+                                 float *scales_out, void *hip_stream);
+
+/* The int8 product of jepa_set_int8_matmul: acc[m, n] = bias[n] + sum over
+ * the K / 32 blocks b of a_scales[m, b] * d_w[n, b] * (the int32 dot product
+ * of a_codes[m, block b] and the weight codes of row n, block b), in f32,
+ * then jepa_op_gemm's epilogue into out (act_dtype F16 / BF16 for STORE /
+ * GELU, f32 for RESID; pitch ldo >= N).  a_codes int8 [M, K], a_scales f32
+ * [M, K / 32] as jepa_op_quantize_act writes them; w packed Q8_0 (codes
+ * int8) or Q4_0 (codes nibble - 8) as for jepa_op_gemm, w_scale their f16
+ * scales [N, K / 32].  K % 128 == 0, N % 64 == 0. */
+jepa_status jepa_op_gemm_i8(int act_dtype, const int8_t *a_codes, const float *a_scales, int64_t M, int64_t K,
+                            const void *w, int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
+                            int epilogue, void *out, int64_t ldo, void *hip_stream);
+
 /* Linear layer (attn_qkv / attn_out / ffn_up / ffn_down, Quantization page
  * "The rule"): acc = a[M, K] * w[N, K]^T in f32, then the epilogue.  a is
  * act_dtype; w is act_dtype (dense) or packed Q8_0 / Q4_0 (see

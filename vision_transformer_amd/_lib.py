@@ -77,11 +77,14 @@ def _load():
         "jepa_quantize": (I, [I, P, I64, I64, P]),
         "jepa_set_profiling": (I, [P, C.c_uint32]),
         "jepa_set_batch_parts": (I, [P, I]),
+        "jepa_set_int8_matmul": (I, [P, I]),
         "jepa_kernel_stats": (I, [P, C.POINTER(jepa_kernel_stat), I]),
         "jepa_reset_kernel_stats": (None, [P]),
         "jepa_op_patchify": (I, [I, P, I, I, I, I, I, I, C.POINTER(C.c_float), C.POINTER(C.c_float), P, I64, P]),
         "jepa_op_layernorm": (I, [P, I64, I, P, P, C.c_float, P, I, P]),
         "jepa_op_gemm": (I, [I, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
+        "jepa_op_quantize_act": (I, [I, P, I64, I64, P, P, P]),
+        "jepa_op_gemm_i8": (I, [I, P, P, I64, I64, P, I, P, I64, P, I, P, I64, P]),
         "jepa_op_gemm_qkv": (I, [I, P, I64, I64, P, I, P, I, I, P, I, P, I64, P, I64, P, C.c_float, P]),
         "jepa_op_attention": (I, [I, P, I64, P, I64, I, I, I, I, I, I, I, I, P, P]),
         "jepa_op_transpose_v": (I, [I, P, I, I, I, I, P, I64, P]),
@@ -258,6 +261,11 @@ def jepa_set_batch_parts(ctx: int, parts: int) -> None:
     _check(_lib.jepa_set_batch_parts(ctx, parts))
 
 
+def jepa_set_int8_matmul(ctx: int, enable: bool) -> None:
+    """Run q8_0 / q4_0 products on int8 MFMA with quantised inputs (or not)."""
+    _check(_lib.jepa_set_int8_matmul(ctx, 1 if enable else 0))
+
+
 def jepa_set_profiling(ctx: int, class_mask: int) -> None:
     """class_mask: bit i times kernel class i (0 = off, 0xffffffff = all)."""
     _check(_lib.jepa_set_profiling(ctx, class_mask & 0xFFFFFFFF))
@@ -303,6 +311,21 @@ def jepa_op_gemm(act_dtype: str, a, w, w_dtype: str, n: int, bias, epilogue: str
     M, K = a.shape
     _check(_lib.jepa_op_gemm(DTYPE[act_dtype], _ptr(a), M, K, _ptr(w), DTYPE[w_dtype], _ptr(w_scale),
                              n, _ptr(bias), EPI[epilogue], _ptr(out), out.shape[1], _stream(stream)))
+
+
+def jepa_op_quantize_act(act_dtype: str, x, codes_out, scales_out, stream=None) -> None:
+    """x act [rows, k] -> codes_out int8 [rows, k], scales_out f32 [rows, k/32]."""
+    rows, k = x.shape
+    _check(_lib.jepa_op_quantize_act(DTYPE[act_dtype], _ptr(x), rows, k, _ptr(codes_out), _ptr(scales_out),
+                                     _stream(stream)))
+
+
+def jepa_op_gemm_i8(act_dtype: str, a_codes, a_scales, w, w_dtype: str, n: int, bias, epilogue: str, out,
+                    w_scale, stream=None) -> None:
+    M, K = a_codes.shape
+    _check(_lib.jepa_op_gemm_i8(DTYPE[act_dtype], _ptr(a_codes), _ptr(a_scales), M, K, _ptr(w),
+                                DTYPE[w_dtype], _ptr(w_scale), n, _ptr(bias), EPI[epilogue], _ptr(out),
+                                out.shape[1], _stream(stream)))
 
 
 def jepa_op_gemm_qkv(act_dtype: str, a, w, w_dtype: str, heads: int, bias, n_tokens: int, qk_out, vt,

@@ -169,6 +169,10 @@ struct Ws {
     float *hx = nullptr, *hl = nullptr;
     void *hh = nullptr, *hq = nullptr, *ho = nullptr, *hu = nullptr;
     float *kpart = nullptr, *kvpart = nullptr;   // f32 models: split partials
+    // int8 path: a product's input quantised per 32-block, codes [rows,
+    // max(D, F)] and f32 scales [rows, max(D, F) / 32]
+    int8_t *qa = nullptr;
+    float *qas = nullptr;
 };
 
 }  // namespace
@@ -213,6 +217,7 @@ struct jepa_ctx {
     bool h_pending = false;
     Ws w;                       // the workspace's buffers
     bool last_expand = false;   // the last encode used the expanded matrices
+    bool int8_mm = false;       // jepa_set_int8_matmul: q8_0 / q4_0 products on int8 MFMA
     // last encode
     const float *last_tokens = nullptr;
     int last_batch = 0;
@@ -238,7 +243,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, kpart, kvpart, total;
+    size_t frames, patch, x, hn, qkv, vt, o, u, y, pool, hx, hh, hq, ho, hu, hl, kpart, kvpart, qa, qas, total;
 };
 
 // with_frames: a region for host frames staged to the device
@@ -270,6 +275,9 @@ WsLayout ws_layout(const jepa_ctx *c, int B, bool with_frames = true) {
     const bool f32 = c->act == JEPA_F32;
     w.kpart = take(f32 ? (size_t)KSPLIT_MAX * M * c->D * 4 : 0);
     w.kvpart = take(f32 ? (size_t)KVSPLIT_MAX * M * c->H * (c->D / c->H + 2) * 4 : 0);
+    const size_t kf = (size_t)std::max(c->D, c->F);
+    w.qa = take(c->int8_mm ? M * kf : 0);
+    w.qas = take(c->int8_mm ? M * (kf / 32) * 4 : 0);
     w.total = off;
     return w;
 }
@@ -315,6 +323,7 @@ size_t expand_bytes(const jepa_ctx *c) {
 bool use_expand(const jepa_ctx *c, int batch, int parts) {
     if (!c->has_q) return false;
     if (c->has_k) return true;
+    if (c->int8_mm) return false;   // the int8 path reads the blocks themselves
     if (const char *e = getenv("JEPA_Q_EXPAND")) {
         if (!strcmp(e, "0")) return false;
         if (!strcmp(e, "1")) return true;
@@ -383,6 +392,8 @@ Ws ws_pointers(const jepa_ctx *c, const WsLayout &w, unsigned char *base) {
     p.hl = (float *)(base + w.hl);
     p.kpart = c->act == JEPA_F32 ? (float *)(base + w.kpart) : nullptr;
     p.kvpart = c->act == JEPA_F32 ? (float *)(base + w.kvpart) : nullptr;
+    p.qa = c->int8_mm ? (int8_t *)(base + w.qa) : nullptr;
+    p.qas = c->int8_mm ? (float *)(base + w.qas) : nullptr;
     return p;
 }
 
@@ -393,6 +404,20 @@ void clear_workspace(jepa_ctx *c) {
     c->ws_batch = 0;
 }
 
+// Free the workspace once the device is idle; nothing may keep pointing into
+// it afterwards (the next encode allocates it again).
+jepa_status release_workspace(jepa_ctx *c) {
+    if (!c->ws) return JEPA_OK;
+    c->encoded = false;
+    c->last_tokens = nullptr;
+    c->last_batch = 0;
+    HIP_TRY(hipDeviceSynchronize());
+    clear_workspace(c);
+    HIP_TRY(hipFree(c->ws));
+    c->ws = nullptr;
+    return JEPA_OK;
+}
+
 jepa_status ensure_workspace(jepa_ctx *c, int B) {
     if (B <= c->ws_batch) return JEPA_OK;
     WsLayout w = ws_layout(c, B);
@@ -400,16 +425,7 @@ jepa_status ensure_workspace(jepa_ctx *c, int B) {
     if (cap && (double)w.total > atof(cap))
         return fail(JEPA_E_OOM, "workspace of %zu bytes for batch %d exceeds JEPA_MAX_WORKSPACE=%s",
                     w.total, B, cap);
-    if (c->ws) {
-        // nothing may keep pointing into the old workspace once it is freed
-        c->encoded = false;
-        c->last_tokens = nullptr;
-        c->last_batch = 0;
-        HIP_TRY(hipDeviceSynchronize());
-        clear_workspace(c);
-        HIP_TRY(hipFree(c->ws));
-        c->ws = nullptr;
-    }
+    if (const jepa_status st = release_workspace(c)) return st;
     if (hipMalloc(&c->ws, w.total) != hipSuccess) {
         c->ws = nullptr;
         (void)hipGetLastError();
@@ -978,6 +994,32 @@ static jepa_status run_block(jepa_ctx *c, const Ws &w, const Layer &L, bool expa
     aa.q_prescaled = 1;
     aa.dh = dh;
     aa.kvpart = w.kvpart ? w.kvpart + (size_t)KVSPLIT_MAX * r0 * c->H * (dh + 2) : nullptr;
+    // the int8 path (jepa_set_int8_matmul) for q8_0 / q4_0 matrices: the
+    // product's input is quantised per 32-block into this part's rows of
+    // qa / qas (pitch K), then multiplied on int8 MFMA
+    const bool i8 = c->int8_mm && !expand;
+    const int64_t kf = std::max(D, F);
+    int8_t *qa = i8 ? w.qa + r0 * kf : nullptr;
+    float *qas = i8 ? w.qas + r0 * (kf / 32) : nullptr;
+    auto run_gemm = [&](int cls, GemmArgs g, int w_dt, int epi) -> jepa_status {
+        if (i8 && (w_dt == JEPA_Q8_0 || w_dt == JEPA_Q4_0)) {
+            const void *in = g.a;
+            const int64_t ld = g.lda;
+            TRY(launch(c, cls, s, [&] { return launch_quant_act(c->act, in, ld, g.M, g.K, qa, g.K, qas, s); }));
+            g.a = qa; g.lda = g.K; g.ascale = qas;
+            return launch(c, cls, s, [&] { return launch_gemm_i8(c->act, w_dt, epi, g, s); });
+        }
+        return launch(c, cls, s, [&] { return launch_gemm(c->act, w_dt, epi, g, s); });
+    };
+    auto mm = [&](int cls, const void *a, int64_t K, const DevTensor &W, const float *bias, int epi, void *out,
+                  int64_t ldo, float *kp) -> jepa_status {
+        GemmArgs g{};
+        g.a = a; g.w = W.ptr; g.wscale = W.scale; g.bias = bias; g.out = out;
+        g.M = M; g.N = W.ne1; g.K = K; g.lda = K; g.ldo = ldo;
+        g.conc = conc;
+        g.kpart = kp;
+        return run_gemm(cls, g, W.dev_dt, epi);
+    };
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln1g, L.ln1b, d.ln_eps, hn, c->act, s); }));
     {   // q, k to qkv; v transposed straight into V^T
         GemmArgs g{};
@@ -987,16 +1029,16 @@ static jepa_status run_block(jepa_ctx *c, const Ws &w, const Layer &L, bool expa
         g.rope = rope; g.head_dim = dh;
         g.qscale = attn_q_scale(dh);   // the softmax scale and base change, folded into q
         g.conc = conc;
-        TRY(launch(c, K_GEMM_QKV, s, [&] { return launch_gemm(c->act, Wqkv.dev_dt, EPI_QKV, g, s); }));
+        TRY(run_gemm(K_GEMM_QKV, g, Wqkv.dev_dt, EPI_QKV));
     }
     TRY(launch(c, K_ATTN, s, [&] { return launch_attention(c->act, aa, s); }));
     // f32 models: scratch for splitting the residual GEMMs' K (each batch
     // part its own rows of it)
     float *kpart = w.kpart ? w.kpart + (size_t)KSPLIT_MAX * r0 * D : nullptr;
-    TRY(gemm(c, K_GEMM_OUT, s, conc, o, M, D, Wout, L.bout, EPI_RESID, x, D, kpart));
+    TRY(mm(K_GEMM_OUT, o, D, Wout, L.bout, EPI_RESID, x, D, kpart));
     TRY(launch(c, K_LN, s, [&] { return launch_layernorm(x, M, D, L.ln2g, L.ln2b, d.ln_eps, hn, c->act, s); }));
-    TRY(gemm(c, K_GEMM_FC1, s, conc, hn, M, D, Wup, L.bup, EPI_GELU, u, F));
-    TRY(gemm(c, K_GEMM_FC2, s, conc, u, M, F, Wdown, L.bdown, EPI_RESID, x, D, kpart));
+    TRY(mm(K_GEMM_FC1, hn, D, Wup, L.bup, EPI_GELU, u, F, nullptr));
+    TRY(mm(K_GEMM_FC2, u, F, Wdown, L.bdown, EPI_RESID, x, D, kpart));
     return JEPA_OK;
 }
 
@@ -1296,6 +1338,21 @@ jepa_status jepa_set_batch_parts(jepa_ctx *c, int parts) {
     return JEPA_OK;
 }
 
+jepa_status jepa_set_int8_matmul(jepa_ctx *c, int enable) {
+    if (!c) return fail(JEPA_E_INVALID_ARG, "set_int8_matmul: null context");
+    if (enable != 0 && enable != 1) return fail(JEPA_E_INVALID_ARG, "set_int8_matmul: enable must be 0 or 1");
+    if (enable && c->act == JEPA_F32) return fail(JEPA_E_UNSUPPORTED, "set_int8_matmul: f32 models have no block matrices");
+    if (enable && c->has_k)
+        return fail(JEPA_E_UNSUPPORTED, "set_int8_matmul: K-quant models run from their expanded act-dtype copies");
+    if (enable && (c->D % 128 || c->F % 128))
+        return fail(JEPA_E_UNSUPPORTED, "set_int8_matmul: dim and mlp_dim must be multiples of 128");
+    if ((bool)enable == c->int8_mm) return JEPA_OK;
+    // the workspace layout changes: the next encode allocates it again
+    TRY(release_workspace(c));
+    c->int8_mm = enable != 0;
+    return JEPA_OK;
+}
+
 jepa_status jepa_pool(jepa_ctx *c, int mode, float *out, void *hip_stream) {
     if (!c || !out) return fail(JEPA_E_INVALID_ARG, "pool: null argument");
     if (!c->encoded) return fail(JEPA_E_STATE, "pool: nothing encoded yet");
@@ -1450,6 +1507,29 @@ jepa_status jepa_op_gemm(int act_dtype, const void *a, int64_t M, int64_t K, con
     g.a = a; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = out;
     g.M = M; g.N = N; g.K = K; g.lda = K; g.ldo = ldo;
     return hip_status(launch_gemm(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm");
+}
+
+jepa_status jepa_op_quantize_act(int act_dtype, const void *x, int64_t rows, int64_t k, int8_t *codes_out,
+                                 float *scales_out, void *hip_stream) {
+    if (!x || !codes_out || !scales_out) return fail(JEPA_E_INVALID_ARG, "op_quantize_act: null argument");
+    if (act_dtype != JEPA_F16 && act_dtype != JEPA_BF16) return fail(JEPA_E_DTYPE, "op_quantize_act: act must be F16 or BF16");
+    if (rows <= 0 || k <= 0 || k % 32) return fail(JEPA_E_SHAPE, "op_quantize_act: rows > 0 and k a multiple of 32 required");
+    return hip_status(launch_quant_act(act_dtype, x, k, rows, k, codes_out, k, scales_out, (hipStream_t)hip_stream),
+                      "op_quantize_act");
+}
+
+jepa_status jepa_op_gemm_i8(int act_dtype, const int8_t *a_codes, const float *a_scales, int64_t M, int64_t K,
+                            const void *w, int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
+                            int epilogue, void *out, int64_t ldo, void *hip_stream) {
+    if (!a_codes || !a_scales || !w || !w_scale || !bias || !out) return fail(JEPA_E_INVALID_ARG, "op_gemm_i8: null argument");
+    if (act_dtype != JEPA_F16 && act_dtype != JEPA_BF16) return fail(JEPA_E_DTYPE, "op_gemm_i8: act must be F16 or BF16");
+    if (w_dtype != JEPA_Q8_0 && w_dtype != JEPA_Q4_0) return fail(JEPA_E_DTYPE, "op_gemm_i8: weights must be Q8_0 or Q4_0");
+    if (epilogue < JEPA_EPI_STORE || epilogue > JEPA_EPI_RESID)
+        return fail(JEPA_E_INVALID_ARG, "op_gemm_i8: unknown epilogue %d", epilogue);
+    GemmArgs g{};
+    g.a = a_codes; g.ascale = a_scales; g.w = w; g.wscale = w_scale; g.bias = bias; g.out = out;
+    g.M = M; g.N = N; g.K = K; g.lda = K; g.ldo = ldo;
+    return hip_status(launch_gemm_i8(act_dtype, w_dtype, epilogue, g, (hipStream_t)hip_stream), "op_gemm_i8");
 }
 
 jepa_status jepa_op_patch_embed(int act_dtype, const uint8_t *frames, int B, int T, int H, int W, int tubelet,

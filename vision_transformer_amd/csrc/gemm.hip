@@ -610,6 +610,212 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// int8 path of q8_0 / q4_0 matrices (the GPU analogue of ggml's integer
+// "mmq" products that the Benchmarks page times): activations arrive
+// quantised per 32-block (int8 codes + f32 scale per block, see
+// launch_quant_act), the weights' codes are int8 (q8_0) or nibbles - 8
+// (q4_0, widened to int8 on the way into LDS).  Each 32-wide K block is one
+// v_mfma_i32_32x32x32_i8 per 32 x 32 output block, started from zero; its
+// int32 result is folded into the f32 accumulators as
+//   acc += f32(i32) * (d_a[row, block] * d_w[col, block])
+// (three VALU operations per output per block: this, not the matrix core,
+// sets the rate on this chip).  Two workgroups share a CU, so one wave's
+// MFMAs run under the other's rescale.
+//
+// Tile, staging and epilogues are gemm_kernel's 128 x 128 form (4 waves of
+// 64 x 64, 128-byte K steps = 4 blocks, LDS rows padded to 144 bytes, next
+// step's loads held in registers); each K step also stages the 128 rows'
+// activation scales and weight scales, [block][row] in f32.  The operand
+// bytes read per lane follow the same layout for both operands, so the K
+// order inside a block is whatever the instruction takes, identically for
+// both, and each block's integer dot product is exact.
+// ---------------------------------------------------------------------------
+typedef signed char i8x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T, int WF, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_i8_kernel(const GemmArgs g) {
+    static_assert(sizeof(T) == 2 && (WF == DT_Q8_0 || WF == DT_Q4_0), "16-bit outputs, block weights");
+    constexpr int TB = 128, WT = 64;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TB * ROWB];
+    __shared__ __attribute__((aligned(16))) float s_sc[2][2][4][TB];   // [buf][a / w][block][row]
+    static_assert(4 * 8192 <= 2 * 2 * TB * ROWB, "epilogue scratch");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = g.m_begin + (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
+    const int nk = (int)(g.K / 128);
+    const int64_t nb = g.K / 32;
+    const unsigned char *A = (const unsigned char *)g.a;
+    const unsigned char *W = (const unsigned char *)g.w;
+
+    uint4 areg[4], wreg[4];
+    float2 asc;
+    uint32_t wsc;
+    // scales: thread t carries blocks 2 (t & 1), +1 of row t >> 1
+    const int sr = tid >> 1, sb = 2 * (tid & 1);
+    auto load_global = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            const int64_t m = m0 + r;
+            areg[i] = make_uint4(0, 0, 0, 0);
+            if (m < g.M) areg[i] = *(const uint4 *)(A + m * g.lda + (int64_t)kt * 128 + (tid & 7) * 16);
+        }
+        if constexpr (WF == DT_Q8_0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (tid >> 3) + 32 * i;
+                const int64_t n = n0 + r;
+                wreg[i] = make_uint4(0, 0, 0, 0);
+                if (n < g.N) wreg[i] = *(const uint4 *)(W + n * g.K + (int64_t)kt * 128 + (tid & 7) * 16);
+            }
+        } else {   // (row, block) pairs tid and tid + 256: 16 bytes of nibbles each
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = tid + 256 * i, r = p >> 2, blk = p & 3;
+                const int64_t n = n0 + r;
+                wreg[i] = make_uint4(0, 0, 0, 0);
+                if (n < g.N) wreg[i] = *(const uint4 *)(W + n * (g.K / 2) + (int64_t)kt * 64 + blk * 16);
+            }
+        }
+        {
+            const int64_t m = m0 + sr, n = n0 + sr;
+            asc = make_float2(0.f, 0.f);
+            wsc = 0;
+            if (m < g.M) asc = *(const float2 *)(g.ascale + m * nb + (int64_t)kt * 4 + sb);
+            if (n < g.N) wsc = *(const uint32_t *)(g.wscale + n * nb + (int64_t)kt * 4 + sb);
+        }
+    };
+    // q4_0 nibble c -> int8 c - 8, four per word: (c + 0x78) ^ 0x80 per byte
+    auto widen4 = [](uint32_t w) -> uint32_t { return ((w & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u; };
+    auto store_lds = [&](int buf) {
+        unsigned char *sa = smem[buf][0];
+        unsigned char *sw = smem[buf][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            *(uint4 *)(sa + r * ROWB + (tid & 7) * 16) = areg[i];
+        }
+        if constexpr (WF == DT_Q8_0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (tid >> 3) + 32 * i;
+                *(uint4 *)(sw + r * ROWB + (tid & 7) * 16) = wreg[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = tid + 256 * i, r = p >> 2, blk = p & 3;
+                const uint4 q = wreg[i];
+                // byte j of a block: code j (low nibble), code j + 16 (high)
+                *(uint4 *)(sw + r * ROWB + blk * 32) = make_uint4(widen4(q.x), widen4(q.y), widen4(q.z), widen4(q.w));
+                *(uint4 *)(sw + r * ROWB + blk * 32 + 16) =
+                    make_uint4(widen4(q.x >> 4), widen4(q.y >> 4), widen4(q.z >> 4), widen4(q.w >> 4));
+            }
+        }
+        s_sc[buf][0][sb][sr] = asc.x;
+        s_sc[buf][0][sb + 1][sr] = asc.y;
+        s_sc[buf][1][sb][sr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wsc & 0xffffu));
+        s_sc[buf][1][sb + 1][sr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wsc >> 16));
+    };
+
+    // accumulators start from the biases (gemm_kernel's layout: element
+    // 4q + r of block (i, j) is row 32 i + lane % 32, column 32 j + 8 q +
+    // 4 (lane / 32) + r of the wave's tile)
+    f32x16 acc[2][2];
+    {
+        const bool with_bias = n0 + wn * WT < g.N;
+        const float *bw = g.bias + n0 + wn * WT;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float bv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (with_bias) b4 = *(const float4 *)(bw + 32 * j + 8 * q + 4 * (lane >> 5));
+                bv[4 * q] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = bv[v];
+        }
+    }
+
+    const int arow = wm * WT + (lane & 31);
+    const int brow = wn * WT + (lane & 31);
+    const int kofs = (lane >> 5) * 16;
+    const int ccol = wn * WT + 4 * (lane >> 5);   // first scale column of the lane
+    const i32x16 zero = {};
+
+    // one block's rescale: acc[i][j] += f32(t[i][j]) * d_a[row] * d_w[col]
+    auto rescale = [&](const i32x16 (&t)[2][2], const float (*sc)[4][TB], int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float da = sc[0][c][arow + 32 * i];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 dw = *(const float4 *)&sc[1][c][ccol + 32 * j + 8 * q];
+                    const float s4[4] = {da * dw.x, da * dw.y, da * dw.z, da * dw.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j][4 * q + r] = fmaf((float)t[i][j][4 * q + r], s4[r], acc[i][j][4 * q + r]);
+                }
+        }
+    };
+
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_global(kt + 1);
+        const unsigned char *sa = smem[buf][0];
+        const unsigned char *sw = smem[buf][1];
+        const float (*sc)[4][TB] = s_sc[buf];
+        // one block per iteration, not unrolled: unrolled, the compiler
+        // hoists every block's scale reads and MFMAs and spills their results
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            i8x16 av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                av[i] = *(const i8x16 *)(sa + (arow + 32 * i) * ROWB + c * 32 + kofs);
+                bv[i] = *(const i8x16 *)(sw + (brow + 32 * i) * ROWB + c * 32 + kofs);
+            }
+            // weights as the A operand: the accumulators come out transposed
+            i32x16 t[2][2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) t[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[j], av[i], zero, 0, 0, 0);
+            rescale(t, sc, c);
+        }
+        if (kt + 1 < nk) store_lds(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (n0 + wn * WT < g.N)   // a wave's columns are all in or all out (N % 64 == 0)
+        epilogue_wave<T, EPI, 2, 2>(g, acc, &smem[0][0][0] + wave * 8192, m0 + wm * WT, n0 + wn * WT, lane);
+}
+
+template <typename T, int WF>
+hipError_t launch_i8_epi(int epi, const GemmArgs &g, hipStream_t s) {
+    const dim3 grid((unsigned)cdiv(g.N, 128), (unsigned)cdiv(g.M, 128));
+    switch (epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemm_i8_kernel<T, WF, EPI_STORE>), grid, dim3(256), 0, s, g); break;
+        case EPI_GELU: hipLaunchKernelGGL((gemm_i8_kernel<T, WF, EPI_GELU>), grid, dim3(256), 0, s, g); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemm_i8_kernel<T, WF, EPI_RESID>), grid, dim3(256), 0, s, g); break;
+        case EPI_QKV: hipLaunchKernelGGL((gemm_i8_kernel<T, WF, EPI_QKV>), grid, dim3(256), 0, s, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Large-tile variant for the encoder's big dense GEMMs: 256 x BN outputs per
 // workgroup of 4 waves (2 x 2), each wave 128 x BN/2 (4 x BN/64 blocks of
 // 32 x 32 accumulators, held in AGPRs), one workgroup per CU.
@@ -1094,6 +1300,27 @@ hipError_t launch_epi(int epi, const GemmArgs &g, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// The output-side contract every GEMM launch checks: the QKV layout, and
+// the epilogue's 32-bit buffer offsets and 16-byte vectors.
+bool epi_ok(int epi, const GemmArgs &g, int es) {
+    if (epi == EPI_QKV) {
+        // v starts at a multiple of 128 columns, so no wave straddles q/k and v
+        if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
+            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15) ||
+            (g.rope && g.head_dim != 32 && g.head_dim != 64))
+            return false;
+        if ((g.M / g.ntok + 1) * (g.N / 3) * g.npad * es >= (1ll << 31)) return false;
+    }
+    // the epilogue addresses the output through a buffer resource with 32-bit
+    // byte offsets (rows up to M + 255 are formed, those past M dropped)
+    if (epi != EPI_PATCH && (g.M + 256) * g.ldo * (epi == EPI_RESID ? 4 : es) >= (1ll << 31))
+        return false;
+    if (32 * g.ldo >= (1ll << 31)) return false;   // in-block row offsets are 32-bit
+    if (((uintptr_t)g.bias | (uintptr_t)g.out) & 15) return false;   // 16-byte vectors
+    if (epi != EPI_PATCH && (g.ldo * (epi == EPI_RESID ? 4 : es)) % 16) return false;
+    return true;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s) {
@@ -1119,21 +1346,7 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
                 return hipErrorInvalidValue;
         }
     }
-    if (epi == EPI_QKV) {
-        // v starts at a multiple of 128 columns, so no wave straddles q/k and v
-        if (!g.vt || g.ntok <= 0 || g.M % g.ntok || g.N % 3 || g.vcol0 != 2 * (g.N / 3) || (g.N / 3) % 64 ||
-            g.vcol0 % 128 || g.npad < cdiv(g.ntok, 16) * 16 || ((uintptr_t)g.rope & 15) ||
-            (g.rope && g.head_dim != 32 && g.head_dim != 64))
-            return hipErrorInvalidValue;
-        if ((g.M / g.ntok + 1) * (g.N / 3) * g.npad * es >= (1ll << 31)) return hipErrorInvalidValue;
-    }
-    // the epilogue addresses the output through a buffer resource with 32-bit
-    // byte offsets (rows up to M + 255 are formed, those past M dropped)
-    if (epi != EPI_PATCH && (g.M + 256) * g.ldo * (epi == EPI_RESID ? 4 : es) >= (1ll << 31))
-        return hipErrorInvalidValue;
-    if (32 * g.ldo >= (1ll << 31)) return hipErrorInvalidValue;   // in-block row offsets are 32-bit
-    if (((uintptr_t)g.bias | (uintptr_t)g.out) & 15) return hipErrorInvalidValue;   // 16-byte vectors
-    if (epi != EPI_PATCH && (g.ldo * (epi == EPI_RESID ? 4 : es)) % 16) return hipErrorInvalidValue;
+    if (!epi_ok(epi, g, es)) return hipErrorInvalidValue;
     const bool dense = (w_dt == act_dt);
     if (!dense && (act_dt == DT_F32 || (w_dt != DT_Q8_0 && w_dt != DT_Q4_0) || !g.wscale))
         return hipErrorInvalidValue;
@@ -1154,6 +1367,27 @@ hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStre
             return launch_epi<f16_t, DT_Q4_0>(epi, ga, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_i8(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s) {
+    if (act_dt != DT_BF16 && act_dt != DT_F16) return hipErrorInvalidValue;
+    if (w_dt != DT_Q8_0 && w_dt != DT_Q4_0) return hipErrorInvalidValue;
+    if (epi != EPI_STORE && epi != EPI_GELU && epi != EPI_RESID && epi != EPI_QKV) return hipErrorInvalidValue;
+    if (!g.a || !g.w || !g.wscale || !g.ascale || !g.bias || !g.out) return hipErrorInvalidValue;
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % 128 || g.N % 64 || g.lda < g.K || g.lda % 16 || g.ldo < g.N)
+        return hipErrorInvalidValue;
+    if (cdiv(g.M, 128) >= 65535) return hipErrorInvalidValue;
+    // 16-byte code rows, 8-byte activation-scale pairs, 4-byte weight-scale pairs
+    if (((uintptr_t)g.a | (uintptr_t)g.w) & 15 || ((uintptr_t)g.ascale & 7) || ((uintptr_t)g.wscale & 3))
+        return hipErrorInvalidValue;
+    if (!epi_ok(epi, g, 2)) return hipErrorInvalidValue;
+    GemmArgs ga = g;
+    ga.m_begin = 0;
+    ga.ksplit = 1;
+    ga.vt_direct = 0;
+    if (act_dt == DT_BF16)
+        return w_dt == DT_Q8_0 ? launch_i8_epi<bf16_t, DT_Q8_0>(epi, ga, s) : launch_i8_epi<bf16_t, DT_Q4_0>(epi, ga, s);
+    return w_dt == DT_Q8_0 ? launch_i8_epi<f16_t, DT_Q8_0>(epi, ga, s) : launch_i8_epi<f16_t, DT_Q4_0>(epi, ga, s);
 }
 
 }  // namespace jepa

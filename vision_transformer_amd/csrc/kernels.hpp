@@ -65,6 +65,9 @@ struct GemmArgs {
     // a second pass adds the bias and the splits in order to the output
     float *kpart;
     int ksplit;              // set by the launcher
+    // int8 path (launch_gemm_i8): a holds int8 codes [M, lda] (lda bytes),
+    // ascale their f32 scales [M, K/32], one per 32-block of a row
+    const float *ascale;
     // EPI_PATCH straight from the frames (implicit GEMM; a unused): uint8
     // [items, fT, fH, fW, 3], row r = b*np + n being patch n of item b, its
     // patch vector (dt, dy, dx, c) gathered and normalised on the way into
@@ -77,6 +80,17 @@ struct GemmArgs {
 };
 constexpr int KSPLIT_MAX = 8;
 hipError_t launch_gemm(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
+// The int8 path of q8_0 / q4_0 matrices: g.a / g.ascale hold activations
+// quantised per 32-block (launch_quant_act), the products of every block
+// run on int8 MFMA and are scaled by d_a * d_w into f32 accumulators; the
+// epilogues (STORE, GELU, RESID, QKV) and out act_dt (16-bit) are
+// launch_gemm's.  K a multiple of 128, N of 64.
+hipError_t launch_gemm_i8(int act_dt, int w_dt, int epi, const GemmArgs &g, hipStream_t s);
+// x act [M, ldx] (16-bit) -> codes int8 [M, ldq] and f32 scales [M, K/32]
+// (pitch K/32): per 32-block of a row d = max|x| / 127 and code
+// round(x / d) half away from zero (0 when d is 0), both in f32
+hipError_t launch_quant_act(int act_dt, const void *x, int64_t ldx, int64_t M, int64_t K, int8_t *q,
+                            int64_t ldq, float *d, hipStream_t s);
 
 // Position of token n in a V^T row: each aligned run of 16 tokens is stored
 // in the order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 swapped), so the eight

@@ -448,6 +448,49 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_probe_kernel(int iters, float 
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Activations quantised per 32-block for the int8 path: one thread per
+// block, 64 bytes in (4 x 16), 32 code bytes and one f32 scale out.
+// d = max|x| / 127 and x / d are single correctly rounded f32 divisions (the
+// default for '/' here), and roundf rounds halves away from zero.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_act_kernel(const T *x, int64_t ldx, int64_t M, int64_t nb,
+                                                        int8_t *q, int64_t ldq, float *d) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * nb) return;
+    const int64_t m = i / nb, b = i - m * nb;
+    const uint4 *src = (const uint4 *)(x + m * ldx + b * 32);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 w = src[c];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[8 * c + 2 * e] = to_f32(__builtin_bit_cast(T, (unsigned short)(u[e] & 0xffffu)));
+            v[8 * c + 2 * e + 1] = to_f32(__builtin_bit_cast(T, (unsigned short)(u[e] >> 16)));
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    const float dd = amax / 127.0f;
+    uint32_t w[8];
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float r = dd == 0.f ? 0.f : fminf(fmaxf(roundf(v[4 * k4 + e] / dd), -127.f), 127.f);
+            word |= ((uint32_t)(int)r & 0xffu) << (8 * e);
+        }
+        w[k4] = word;
+    }
+    uint4 *dst = (uint4 *)(q + m * ldq + b * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    d[m * nb + b] = dd;
+}
+
 // f32 values rounded to the act dtype, and a fill (graph-capturable, unlike
 // a memset node)
 template <typename T>
@@ -494,6 +537,27 @@ hipError_t launch_cast(const float *x, int64_t n, void *y, int y_dt, hipStream_t
         case DT_F32: hipLaunchKernelGGL(cast_kernel<float>, grid, dim3(256), 0, s, x, n, (float *)y); break;
         case DT_BF16: hipLaunchKernelGGL(cast_kernel<bf16_t>, grid, dim3(256), 0, s, x, n, (bf16_t *)y); break;
         case DT_F16: hipLaunchKernelGGL(cast_kernel<f16_t>, grid, dim3(256), 0, s, x, n, (f16_t *)y); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(int act_dt, const void *x, int64_t ldx, int64_t M, int64_t K, int8_t *q,
+                            int64_t ldq, float *d, hipStream_t s) {
+    // 16-byte rows of both sides: pitches and pointers
+    if (M <= 0 || K <= 0 || K % 32 || ldx < K || ldq < K || ldq % 16 || ldx % 8 || ((uintptr_t)x & 15) ||
+        ((uintptr_t)q & 15) || ((uintptr_t)d & 3))
+        return hipErrorInvalidValue;
+    const int64_t nb = K / 32, n = M * nb;
+    if (cdiv(n, 256) >= (1ll << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)cdiv(n, 256));
+    switch (act_dt) {
+        case DT_BF16:
+            hipLaunchKernelGGL(quant_act_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)x, ldx, M, nb, q, ldq, d);
+            break;
+        case DT_F16:
+            hipLaunchKernelGGL(quant_act_kernel<f16_t>, grid, dim3(256), 0, s, (const f16_t *)x, ldx, M, nb, q, ldq, d);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

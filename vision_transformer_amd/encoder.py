@@ -112,6 +112,17 @@ class Encoder:
         _lib.jepa_classify(self.ctx, out, stream)
         return out
 
+    def set_int8_matmul(self, enable: bool) -> None:
+        """q8_0 / q4_0 products on int8 MFMA with inputs quantised per
+        32-block (enable), or on dequantised weights (the default).  A change
+        frees the library's workspace and with it the last encode's state."""
+        enable = bool(enable)
+        if enable != getattr(self, "int8_matmul", False):
+            _lib.jepa_set_int8_matmul(self.ctx, enable)
+            self._last_tokens = None
+            self.last_batch = 0
+        self.int8_matmul = enable
+
     def dequant(self, name: str, shape, stream=None):
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
         _lib.jepa_dequant_tensor(self.ctx, name, out, stream)
