@@ -40,6 +40,7 @@ from vision_transformer_amd import synth  # noqa: E402
 
 METRIC = "encoder tokens/sec + clips/sec (ViT-L/16, 16 frames), MFMA util % of peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_INT8_TOPS = 5000.0                                          # dense int8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 
 
@@ -318,12 +319,14 @@ def gemm_k_sweep() -> int:
 # which stays the headline workload's.
 OTHER_WORKLOADS = ["vit_ti14_image_f32", "vit_l16_image_bf16_b32", "vjepa2_vit_l16_16f256_q8_0_b4",
                    "vjepa2_vit_l16_64f256_f16", "vjepa2_vit_l16_64f256_q4_0"]
+INT8_WORKLOADS = ["vjepa2_vit_l16_16f256_q8_0_b4", "vjepa2_vit_l16_64f256_q4_0"]
 
 
-def time_workload(name: str, steps: int, warmup: int) -> dict:
+def time_workload(name: str, steps: int, warmup: int, int8: bool = False) -> dict:
     """ms per step, tokens/s, clips/s and MFMA utilisation of one workload's
     forward + its reported pool (+ class scores), the batch in the library's
-    default concurrent parts, frames resident."""
+    default concurrent parts, frames resident.  int8: the block matrices'
+    products on the int8 path (jepa_set_int8_matmul)."""
     import torch
     from vision_transformer_amd import _lib
     from vision_transformer_amd.encoder import Encoder
@@ -335,6 +338,8 @@ def time_workload(name: str, steps: int, warmup: int) -> dict:
                                   quantize=_lib.jepa_quantize)
     enc = Encoder(dims, stored)
     del stored
+    if int8:
+        enc.set_int8_matmul(True)
     fr = torch.from_numpy(frames).cuda()
     tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, device="cuda")
     pool_mode = "cls" if dims["has_cls"] else "mean"
@@ -355,11 +360,11 @@ def time_workload(name: str, steps: int, warmup: int) -> dict:
     enc.close()
     act = dims["act_dtype"]
     util = forward_flops(dims, B) / (ms * 1e-3) / (PEAK_TFLOPS[act] * 1e12)
-    print(f"[bench] {name}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
+    print(f"[bench] {name}{' (int8 products)' if int8 else ''}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
             "clips_per_s": round(B / (ms * 1e-3), 2), "mfma_util_pct": round(100 * util, 2),
             "batch": B, "tokens_per_clip": N, "dtype": act, "weights": dims["mat_dtype"],
-            "mask": dims["mask"], "steps": steps, "warmup": warmup}
+            "mask": dims["mask"], "steps": steps, "warmup": warmup, "int8_products": int8}
 
 
 def main() -> int:
@@ -375,6 +380,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=24)
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel-class times to stderr")
+    ap.add_argument("--int8", action="store_true",
+                    help="run the block matrices' products on the int8 path (q8_0 / q4_0 workloads)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the other specified workloads after the headline one")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -411,6 +418,8 @@ def main() -> int:
     stored = synth.stored_weights(dims, synth.make_f32_weights(dims, wl["weight_seed"]),
                                   quantize=_lib.jepa_quantize)
     enc = Encoder(dims, stored)
+    if args.int8:
+        enc.set_int8_matmul(True)
     fr = torch.from_numpy(frames).cuda()
     tokens = torch.empty((B, N, dims["dim"]), dtype=torch.float32, device="cuda")
     pool_mode = "cls" if dims["has_cls"] else "mean"
@@ -532,9 +541,13 @@ def main() -> int:
     avg_ms = st["total_ms"] / max(1, st["launches"])
     cf, cb = class_flops(dims, B), class_bytes(dims, B)
     if dominant in cf:
+        # the int8 path's products run on the int8 MFMA (dense peak 5.0 POP/s)
+        i8 = args.int8 and dims["mat_dtype"] in ("q8_0", "q4_0") and dominant.startswith("gemm_") \
+            and dominant != "gemm_patch"
+        kpeak, kunit = (PEAK_INT8_TOPS, "TOP/s") if i8 else (peak, "TFLOP/s")
         achieved = cf[dominant] / (avg_ms * 1e-3) / 1e12
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": kpeak,
+                "unit": kunit, "frac": round(achieved / kpeak, 4), "traffic": None,
                 "work_per_launch": cf[dominant], "avg_launch_ms": round(avg_ms, 5),
                 "launches_timed": st["launches"]}
     else:
@@ -562,7 +575,8 @@ def main() -> int:
         "config": {"workload": args.workload, "batch": B, "tokens_per_clip": N,
                    "frames": dims["frames"], "img": [dims["img_h"], dims["img_w"]],
                    "tubelet": dims["tubelet"], "mask": dims["mask"], "weights": dims["mat_dtype"],
-                   "parallelism": f"single GPU, batch in {parts} concurrent parts"},
+                   "parallelism": f"single GPU, batch in {parts} concurrent parts",
+                   "int8_products": bool(args.int8)},
         "clips_per_s": round(B * args.steps / wall, 2),
         "mfma_util_pct": round(100 * util, 2),
         "forward_tflop": round(flops / 1e12, 4),
@@ -587,6 +601,14 @@ def main() -> int:
             except Exception as e:   # an extra row: report, do not fail the bench
                 print(f"[bench] {name} not measured: {e}", file=sys.stderr, flush=True)
                 others[name] = None
+            torch.cuda.empty_cache()
+        # the block-format workloads again with their products on the int8 path
+        for name in INT8_WORKLOADS:
+            try:
+                others[name + "+int8"] = time_workload(name, max(3, min(args.steps, 10)), 2, int8=True)
+            except Exception as e:
+                print(f"[bench] {name} (int8) not measured: {e}", file=sys.stderr, flush=True)
+                others[name + "+int8"] = None
             torch.cuda.empty_cache()
         out["other_workloads"] = others
     if not args.no_cpu_baseline:

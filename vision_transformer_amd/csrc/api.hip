@@ -124,9 +124,9 @@ float stored_to_f32(int dt, const void *data, int64_t i) {
 
 const char *kClassNames[] = {"patchify", "gemm_patch", "cls_rows", "layernorm", "gemm_qkv",
                              "transpose_v", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                             "final_ln", "pool", "expand_weights", "head"};
+                             "final_ln", "pool", "expand_weights", "head", "quant_act"};
 enum KClass { K_PATCHIFY, K_GEMM_PATCH, K_CLS_ROWS, K_LN, K_GEMM_QKV, K_TRANSPOSE_V, K_ATTN,
-              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_EXPAND, K_HEAD, K_COUNT };
+              K_GEMM_OUT, K_GEMM_FC1, K_GEMM_FC2, K_FINAL_LN, K_POOL, K_EXPAND, K_HEAD, K_QUANT_ACT, K_COUNT };
 
 struct DevTensor {
     void *ptr = nullptr;        // device data
@@ -1005,7 +1005,7 @@ static jepa_status run_block(jepa_ctx *c, const Ws &w, const Layer &L, bool expa
         if (i8 && (w_dt == JEPA_Q8_0 || w_dt == JEPA_Q4_0)) {
             const void *in = g.a;
             const int64_t ld = g.lda;
-            TRY(launch(c, cls, s, [&] { return launch_quant_act(c->act, in, ld, g.M, g.K, qa, g.K, qas, s); }));
+            TRY(launch(c, K_QUANT_ACT, s, [&] { return launch_quant_act(c->act, in, ld, g.M, g.K, qa, g.K, qas, s); }));
             g.a = qa; g.lda = g.K; g.ascale = qas;
             return launch(c, cls, s, [&] { return launch_gemm_i8(c->act, w_dt, epi, g, s); });
         }
