@@ -93,8 +93,13 @@ def class_bytes(dims: dict, B: int) -> dict:
     M = B * synth.n_tokens(dims)
     es = 4 if dims["act_dtype"] == "f32" else 2
     npad = -(-synth.n_tokens(dims) // 64) * 64
+    F = dims["mlp_dim"]
+    # the int8 path's input quantiser: per block's four products, three of
+    # width D and one of width F, each read in the act dtype and written as
+    # int8 codes plus one f32 scale per 32 values (the average launch)
+    quant = M * (3 * D + F) * (es + 1 + 4 / 32) / 4
     return {"layernorm": M * D * (4 + es), "final_ln": M * D * 8,
-            "transpose_v": M * D * es + B * D * npad * es}
+            "transpose_v": M * D * es + B * D * npad * es, "quant_act": int(quant)}
 
 
 def measured_traffic(workload: str, cls: str):
