@@ -85,7 +85,9 @@ jepa_status jepa_op_quantize_act(int act_dtype, const void *x, int64_t rows, int
  * GELU, f32 for RESID; pitch ldo >= N).  a_codes int8 [M, K], a_scales f32
  * [M, K / 32] as jepa_op_quantize_act writes them; w packed Q8_0 (codes
  * int8) or Q4_0 (codes nibble - 8) as for jepa_op_gemm, w_scale their f16
- * scales [N, K / 32].  K % 128 == 0, N % 64 == 0. */
+ * scales [N, K / 32].  K % 128 == 0, N % 64 == 0; a_codes and w 16-byte
+ * aligned, a_scales 8-byte, w_scale 4-byte, bias and out 16-byte.
+ * JEPA_E_HIP (invalid value) for shapes or alignments outside these. */
 jepa_status jepa_op_gemm_i8(int act_dtype, const int8_t *a_codes, const float *a_scales, int64_t M, int64_t K,
                             const void *w, int w_dtype, const uint16_t *w_scale, int64_t N, const float *bias,
                             int epilogue, void *out, int64_t ldo, void *hip_stream);
