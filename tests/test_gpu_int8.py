@@ -191,3 +191,71 @@ def test_int8_switch_errors(Encoder):
             enc.set_int8_matmul(True)
         assert e.value.status == -7     # f32 model; dim 192; K-quants
         enc.close()
+
+
+def test_int8_batch_parts_and_graph_replay_bit_exact(Encoder):
+    """With the int8 path on, 1 to 4 concurrent batch parts give
+    bit-identical tokens (batch 5), and encode + pool captured into one HIP
+    graph replays to the eager result, with eager work in between."""
+    from vision_transformer_amd import _lib
+    wl, dims, _, stored = H.workload_inputs("small_tubelet2_q4_0")
+    frames = H.synth.make_frames(dims, 5, 79)
+    enc = Encoder(dims, stored)
+    enc.set_int8_matmul(True)
+    fr = torch.from_numpy(frames).cuda()
+    ys = []
+    for parts in (1, 2, 3, 4):
+        say(f"int8 encoder batch 5 in {parts} parts")
+        _lib.jepa_set_batch_parts(enc.ctx, parts)
+        ys.append(_encode(enc, frames).cpu().clone())
+    for y in ys[1:]:
+        assert torch.equal(ys[0], y)
+    B = 5
+    tokens = torch.empty((B, enc.n_tokens, dims["dim"]), dtype=torch.float32, device="cuda")
+    pooled = torch.empty((B, dims["dim"]), dtype=torch.float32, device="cuda")
+    enc.encode(fr, tokens)
+    enc.pool("mean", B, pooled)
+    torch.cuda.synchronize()
+    want_t, want_p = tokens.clone(), pooled.clone()
+    assert torch.equal(want_t.cpu(), ys[-1])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enc.encode(fr, tokens)
+        enc.pool("mean", B, pooled)
+    for r in range(3):
+        say(f"int8 graph replay {r}")
+        tokens.zero_()
+        pooled.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, want_t) and torch.equal(pooled, want_p)
+        enc.encode(fr, tokens)
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, want_t)
+    del graph
+    enc.close()
+
+
+def test_int8_noalloc_matches_encode(lib):
+    """jepa_encode_noalloc with the int8 path on (its quantised inputs in the
+    static array too) equals jepa_encode bit for bit, on two calls in a row,
+    the second with a smaller batch."""
+    wl, dims, _, stored = H.workload_inputs("small_tubelet2_q8_0")
+    frames = H.synth.make_frames(dims, 3, 95)
+    ctx = lib.jepa_create(dims, stored)
+    lib.jepa_set_int8_matmul(ctx, True)
+    lib.jepa_set_batch_parts(ctx, 1)
+    N, D = H.synth.n_tokens(dims), dims["dim"]
+    try:
+        for B in (3, 1):
+            say(f"int8 encode_noalloc batch {B}")
+            fr = torch.from_numpy(np.ascontiguousarray(frames[:B])).cuda()
+            want = torch.empty((B, N, D), device="cuda")
+            got = torch.full((B, N, D), float("nan"), device="cuda")
+            lib.jepa_encode(ctx, fr, B, want)
+            torch.cuda.synchronize()
+            lib.jepa_encode_noalloc(ctx, fr, B, got)
+            torch.cuda.synchronize()
+            assert torch.equal(got, want)
+    finally:
+        lib.jepa_free(ctx)
