@@ -182,6 +182,8 @@ def test_null_context_calls_fail_cleanly(lib):
         lib.jepa_pool(None, "cls", np.zeros(4, np.float32))
     with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
         lib.jepa_set_batch_parts(None, 2)
+    with pytest.raises(lib.JepaError, match="JEPA_E_INVALID_ARG"):
+        lib.jepa_set_int8_matmul(None, True)
     assert lib.jepa_last_compute_ms(None) < 0
     assert lib.jepa_model_n_bytes(None) == 0
     lib.jepa_free(None)
