@@ -259,3 +259,22 @@ def test_int8_noalloc_matches_encode(lib):
             assert torch.equal(got, want)
     finally:
         lib.jepa_free(ctx)
+
+
+@pytest.mark.parametrize("mat", ["q8_0", "q4_0"])
+def test_int8_encoder_bf16_activations_every_token(Encoder, mat):
+    """The small tubelet-2 model with bf16 activations (LN, biases and the
+    patch table bf16 too) and q8_0 / q4_0 matrices: every token with the int8
+    path on against the int8 oracle."""
+    from vision_transformer_amd import synth
+    wl = synth.workload("small_tubelet2_q8_0")
+    dims = dict(wl["dims"], act_dtype="bf16", rest_dtype="bf16", mat_dtype=mat)
+    frames = synth.make_frames(dims, wl["batch"], 31)
+    stored = synth.stored_weights(dims, synth.make_f32_weights(dims, 32, ln_affine=True), quantize=Q.quantize)
+    say(f"int8 encoder, bf16 activations, {mat}")
+    ref8 = E.encode(dims, E.weights_f64(stored), frames, act_q8=True)
+    enc = Encoder(dims, stored)
+    enc.set_int8_matmul(True)
+    y8 = _encode(enc, frames).cpu().numpy()
+    enc.close()
+    H.check_rows("bf16", y8, ref8, "tokens (int8 path vs int8 oracle)")
