@@ -334,7 +334,10 @@ size_t jepa_device_weight_bytes(const jepa_ctx *ctx);
  * held until jepa_free; smaller batches dequantise inside the GEMM and need
  * no copy.  The environment variable
  * JEPA_Q_EXPAND = 0 or 1 forces either way, except that a model with a
- * Q4_K / Q6_K matrix always takes the copy. */
+ * Q4_K / Q6_K matrix always takes the copy.  With the int8 path on
+ * (jepa_set_int8_matmul) no copy is made, and the workspace holds the
+ * quantised inputs instead: 1 + 4/32 bytes per value of a
+ * [batch * tokens, max(dim, mlp_dim)] matrix. */
 size_t jepa_workspace_bytes(const jepa_ctx *ctx, int batch);
 
 /* Write the f32 value of every element of the named tensor, as the GEMMs
