@@ -254,13 +254,30 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
         }
         return 1.f;
     };
+    // RESID: X, PATCH: the pos rows (and the mapped output rows), read one
+    // block ahead of their use
     float4 xv[2][NRD];
+    uint32_t pout[EPI == EPI_PATCH ? 2 : 1][EPI == EPI_PATCH ? NRD : 1];
     auto load_x = [&](int i, int bf) {
         if constexpr (EPI == EPI_RESID) {
 #pragma unroll
             for (int t = 0; t < NRD; ++t)
                 xv[bf][t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                     rs, gbase + (32 * i + t * RPI) * rowb, 0, 0));
+        }
+        if constexpr (EPI == EPI_PATCH) {
+            // rows past M map past the output's end, where the store is dropped
+            const uint32_t cb = (uint32_t)(col0 * 4) + rc * 16;
+#pragma unroll
+            for (int t = 0; t < NRD; ++t) {
+                const uint32_t m = (uint32_t)(row0 + 32 * i + t * RPI + rr);
+                const uint32_t b = m / (uint32_t)g.np, n = m - b * (uint32_t)g.np;
+                const uint32_t t_ = (uint32_t)g.has_cls + n;
+                pout[bf][t] = (b * (uint32_t)g.ntok + t_) * rowb + cb;
+                xv[bf][t] = g.pos ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rpos, t_ * rowb + cb, 0, 0))
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
     load_x(0, 0);
@@ -326,18 +343,9 @@ __device__ __forceinline__ void epilogue_wave(const GemmArgs &g, const f32x16 (&
                 v.x = x.x + v.x; v.y = x.y + v.y; v.z = x.z + v.z; v.w = x.w + v.w;
             }
             if constexpr (EPI == EPI_PATCH) {
-                // rows past M map past the output's end, where the store is dropped
-                const uint32_t m = (uint32_t)(row0 + 32 * i + r);
-                const uint32_t b = m / (uint32_t)g.np, n = m - b * (uint32_t)g.np;
-                const uint32_t t_ = (uint32_t)g.has_cls + n;
-                const uint32_t cb = (uint32_t)(col0 * 4) + rc * 16;
-                if (g.pos) {
-                    const float4 q = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rpos, t_ * rowb + cb, 0, 0));
-                    v.x = v.x + q.x; v.y = v.y + q.y; v.z = v.z + q.z; v.w = v.w + q.w;
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
-                                                       (b * (uint32_t)g.ntok + t_) * rowb + cb, 0, 0);
+                const float4 q = xv[i & 1][t];      // 0 without a pos table
+                v.x = v.x + q.x; v.y = v.y + q.y; v.z = v.z + q.z; v.w = v.w + q.w;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, pout[i & 1][t], 0, 0);
             } else {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
                                                        gbase + (32 * i + t * RPI) * rowb, 0, 0);
