@@ -46,6 +46,28 @@ __global__ __launch_bounds__(256) void patchify_kernel(const PatchifyArgs a, int
     ((T *)a.out)[idx] = from_f32<T>(val);
 }
 
+// The sum over a wave's 64 lanes, returned uniform: within each quad by two
+// DPP lane swaps (xor 1, xor 2), within each row of 16 by DPP rotations by 4
+// and 8 (every lane then holds its row's sum), then the four rows' sums read
+// from lanes 0, 16, 32 and 48 and added in that order.  No LDS round trip,
+// unlike the xor shuffles.  Every lane of the wave must be active (the
+// LayerNorm kernels give a whole wave to each row).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    auto dpp = [](float x, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                                    0xF, 0xF, true));
+    };
+    v += dpp(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
+    v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+    v += dpp(v, std::integral_constant<int, 0x124>{});   // row_ror:4
+    v += dpp(v, std::integral_constant<int, 0x128>{});   // row_ror:8
+    const int b = __builtin_bit_cast(int, v);
+    return ((__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32))) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+}
+
 // ---------------------------------------------------------------------------
 // LayerNorm over D = 64*EPL features, one wavefront per row: biased
 // variance, eps inside the square root, f32 statistics.
@@ -67,14 +89,14 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
         v[i] = xr[lane + 64 * i];
         s += v[i];
     }
-    const float mean = wave_sum(s) * (1.f / D);
+    const float mean = wave_sum_dpp(s) * (1.f / D);
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const float c = v[i] - mean;
         q = fmaf(c, c, q);
     }
-    const float rs = rsqrtf(wave_sum(q) * (1.f / D) + eps);
+    const float rs = rsqrtf(wave_sum_dpp(q) * (1.f / D) + eps);
     TO *yr = y + row * D;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -85,27 +107,6 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict_
 
 // The same LayerNorm for D a multiple of 256, one wavefront per row with
 // 16-byte accesses: lane l holds elements 4 l + 256 i + {0..3}.
-// The sum over a wave's 64 lanes, returned uniform: within each quad by two
-// DPP lane swaps (xor 1, xor 2), within each row of 16 by DPP rotations by 4
-// and 8 (every lane then holds its row's sum), then the four rows' sums read
-// from lanes 0, 16, 32 and 48 and added in that order.  No LDS round trip,
-// unlike the xor shuffles.
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    auto dpp = [](float x, auto ctrl) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value,
-                                                                    0xF, 0xF, true));
-    };
-    v += dpp(v, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
-    v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
-    v += dpp(v, std::integral_constant<int, 0x124>{});   // row_ror:4
-    v += dpp(v, std::integral_constant<int, 0x128>{});   // row_ror:8
-    const int b = __builtin_bit_cast(int, v);
-    return ((__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-             __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32))) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-}
-
 template <int EV, typename TO>
 __global__ __launch_bounds__(256) void layernorm_vec_kernel(const float *__restrict__ x, int64_t rows,
                                                             const float *__restrict__ gam,
